@@ -1,0 +1,173 @@
+/*
+ * xq.h — C ABI of the TurboQuant paged KV cache for MI355X (gfx950).
+ *
+ * What the operations compute comes from the pages on xInfer's TurboQuant KV cache:
+ *   - "xInfer: Pure-Rust LLM Inference Without a Python Runtime" (hysenlabs.com),
+ *     section "What actually sits between the request and the tokens": each K/V head
+ *     vector is rotated by a Walsh-Hadamard transform, then quantized with one absmax
+ *     scale per head, so that the rotation spreads outlier channels before the absmax.
+ *   - same page, section "Getting a server up: the commands in the README": the KV cache
+ *     type is one of fp8, turbo8, turbo4, turbo3, and BF16 when no type is given.
+ *   - same page, section "TurboQuant is a memory trade, and the README does not price it
+ *     fully": a low-bit cache is dequantized on every attention step.
+ *   - "infero" landing page (jackwangfeng.github.io/infero), section "Beyond plain text
+ *     decode", item "Continuous batching": requests share the GPU through a paged KV cache.
+ *
+ * The pages leave the number format open. This library fixes it as follows:
+ *   - rotation: orthonormal fast Walsh-Hadamard transform over head_dim = 128, natural
+ *     (Sylvester) order, no random signs; stages h = 1, 2, 4, ..., 64 of (a+b, a-b) in
+ *     fp32, then one multiply by C = fp32(1/sqrt(128)) = 0x3DB504F3;
+ *   - scale: one fp16 per (token, kv_head), s = fp16_rne(min(absmax / qmax, 65504)),
+ *     qmax = 2^(bits-1) - 1 (127, 7, 3), division in fp32;
+ *   - codes: c = clamp(rint_half_even(x / s), -qmax, qmax) in fp32; all zero when s == 0;
+ *   - packing: code d of a row occupies bits [bits*d, bits*d + bits) of the row's
+ *     little-endian bitstream, as a bits-wide two's complement field.
+ *
+ * Memory layout (both pools, K and V, have the same layout):
+ *   pool + page * page_stride + kv_head * block_bytes   is one (page, kv_head) block;
+ *   a turbo block is page_size code rows of 16*bits bytes (slot s at s * 16 * bits),
+ *   followed by page_size fp16 scales (slot s at page_size * 16 * bits + 2 * s);
+ *   a bf16 block is page_size rows of 128 bf16 values (256 bytes per row).
+ *   block_bytes is a multiple of 16. Physical page ids come from a per-sequence block
+ *   table: token position p of sequence b lives in page block_tables[b][p / page_size],
+ *   slot p % page_size.
+ *
+ * Ownership: the caller owns every buffer (device memory unless noted). The library
+ * allocates and frees nothing and keeps no state beyond a thread-local error string.
+ * Every operation is enqueued on the caller's HIP stream (NULL = the default stream)
+ * and the call returns after the launch; the caller orders appends before the decode
+ * that reads them and keeps buffers alive until the stream has run them.
+ *
+ * Errors: functions return an xq_status. Only host-visible arguments are validated
+ * (dtype, head_dim, page_size, head counts, null pointers, 16-byte alignment of pools,
+ * workspace size); a failed check launches nothing. A failed launch returns XQ_EHIP.
+ * The contents of device arrays are the caller's contract: page ids < num_pages,
+ * context_lens[b] <= max_pages_per_seq * page_size and <= max_context_len, and no two
+ * tokens of one append writing the same slot. Nothing throws across this boundary.
+ */
+#ifndef XQ_H
+#define XQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* KV cache element type. The value is the code width in bits (0 for bf16). */
+typedef enum {
+  XQ_KV_BF16 = 0,   /* unquantized: the cache type used when none is given */
+  XQ_KV_TURBO8 = 8, /* 8-bit codes, 130 bytes per row (128 codes + fp16 scale) */
+  XQ_KV_TURBO4 = 4, /* 4-bit codes, 66 bytes per row */
+  XQ_KV_TURBO3 = 3  /* 3-bit codes in a dense bitstream, 50 bytes per row */
+} xq_kv_dtype;
+
+typedef enum {
+  XQ_OK = 0,
+  XQ_EINVAL = 1,        /* an argument is out of range or a pointer is null/misaligned */
+  XQ_EUNSUPPORTED = 2,  /* a valid combination this build does not implement */
+  XQ_EWORKSPACE = 3,    /* workspace too small or null */
+  XQ_EHIP = 4           /* the HIP runtime reported an error */
+} xq_status;
+
+/* Geometry of one KV pool (K and V pools share it). */
+typedef struct {
+  int32_t kv_dtype;     /* an xq_kv_dtype */
+  int32_t head_dim;     /* must be 128 */
+  int32_t num_kv_heads; /* >= 1 */
+  int32_t page_size;    /* tokens per page: a power of two in [16, 256] */
+  int64_t num_pages;    /* physical pages in the pool, >= 1 */
+} xq_cache_layout;
+
+/* Bytes of one (page, kv_head) block; -1 if the layout is invalid. */
+int64_t xq_block_bytes(const xq_cache_layout* layout);
+/* Bytes between consecutive pages: num_kv_heads * xq_block_bytes; -1 if invalid. */
+int64_t xq_page_stride_bytes(const xq_cache_layout* layout);
+/* Bytes of one pool (K or V): num_pages * xq_page_stride_bytes; -1 if invalid. */
+int64_t xq_pool_bytes(const xq_cache_layout* layout);
+
+/*
+ * Number of sequence partitions ("splits") the decode uses for a sequence of up to
+ * max_context_len tokens. num_splits_hint = 0 lets the library choose from the batch
+ * shape; a positive hint asks for that many page-aligned partitions (capped so that every
+ * partition holds at least one page). Returns -1 on invalid arguments.
+ */
+int32_t xq_decode_num_splits(const xq_cache_layout* layout, int32_t batch,
+                             int32_t num_q_heads, int32_t max_context_len,
+                             int32_t num_splits_hint);
+
+/*
+ * Workspace bytes xq_paged_decode_attention needs for these arguments (0 when every
+ * sequence fits one partition). Returns -1 on invalid arguments.
+ */
+int64_t xq_decode_workspace_bytes(const xq_cache_layout* layout, int32_t batch,
+                                  int32_t num_q_heads, int32_t max_context_len,
+                                  int32_t num_splits_hint);
+
+/* Static description of a status code. */
+const char* xq_status_string(int32_t status);
+/* Message of the last failed call on this host thread ("" if none). */
+const char* xq_last_error(void);
+
+/*
+ * Rotate, quantize and pack new K and V rows, and store them in their pages.
+ * Defined by the xInfer page, section "What actually sits between the request and the
+ * tokens" (rotation, then per-head absmax quantization), with the number format fixed above.
+ *
+ *   k_new, v_new       bf16 [n_tokens][num_kv_heads][128], row-major, 16-byte aligned
+ *   n_tokens           rows per head to append (0 is a no-op)
+ *   token_seq          int32 [n_tokens]: sequence index of each token
+ *   token_pos          int32 [n_tokens]: position of the token in its sequence
+ *   block_tables       int32 [num_seqs][max_pages_per_seq]: physical page per logical page
+ *   k_pool, v_pool     pools of xq_pool_bytes(layout) bytes, 16-byte aligned
+ *   stream             hipStream_t (NULL = default stream)
+ * Each (token, kv_head) row of K and of V becomes one code row and one fp16 scale at
+ * page block_tables[token_seq[i]][token_pos[i] / page_size], slot token_pos[i] % page_size.
+ * In bf16 mode the row is copied unchanged. Bytes of other slots are not touched.
+ */
+xq_status xq_quantize_append(const xq_cache_layout* layout,
+                             const void* k_new, const void* v_new, int32_t n_tokens,
+                             const int32_t* token_seq, const int32_t* token_pos,
+                             const int32_t* block_tables, int32_t max_pages_per_seq,
+                             void* k_pool, void* v_pool, void* stream);
+
+/*
+ * Single-token decode attention over the paged (and, for turbo types, quantized) cache.
+ * Defined by the xInfer page, section "TurboQuant is a memory trade, and the README does
+ * not price it fully" (every attention step reads and dequantizes the cache), and the
+ * infero page, section "Beyond plain text decode", item "Continuous batching" (paged KV).
+ *
+ * For sequence b and query head j (kv head j / (num_q_heads / num_kv_heads)):
+ *   turbo types:  q' = H q;  k'_t = s_k[t] c_k[t];  v'_t = s_v[t] c_v[t]   (rotated space)
+ *                 z_t = softmax_scale * (q' . k'_t);  o = sum_t softmax(z)_t v'_t;  out = H o
+ *   bf16:         the same without H, over the stored bf16 rows.
+ * H is the orthonormal Walsh-Hadamard matrix (symmetric, its own inverse), t runs over
+ * positions 0 .. context_lens[b]-1 with no mask, and context_lens[b] = 0 gives zeros.
+ *
+ *   q                  bf16 [batch][num_q_heads][128], 16-byte aligned
+ *   k_pool, v_pool     pools written by xq_quantize_append
+ *   block_tables       int32 [batch][max_pages_per_seq]
+ *   context_lens       int32 [batch] (device)
+ *   max_context_len    host upper bound of context_lens (sizes the launch)
+ *   softmax_scale      multiplies q . k (e.g. 1/sqrt(128))
+ *   num_splits_hint    0 = library policy, else as for xq_decode_num_splits
+ *   workspace          device scratch of >= xq_decode_workspace_bytes(...) bytes, 16-byte
+ *                      aligned; may be NULL when that size is 0. Its contents on entry do
+ *                      not matter; calls that share a workspace must not overlap.
+ *   out                fp32 [batch][num_q_heads][128]
+ * num_q_heads must be a multiple of num_kv_heads with a group size of at most 8.
+ */
+xq_status xq_paged_decode_attention(const xq_cache_layout* layout,
+                                    const void* q, int32_t batch, int32_t num_q_heads,
+                                    const void* k_pool, const void* v_pool,
+                                    const int32_t* block_tables, int32_t max_pages_per_seq,
+                                    const int32_t* context_lens, int32_t max_context_len,
+                                    float softmax_scale, int32_t num_splits_hint,
+                                    void* workspace, int64_t workspace_bytes,
+                                    float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XQ_H */
