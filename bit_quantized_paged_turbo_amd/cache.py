@@ -1,0 +1,57 @@
+"""PagedKVCache: device memory for one layer's K/V pools, driven through the C ABI.
+
+torch provides the allocations and the stream; appends and decodes are single calls
+into libxq.so (no computation happens here).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (CacheLayout, load, xq_decode_workspace_bytes, xq_paged_decode_attention,
+               xq_pool_bytes, xq_quantize_append)
+
+
+class PagedKVCache:
+    def __init__(self, kv_dtype: int, num_kv_heads: int, page_size: int, num_pages: int,
+                 device="cuda", fill_byte: int | None = None):
+        load()
+        self.layout = CacheLayout(kv_dtype, num_kv_heads, page_size, num_pages)
+        self.pool_bytes = xq_pool_bytes(self.layout)
+        if self.pool_bytes <= 0:
+            raise ValueError("invalid cache layout")
+        alloc = torch.empty if fill_byte is None else torch.full
+        args = () if fill_byte is None else (fill_byte,)
+        self.k_pool = alloc((self.pool_bytes,), *args, dtype=torch.uint8, device=device)
+        self.v_pool = alloc((self.pool_bytes,), *args, dtype=torch.uint8, device=device)
+        self._ws = None
+
+    def append(self, k_new: torch.Tensor, v_new: torch.Tensor, token_seq: torch.Tensor,
+               token_pos: torch.Tensor, block_tables: torch.Tensor, stream=None):
+        """k_new/v_new bf16 [n, Hkv, 128]; token_seq/token_pos int32 [n]; block_tables int32 [S, P]."""
+        xq_quantize_append(self.layout, k_new, v_new, int(k_new.shape[0]), token_seq, token_pos,
+                           block_tables, int(block_tables.shape[1]), self.k_pool, self.v_pool,
+                           stream)
+
+    def workspace_bytes(self, batch, num_q_heads, max_context_len, num_splits=0) -> int:
+        return xq_decode_workspace_bytes(self.layout, batch, num_q_heads, max_context_len,
+                                         num_splits)
+
+    def decode(self, q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+               max_context_len: int, softmax_scale: float, num_splits: int = 0,
+               out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+        """q bf16 [B, Hq, 128] -> out fp32 [B, Hq, 128]."""
+        batch, hq = int(q.shape[0]), int(q.shape[1])
+        if out is None:
+            out = torch.empty((batch, hq, 128), dtype=torch.float32, device=q.device)
+        need = self.workspace_bytes(batch, hq, max_context_len, num_splits)
+        if workspace is None and need > 0:
+            if self._ws is None or self._ws.numel() < need:
+                self._ws = torch.empty((need,), dtype=torch.uint8, device=q.device)
+            workspace = self._ws
+        wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        xq_paged_decode_attention(self.layout, q, batch, hq, self.k_pool, self.v_pool,
+                                  block_tables, int(block_tables.shape[1]), context_lens,
+                                  int(max_context_len), softmax_scale, num_splits, workspace,
+                                  wbytes, out, stream)
+        return out

@@ -1,0 +1,159 @@
+// Fused rotate + quantize + pack + page scatter for new K/V rows (gfx950).
+//
+// Method: "xInfer: Pure-Rust LLM Inference Without a Python Runtime" (hysenlabs.com),
+// section "What actually sits between the request and the tokens": every K/V head vector
+// is rotated by a Walsh-Hadamard transform and then quantized with a per-head absmax
+// scale. Number format fixed by this library (the pages leave it open): fp32 FWHT stages
+// h = 1..64 of (a+b, a-b), one multiply by C = fp32(1/sqrt(128)), s16 = fp16_rne(
+// min(absmax/qmax, 65504)), c = clamp(rint_half_even(x/s16), +-qmax), bits-wide two's
+// complement fields packed little-endian. Codes and scales must be bit-identical to the
+// CPU definition, so this file is compiled without FP contraction and keeps IEEE division.
+//
+// Work layout: one row = one (token, kv head) vector of K or V. Sixteen lanes own a row,
+// eight consecutive elements each (one 16-byte load of bf16). Butterfly stages h = 1, 2, 4
+// run inside a lane, h = 8..64 across lanes (partner lane = lane ^ h/8). A 256-thread
+// workgroup handles 16 rows of K (blockIdx.y = 0) or V (blockIdx.y = 1); a row's 16 lanes
+// store its code bytes as one contiguous 16*bits-byte segment of the page block.
+#include "xq_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace xq {
+namespace {
+
+constexpr float kRotC = 0x1.6a09e6p-4f;   // fp32 nearest to 1/sqrt(128), bits 0x3DB504F3
+constexpr int kRowsPerBlock = 16;
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float shfl_xor16(float v, int mask) {
+  // exchange within the 16-lane group that owns a row
+  return __shfl_xor(v, mask, 16);
+}
+
+template <int BITS>
+__global__ __launch_bounds__(kThreads) void quantize_append_kernel(AppendParams p) {
+  const int lane16 = threadIdx.x & 15;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4);  // (token, head)
+  const int64_t nrows = (int64_t)p.n_tokens * p.hkv;
+  if (row >= nrows) return;  // uniform within the 16-lane group
+  const bool is_v = blockIdx.y != 0;
+  const int tok = (int)(row / p.hkv);
+  const int head = (int)(row - (int64_t)tok * p.hkv);
+
+  const int seq = p.token_seq[tok];
+  const int pos = p.token_pos[tok];
+  const int page = p.block_tables[(int64_t)seq * p.maxp + pos / p.page_size];
+  const int slot = pos % p.page_size;
+  uint8_t* block = (is_v ? p.v_pool : p.k_pool) + (int64_t)page * p.page_stride +
+                   (int64_t)head * p.block_bytes;
+
+  const uint16_t* src = (is_v ? p.v_new : p.k_new) + row * kHeadDim + lane16 * 8;
+  const uint4 raw = *reinterpret_cast<const uint4*>(src);
+
+  if constexpr (BITS == 0) {
+    // unquantized cache: copy the bf16 row into its slot
+    *reinterpret_cast<uint4*>(block + (int64_t)slot * 256 + lane16 * 16) = raw;
+    return;
+  } else {
+    constexpr int qmax = (1 << (BITS - 1)) - 1;
+    float r[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
+                  bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
+    // in-lane stages h = 1, 2, 4 (element index 8*lane16 + e)
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if ((e & h) == 0) {
+          const float a = r[e], b = r[e + h];
+          r[e] = a + b;
+          r[e + h] = a - b;
+        }
+      }
+    }
+    // cross-lane stages h = 8, 16, 32, 64: the lane with bit (h/8) clear holds the lower
+    // element of every pair and keeps a + b; its partner keeps a - b.
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      const bool upper = (lane16 & m) != 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float other = shfl_xor16(r[e], m);
+        r[e] = upper ? (other - r[e]) : (r[e] + other);
+      }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      r[e] = r[e] * kRotC;
+      amax = fmaxf(amax, fabsf(r[e]));
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, shfl_xor16(amax, m));
+
+    const float s32 = amax / (float)qmax;
+    const _Float16 s16 = (_Float16)fminf(s32, 65504.f);
+    const float sf = (float)s16;
+    int code[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float c = 0.f;
+      if (sf != 0.f) c = fminf(fmaxf(rintf(r[e] / sf), (float)-qmax), (float)qmax);
+      code[e] = (int)c;
+    }
+
+    constexpr int rowb = 16 * BITS;
+    uint8_t* dst = block + (int64_t)slot * rowb;
+    if constexpr (BITS == 4) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w |= (uint32_t)(code[e] & 0xf) << (4 * e);
+      *reinterpret_cast<uint32_t*>(dst + 4 * lane16) = w;
+    } else if constexpr (BITS == 8) {
+      uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w0 |= (uint32_t)(code[e] & 0xff) << (8 * e);
+        w1 |= (uint32_t)(code[e + 4] & 0xff) << (8 * e);
+      }
+      *reinterpret_cast<uint2*>(dst + 8 * lane16) = make_uint2(w0, w1);
+    } else {  // BITS == 3: 24 bits per lane at bit offset 24*lane16; 12 dwords per row
+      uint32_t v = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v |= (uint32_t)(code[e] & 0x7) << (3 * e);
+      // dword k of the row starts in lane (32k)/24 at bit offset 32k mod 24
+      const int k = lane16;
+      const int src_lane = (32 * k) / 24;
+      const int off = (32 * k) % 24;
+      const int base = threadIdx.x & ~15;
+      const uint32_t lo = (uint32_t)__shfl((int)v, base + min(src_lane, 15), 64);
+      const uint32_t hi = (uint32_t)__shfl((int)v, base + min(src_lane + 1, 15), 64);
+      const uint32_t w = (lo >> off) | (hi << (24 - off));
+      if (k < 12) *reinterpret_cast<uint32_t*>(dst + 4 * k) = w;
+    }
+    if (lane16 == 0) {
+      uint16_t* sdst = reinterpret_cast<uint16_t*>(block + (int64_t)p.page_size * rowb) + slot;
+      *sdst = __builtin_bit_cast(uint16_t, s16);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_append(int dtype, const AppendParams& p, hipStream_t stream) {
+  if (p.n_tokens <= 0) return hipSuccess;
+  const int64_t rows = (int64_t)p.n_tokens * p.hkv;
+  dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock), 2, 1);
+  switch (dtype) {
+    case 0: hipLaunchKernelGGL(quantize_append_kernel<0>, grid, dim3(kThreads), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL(quantize_append_kernel<8>, grid, dim3(kThreads), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL(quantize_append_kernel<4>, grid, dim3(kThreads), 0, stream, p); break;
+    case 3: hipLaunchKernelGGL(quantize_append_kernel<3>, grid, dim3(kThreads), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace xq

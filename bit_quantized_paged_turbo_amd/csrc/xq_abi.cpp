@@ -1,0 +1,214 @@
+// C ABI of the TurboQuant paged KV cache: argument validation, split planning and launch.
+// Declarations and the full contract are in include/xq.h.
+#include "../../include/xq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "xq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+xq_status fail(xq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+bool is_dtype(int32_t d) { return d == XQ_KV_BF16 || d == XQ_KV_TURBO8 || d == XQ_KV_TURBO4 || d == XQ_KV_TURBO3; }
+bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+xq_status check_layout(const xq_cache_layout* L) {
+  if (!L) return fail(XQ_EINVAL, "layout is NULL");
+  if (!is_dtype(L->kv_dtype)) return fail(XQ_EINVAL, "kv_dtype %d is not one of 0 (bf16), 8, 4, 3", L->kv_dtype);
+  if (L->head_dim != 128) return fail(XQ_EUNSUPPORTED, "head_dim %d: only 128 is supported", L->head_dim);
+  if (L->num_kv_heads < 1) return fail(XQ_EINVAL, "num_kv_heads %d < 1", L->num_kv_heads);
+  if (!pow2(L->page_size) || L->page_size < 16 || L->page_size > 256)
+    return fail(XQ_EINVAL, "page_size %d is not a power of two in [16, 256]", L->page_size);
+  if (L->num_pages < 1) return fail(XQ_EINVAL, "num_pages %lld < 1", (long long)L->num_pages);
+  return XQ_OK;
+}
+
+int64_t block_bytes_of(const xq_cache_layout* L) {
+  const int64_t row = xq::row_code_bytes(L->kv_dtype);
+  const int64_t bytes = L->page_size * row + (L->kv_dtype == XQ_KV_BF16 ? 0 : 2 * L->page_size);
+  return (bytes + 15) & ~int64_t(15);
+}
+
+// Tokens per split: page aligned, a multiple of 16. hint > 0 asks for that many splits of
+// the longest sequence; 0 sizes splits so that the grid has about 2048 workgroups
+// (8 per compute unit on 256 CUs), with 64..1024 tokens per split.
+int32_t plan_tokens_per_split(const xq_cache_layout* L, int32_t batch, int32_t max_ctx, int32_t hint) {
+  const int32_t ps = L->page_size;
+  int64_t tps;
+  if (hint > 0) {
+    tps = (max_ctx + hint - 1) / hint;
+  } else {
+    const int64_t units = (int64_t)batch * L->num_kv_heads;
+    int64_t want = (int64_t)max_ctx * units / 2048;
+    tps = 64;
+    while (tps < want && tps < 1024) tps <<= 1;
+  }
+  tps = ((tps + ps - 1) / ps) * ps;
+  if (tps < ps) tps = ps;
+  if (tps > (int64_t)1 << 30) tps = (int64_t)1 << 30;
+  return (int32_t)tps;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t xq_block_bytes(const xq_cache_layout* layout) {
+  if (check_layout(layout) != XQ_OK) return -1;
+  return block_bytes_of(layout);
+}
+
+int64_t xq_page_stride_bytes(const xq_cache_layout* layout) {
+  if (check_layout(layout) != XQ_OK) return -1;
+  return block_bytes_of(layout) * layout->num_kv_heads;
+}
+
+int64_t xq_pool_bytes(const xq_cache_layout* layout) {
+  if (check_layout(layout) != XQ_OK) return -1;
+  return block_bytes_of(layout) * layout->num_kv_heads * layout->num_pages;
+}
+
+int32_t xq_decode_num_splits(const xq_cache_layout* layout, int32_t batch, int32_t num_q_heads,
+                             int32_t max_context_len, int32_t num_splits_hint) {
+  if (check_layout(layout) != XQ_OK) return -1;
+  if (batch < 0 || num_q_heads < 1 || max_context_len < 0 || num_splits_hint < 0) return -1;
+  if (max_context_len == 0) return 1;
+  const int32_t tps = plan_tokens_per_split(layout, batch, max_context_len, num_splits_hint);
+  return (max_context_len + tps - 1) / tps;
+}
+
+int64_t xq_decode_workspace_bytes(const xq_cache_layout* layout, int32_t batch, int32_t num_q_heads,
+                                  int32_t max_context_len, int32_t num_splits_hint) {
+  const int32_t ns = xq_decode_num_splits(layout, batch, num_q_heads, max_context_len, num_splits_hint);
+  if (ns < 0) return -1;
+  if (ns <= 1) return 0;
+  return (int64_t)batch * num_q_heads * ns * xq::kPartialStride * (int64_t)sizeof(float);
+}
+
+const char* xq_status_string(int32_t status) {
+  switch (status) {
+    case XQ_OK: return "ok";
+    case XQ_EINVAL: return "invalid argument";
+    case XQ_EUNSUPPORTED: return "unsupported configuration";
+    case XQ_EWORKSPACE: return "workspace too small";
+    case XQ_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* xq_last_error(void) { return g_last_error.c_str(); }
+
+xq_status xq_quantize_append(const xq_cache_layout* layout, const void* k_new, const void* v_new,
+                             int32_t n_tokens, const int32_t* token_seq, const int32_t* token_pos,
+                             const int32_t* block_tables, int32_t max_pages_per_seq,
+                             void* k_pool, void* v_pool, void* stream) {
+  if (xq_status st = check_layout(layout)) return st;
+  if (n_tokens < 0) return fail(XQ_EINVAL, "n_tokens %d < 0", n_tokens);
+  if (n_tokens == 0) return XQ_OK;
+  if (!k_new || !v_new || !token_seq || !token_pos || !block_tables || !k_pool || !v_pool)
+    return fail(XQ_EINVAL, "a required pointer is NULL");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(XQ_EINVAL, "k_new, v_new and the pools must be 16-byte aligned");
+  if (max_pages_per_seq < 1) return fail(XQ_EINVAL, "max_pages_per_seq %d < 1", max_pages_per_seq);
+  if ((int64_t)n_tokens * layout->num_kv_heads > ((int64_t)1 << 31) * 16)
+    return fail(XQ_EINVAL, "n_tokens * num_kv_heads too large for one launch");
+  xq::AppendParams p{};
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.token_seq = token_seq;
+  p.token_pos = token_pos;
+  p.block_tables = block_tables;
+  p.k_pool = static_cast<uint8_t*>(k_pool);
+  p.v_pool = static_cast<uint8_t*>(v_pool);
+  p.block_bytes = block_bytes_of(layout);
+  p.page_stride = p.block_bytes * layout->num_kv_heads;
+  p.n_tokens = n_tokens;
+  p.hkv = layout->num_kv_heads;
+  p.page_size = layout->page_size;
+  p.maxp = max_pages_per_seq;
+  const hipError_t e = xq::launch_quantize_append(layout->kv_dtype, p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(XQ_EHIP, "quantize_append launch: %s", hipGetErrorString(e));
+  return XQ_OK;
+}
+
+xq_status xq_paged_decode_attention(const xq_cache_layout* layout, const void* q, int32_t batch,
+                                    int32_t num_q_heads, const void* k_pool, const void* v_pool,
+                                    const int32_t* block_tables, int32_t max_pages_per_seq,
+                                    const int32_t* context_lens, int32_t max_context_len,
+                                    float softmax_scale, int32_t num_splits_hint, void* workspace,
+                                    int64_t workspace_bytes, float* out, void* stream) {
+  if (xq_status st = check_layout(layout)) return st;
+  if (batch < 0) return fail(XQ_EINVAL, "batch %d < 0", batch);
+  if (batch == 0) return XQ_OK;
+  if (batch > 65535) return fail(XQ_EUNSUPPORTED, "batch %d > 65535", batch);
+  if (num_q_heads < 1 || num_q_heads % layout->num_kv_heads != 0)
+    return fail(XQ_EINVAL, "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads,
+                layout->num_kv_heads);
+  const int32_t g = num_q_heads / layout->num_kv_heads;
+  if (g > xq::kMaxGroup) return fail(XQ_EUNSUPPORTED, "group size %d > %d", g, xq::kMaxGroup);
+  if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out)
+    return fail(XQ_EINVAL, "a required pointer is NULL");
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(XQ_EINVAL, "q and the pools must be 16-byte aligned");
+  if (max_context_len < 0) return fail(XQ_EINVAL, "max_context_len %d < 0", max_context_len);
+  if (max_pages_per_seq < 1) return fail(XQ_EINVAL, "max_pages_per_seq %d < 1", max_pages_per_seq);
+  if ((int64_t)max_context_len > (int64_t)max_pages_per_seq * layout->page_size)
+    return fail(XQ_EINVAL, "max_context_len %d exceeds max_pages_per_seq * page_size", max_context_len);
+  if (num_splits_hint < 0) return fail(XQ_EINVAL, "num_splits_hint %d < 0", num_splits_hint);
+  if (!(softmax_scale == softmax_scale)) return fail(XQ_EINVAL, "softmax_scale is NaN");
+
+  const int32_t ctx = max_context_len > 0 ? max_context_len : 1;
+  const int32_t tps = plan_tokens_per_split(layout, batch, ctx, num_splits_hint);
+  const int32_t nsplits = (ctx + tps - 1) / tps;
+  const int64_t need = nsplits > 1 ? (int64_t)batch * num_q_heads * nsplits * xq::kPartialStride * 4 : 0;
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(XQ_EWORKSPACE, "workspace of %lld bytes needed, %lld given", (long long)need,
+                  (long long)workspace_bytes);
+    if (!aligned16(workspace)) return fail(XQ_EINVAL, "workspace must be 16-byte aligned");
+  }
+  if (nsplits > 65535) return fail(XQ_EUNSUPPORTED, "%d splits > 65535", nsplits);
+
+  xq::DecodeParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_pool = static_cast<const uint8_t*>(k_pool);
+  p.v_pool = static_cast<const uint8_t*>(v_pool);
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.out = out;
+  p.partials = static_cast<float*>(workspace);
+  p.block_bytes = block_bytes_of(layout);
+  p.page_stride = p.block_bytes * layout->num_kv_heads;
+  p.batch = batch;
+  p.hq = num_q_heads;
+  p.hkv = layout->num_kv_heads;
+  p.page_size = layout->page_size;
+  p.page_shift = __builtin_ctz((unsigned)layout->page_size);
+  p.maxp = max_pages_per_seq;
+  p.tokens_per_split = tps;
+  p.nsplits = nsplits;
+  p.max_context_len = max_context_len;
+  p.softmax_scale = softmax_scale;
+  const hipError_t e = xq::launch_decode(layout->kv_dtype, g, p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(XQ_EHIP, "decode launch: %s", hipGetErrorString(e));
+  return XQ_OK;
+}
+
+}  // extern "C"

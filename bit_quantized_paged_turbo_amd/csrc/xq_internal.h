@@ -1,0 +1,57 @@
+// Internal interface between the C ABI (xq_abi.cpp) and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace xq {
+
+constexpr int kHeadDim = 128;
+constexpr int kMaxGroup = 8;          // query heads per kv head handled in one pass
+constexpr int kPartialStride = 132;   // floats per (seq, q head, split) partial: m, l, pad, acc[128]
+
+// Bytes of one stored code row for a dtype (bf16: 256).
+inline constexpr int row_code_bytes(int dtype) { return dtype == 0 ? 256 : 16 * dtype; }
+
+struct AppendParams {
+  const uint16_t* k_new;        // bf16 [n_tokens][hkv][128]
+  const uint16_t* v_new;
+  const int32_t* token_seq;     // [n_tokens]
+  const int32_t* token_pos;     // [n_tokens]
+  const int32_t* block_tables;  // [num_seqs][maxp]
+  uint8_t* k_pool;
+  uint8_t* v_pool;
+  int64_t page_stride;          // bytes
+  int64_t block_bytes;          // bytes
+  int32_t n_tokens;
+  int32_t hkv;
+  int32_t page_size;
+  int32_t maxp;
+};
+
+struct DecodeParams {
+  const uint16_t* q;            // bf16 [batch][hq][128]
+  const uint8_t* k_pool;
+  const uint8_t* v_pool;
+  const int32_t* block_tables;  // [batch][maxp]
+  const int32_t* context_lens;  // [batch]
+  float* out;                   // [batch][hq][128]
+  float* partials;              // [batch][hq][nsplits][kPartialStride] (nsplits > 1)
+  int64_t page_stride;
+  int64_t block_bytes;
+  int32_t batch;
+  int32_t hq;
+  int32_t hkv;
+  int32_t page_size;
+  int32_t page_shift;           // log2(page_size)
+  int32_t maxp;
+  int32_t tokens_per_split;     // multiple of page_size and of 16
+  int32_t nsplits;              // splits of the longest sequence (grid x)
+  int32_t max_context_len;      // context_lens are clamped to this
+  float softmax_scale;
+};
+
+hipError_t launch_quantize_append(int dtype, const AppendParams& p, hipStream_t stream);
+hipError_t launch_decode(int dtype, int group, const DecodeParams& p, hipStream_t stream);
+
+}  // namespace xq

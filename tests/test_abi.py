@@ -1,0 +1,97 @@
+"""The C-ABI library loads, exports every symbol include/xq.h declares, and validates
+host-visible arguments without touching the GPU (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_quantized_paged_turbo_amd as xq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(xq.LIB_PATH):
+        from bit_quantized_paged_turbo_amd import build
+        build.build()
+    return xq.load()
+
+
+def test_exports_match_header(lib):
+    header = open(os.path.join(ROOT, "include", "xq.h")).read()
+    declared = set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(xq_\w+)\s*\(", header, re.M))
+    assert declared == set(xq.EXPORTS)
+    for name in declared:
+        assert getattr(lib, name) is not None
+
+
+@pytest.mark.parametrize("dtype,ps,block", [(4, 16, 1056), (8, 16, 2080), (3, 64, 3200),
+                                            (0, 16, 4096), (3, 16, 800), (4, 256, 16896)])
+def test_block_geometry(lib, dtype, ps, block):
+    L = xq.CacheLayout(dtype, 8, ps, 10)
+    assert xq.xq_block_bytes(L) == block
+    assert xq.xq_page_stride_bytes(L) == 8 * block
+    assert xq.xq_pool_bytes(L) == 80 * block
+
+
+@pytest.mark.parametrize("bad", [dict(kv_dtype=5), dict(head_dim=64), dict(num_kv_heads=0),
+                                 dict(page_size=24), dict(page_size=8), dict(page_size=512),
+                                 dict(num_pages=0)])
+def test_invalid_layouts(lib, bad):
+    args = dict(kv_dtype=4, num_kv_heads=8, page_size=16, num_pages=10)
+    head_dim = bad.pop("head_dim", 128)
+    args.update(bad)
+    L = xq.CacheLayout(head_dim=head_dim, **args)
+    assert xq.xq_block_bytes(L) == -1
+    assert xq.xq_pool_bytes(L) == -1
+
+
+def test_split_planning(lib):
+    L = xq.CacheLayout(3, 8, 64, 4096)
+    assert xq.xq_decode_num_splits(L, 1, 40, 262144, 256) == 256
+    assert xq.xq_decode_workspace_bytes(L, 1, 40, 262144, 256) == 40 * 256 * 132 * 4
+    L = xq.CacheLayout(4, 8, 16, 9000)
+    assert xq.xq_decode_num_splits(L, 256, 16, 1022, 0) == 1
+    assert xq.xq_decode_workspace_bytes(L, 256, 16, 1022, 0) == 0
+    assert xq.xq_decode_num_splits(L, 4, 16, 1000, 7) == 7
+    assert xq.xq_decode_num_splits(L, 4, 16, 0, 0) == 1
+    assert xq.xq_decode_num_splits(L, 4, 16, 100, -1) == -1
+
+
+def _decode_status(lib, L, **kw):
+    a = dict(q=16, batch=1, hq=8, k=16, v=16, bt=16, maxp=4, cl=16, maxctx=64, scale=0.1,
+             splits=0, ws=None, wsb=0, out=16, stream=None)
+    a.update(kw)
+    return lib.xq_paged_decode_attention(ctypes.byref(L), a["q"], a["batch"], a["hq"], a["k"],
+                                         a["v"], a["bt"], a["maxp"], a["cl"], a["maxctx"],
+                                         a["scale"], a["splits"], a["ws"], a["wsb"], a["out"],
+                                         a["stream"])
+
+
+def test_decode_argument_errors(lib):
+    L = xq.CacheLayout(4, 2, 16, 10)
+    assert _decode_status(lib, L, hq=7) == xq.EINVAL           # not a multiple of Hkv
+    assert _decode_status(lib, L, hq=18) == xq.EUNSUPPORTED    # group 9 > 8
+    assert _decode_status(lib, L, q=None) == xq.EINVAL
+    assert _decode_status(lib, L, k=8) == xq.EINVAL            # misaligned pool
+    assert _decode_status(lib, L, maxctx=65) == xq.EINVAL      # > maxp * page_size
+    assert _decode_status(lib, L, splits=2) == xq.EWORKSPACE   # partials need a workspace
+    assert b"workspace" in lib.xq_last_error()
+    assert _decode_status(lib, L, batch=0) == xq.OK            # nothing to do
+    bad = xq.CacheLayout(4, 2, 20, 10)
+    assert _decode_status(lib, bad) == xq.EINVAL
+
+
+def test_append_argument_errors(lib):
+    L = xq.CacheLayout(4, 2, 16, 10)
+    call = lambda **kw: lib.xq_quantize_append(
+        ctypes.byref(L), kw.get("k", 16), kw.get("v", 16), kw.get("n", 4), kw.get("s", 16),
+        kw.get("p", 16), kw.get("bt", 16), kw.get("maxp", 4), kw.get("kp", 16), kw.get("vp", 16), None)
+    assert call(n=-1) == xq.EINVAL
+    assert call(n=0) == xq.OK
+    assert call(s=None) == xq.EINVAL
+    assert call(kp=24) == xq.EINVAL
+    assert call(maxp=0) == xq.EINVAL
+    assert lib.xq_status_string(xq.EHIP) == b"HIP runtime error"

@@ -1,0 +1,239 @@
+"""GPU parity: the HIP path against the oracle on the same seeded inputs.
+
+Bar: packed codes and fp16 scales bit-exact; attention outputs within 2e-3 max-abs
+(fp32 accumulation against the oracle's float64). Unused page slots are poisoned with
+0xFF bytes (a NaN pattern in bf16 and fp16) before the cache is filled.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from bit_quantized_paged_turbo_amd import xq_block_bytes
+from tests.gpu_util import fill, gather, make_cache, to_dev, upload_tables
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def _print_case(*a):
+    print("CASE", *a, flush=True)
+
+
+def _codec_check(W, cache, seqs):
+    bb = xq_block_bytes(cache.layout)
+    kp = cache.k_pool.cpu().numpy()
+    vp = cache.v_pool.cpu().numpy()
+    for b in seqs:
+        L = W.seq_len(b)
+        if L == 0:
+            continue
+        k, v = W.kv_bits(b)
+        pos = np.arange(L)
+        if L > 20000:   # sample positions of long sequences (first, last and random ones)
+            pos = np.unique(np.concatenate([pos[:2048], pos[-2048:],
+                                            np.random.default_rng(b).choice(L, 4096)]))
+            k, v = k[pos], v[pos]
+        for pool, rows in ((kp, k), (vp, v)):
+            codes, scales = gather(pool, W, bb, b, pos)
+            if W.dtype == 0:
+                assert np.array_equal(codes.view(np.uint16).reshape(rows.shape), rows)
+                continue
+            c, s = oracle.quantize_rows_bf16(rows, W.dtype)
+            want = oracle.pack_codes(c, W.dtype)
+            bad = np.argwhere(codes != want)
+            assert bad.size == 0, f"seq {b}: {len(bad)} code bytes differ, first {bad[:3]}"
+            assert np.array_equal(scales, s.view(np.uint16)), f"seq {b}: scales differ"
+
+
+def _decode(W, cache, bt, cl, num_splits=0, q=None):
+    q = to_dev(W.q_bits()) if q is None else q
+    out = cache.decode(q, bt[: W.batch], cl, W.max_context_len, W.softmax_scale, num_splits)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def _oracle_out(W, b, q_bits, kv=None):
+    k, v = kv if kv is not None else W.kv_bits(b)
+    out, _ = oracle.decode_sequence(W.dtype, q_bits[b], k, v, W.softmax_scale)
+    return out
+
+
+# ------------------------------------------------------------------------------------
+# codec
+# ------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,ps", [(4, 16), (4, 64), (8, 16), (8, 32), (3, 64), (3, 16), (0, 16)])
+def test_append_codes_bit_exact(dtype, ps):
+    _print_case("append", dtype, ps)
+    W = workloads.make(f"codec-{dtype}-{ps}", 100 + dtype, dtype, [1, 37, 130, 16], 8, 2, ps)
+    cache = make_cache(W)
+    bt, _ = upload_tables(W)
+    fill(cache, W, bt)
+    torch.cuda.synchronize()
+    _codec_check(W, cache, range(W.batch))
+    # slots past each sequence's end keep the poison bytes
+    bb = xq_block_bytes(cache.layout)
+    kp = cache.k_pool.cpu().numpy().reshape(W.num_pages, W.num_kv_heads, bb)
+    rowb = 256 if dtype == 0 else 16 * dtype
+    for b in range(W.batch):
+        L = int(W.context_lens[b])
+        if L % ps:
+            page = W.block_tables[b, L // ps]
+            assert np.all(kp[page, :, (L % ps) * rowb: ps * rowb] == 0xFF)
+
+
+@pytest.mark.parametrize("dtype", [8, 4, 3])
+def test_append_edge_rows(dtype):
+    """Zero rows, rows whose scale underflows or saturates, subnormal bf16 inputs, rows
+    already on the quantization grid, and ties."""
+    _print_case("edge-rows", dtype)
+    rows = np.zeros((8, 1, 128), np.float32)
+    g = np.random.default_rng(dtype)
+    rows[1, 0] = g.standard_normal(128) * 1e-9          # scale rounds to 0 -> all-zero codes
+    rows[2, 0] = g.standard_normal(128) * 1e35          # scale saturates at 65504
+    rows[3, 0] = g.standard_normal(128) * 1e-39         # bf16 subnormals
+    rows[4, 0, ::3] = 1.0                               # sparse, exact after rotation
+    rows[5, 0] = g.standard_normal(128) * 1e4
+    rows[6, 0] = np.arange(128) - 64.0
+    rows[7, 0, 0] = 1.0
+    bits = workloads.round_to_bf16_bits(rows)
+    W = workloads.make("edge", 200 + dtype, dtype, [8], 1, 1, 16)
+    cache = make_cache(W)
+    bt, _ = upload_tables(W)
+    k = to_dev(bits)
+    pos = to_dev(np.arange(8, dtype=np.int32))
+    seq = to_dev(np.zeros(8, np.int32))
+    cache.append(k, k, seq, pos, bt)
+    torch.cuda.synchronize()
+    codes, scales = gather(cache.k_pool.cpu().numpy(), W, xq_block_bytes(cache.layout), 0, np.arange(8))
+    c, s = oracle.quantize_rows_bf16(bits, dtype)
+    assert np.array_equal(codes, oracle.pack_codes(c, dtype))
+    assert np.array_equal(scales, s.view(np.uint16))
+
+
+# ------------------------------------------------------------------------------------
+# decode on the presets (scaled-down versions run the oracle on every sequence)
+# ------------------------------------------------------------------------------------
+SMALL = [
+    ("c0", 0, None, None, 1.0),
+    ("c1-b24", 1, None, 24, 1.0),
+    ("c2-turbo8-b2", 2, 8, 2, 1 / 8),
+    ("c2-bf16-b2", 2, 0, 2, 1 / 8),
+    ("c3-1/64", 3, None, None, 1 / 64),
+    ("c4-b6-1/8", 4, None, 6, 1 / 8),
+]
+
+
+@pytest.mark.parametrize("name,cfg,dtype,batch,scale", SMALL, ids=[s[0] for s in SMALL])
+def test_decode_matches_oracle(name, cfg, dtype, batch, scale):
+    _print_case("decode", name)
+    W = workloads.config(cfg, dtype=dtype, batch=batch, context_scale=scale)
+    cache = make_cache(W)
+    bt, cl = upload_tables(W)
+    kv = {b: W.kv_bits(b) for b in range(W.num_seqs)}
+    fill(cache, W, bt, kv=kv)
+    torch.cuda.synchronize()
+    _codec_check(W, cache, range(W.num_seqs))
+    qb = W.q_bits()
+    splits = W.num_splits if W.num_splits and W.max_context_len >= W.num_splits * W.page_size else 0
+    got = _decode(W, cache, bt, cl, splits, to_dev(qb))
+    for b in range(W.batch):
+        want = _oracle_out(W, b, qb, kv[b])
+        err = np.max(np.abs(got[b] - want))
+        assert err <= TOL, f"{name} seq {b}: max abs err {err:.3e}"
+
+
+# ------------------------------------------------------------------------------------
+# decode on the full presets, in the launch configuration the benchmark uses; the oracle
+# recomputes a sample of sequences
+# ------------------------------------------------------------------------------------
+FULL = [("c1", 1, None, list(range(0, 256, 17))), ("c2-turbo8", 2, 8, [0, 31]),
+        ("c2-bf16", 2, 0, [5]), ("c3", 3, None, [0]), ("c4", 4, None, [0, 13, 63])]
+
+
+@pytest.mark.parametrize("name,cfg,dtype,sample", FULL, ids=[f[0] for f in FULL])
+def test_full_size_sampled(name, cfg, dtype, sample):
+    _print_case("full", name)
+    W = workloads.config(cfg, dtype=dtype)
+    cache = make_cache(W, fill_byte=None)
+    bt, cl = upload_tables(W)
+    fill(cache, W, bt)
+    torch.cuda.synchronize()
+    check_codes = sample[:1] + ([W.batch] if W.chunk_tokens else [])
+    _codec_check(W, cache, check_codes)
+    qb = W.q_bits()
+    got = _decode(W, cache, bt, cl, W.num_splits, to_dev(qb))
+    assert np.all(np.isfinite(got))
+    for b in sample:
+        want = _oracle_out(W, b, qb)
+        err = np.max(np.abs(got[b] - want))
+        assert err <= TOL, f"{name} seq {b}: max abs err {err:.3e}"
+
+
+# ------------------------------------------------------------------------------------
+# edge cases and properties
+# ------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,ps,hq,hkv", [(4, 16, 8, 8), (4, 32, 24, 8), (4, 128, 16, 2),
+                                             (4, 256, 8, 1), (3, 64, 6, 2), (8, 64, 14, 2),
+                                             (0, 32, 8, 1), (8, 16, 7, 7)])
+def test_decode_shapes_and_ragged(dtype, ps, hq, hkv):
+    _print_case("shapes", dtype, ps, hq, hkv)
+    lens = [0, 1, 15, 17, ps + 3, 3 * ps - 1, 700]
+    W = workloads.make(f"shape-{dtype}-{ps}", 300 + dtype, dtype, lens, hq, hkv, ps)
+    cache = make_cache(W)
+    bt, cl = upload_tables(W)
+    kv = {b: W.kv_bits(b) for b in range(W.batch)}
+    fill(cache, W, bt, kv=kv)
+    qb = W.q_bits()
+    for splits in (0, 1, 5):
+        got = _decode(W, cache, bt, cl, splits, to_dev(qb))
+        assert np.all(got[0] == 0)                       # empty context -> zeros
+        for b in range(1, W.batch):
+            want = _oracle_out(W, b, qb, kv[b])
+            err = np.max(np.abs(got[b] - want))
+            assert err <= TOL, f"splits {splits} seq {b} (L={lens[b]}): {err:.3e}"
+
+
+def test_splits_agree_and_repeat_is_deterministic():
+    _print_case("splits")
+    W = workloads.config(1, batch=16)
+    cache = make_cache(W)
+    bt, cl = upload_tables(W)
+    fill(cache, W, bt)
+    q = to_dev(W.q_bits())
+    a = _decode(W, cache, bt, cl, 1, q)
+    b = _decode(W, cache, bt, cl, 1, q)
+    assert np.array_equal(a, b)
+    for s in (2, 8, 64):
+        c = _decode(W, cache, bt, cl, s, q)
+        assert np.max(np.abs(c - a)) < 2e-5
+
+
+def test_page_placement_does_not_change_output():
+    """Two caches with the same logical content in different physical pages give
+    bit-identical outputs (the kernel walks pages in logical order)."""
+    _print_case("placement")
+    W1 = workloads.make("placeA", 400, 4, [300, 45], 8, 2, 16, permute=False)
+    W2 = workloads.make("placeA", 400, 4, [300, 45], 8, 2, 16, pool_pages=64)
+    outs = []
+    for W in (W1, W2):
+        cache = make_cache(W)
+        bt, cl = upload_tables(W)
+        fill(cache, W, bt)
+        outs.append(_decode(W, cache, bt, cl, 0))
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_shared_prefix_pages():
+    """Two sequences may point at the same physical pages (a shared prefix)."""
+    _print_case("shared")
+    W = workloads.make("shared", 401, 4, [64, 64], 8, 2, 16)
+    W.block_tables[1] = W.block_tables[0]
+    cache = make_cache(W)
+    bt, cl = upload_tables(W)
+    fill(cache, W, bt, seqs=[0])
+    qb = W.q_bits()
+    qb[1] = qb[0]
+    got = _decode(W, cache, bt, cl, 0, to_dev(qb))
+    assert np.array_equal(got[0], got[1])
