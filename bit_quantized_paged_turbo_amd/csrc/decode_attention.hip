@@ -10,28 +10,48 @@
 //   infr: A Pure-Rust, Vulkan-First LLM Inference Engine", section "Configuration Without
 //   Surprises").
 //
-// Because H is orthonormal, q.k = (Hq).(Hk): the query is rotated once (q' = Hq) and the
-// scores are taken against the stored rotated rows; the value sum is formed in the rotated
-// space and rotated back at the end (H is its own inverse).
+// H is orthonormal, so q.k = (Hq).(Hk): the query is rotated once (q' = Hq), scores are taken
+// against the stored rotated rows, and the value sum, formed in the rotated space, is rotated
+// back at the end (H is its own inverse).
 //
-// Kernel structure (one workgroup of 4 waves per (split, kv head, sequence)):
-//   * the g = Hq/Hkv query heads of the kv head are rotated in LDS and quantized to
-//     16-bit (turbo4/3: four signed 4-bit digits; turbo8: three signed 8-bit digits)
-//     integers with one fp32 scale per head, so q'.c reduces to exact integer dot
-//     products (v_dot8_i32_i4 / v_dot4_i32_i8 on the raw codes);
-//   * every KV byte is read once per group: a wave step covers 16 tokens, lane l owns
-//     token l/4 and dims [32*(l%4), +32) of it, so a step is one coalesced load of whole
-//     code rows (a 1 KB turbo4 block at page size 16);
-//   * the four partial dot products of a token are summed with two DPP quad exchanges;
-//   * each lane keeps its own online-softmax state per head (running reference max m,
-//     sum l, value sum acc[32]); m moves only when a score exceeds it by more than 2^8,
-//     so rescaling is rare and exact in effect (any reference keeps the ratios);
-//   * value codes are widened to fp32 with v_cvt_f32_ubyte after an offset-binary XOR,
-//     the offset is removed once at the end from the sum of weights;
-//   * at the end the 16 token lanes of each dim chunk and then the 4 waves are merged
-//     with log-sum-exp; a sequence that fits one split is normalized, rotated back with
-//     an in-LDS FWHT and stored; otherwise (m, l, acc) partials go to the workspace and
-//     the combine kernel merges them.
+// The grouped-query tile is a dense contraction, so both products run on the matrix cores:
+//
+//   QK  v_mfma_i32_16x16x64_i8. Rows = 16 tokens, columns = the g query heads of the kv head
+//       (g <= 16). The rotated query is rounded to an integer q (|q| <= 32000, one fp32 scale
+//       per head) and split into two signed 8-bit digits, q = 256 d1 + d0; the K codes enter
+//       as bytes (turbo4/3 with a +8/+4 bias so a nibble is an unsigned byte, turbo8 as its
+//       signed byte). The integer dot products are exact; the bias is removed with the digit
+//       sums. Two MFMAs per digit cover the 128 dimensions.
+//   PV  v_mfma_f32_16x16x32_f16. Rows = heads, k = 32 tokens, columns = 16 dimensions (eight
+//       MFMAs cover 128). The weight of token t for head h is P'[h,t] = p[h,t] * s_v[t], split
+//       into an fp16 high part (round toward zero) and the fp16 remainder; each enters its own
+//       MFMA, so the weights carry ~22 bits. A V code c enters as an fp16 subnormal whose
+//       mantissa holds (c + bias) in its top bits, exact, made with one byte permute per pair
+//       of tokens; the bias is removed at the end with sum(P'). (Measured on gfx950: with the
+//       code in the low mantissa bits instead, the accumulating MFMA loses up to 2^-13 of a
+//       code step; in the top bits of the low byte the loss is below 2^-18.)
+//   bf16 cache: q and K are bf16 operands of v_mfma_f32_16x16x32_bf16 (exact products), the
+//       weights are split into bf16 high and low parts against bf16 V.
+//
+// Online softmax runs in the log2 domain against a per-head reference m that moves only when
+// a score beats it by more than 2^8. For turbo caches the reference tracks
+// w = score + log2(s_v), so every fp16 weight P' = 2^(w - m) is at most 2^8 whatever the
+// scales are; the normaliser sum(p) uses p = 2^(score - m) in fp32.
+//
+// Work split: one workgroup of four waves per (split, kv head, sequence); wave w takes the
+// 32-token tiles w, w+4, ... of the split and keeps its own softmax state; a tile is two
+// 16-token halves (two pages at page size 16). Lane l = 16 g + c loads, per half, token c's
+// K code bytes for dimensions [32 g, 32 g + 32) (a 16-lane group reads whole rows: one
+// coalesced 1 KB block at turbo4 / page size 16), and for V the c-th 4-byte group of the rows
+// of tokens 4 g + r, which is the transposed operand the PV MFMA needs. Scores come out of the
+// QK MFMA exactly where the PV MFMA wants its weights (lane l: head c, tokens 4 g + r), so no
+// data moves between the two products. Tiles are double-buffered in registers.
+//
+// The query digits are prepared once per (sequence, query head) by q_prep_kernel (rotation by
+// an in-register FWHT, scaling, digit split, packing in the operand layout) into the workspace.
+// At the end the four waves are merged by log-sum-exp in LDS; a sequence that fits one split is
+// normalised, rotated back and stored, otherwise (m, l, acc) partials go to the workspace and
+// decode_combine_kernel merges them.
 #include "xq_internal.h"
 
 namespace xq {
@@ -43,239 +63,438 @@ constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRotC = 0x1.6a09e6p-4f;   // fp32 nearest to 1/sqrt(128)
 constexpr float kLazy = 8.0f;             // rescale only when a score beats m by > 2^8
-constexpr float kQiMax4 = 30000.f;        // |q| bound for four signed 4-bit digits
-constexpr float kQiMax8 = 8300000.f;      // |q| bound for three signed 8-bit digits
+constexpr float kQiMax = 32000.f;         // |q| bound for two signed 8-bit digits
+constexpr float kTinyScale = 0x1p-40f;    // log2 floor for zero value scales
 
-// Per-dtype geometry: bytes of a code row, bytes a lane loads per row, q digits and
-// digit dwords per lane, and the offset-binary bias of value codes.
-template <int DT> struct Fmt;
-template <> struct Fmt<4> {
-  static constexpr int kRow = 64, kLane = 16, kRaw = 4, kDig = 4, kQdw = 4, kQtot = 16;
-  static constexpr float kOff = 8.f;
-};
-template <> struct Fmt<3> {
-  static constexpr int kRow = 48, kLane = 12, kRaw = 3, kDig = 4, kQdw = 4, kQtot = 16;
-  static constexpr float kOff = 8.f;
-};
-template <> struct Fmt<8> {
-  static constexpr int kRow = 128, kLane = 32, kRaw = 8, kDig = 3, kQdw = 8, kQtot = 32;
-  static constexpr float kOff = 128.f;
-};
-template <> struct Fmt<0> {
-  static constexpr int kRow = 256, kLane = 64, kRaw = 16, kDig = 1, kQdw = 16, kQtot = 64;
-  static constexpr float kOff = 0.f;
-};
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// Per cache type: bytes of a code row, bias of K codes in the QK product, bias of V codes
+// in the PV product, and the power of two a V operand carries ((c + bias) * 2^-kVShift).
+template <int DT> struct Codec;
+template <> struct Codec<4> { static constexpr int kRow = 64, kKBias = 8, kVBias = 8, kVShift = 20; };
+template <> struct Codec<3> { static constexpr int kRow = 48, kKBias = 4, kVBias = 4, kVShift = 19; };
+template <> struct Codec<8> { static constexpr int kRow = 128, kKBias = 0, kVBias = 128, kVShift = 24; };
+template <> struct Codec<0> { static constexpr int kRow = 256, kKBias = 0, kVBias = 0, kVShift = 0; };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+__device__ __forceinline__ float half_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float half_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// DPP quad exchanges (lanes 4t..4t+3 hold the four dim chunks of one token)
-__device__ __forceinline__ int quad_xor1(int v) { return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false); }
-__device__ __forceinline__ int quad_xor2(int v) { return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false); }
-__device__ __forceinline__ float quad_xor1f(float v) { return __int_as_float(quad_xor1(__float_as_int(v))); }
-__device__ __forceinline__ float quad_xor2f(float v) { return __int_as_float(quad_xor2(__float_as_int(v))); }
-
-// 3-bit fields [3k, 3k+3) of a 24-bit value -> sign-extended 4-bit nibbles k of a dword.
+// Eight 3-bit fields of a 24-bit value (each already biased to 0..7) -> eight nibbles.
 __device__ __forceinline__ uint32_t spread3to4(uint32_t x) {
-  x = (x & 0xfffu) | ((x & 0xfff000u) << 4);            // 4 fields per 16-bit half
-  x = (x & 0x003f003fu) | ((x & 0x0fc00fc0u) << 2);     // 2 fields per byte
-  x = (x & 0x07070707u) | ((x & 0x38383838u) << 1);     // 1 field per nibble
-  return x | ((x & 0x44444444u) << 1);                  // copy sign bit 2 -> bit 3
+  x = (x & 0xfffu) | ((x & 0xfff000u) << 4);
+  x = (x & 0x003f003fu) | ((x & 0x0fc00fc0u) << 2);
+  return (x & 0x07070707u) | ((x & 0x38383838u) << 1);
+}
+constexpr uint32_t kBias3 = 0x924924u;   // bit 2 of every 3-bit field: c -> c + 4
+
+// ---------------------------------------------------------------------------------------
+// Query preparation: q' = H q, q = rint(q' * 32000 / max|q'|), two signed digits, packed in
+// the QK operand layout. One wave per (kv head, sequence); lane 16 g + c owns query head c of
+// the group and dimensions [32 g, 32 g + 32).
+// ---------------------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(64) void q_prep_kernel(DecodeParams p) {
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x, col = lane & 15, g = lane >> 4;
+  if (col >= p.group) return;   // partner lanes (same column) exit together
+  const int64_t row = (int64_t)b * p.hq + (int64_t)kvh * p.group + col;
+  const uint4* src = reinterpret_cast<const uint4*>(p.q + row * D + 32 * g);
+  float x[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 w = src[i];
+    x[8 * i + 0] = bf16_lo(w.x); x[8 * i + 1] = bf16_hi(w.x);
+    x[8 * i + 2] = bf16_lo(w.y); x[8 * i + 3] = bf16_hi(w.y);
+    x[8 * i + 4] = bf16_lo(w.z); x[8 * i + 5] = bf16_hi(w.z);
+    x[8 * i + 6] = bf16_lo(w.w); x[8 * i + 7] = bf16_hi(w.w);
+  }
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      if ((e & h) == 0) {
+        const float a = x[e], c = x[e + h];
+        x[e] = a + c;
+        x[e + h] = a - c;
+      }
+    }
+  }
+  // stages h = 32, 64: the partner of dimension 32 g + e is lane ^ 16, lane ^ 32
+#pragma unroll
+  for (int m = 16; m <= 32; m <<= 1) {
+    const bool upper = (lane & m) != 0;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const float other = __shfl_xor(x[e], m);
+      x[e] = upper ? other - x[e] : x[e] + other;
+    }
+  }
+  float am = 0.f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    x[e] *= kRotC;
+    am = fmaxf(am, fabsf(x[e]));
+  }
+  am = fmaxf(am, __shfl_xor(am, 16));
+  am = fmaxf(am, __shfl_xor(am, 32));
+  const float inv = am > 0.f ? kQiMax / am : 0.f;
+  int qi[32];
+  int sum = 0;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    qi[e] = (int)rintf(x[e] * inv);
+    sum += qi[e];
+  }
+  sum += __shfl_xor(sum, 16);
+  sum += __shfl_xor(sum, 32);
+  // operand m (k-chunk), digit dg, dword w, byte b holds dimension
+  //   turbo4/3: 32 g + 8 w + 2 b + m      turbo8: 32 g + 16 m + 4 w + b
+  uint32_t word[2][2][4];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const int e = (DT == 8) ? (16 * m + 4 * w + bb) : (8 * w + 2 * bb + m);
+        const int q = qi[e];
+        const int d0 = ((q + 128) & 255) - 128;
+        const int d1 = (q - d0) >> 8;
+        lo |= (uint32_t)(d0 & 255) << (8 * bb);
+        hi |= (uint32_t)(d1 & 255) << (8 * bb);
+      }
+      word[m][0][w] = lo;
+      word[m][1][w] = hi;
+    }
+  }
+  uint4* dst = reinterpret_cast<uint4*>(p.qdig + (row * 4 + g) * 64);
+  dst[0] = make_uint4(word[0][0][0], word[0][0][1], word[0][0][2], word[0][0][3]);
+  dst[1] = make_uint4(word[0][1][0], word[0][1][1], word[0][1][2], word[0][1][3]);
+  dst[2] = make_uint4(word[1][0][0], word[1][0][1], word[1][0][2], word[1][0][3]);
+  dst[3] = make_uint4(word[1][1][0], word[1][1][1], word[1][1][2], word[1][1][3]);
+  if (g == 0) {
+    p.qscale[row] = am > 0.f ? (am / kQiMax) * p.softmax_scale * kLog2e : 0.f;
+    p.qoff[row] = Codec<DT>::kKBias * sum;
+  }
 }
 
-// Raw per-lane data of one 16-token step.
-template <int DT> struct Raw {
-  uint32_t k[Fmt<DT>::kRaw];
-  uint32_t v[Fmt<DT>::kRaw];
-  uint32_t ks, vs;
+// ---------------------------------------------------------------------------------------
+// Raw bytes of one 32-token tile as one lane holds them.
+// ---------------------------------------------------------------------------------------
+template <int DT> struct Tile;
+template <> struct Tile<4> { uint32_t k[2][4]; uint32_t v[8]; uint2 ks[2], vs[2]; };
+template <> struct Tile<3> { uint32_t k[2][3]; uint32_t v[8][2]; uint2 ks[2], vs[2]; };
+template <> struct Tile<8> { uint32_t k[2][8]; uint32_t v[8][2]; uint2 ks[2], vs[2]; };
+template <> struct Tile<0> { uint32_t k[2][16]; uint32_t v[8][4]; };
+
+// Wave-uniform addresses of one tile: for each 16-token half, the first code row of the half
+// in the K and V blocks of its page. Lane offsets are added as 32-bit values, so the loads
+// take the scalar-base form and the per-tile address work is scalar.
+struct TileAddr {
+  const uint8_t* k[2];
+  const uint8_t* v[2];
+};
+
+// Loop-invariant lane offsets (bytes) from a half's first row.
+struct LaneOffsets {
+  uint32_t k;      // this lane's K bytes: row c, dimension group g
+  uint32_t v;      // this lane's V bytes of row 4 g (rows 4 g + r follow at r * row bytes)
+  uint32_t s;      // this lane's four scales (tokens 4 g .. 4 g + 3), from the first row
 };
 
 template <int DT>
-__device__ __forceinline__ void load_raw(Raw<DT>& r, const uint8_t* kb, const uint8_t* vb,
-                                         int slot, int c, int ps) {
-  constexpr int RB = Fmt<DT>::kRow, LB = Fmt<DT>::kLane;
-  const uint8_t* kp = kb + slot * RB + c * LB;
-  const uint8_t* vp = vb + slot * RB + c * LB;
-  if constexpr (DT == 3) {
+__device__ __forceinline__ LaneOffsets lane_offsets(int col, int g, int ps) {
+  constexpr int R = Codec<DT>::kRow;
+  LaneOffsets o;
+  o.k = (uint32_t)(col * R + g * (R / 4));
+  if constexpr (DT == 4) o.v = (uint32_t)(4 * g * R + 4 * col);
+  else if constexpr (DT == 3) o.v = (uint32_t)(4 * g * R + 4 * ((3 * col) >> 2));
+  else if constexpr (DT == 8) o.v = (uint32_t)(4 * g * R + 8 * col);
+  else o.v = (uint32_t)(4 * g * R + 16 * col);
+  // scales sit after the page's ps code rows; the half starts at row `slot`, whose scale is
+  // at ps * R + 2 slot: relative to row `slot` that is ps * R - slot * R + 2 slot, folded in
+  // by the caller through the scale base pointer
+  o.s = (uint32_t)(8 * g);
+  return o;
+}
+
+template <int DT>
+__device__ __forceinline__ void load_tile(Tile<DT>& t, const TileAddr& a, const TileAddr& sc,
+                                          const LaneOffsets& o) {
+  constexpr int R = Codec<DT>::kRow;
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      r.k[i] = reinterpret_cast<const uint32_t*>(kp)[i];
-      r.v[i] = reinterpret_cast<const uint32_t*>(vp)[i];
-    }
-  } else {
+  for (int h = 0; h < 2; ++h) {
+    const uint8_t* kp = a.k[h] + o.k;
+    if constexpr (DT == 4) {
+      const uint4 x = *reinterpret_cast<const uint4*>(kp);
+      t.k[h][0] = x.x; t.k[h][1] = x.y; t.k[h][2] = x.z; t.k[h][3] = x.w;
+    } else if constexpr (DT == 3) {
+      const uint32_t* kw = reinterpret_cast<const uint32_t*>(kp);
+      t.k[h][0] = kw[0]; t.k[h][1] = kw[1]; t.k[h][2] = kw[2];
+    } else {
 #pragma unroll
-    for (int i = 0; i < Fmt<DT>::kRaw / 4; ++i) {
-      const uint4 a = reinterpret_cast<const uint4*>(kp)[i];
-      const uint4 b = reinterpret_cast<const uint4*>(vp)[i];
-      r.k[4 * i] = a.x; r.k[4 * i + 1] = a.y; r.k[4 * i + 2] = a.z; r.k[4 * i + 3] = a.w;
-      r.v[4 * i] = b.x; r.v[4 * i + 1] = b.y; r.v[4 * i + 2] = b.z; r.v[4 * i + 3] = b.w;
+      for (int i = 0; i < R / 64; ++i) {
+        const uint4 x = reinterpret_cast<const uint4*>(kp)[i];
+        t.k[h][4 * i] = x.x; t.k[h][4 * i + 1] = x.y; t.k[h][4 * i + 2] = x.z; t.k[h][4 * i + 3] = x.w;
+      }
     }
-  }
-  if constexpr (DT != 0) {
-    r.ks = reinterpret_cast<const uint16_t*>(kb + ps * RB)[slot];
-    r.vs = reinterpret_cast<const uint16_t*>(vb + ps * RB)[slot];
-  } else {
-    r.ks = r.vs = 0;
+    if constexpr (DT != 0) {
+      t.ks[h] = *reinterpret_cast<const uint2*>(sc.k[h] + o.s);
+      t.vs[h] = *reinterpret_cast<const uint2*>(sc.v[h] + o.s);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = 4 * h + r;
+      const uint8_t* vp = a.v[h] + o.v + r * R;
+      if constexpr (DT == 4) {
+        t.v[j] = *reinterpret_cast<const uint32_t*>(vp);
+      } else if constexpr (DT == 3) {
+        // dims 8c..8c+7 are bits [24c, 24c+24) of the row; the second dword of the last
+        // group lies in the next row or the block's scale area, both inside the block
+        t.v[j][0] = reinterpret_cast<const uint32_t*>(vp)[0];
+        t.v[j][1] = reinterpret_cast<const uint32_t*>(vp)[1];
+      } else if constexpr (DT == 8) {
+        const uint2 x = *reinterpret_cast<const uint2*>(vp);
+        t.v[j][0] = x.x; t.v[j][1] = x.y;
+      } else {
+        const uint4 x = *reinterpret_cast<const uint4*>(vp);
+        t.v[j][0] = x.x; t.v[j][1] = x.y; t.v[j][2] = x.z; t.v[j][3] = x.w;
+      }
+    }
   }
 }
 
-template <int DT, int G>
-struct State {
-  float m[G], l[G], ws[G];
-  float acc[G][32];
+// K code bytes of one half for the two k-chunks of the QK MFMA.
+template <int DT>
+__device__ __forceinline__ void k_operands(const Tile<DT>& t, int h, v4i& a0, v4i& a1) {
+  if constexpr (DT == 4) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t u = t.k[h][w] ^ 0x88888888u;   // two's complement nibble -> c + 8
+      a0[w] = (int)(u & 0x0f0f0f0fu);                 // dims 32g + 8w + 2b
+      a1[w] = (int)((u >> 4) & 0x0f0f0f0fu);          // dims 32g + 8w + 2b + 1
+    }
+  } else if constexpr (DT == 3) {
+    const uint32_t d0 = t.k[h][0], d1 = t.k[h][1], d2 = t.k[h][2];
+    const uint32_t grp[4] = {d0 & 0xffffffu, __builtin_amdgcn_alignbit(d1, d0, 24) & 0xffffffu,
+                             __builtin_amdgcn_alignbit(d2, d1, 16) & 0xffffffu, d2 >> 8};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t n = spread3to4(grp[w] ^ kBias3);  // c + 4 per nibble
+      a0[w] = (int)(n & 0x0f0f0f0fu);
+      a1[w] = (int)((n >> 4) & 0x0f0f0f0fu);
+    }
+  } else {  // turbo8: signed bytes as stored
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      a0[w] = (int)t.k[h][w];
+      a1[w] = (int)t.k[h][4 + w];
+    }
+  }
+}
+
+// V codes of the eight token slots as bytes whose top bits hold (code + bias): byte i of e[j]
+// is dimension 8 c + 2 i (turbo8: 8 c + i), of o[j] dimension 8 c + 2 i + 1 (turbo8: 8 c + 4 + i).
+// Paired with a zero byte, such a byte is an fp16 subnormal, exactly (code + bias) * 2^-kVShift.
+// The matrix cores keep full precision only when that subnormal's mantissa has few leading
+// zeros, so the 4-bit (3-bit) codes are placed in the top bits of the byte.
+template <int DT>
+__device__ __forceinline__ void v_bytes(const Tile<DT>& t, uint32_t (&e)[8], uint32_t (&o)[8], int col) {
+  if constexpr (DT == 4) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t u = t.v[j] ^ 0x88888888u;      // c + 8 per nibble
+      e[j] = (u << 4) & 0xf0f0f0f0u;                // even dims, (c + 8) << 4
+      o[j] = u & 0xf0f0f0f0u;                       // odd dims, already in the high nibble
+    }
+  } else if constexpr (DT == 3) {
+    const uint32_t sh = (24u * col) & 31u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t x = __builtin_amdgcn_alignbit(t.v[j][1], t.v[j][0], sh) & 0xffffffu;
+      const uint32_t n = spread3to4(x ^ kBias3);    // c + 4 per nibble (0..7)
+      e[j] = (n << 5) & 0xe0e0e0e0u;                // (c + 4) << 5
+      o[j] = (n << 1) & 0xe0e0e0e0u;
+    }
+  } else if constexpr (DT == 8) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      e[j] = t.v[j][0] ^ 0x80808080u;               // c + 128
+      o[j] = t.v[j][1] ^ 0x80808080u;
+    }
+  }
+}
+
+template <int DT>
+struct WaveState {
+  v4f acc[8];          // PV accumulators: lane (g, c) reg r = head 4g + r, dimension 8c + tau
+  float m;             // reference of head c (log2 domain)
+  float l;             // partial sum of p over this lane's tokens
+  float ps;            // partial sum of P' (bias removal)
 };
 
-// One 16-token step for one lane: scores, online softmax, value accumulation.
-template <int DT, int G>
-__device__ __forceinline__ void process(const Raw<DT>& r, bool valid,
-                                        const uint32_t (&qr)[G][Fmt<DT>::kDig][Fmt<DT>::kQdw],
-                                        const float (&qs)[G], State<DT, G>& st) {
-  // ---- scores z (log2 domain) ----------------------------------------------------------
-  float z[G];
-  if constexpr (DT == 4 || DT == 3) {
-    uint32_t kc[4];
-    if constexpr (DT == 4) {
+// One 32-token tile: QK, online softmax, PV.
+template <int DT, bool kFull>
+__device__ __forceinline__ void process_tile(const Tile<DT>& t, WaveState<DT>& st,
+                                             const v4i (&qi)[2][2], const v8bf (&qb)[4],
+                                             float qs, int qoff, int lim, int col, int g) {
+  // ---- scores: y = log2-domain score, w = y + log2(s_v) ------------------------------------
+  float y[8], w[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kc[i] = r.k[i];
+  for (int h = 0; h < 2; ++h) {
+    if constexpr (DT != 0) {
+      v4i a0, a1;
+      k_operands<DT>(t, h, a0, a1);
+      const v4i z = {0, 0, 0, 0};
+      v4i s0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, qi[0][0], z, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, qi[1][0], s0, 0, 0, 0);
+      v4i s1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, qi[0][1], z, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, qi[1][1], s1, 0, 0, 0);
+      const uint32_t ks[4] = {t.ks[h].x, t.ks[h].x >> 16, t.ks[h].y, t.ks[h].y >> 16};
+      const uint32_t vs[4] = {t.vs[h].x, t.vs[h].x >> 16, t.vs[h].y, t.vs[h].y >> 16};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int zi = (s1[r] << 8) + s0[r] - qoff;
+        const float sk = half_lo(ks[r]);
+        const float sv = half_lo(vs[r]);
+        y[4 * h + r] = (float)zi * (qs * sk);
+        w[4 * h + r] = y[4 * h + r] + __builtin_amdgcn_logf(fmaxf(sv, kTinyScale));
+      }
     } else {
-      kc[0] = r.k[0] & 0xffffffu;
-      kc[1] = __builtin_amdgcn_alignbit(r.k[1], r.k[0], 24) & 0xffffffu;
-      kc[2] = __builtin_amdgcn_alignbit(r.k[2], r.k[1], 16) & 0xffffffu;
-      kc[3] = r.k[2] >> 8;
+      v4f s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kc[i] = spread3to4(kc[i]);
+      for (int m = 0; m < 4; ++m) {
+        const v8bf a = __builtin_bit_cast(v8bf, make_uint4(t.k[h][4 * m], t.k[h][4 * m + 1],
+                                                           t.k[h][4 * m + 2], t.k[h][4 * m + 3]));
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[m], s, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        y[4 * h + r] = s[r] * qs;
+        w[4 * h + r] = y[4 * h + r];
+      }
     }
-    const float sk = half_bits_to_f32(r.ks);
+  }
+  if constexpr (!kFull) {
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      int a[4] = {0, 0, 0, 0};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int dg = 0; dg < 4; ++dg) a[dg] = __builtin_amdgcn_sdot8((int)qr[j][dg][i], (int)kc[i], a[dg], false);
-      }
-      int s = a[0] + (a[1] << 4) + (a[2] << 8) + (a[3] << 12);
-      s += quad_xor1(s);
-      s += quad_xor2(s);
-      z[j] = valid ? (float)s * (sk * qs[j]) : -INFINITY;
-    }
-  } else if constexpr (DT == 8) {
-    const float sk = half_bits_to_f32(r.ks);
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      int a[3] = {0, 0, 0};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-#pragma unroll
-        for (int dg = 0; dg < 3; ++dg) a[dg] = __builtin_amdgcn_sdot4((int)qr[j][dg][i], (int)r.k[i], a[dg], false);
-      }
-#pragma unroll
-      for (int dg = 0; dg < 3; ++dg) {
-        a[dg] += quad_xor1(a[dg]);
-        a[dg] += quad_xor2(a[dg]);
-      }
-      const float s = (float)a[2] * 65536.f + ((float)a[1] * 256.f + (float)a[0]);
-      z[j] = valid ? s * (sk * qs[j]) : -INFINITY;
-    }
-  } else {  // bf16: q and k are bf16, exact products summed in fp32
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      float a = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, qr[j][0][i]),
-                                            __builtin_bit_cast(v2bf, r.k[i]), a, false);
-      }
-      a += quad_xor1f(a);
-      a += quad_xor2f(a);
-      z[j] = valid ? a * qs[j] : -INFINITY;
+    for (int j = 0; j < 8; ++j) {
+      const bool ok = 16 * (j >> 2) + (j & 3) < lim;
+      y[j] = ok ? y[j] : -INFINITY;
+      w[j] = ok ? w[j] : -INFINITY;
     }
   }
 
-  // ---- online softmax with a lazily moved reference ----------------------------------
-  bool need = false;
+  // ---- lazily moved reference -------------------------------------------------------------
+  float mx = w[0];
 #pragma unroll
-  for (int j = 0; j < G; ++j) need |= z[j] > st.m[j] + kLazy;
-  if (__builtin_expect(__any(need), 0)) {
+  for (int j = 1; j < 8; ++j) mx = fmaxf(mx, w[j]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const bool up = mx > st.m + kLazy;
+  if (__builtin_expect(__any(up), 0)) {
+    const float f = up ? __builtin_amdgcn_exp2f(st.m - mx) : 1.f;
+    st.m = up ? mx : st.m;
+    st.l *= f;
+    st.ps *= f;
+    float fr[4];
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const bool up = z[j] > st.m[j] + kLazy;
-      const float f = up ? __builtin_amdgcn_exp2f(st.m[j] - z[j]) : 1.f;
-      st.m[j] = up ? z[j] : st.m[j];
-      st.l[j] *= f;
-      st.ws[j] *= f;
+    for (int r = 0; r < 4; ++r) fr[r] = __shfl(f, 4 * g + r);
 #pragma unroll
-      for (int d = 0; d < 32; ++d) st.acc[j][d] *= f;
-    }
-  }
-  float w[G];
-  const float sv = (DT == 0) ? 1.f : half_bits_to_f32(r.vs);
+    for (int tau = 0; tau < 8; ++tau)
 #pragma unroll
-  for (int j = 0; j < G; ++j) {
-    const float pj = valid ? __builtin_amdgcn_exp2f(z[j] - st.m[j]) : 0.f;
-    st.l[j] += pj;
-    w[j] = valid ? pj * sv : 0.f;
-    st.ws[j] += w[j];
+      for (int r = 0; r < 4; ++r) st.acc[tau][r] *= fr[r];
   }
 
-  // ---- values --------------------------------------------------------------------------
-  float v[32];
-  if constexpr (DT == 4 || DT == 3) {
-    uint32_t vc[4];
-    if constexpr (DT == 4) {
+  // ---- weights --------------------------------------------------------------------------------
+  float pw[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vc[i] = r.v[i];
+  for (int j = 0; j < 8; ++j) {
+    pw[j] = __builtin_amdgcn_exp2f(w[j] - st.m);
+    st.l += (DT != 0) ? __builtin_amdgcn_exp2f(y[j] - st.m) : pw[j];
+  }
+  uint32_t ahi[4], alo[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if constexpr (DT != 0) {
+      const auto hi2 = __builtin_amdgcn_cvt_pkrtz(pw[2 * k], pw[2 * k + 1]);
+      const float h0 = (float)hi2[0], h1 = (float)hi2[1];
+      const auto lo2 = __builtin_amdgcn_cvt_pkrtz(pw[2 * k] - h0, pw[2 * k + 1] - h1);
+      ahi[k] = __builtin_bit_cast(uint32_t, hi2);
+      alo[k] = __builtin_bit_cast(uint32_t, lo2);
+      // the bias is removed with the weights exactly as the MFMAs see them
+      st.ps += (h0 + (float)lo2[0]) + (h1 + (float)lo2[1]);
     } else {
-      vc[0] = r.v[0] & 0xffffffu;
-      vc[1] = __builtin_amdgcn_alignbit(r.v[1], r.v[0], 24) & 0xffffffu;
-      vc[2] = __builtin_amdgcn_alignbit(r.v[2], r.v[1], 16) & 0xffffffu;
-      vc[3] = r.v[2] >> 8;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vc[i] = spread3to4(vc[i]);
+      const uint32_t b0 = __float_as_uint(pw[2 * k]), b1 = __float_as_uint(pw[2 * k + 1]);
+      const float r0 = pw[2 * k] - __uint_as_float(b0 & 0xffff0000u);
+      const float r1 = pw[2 * k + 1] - __uint_as_float(b1 & 0xffff0000u);
+      ahi[k] = perm(b1, b0, 0x07060302u);
+      alo[k] = perm(__float_as_uint(r1), __float_as_uint(r0), 0x07060302u);
     }
+  }
+
+  // ---- PV -----------------------------------------------------------------------------------
+  if constexpr (DT != 0) {
+    const v8h Ahi = __builtin_bit_cast(v8h, make_uint4(ahi[0], ahi[1], ahi[2], ahi[3]));
+    const v8h Alo = __builtin_bit_cast(v8h, make_uint4(alo[0], alo[1], alo[2], alo[3]));
+    uint32_t e[8], o[8];
+    v_bytes<DT>(t, e, o, col);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t x = vc[i] ^ 0x88888888u;     // code + 8, 0..15 per nibble
-      const uint32_t e = x & 0x0f0f0f0fu;          // nibbles 0,2,4,6
-      const uint32_t o = (x >> 4) & 0x0f0f0f0fu;   // nibbles 1,3,5,7
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        v[8 * i + 2 * k] = (float)((e >> (8 * k)) & 0xffu);
-        v[8 * i + 2 * k + 1] = (float)((o >> (8 * k)) & 0xffu);
+    for (int tau = 0; tau < 8; ++tau) {
+      const uint32_t* src;
+      int i;
+      if constexpr (DT == 8) {
+        src = tau < 4 ? e : o;
+        i = tau & 3;
+      } else {
+        src = (tau & 1) ? o : e;
+        i = tau >> 1;
       }
-    }
-  } else if constexpr (DT == 8) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t x = r.v[i] ^ 0x80808080u;    // code + 128
-#pragma unroll
-      for (int k = 0; k < 4; ++k) v[4 * i + k] = (float)((x >> (8 * k)) & 0xffu);
+      const uint32_t sel = (uint32_t)i | (0x0cu << 8) | ((uint32_t)(4 + i) << 16) | (0x0cu << 24);
+      const v8h B = __builtin_bit_cast(v8h, make_uint4(perm(src[1], src[0], sel), perm(src[3], src[2], sel),
+                                                       perm(src[5], src[4], sel), perm(src[7], src[6], sel)));
+      st.acc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, B, st.acc[tau], 0, 0, 0);
+      st.acc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, B, st.acc[tau], 0, 0, 0);
     }
   } else {
+    const v8bf Ahi = __builtin_bit_cast(v8bf, make_uint4(ahi[0], ahi[1], ahi[2], ahi[3]));
+    const v8bf Alo = __builtin_bit_cast(v8bf, make_uint4(alo[0], alo[1], alo[2], alo[3]));
+    uint32_t vv[8][4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t x = valid ? r.v[i] : 0u;     // unwritten slots may hold NaN patterns
-      v[2 * i] = bf16_lo(x);
-      v[2 * i + 1] = bf16_hi(x);
+    for (int j = 0; j < 8; ++j) {
+      const bool ok = kFull || (16 * (j >> 2) + (j & 3) < lim);   // unwritten slots may be NaN
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vv[j][i] = ok ? t.v[j][i] : 0u;
     }
-  }
 #pragma unroll
-  for (int j = 0; j < G; ++j) {
-#pragma unroll
-    for (int d = 0; d < 32; ++d) st.acc[j][d] = fmaf(w[j], v[d], st.acc[j][d]);
+    for (int tau = 0; tau < 8; ++tau) {
+      const int i = tau >> 1;
+      const uint32_t sel = (tau & 1) ? 0x07060302u : 0x05040100u;
+      const v8bf B = __builtin_bit_cast(v8bf, make_uint4(perm(vv[1][i], vv[0][i], sel), perm(vv[3][i], vv[2][i], sel),
+                                                         perm(vv[5][i], vv[4][i], sel), perm(vv[7][i], vv[6][i], sel)));
+      st.acc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ahi, B, st.acc[tau], 0, 0, 0);
+      st.acc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Alo, B, st.acc[tau], 0, 0, 0);
+    }
   }
 }
 
-template <int G>
-__device__ void fwht_lds(float (*x)[D + 4], int tid) {
-  // in-place unnormalized FWHT of G rows of 128 floats; ends with a barrier
+__device__ void fwht_lds(float (*x)[D + 4], int rows, int tid) {
+  // in-place unnormalized FWHT of `rows` rows of 128 floats; ends with a barrier
   for (int h = 1; h < D; h <<= 1) {
     __syncthreads();
-    for (int k = tid; k < G * 64; k += kThreads) {
+    for (int k = tid; k < rows * 64; k += kThreads) {
       const int j = k >> 6, r = k & 63;
       const int i = ((r / h) * 2 * h) + (r % h);
       const float a = x[j][i], b = x[j][i + h];
@@ -286,11 +505,11 @@ __device__ void fwht_lds(float (*x)[D + 4], int tid) {
   __syncthreads();
 }
 
-template <int DT, int G>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
-  using F = Fmt<DT>;
+template <int DT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(DecodeParams p) {
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
+  const int G = p.group;
   const int qh0 = kvh * G;
   const int L = min(p.context_lens[b], p.max_context_len);
   float* outp = p.out + ((int64_t)b * p.hq + qh0) * D;
@@ -305,165 +524,125 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   const int tok_end = min(L, tok_begin + tps);
   const int nsplit_b = (L + tps - 1) / tps;
 
-  __shared__ float qf[G][D + 4];
-  __shared__ uint32_t qd[G][F::kDig][F::kQtot];
-  __shared__ float qsc[G];
-  __shared__ float red[kWaves][G][D + 4];
-
-  // ---- query: load, rotate, quantize -----------------------------------------------------
-  const uint16_t* qp = p.q + ((int64_t)b * p.hq + qh0) * D;
-  if constexpr (DT == 0) {
-    for (int k = tid; k < G * 64; k += kThreads)
-      qd[k >> 6][0][k & 63] = reinterpret_cast<const uint32_t*>(qp)[k];
-    if (tid < G) qsc[tid] = p.softmax_scale * kLog2e;
-    __syncthreads();
-  } else {
-    for (int k = tid; k < G * D; k += kThreads) qf[k >> 7][k & 127] = __uint_as_float((uint32_t)qp[k] << 16);
-    fwht_lds<G>(qf, tid);
-    constexpr float qimax = (DT == 8) ? kQiMax8 : kQiMax4;
-    const int lane = tid & 63, wv = tid >> 6;
-    for (int j = wv; j < G; j += kWaves) {
-      const float a0 = qf[j][lane] * kRotC, a1 = qf[j][lane + 64] * kRotC;
-      float am = fmaxf(fabsf(a0), fabsf(a1));
-      for (int msk = 1; msk < 64; msk <<= 1) am = fmaxf(am, __shfl_xor(am, msk));
-      const float inv = am > 0.f ? qimax / am : 0.f;
-      // q integers, kept as floats (exact: |q| < 2^24)
-      qf[j][lane] = rintf(a0 * inv);
-      qf[j][lane + 64] = rintf(a1 * inv);
-      if (lane == 0) qsc[j] = am > 0.f ? (am / qimax) * p.softmax_scale * kLog2e : 0.f;
-    }
-    __syncthreads();
-    // pack digits: turbo4/3 -> dword i holds dims 8i..8i+7, one signed nibble each;
-    // turbo8 -> dword i holds dims 4i..4i+3, one signed byte each
-    for (int k = tid; k < G * F::kDig * F::kQtot; k += kThreads) {
-      const int j = k / (F::kDig * F::kQtot);
-      const int dg = (k / F::kQtot) % F::kDig;
-      const int i = k % F::kQtot;
-      uint32_t word = 0;
-      if constexpr (DT == 8) {
-        for (int e = 0; e < 4; ++e) {
-          int q = (int)qf[j][4 * i + e];
-          int dgt = 0;
-          for (int t = 0; t <= dg; ++t) {
-            dgt = ((q + 128) & 255) - 128;
-            q = (q - dgt) >> 8;
-          }
-          word |= (uint32_t)(dgt & 0xff) << (8 * e);
-        }
-      } else {
-        for (int e = 0; e < 8; ++e) {
-          int q = (int)qf[j][8 * i + e];
-          int dgt = 0;
-          for (int t = 0; t <= dg; ++t) {
-            dgt = ((q + 8) & 15) - 8;
-            q = (q - dgt) >> 4;
-          }
-          word |= (uint32_t)(dgt & 0xf) << (4 * e);
-        }
-      }
-      qd[j][dg][i] = word;
-    }
-    __syncthreads();
-  }
+  __shared__ float red[kWaves][kMaxGroup][D + 4];
+  __shared__ float ob[kMaxGroup][D + 4];
 
   const int lane = tid & 63;
-  const int t = lane >> 2, c = lane & 3;
+  const int col = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  uint32_t qr[G][F::kDig][F::kQdw];
-  float qs[G];
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    qs[j] = qsc[j];
-#pragma unroll
-    for (int dg = 0; dg < F::kDig; ++dg)
-#pragma unroll
-      for (int i = 0; i < F::kQdw; ++i) qr[j][dg][i] = qd[j][dg][c * F::kQdw + i];
+
+  // ---- query operands ---------------------------------------------------------------------
+  v4i qi[2][2] = {};
+  v8bf qb[4] = {};
+  float qs = 0.f;
+  int qoff = 0;
+  if (col < G) {
+    const int64_t row = (int64_t)b * p.hq + qh0 + col;
+    if constexpr (DT != 0) {
+      const v4i* s = reinterpret_cast<const v4i*>(p.qdig + (row * 4 + g) * 64);
+      qi[0][0] = s[0]; qi[0][1] = s[1]; qi[1][0] = s[2]; qi[1][1] = s[3];
+      qs = p.qscale[row];
+      qoff = p.qoff[row];
+    } else {
+      const v8bf* s = reinterpret_cast<const v8bf*>(p.q + row * D + 32 * g);
+      qb[0] = s[0]; qb[1] = s[1]; qb[2] = s[2]; qb[3] = s[3];
+      qs = p.softmax_scale * kLog2e;
+    }
   }
 
-  State<DT, G> st;
+  WaveState<DT> st;
 #pragma unroll
-  for (int j = 0; j < G; ++j) {
-    st.m[j] = -INFINITY;
-    st.l[j] = 0.f;
-    st.ws[j] = 0.f;
-#pragma unroll
-    for (int d = 0; d < 32; ++d) st.acc[j][d] = 0.f;
-  }
+  for (int tau = 0; tau < 8; ++tau) st.acc[tau] = v4f{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+  st.ps = 0.f;
 
-  // ---- main loop: wave w takes 16-token steps w, w+4, ... ------------------------------
-  const int nsteps = (tok_end - tok_begin + 15) >> 4;
+  // ---- main loop: wave w takes tiles w, w + 4, ...; two tiles in flight -------------------
+  const int ntiles = (tok_end - tok_begin + 31) >> 5;
   const int ps = p.page_size;
+  const int last_page = (L - 1) >> p.page_shift;
   const int64_t head_off = (int64_t)kvh * p.block_bytes;
   const int32_t* bt = p.block_tables + (int64_t)b * p.maxp;
-  auto block_of = [&](int tok0, const uint8_t* pool) {
-    const int phys = bt[tok0 >> p.page_shift];
-    return pool + (int64_t)phys * p.page_stride + head_off;
-  };
-  int s = wave;
-  if (s < nsteps) {
-    Raw<DT> cur;
-    int tok0 = tok_begin + (s << 4);
-    load_raw<DT>(cur, block_of(tok0, p.k_pool), block_of(tok0, p.v_pool), (tok0 & (ps - 1)) + t, c, ps);
-    for (; s < nsteps; s += kWaves) {
-      Raw<DT> nxt;
-      const int tok1 = tok0 + (kWaves << 4);
-      const bool more = s + kWaves < nsteps;
-      if (more)
-        load_raw<DT>(nxt, block_of(tok1, p.k_pool), block_of(tok1, p.v_pool), (tok1 & (ps - 1)) + t, c, ps);
-      process<DT, G>(cur, tok0 + t < tok_end, qr, qs, st);
-      if (more) cur = nxt;
-      tok0 = tok1;
+  const LaneOffsets lo = lane_offsets<DT>(col, g, ps);
+  constexpr int R = Codec<DT>::kRow;
+  // row bases (a) and scale bases (sc) of the two halves of the tile starting at t0
+  auto addr = [&](int t0, TileAddr& a, TileAddr& sc) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int th = t0 + 16 * h;
+      const int lp = min(th >> p.page_shift, last_page);   // never read a table entry past the context
+      const int phys = __builtin_amdgcn_readfirstlane(bt[lp]);
+      const int slot = th & (ps - 1);
+      const int64_t off = (int64_t)phys * p.page_stride + head_off;
+      a.k[h] = p.k_pool + off + slot * R;
+      a.v[h] = p.v_pool + off + slot * R;
+      sc.k[h] = p.k_pool + off + ps * R + 2 * slot;
+      sc.v[h] = p.v_pool + off + ps * R + 2 * slot;
     }
+  };
+  auto fetch = [&](Tile<DT>& t, int i) {
+    TileAddr a, sc;
+    addr(tok_begin + 32 * i, a, sc);
+    load_tile<DT>(t, a, sc, lo);
+  };
+  auto run = [&](const Tile<DT>& t, int t0) {
+    const int lim = tok_end - t0 - 4 * g;
+    if (t0 + 32 <= tok_end)
+      process_tile<DT, true>(t, st, qi, qb, qs, qoff, lim, col, g);
+    else
+      process_tile<DT, false>(t, st, qi, qb, qs, qoff, lim, col, g);
+  };
+  Tile<DT> ta, tb;
+  int it = wave;
+  if (it < ntiles) fetch(ta, it);
+  while (it < ntiles) {
+    if (it + kWaves < ntiles) fetch(tb, it + kWaves);
+    run(ta, tok_begin + 32 * it);
+    it += kWaves;
+    if (it >= ntiles) break;
+    if (it + kWaves < ntiles) fetch(ta, it + kWaves);
+    run(tb, tok_begin + 32 * it);
+    it += kWaves;
   }
 
-  // ---- merge the 16 token lanes of each dim chunk ---------------------------------------
+  // ---- merge: lanes of a head, then the four waves -------------------------------------------
+  st.l += __shfl_xor(st.l, 16);
+  st.l += __shfl_xor(st.l, 32);
+  st.ps += __shfl_xor(st.ps, 16);
+  st.ps += __shfl_xor(st.ps, 32);
 #pragma unroll
-  for (int j = 0; j < G; ++j) {
-    float mx = st.m[j];
+  for (int tau = 0; tau < 8; ++tau)
 #pragma unroll
-    for (int msk = 4; msk < 64; msk <<= 1) mx = fmaxf(mx, __shfl_xor(mx, msk));
-    const float f = (st.m[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(st.m[j] - mx);
-    float l = st.l[j] * f;
-    const float off = F::kOff * st.ws[j];
-#pragma unroll
-    for (int d = 0; d < 32; ++d) st.acc[j][d] = (st.acc[j][d] - off) * f;
-#pragma unroll
-    for (int msk = 4; msk < 64; msk <<= 1) {
-      l += __shfl_xor(l, msk);
-#pragma unroll
-      for (int d = 0; d < 32; ++d) st.acc[j][d] += __shfl_xor(st.acc[j][d], msk);
-    }
-    if (t == 0) {
-#pragma unroll
-      for (int d = 0; d < 32; ++d) red[wave][j][32 * c + d] = st.acc[j][d];
-      if (c == 0) {
-        red[wave][j][D] = mx;
-        red[wave][j][D + 1] = l;
-      }
-    }
+    for (int r = 0; r < 4; ++r)
+      if (4 * g + r < G) red[wave][4 * g + r][8 * col + tau] = st.acc[tau][r];
+  if (g == 0 && col < G) {
+    red[wave][col][D] = st.m;
+    red[wave][col][D + 1] = st.l;
+    red[wave][col][D + 2] = st.ps;
   }
   __syncthreads();
 
-  // ---- merge the 4 waves ------------------------------------------------------------------
   const bool single = nsplit_b == 1;
+  const float unit = (float)(1 << Codec<DT>::kVShift);
+  constexpr float bias = (float)Codec<DT>::kVBias;
   for (int k = tid; k < G * D; k += kThreads) {
     const int j = k >> 7, d = k & 127;
     float mx = -INFINITY;
 #pragma unroll
     for (int wv = 0; wv < kWaves; ++wv) mx = fmaxf(mx, red[wv][j][D]);
-    float acc = 0.f, l = 0.f;
+    float num = 0.f, l = 0.f;
 #pragma unroll
     for (int wv = 0; wv < kWaves; ++wv) {
       const float mw = red[wv][j][D];
       const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - mx);
-      acc += red[wv][j][d] * f;
+      num += (red[wv][j][d] * unit - bias * red[wv][j][D + 2]) * f;
       l += red[wv][j][D + 1] * f;
     }
     if (single) {
-      qf[j][d] = acc / l;
+      ob[j][d] = num / l;
     } else {
       float* part = p.partials + (((int64_t)b * p.hq + qh0 + j) * p.nsplits + split) * kPartialStride;
-      part[4 + d] = acc;
+      part[4 + d] = num;
       if (d == 0) {
         part[0] = mx;
         part[1] = l;
@@ -472,11 +651,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   }
   if (!single) return;
   if constexpr (DT != 0) {
-    fwht_lds<G>(qf, tid);
-    for (int k = tid; k < G * D; k += kThreads) outp[k] = qf[k >> 7][k & 127] * kRotC;
+    fwht_lds(ob, G, tid);
+    for (int k = tid; k < G * D; k += kThreads) outp[k] = ob[k >> 7][k & 127] * kRotC;
   } else {
     __syncthreads();
-    for (int k = tid; k < G * D; k += kThreads) outp[k] = qf[k >> 7][k & 127];
+    for (int k = tid; k < G * D; k += kThreads) outp[k] = ob[k >> 7][k & 127];
   }
 }
 
@@ -517,39 +696,24 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
   }
 }
 
-template <int DT, int G>
-hipError_t launch_g(const DecodeParams& p, hipStream_t stream) {
-  dim3 grid(p.nsplits, p.hkv, p.batch);
-  hipLaunchKernelGGL((decode_split_kernel<DT, G>), grid, dim3(kThreads), 0, stream, p);
-  if (p.nsplits > 1) {
-    hipLaunchKernelGGL((decode_combine_kernel<DT>), dim3(p.hq, p.batch), dim3(128), 0, stream, p);
-  }
-  return hipGetLastError();
-}
-
 template <int DT>
-hipError_t launch_dt(int g, const DecodeParams& p, hipStream_t stream) {
-  switch (g) {
-    case 1: return launch_g<DT, 1>(p, stream);
-    case 2: return launch_g<DT, 2>(p, stream);
-    case 3: return launch_g<DT, 3>(p, stream);
-    case 4: return launch_g<DT, 4>(p, stream);
-    case 5: return launch_g<DT, 5>(p, stream);
-    case 6: return launch_g<DT, 6>(p, stream);
-    case 7: return launch_g<DT, 7>(p, stream);
-    case 8: return launch_g<DT, 8>(p, stream);
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_dt(const DecodeParams& p, hipStream_t stream) {
+  if constexpr (DT != 0)
+    hipLaunchKernelGGL((q_prep_kernel<DT>), dim3(p.hkv, p.batch), dim3(64), 0, stream, p);
+  hipLaunchKernelGGL((decode_split_kernel<DT>), dim3(p.nsplits, p.hkv, p.batch), dim3(kThreads), 0, stream, p);
+  if (p.nsplits > 1)
+    hipLaunchKernelGGL((decode_combine_kernel<DT>), dim3(p.hq, p.batch), dim3(128), 0, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode(int dtype, int group, const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_decode(int dtype, const DecodeParams& p, hipStream_t stream) {
   switch (dtype) {
-    case 0: return launch_dt<0>(group, p, stream);
-    case 8: return launch_dt<8>(group, p, stream);
-    case 4: return launch_dt<4>(group, p, stream);
-    case 3: return launch_dt<3>(group, p, stream);
+    case 0: return launch_dt<0>(p, stream);
+    case 8: return launch_dt<8>(p, stream);
+    case 4: return launch_dt<4>(p, stream);
+    case 3: return launch_dt<3>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

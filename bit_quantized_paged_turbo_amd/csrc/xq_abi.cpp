@@ -46,7 +46,7 @@ int64_t block_bytes_of(const xq_cache_layout* L) {
   return (bytes + 15) & ~int64_t(15);
 }
 
-// Tokens per split: page aligned, a multiple of 16. hint > 0 asks for that many splits of
+// Tokens per split: page aligned and a multiple of 32 (one tile of the decode kernel). hint > 0 asks for that many splits of
 // the longest sequence; 0 sizes splits so that the grid has about 2048 workgroups
 // (8 per compute unit on 256 CUs), with 64..1024 tokens per split.
 int32_t plan_tokens_per_split(const xq_cache_layout* L, int32_t batch, int32_t max_ctx, int32_t hint) {
@@ -60,8 +60,8 @@ int32_t plan_tokens_per_split(const xq_cache_layout* L, int32_t batch, int32_t m
     tps = 64;
     while (tps < want && tps < 1024) tps <<= 1;
   }
-  tps = ((tps + ps - 1) / ps) * ps;
-  if (tps < ps) tps = ps;
+  const int64_t unit = ps > 32 ? ps : 32;   // whole pages and whole 32-token tiles
+  tps = ((tps + unit - 1) / unit) * unit;
   if (tps > (int64_t)1 << 30) tps = (int64_t)1 << 30;
   return (int32_t)tps;
 }
@@ -98,8 +98,7 @@ int64_t xq_decode_workspace_bytes(const xq_cache_layout* layout, int32_t batch, 
                                   int32_t max_context_len, int32_t num_splits_hint) {
   const int32_t ns = xq_decode_num_splits(layout, batch, num_q_heads, max_context_len, num_splits_hint);
   if (ns < 0) return -1;
-  if (ns <= 1) return 0;
-  return (int64_t)batch * num_q_heads * ns * xq::kPartialStride * (int64_t)sizeof(float);
+  return xq::workspace_layout(layout->kv_dtype, batch, num_q_heads, ns).total;
 }
 
 const char* xq_status_string(int32_t status) {
@@ -177,14 +176,15 @@ xq_status xq_paged_decode_attention(const xq_cache_layout* layout, const void* q
   const int32_t ctx = max_context_len > 0 ? max_context_len : 1;
   const int32_t tps = plan_tokens_per_split(layout, batch, ctx, num_splits_hint);
   const int32_t nsplits = (ctx + tps - 1) / tps;
-  const int64_t need = nsplits > 1 ? (int64_t)batch * num_q_heads * nsplits * xq::kPartialStride * 4 : 0;
-  if (need > 0) {
-    if (!workspace || workspace_bytes < need)
-      return fail(XQ_EWORKSPACE, "workspace of %lld bytes needed, %lld given", (long long)need,
+  if (nsplits > 65535) return fail(XQ_EUNSUPPORTED, "%d splits > 65535", nsplits);
+  const xq::WorkspaceLayout ws = xq::workspace_layout(layout->kv_dtype, batch, num_q_heads, nsplits);
+  if (ws.total > 0) {
+    if (!workspace || workspace_bytes < ws.total)
+      return fail(XQ_EWORKSPACE, "workspace of %lld bytes needed, %lld given", (long long)ws.total,
                   (long long)workspace_bytes);
     if (!aligned16(workspace)) return fail(XQ_EINVAL, "workspace must be 16-byte aligned");
   }
-  if (nsplits > 65535) return fail(XQ_EUNSUPPORTED, "%d splits > 65535", nsplits);
+  uint8_t* wsp = static_cast<uint8_t*>(workspace);
 
   xq::DecodeParams p{};
   p.q = static_cast<const uint16_t*>(q);
@@ -193,12 +193,16 @@ xq_status xq_paged_decode_attention(const xq_cache_layout* layout, const void* q
   p.block_tables = block_tables;
   p.context_lens = context_lens;
   p.out = out;
-  p.partials = static_cast<float*>(workspace);
+  p.qdig = ws.qdig_bytes ? wsp + ws.qdig_off : nullptr;
+  p.qscale = ws.qaux_bytes ? reinterpret_cast<float*>(wsp + ws.qaux_off) : nullptr;
+  p.qoff = ws.qaux_bytes ? reinterpret_cast<int32_t*>(wsp + ws.qaux_off) + (int64_t)batch * num_q_heads : nullptr;
+  p.partials = ws.part_bytes ? reinterpret_cast<float*>(wsp + ws.part_off) : nullptr;
   p.block_bytes = block_bytes_of(layout);
   p.page_stride = p.block_bytes * layout->num_kv_heads;
   p.batch = batch;
   p.hq = num_q_heads;
   p.hkv = layout->num_kv_heads;
+  p.group = g;
   p.page_size = layout->page_size;
   p.page_shift = __builtin_ctz((unsigned)layout->page_size);
   p.maxp = max_pages_per_seq;
@@ -206,7 +210,7 @@ xq_status xq_paged_decode_attention(const xq_cache_layout* layout, const void* q
   p.nsplits = nsplits;
   p.max_context_len = max_context_len;
   p.softmax_scale = softmax_scale;
-  const hipError_t e = xq::launch_decode(layout->kv_dtype, g, p, static_cast<hipStream_t>(stream));
+  const hipError_t e = xq::launch_decode(layout->kv_dtype, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(XQ_EHIP, "decode launch: %s", hipGetErrorString(e));
   return XQ_OK;
 }

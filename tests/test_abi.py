@@ -51,13 +51,18 @@ def test_invalid_layouts(lib, bad):
 def test_split_planning(lib):
     L = xq.CacheLayout(3, 8, 64, 4096)
     assert xq.xq_decode_num_splits(L, 1, 40, 262144, 256) == 256
-    assert xq.xq_decode_workspace_bytes(L, 1, 40, 262144, 256) == 40 * 256 * 132 * 4
+    # query digits (256 B) and scale/offset (8 B) per (sequence, q head), then the partials
+    qdig, qaux = 40 * 256, 512
+    assert xq.xq_decode_workspace_bytes(L, 1, 40, 262144, 256) == qdig + qaux + 40 * 256 * 132 * 4
     L = xq.CacheLayout(4, 8, 16, 9000)
     assert xq.xq_decode_num_splits(L, 256, 16, 1022, 0) == 1
-    assert xq.xq_decode_workspace_bytes(L, 256, 16, 1022, 0) == 0
+    assert xq.xq_decode_workspace_bytes(L, 256, 16, 1022, 0) == 256 * 16 * 256 + 256 * 16 * 8
     assert xq.xq_decode_num_splits(L, 4, 16, 1000, 7) == 7
     assert xq.xq_decode_num_splits(L, 4, 16, 0, 0) == 1
     assert xq.xq_decode_num_splits(L, 4, 16, 100, -1) == -1
+    # bf16 needs no query preparation: no workspace for a single split
+    L = xq.CacheLayout(0, 8, 16, 9000)
+    assert xq.xq_decode_workspace_bytes(L, 256, 16, 1022, 0) == 0
 
 
 def _decode_status(lib, L, **kw):
@@ -73,11 +78,11 @@ def _decode_status(lib, L, **kw):
 def test_decode_argument_errors(lib):
     L = xq.CacheLayout(4, 2, 16, 10)
     assert _decode_status(lib, L, hq=7) == xq.EINVAL           # not a multiple of Hkv
-    assert _decode_status(lib, L, hq=18) == xq.EUNSUPPORTED    # group 9 > 8
+    assert _decode_status(lib, L, hq=34) == xq.EUNSUPPORTED    # group 17 > 16
     assert _decode_status(lib, L, q=None) == xq.EINVAL
     assert _decode_status(lib, L, k=8) == xq.EINVAL            # misaligned pool
     assert _decode_status(lib, L, maxctx=65) == xq.EINVAL      # > maxp * page_size
-    assert _decode_status(lib, L, splits=2) == xq.EWORKSPACE   # partials need a workspace
+    assert _decode_status(lib, L, splits=2) == xq.EWORKSPACE   # query digits and partials
     assert b"workspace" in lib.xq_last_error()
     assert _decode_status(lib, L, batch=0) == xq.OK            # nothing to do
     bad = xq.CacheLayout(4, 2, 20, 10)
