@@ -18,25 +18,26 @@
 //
 //   QK  v_mfma_i32_16x16x64_i8. Rows = 16 tokens, columns = the g query heads of the kv head
 //       (g <= 16). The rotated query is rounded to an integer q (|q| <= 32000, one fp32 scale
-//       per head) and split into two signed 8-bit digits, q = 256 d1 + d0; the K codes enter
-//       as bytes (turbo4/3 with a +8/+4 bias so a nibble is an unsigned byte, turbo8 as its
-//       signed byte). The integer dot products are exact; the bias is removed with the digit
-//       sums. Two MFMAs per digit cover the 128 dimensions.
+//       per head) and split into two signed 8-bit digits, q = 256 d1 + d0. A K code c enters
+//       as the signed byte c * 2^(8 - bits) (the code's bits moved to the top of the byte:
+//       two instructions per four codes, no bias), so the integer dot products are exact up
+//       to that power of two, folded into the query scale. Two MFMAs per digit cover 128 dims.
 //   PV  v_mfma_f32_16x16x32_f16. Rows = heads, k = 32 tokens, columns = 16 dimensions (eight
 //       MFMAs cover 128). The weight of token t for head h is P'[h,t] = p[h,t] * s_v[t], split
 //       into an fp16 high part (round toward zero) and the fp16 remainder; each enters its own
 //       MFMA, so the weights carry ~22 bits. A V code c enters as an fp16 subnormal whose
-//       mantissa holds (c + bias) in its top bits, exact, made with one byte permute per pair
-//       of tokens; the bias is removed at the end with sum(P'). (Measured on gfx950: with the
-//       code in the low mantissa bits instead, the accumulating MFMA loses up to 2^-13 of a
-//       code step; in the top bits of the low byte the loss is below 2^-18.)
+//       mantissa holds (c + bias) in the top bits of its low byte, exact, made with one byte
+//       permute per pair of tokens. The same weights times the bias alone accumulate in one
+//       more tile (two MFMAs against a constant operand) and are subtracted at the end.
+//       (Measured on gfx950: with the code in the low mantissa bits instead, the accumulating
+//       MFMA loses up to 2^-13 of a code step; in the top bits of the low byte below 2^-18.)
 //   bf16 cache: q and K are bf16 operands of v_mfma_f32_16x16x32_bf16 (exact products), the
 //       weights are split into bf16 high and low parts against bf16 V.
 //
-// Online softmax runs in the log2 domain against a per-head reference m that moves only when
-// a score beats it by more than 2^8. For turbo caches the reference tracks
-// w = score + log2(s_v), so every fp16 weight P' = 2^(w - m) is at most 2^8 whatever the
-// scales are; the normaliser sum(p) uses p = 2^(score - m) in fp32.
+// Online softmax runs in the log2 domain against a per-head reference that moves only when a
+// score beats it by more than 2^8. For turbo caches the reference tracks score + e(s_v), e the
+// fp16 exponent field of the value scale, so every fp16 weight P' stays below 2^15 whatever
+// the scales are, while the normaliser sum(p) is kept in fp32.
 //
 // Work split: one workgroup of four waves per (split, kv head, sequence); wave w takes the
 // 32-token tiles w, w+4, ... of the split and keeps its own softmax state; a tile is two
@@ -45,7 +46,9 @@
 // coalesced 1 KB block at turbo4 / page size 16), and for V the c-th 4-byte group of the rows
 // of tokens 4 g + r, which is the transposed operand the PV MFMA needs. Scores come out of the
 // QK MFMA exactly where the PV MFMA wants its weights (lane l: head c, tokens 4 g + r), so no
-// data moves between the two products. Tiles are double-buffered in registers.
+// data moves between the two products. Loads are buffer loads against a per-page resource
+// descriptor (scalar base and bound, constant lane offsets: no per-tile address arithmetic in
+// the vector unit, and a read past the page block returns zero); tiles are double-buffered.
 //
 // The query digits are prepared once per (sequence, query head) by q_prep_kernel (rotation by
 // an in-register FWHT, scaling, digit split, packing in the operand layout) into the workspace.
@@ -64,34 +67,35 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRotC = 0x1.6a09e6p-4f;   // fp32 nearest to 1/sqrt(128)
 constexpr float kLazy = 8.0f;             // rescale only when a score beats m by > 2^8
 constexpr float kQiMax = 32000.f;         // |q| bound for two signed 8-bit digits
-constexpr float kTinyScale = 0x1p-40f;    // log2 floor for zero value scales
+constexpr float kWeightExp = 21.f;        // P' < 2^(w - m + 7): at most 2^15 in fp16
+constexpr int kBufferConfig = 0x00020000;   // gfx9 buffer descriptor word 3
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v3i __attribute__((ext_vector_type(3)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
-// Per cache type: bytes of a code row, bias of K codes in the QK product, bias of V codes
-// in the PV product, and the power of two a V operand carries ((c + bias) * 2^-kVShift).
+// Per cache type: bytes of a code row; the power of two a K code carries in its QK byte
+// (c * kKMul); the bias of V codes and the power of two a V operand carries
+// ((c + bias) * 2^-kVShift).
 template <int DT> struct Codec;
-template <> struct Codec<4> { static constexpr int kRow = 64, kKBias = 8, kVBias = 8, kVShift = 20; };
-template <> struct Codec<3> { static constexpr int kRow = 48, kKBias = 4, kVBias = 4, kVShift = 19; };
-template <> struct Codec<8> { static constexpr int kRow = 128, kKBias = 0, kVBias = 128, kVShift = 24; };
-template <> struct Codec<0> { static constexpr int kRow = 256, kKBias = 0, kVBias = 0, kVShift = 0; };
+template <> struct Codec<4> { static constexpr int kRow = 64, kKMul = 16, kVBias = 8, kVShift = 20; };
+template <> struct Codec<3> { static constexpr int kRow = 48, kKMul = 32, kVBias = 4, kVShift = 19; };
+template <> struct Codec<8> { static constexpr int kRow = 128, kKMul = 1, kVBias = 128, kVShift = 24; };
+template <> struct Codec<0> { static constexpr int kRow = 256, kKMul = 1, kVBias = 0, kVShift = 0; };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float half_lo(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
 }
-__device__ __forceinline__ float half_hi(uint32_t w) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-}
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// Eight 3-bit fields of a 24-bit value (each already biased to 0..7) -> eight nibbles.
+// Eight 3-bit fields of a 24-bit value -> eight nibbles (fields in bits 0..2 of each).
 __device__ __forceinline__ uint32_t spread3to4(uint32_t x) {
   x = (x & 0xfffu) | ((x & 0xfff000u) << 4);
   x = (x & 0x003f003fu) | ((x & 0x0fc00fc0u) << 2);
@@ -101,15 +105,17 @@ constexpr uint32_t kBias3 = 0x924924u;   // bit 2 of every 3-bit field: c -> c +
 
 // ---------------------------------------------------------------------------------------
 // Query preparation: q' = H q, q = rint(q' * 32000 / max|q'|), two signed digits, packed in
-// the QK operand layout. One wave per (kv head, sequence); lane 16 g + c owns query head c of
-// the group and dimensions [32 g, 32 g + 32).
+// the QK operand layout. Four lanes per (sequence, query head) row, lane g owning dimensions
+// [32 g, 32 g + 32); sixteen rows per wave.
 // ---------------------------------------------------------------------------------------
+constexpr int kPrepThreads = 256;
+
 template <int DT>
-__global__ __launch_bounds__(64) void q_prep_kernel(DecodeParams p) {
-  const int kvh = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x, col = lane & 15, g = lane >> 4;
-  if (col >= p.group) return;   // partner lanes (same column) exit together
-  const int64_t row = (int64_t)b * p.hq + (int64_t)kvh * p.group + col;
+__global__ __launch_bounds__(kPrepThreads) void q_prep_kernel(DecodeParams p) {
+  const int64_t t = (int64_t)blockIdx.x * kPrepThreads + threadIdx.x;
+  const int64_t row = t >> 2;                      // b * hq + j
+  const int g = (int)(t & 3);
+  if (row >= (int64_t)p.batch * p.hq) return;      // the four lanes of a row exit together
   const uint4* src = reinterpret_cast<const uint4*>(p.q + row * D + 32 * g);
   float x[32];
 #pragma unroll
@@ -131,10 +137,10 @@ __global__ __launch_bounds__(64) void q_prep_kernel(DecodeParams p) {
       }
     }
   }
-  // stages h = 32, 64: the partner of dimension 32 g + e is lane ^ 16, lane ^ 32
+  // stages h = 32, 64: the partner of dimension 32 g + e is lane ^ 1, lane ^ 2
 #pragma unroll
-  for (int m = 16; m <= 32; m <<= 1) {
-    const bool upper = (lane & m) != 0;
+  for (int m = 1; m <= 2; m <<= 1) {
+    const bool upper = (g & m) != 0;
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
       const float other = __shfl_xor(x[e], m);
@@ -147,18 +153,12 @@ __global__ __launch_bounds__(64) void q_prep_kernel(DecodeParams p) {
     x[e] *= kRotC;
     am = fmaxf(am, fabsf(x[e]));
   }
-  am = fmaxf(am, __shfl_xor(am, 16));
-  am = fmaxf(am, __shfl_xor(am, 32));
+  am = fmaxf(am, __shfl_xor(am, 1));
+  am = fmaxf(am, __shfl_xor(am, 2));
   const float inv = am > 0.f ? kQiMax / am : 0.f;
   int qi[32];
-  int sum = 0;
 #pragma unroll
-  for (int e = 0; e < 32; ++e) {
-    qi[e] = (int)rintf(x[e] * inv);
-    sum += qi[e];
-  }
-  sum += __shfl_xor(sum, 16);
-  sum += __shfl_xor(sum, 32);
+  for (int e = 0; e < 32; ++e) qi[e] = (int)rintf(x[e] * inv);
   // operand m (k-chunk), digit dg, dword w, byte b holds dimension
   //   turbo4/3: 32 g + 8 w + 2 b + m      turbo8: 32 g + 16 m + 4 w + b
   uint32_t word[2][2][4];
@@ -186,8 +186,9 @@ __global__ __launch_bounds__(64) void q_prep_kernel(DecodeParams p) {
   dst[2] = make_uint4(word[1][0][0], word[1][0][1], word[1][0][2], word[1][0][3]);
   dst[3] = make_uint4(word[1][1][0], word[1][1][1], word[1][1][2], word[1][1][3]);
   if (g == 0) {
-    p.qscale[row] = am > 0.f ? (am / kQiMax) * p.softmax_scale * kLog2e : 0.f;
-    p.qoff[row] = Codec<DT>::kKBias * sum;
+    // a K byte is c * kKMul, so the integer dot product is kKMul times q.c
+    p.qscale[row] = am > 0.f ? (am / kQiMax) * p.softmax_scale * kLog2e / (float)Codec<DT>::kKMul : 0.f;
+    p.qoff[row] = 0;
   }
 }
 
@@ -195,136 +196,118 @@ __global__ __launch_bounds__(64) void q_prep_kernel(DecodeParams p) {
 // Raw bytes of one 32-token tile as one lane holds them.
 // ---------------------------------------------------------------------------------------
 template <int DT> struct Tile;
-template <> struct Tile<4> { uint32_t k[2][4]; uint32_t v[8]; uint2 ks[2], vs[2]; };
-template <> struct Tile<3> { uint32_t k[2][3]; uint32_t v[8][2]; uint2 ks[2], vs[2]; };
-template <> struct Tile<8> { uint32_t k[2][8]; uint32_t v[8][2]; uint2 ks[2], vs[2]; };
-template <> struct Tile<0> { uint32_t k[2][16]; uint32_t v[8][4]; };
+template <> struct Tile<4> { v4i k[2]; int v[8]; v2i ks[2], vs[2]; };
+template <> struct Tile<3> { v3i k[2]; v2i v[8]; v2i ks[2], vs[2]; };
+template <> struct Tile<8> { v4i k[2][2]; v2i v[8]; v2i ks[2], vs[2]; };
+template <> struct Tile<0> { v4i k[2][4]; v4i v[8]; };
 
-// Wave-uniform addresses of one tile: for each 16-token half, the first code row of the half
-// in the K and V blocks of its page. Lane offsets are added as 32-bit values, so the loads
-// take the scalar-base form and the per-tile address work is scalar.
-struct TileAddr {
-  const uint8_t* k[2];
-  const uint8_t* v[2];
+// Wave-uniform view of one 16-token half of a tile: buffer descriptors of the page's K and V
+// blocks, the byte offset of the half's first code row and of its first scale.
+struct HalfAddr {
+  __amdgpu_buffer_rsrc_t k, v;
+  int row, scale;
 };
 
-// Loop-invariant lane offsets (bytes) from a half's first row.
+// Loop-invariant lane offsets (bytes) from a half's first row (K, V) or first scale.
 struct LaneOffsets {
-  uint32_t k;      // this lane's K bytes: row c, dimension group g
-  uint32_t v;      // this lane's V bytes of row 4 g (rows 4 g + r follow at r * row bytes)
-  uint32_t s;      // this lane's four scales (tokens 4 g .. 4 g + 3), from the first row
+  int k;      // this lane's K bytes: row c, dimension group g
+  int v;      // this lane's V bytes of row 4 g (rows 4 g + r follow at r * row bytes)
+  int s;      // this lane's four scales (tokens 4 g .. 4 g + 3)
 };
 
 template <int DT>
-__device__ __forceinline__ LaneOffsets lane_offsets(int col, int g, int ps) {
+__device__ __forceinline__ LaneOffsets lane_offsets(int col, int g) {
   constexpr int R = Codec<DT>::kRow;
   LaneOffsets o;
-  o.k = (uint32_t)(col * R + g * (R / 4));
-  if constexpr (DT == 4) o.v = (uint32_t)(4 * g * R + 4 * col);
-  else if constexpr (DT == 3) o.v = (uint32_t)(4 * g * R + 4 * ((3 * col) >> 2));
-  else if constexpr (DT == 8) o.v = (uint32_t)(4 * g * R + 8 * col);
-  else o.v = (uint32_t)(4 * g * R + 16 * col);
-  // scales sit after the page's ps code rows; the half starts at row `slot`, whose scale is
-  // at ps * R + 2 slot: relative to row `slot` that is ps * R - slot * R + 2 slot, folded in
-  // by the caller through the scale base pointer
-  o.s = (uint32_t)(8 * g);
+  o.k = col * R + g * (R / 4);
+  if constexpr (DT == 4) o.v = 4 * g * R + 4 * col;
+  else if constexpr (DT == 3) o.v = 4 * g * R + 4 * ((3 * col) >> 2);
+  else if constexpr (DT == 8) o.v = 4 * g * R + 8 * col;
+  else o.v = 4 * g * R + 16 * col;
+  o.s = 8 * g;
   return o;
 }
 
 template <int DT>
-__device__ __forceinline__ void load_tile(Tile<DT>& t, const TileAddr& a, const TileAddr& sc,
-                                          const LaneOffsets& o) {
+__device__ __forceinline__ void load_tile(Tile<DT>& t, const HalfAddr (&a)[2], const LaneOffsets& o) {
   constexpr int R = Codec<DT>::kRow;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const uint8_t* kp = a.k[h] + o.k;
     if constexpr (DT == 4) {
-      const uint4 x = *reinterpret_cast<const uint4*>(kp);
-      t.k[h][0] = x.x; t.k[h][1] = x.y; t.k[h][2] = x.z; t.k[h][3] = x.w;
+      t.k[h] = __builtin_amdgcn_raw_buffer_load_b128(a[h].k, o.k, a[h].row, 0);
     } else if constexpr (DT == 3) {
-      const uint32_t* kw = reinterpret_cast<const uint32_t*>(kp);
-      t.k[h][0] = kw[0]; t.k[h][1] = kw[1]; t.k[h][2] = kw[2];
+      t.k[h] = __builtin_amdgcn_raw_buffer_load_b96(a[h].k, o.k, a[h].row, 0);
+    } else if constexpr (DT == 8) {
+      t.k[h][0] = __builtin_amdgcn_raw_buffer_load_b128(a[h].k, o.k, a[h].row, 0);
+      t.k[h][1] = __builtin_amdgcn_raw_buffer_load_b128(a[h].k, o.k + 16, a[h].row, 0);
     } else {
 #pragma unroll
-      for (int i = 0; i < R / 64; ++i) {
-        const uint4 x = reinterpret_cast<const uint4*>(kp)[i];
-        t.k[h][4 * i] = x.x; t.k[h][4 * i + 1] = x.y; t.k[h][4 * i + 2] = x.z; t.k[h][4 * i + 3] = x.w;
-      }
+      for (int i = 0; i < 4; ++i)
+        t.k[h][i] = __builtin_amdgcn_raw_buffer_load_b128(a[h].k, o.k + 16 * i, a[h].row, 0);
     }
     if constexpr (DT != 0) {
-      t.ks[h] = *reinterpret_cast<const uint2*>(sc.k[h] + o.s);
-      t.vs[h] = *reinterpret_cast<const uint2*>(sc.v[h] + o.s);
+      t.ks[h] = __builtin_amdgcn_raw_buffer_load_b64(a[h].k, o.s, a[h].scale, 0);
+      t.vs[h] = __builtin_amdgcn_raw_buffer_load_b64(a[h].v, o.s, a[h].scale, 0);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = 4 * h + r;
-      const uint8_t* vp = a.v[h] + o.v + r * R;
       if constexpr (DT == 4) {
-        t.v[j] = *reinterpret_cast<const uint32_t*>(vp);
-      } else if constexpr (DT == 3) {
-        // dims 8c..8c+7 are bits [24c, 24c+24) of the row; the second dword of the last
-        // group lies in the next row or the block's scale area, both inside the block
-        t.v[j][0] = reinterpret_cast<const uint32_t*>(vp)[0];
-        t.v[j][1] = reinterpret_cast<const uint32_t*>(vp)[1];
-      } else if constexpr (DT == 8) {
-        const uint2 x = *reinterpret_cast<const uint2*>(vp);
-        t.v[j][0] = x.x; t.v[j][1] = x.y;
+        t.v[j] = __builtin_amdgcn_raw_buffer_load_b32(a[h].v, o.v + r * R, a[h].row, 0);
+      } else if constexpr (DT == 3 || DT == 8) {
+        // turbo3: dims 8c..8c+7 are bits [24c, 24c+24) of the row; the second dword of the
+        // last group lies in the next row or the block's scale area, both inside the block
+        t.v[j] = __builtin_amdgcn_raw_buffer_load_b64(a[h].v, o.v + r * R, a[h].row, 0);
       } else {
-        const uint4 x = *reinterpret_cast<const uint4*>(vp);
-        t.v[j][0] = x.x; t.v[j][1] = x.y; t.v[j][2] = x.z; t.v[j][3] = x.w;
+        t.v[j] = __builtin_amdgcn_raw_buffer_load_b128(a[h].v, o.v + r * R, a[h].row, 0);
       }
     }
   }
 }
 
-// K code bytes of one half for the two k-chunks of the QK MFMA.
+// K codes of one half as QK operand bytes c * kKMul, for the two k-chunks of the MFMA.
 template <int DT>
 __device__ __forceinline__ void k_operands(const Tile<DT>& t, int h, v4i& a0, v4i& a1) {
   if constexpr (DT == 4) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const uint32_t u = t.k[h][w] ^ 0x88888888u;   // two's complement nibble -> c + 8
-      a0[w] = (int)(u & 0x0f0f0f0fu);                 // dims 32g + 8w + 2b
-      a1[w] = (int)((u >> 4) & 0x0f0f0f0fu);          // dims 32g + 8w + 2b + 1
+      const uint32_t x = (uint32_t)t.k[h][w];
+      a0[w] = (int)((x << 4) & 0xf0f0f0f0u);        // dims 32g + 8w + 2b: 16 c
+      a1[w] = (int)(x & 0xf0f0f0f0u);               // dims 32g + 8w + 2b + 1: 16 c
     }
   } else if constexpr (DT == 3) {
-    const uint32_t d0 = t.k[h][0], d1 = t.k[h][1], d2 = t.k[h][2];
-    const uint32_t grp[4] = {d0 & 0xffffffu, __builtin_amdgcn_alignbit(d1, d0, 24) & 0xffffffu,
-                             __builtin_amdgcn_alignbit(d2, d1, 16) & 0xffffffu, d2 >> 8};
+    const uint32_t d0 = (uint32_t)t.k[h][0], d1 = (uint32_t)t.k[h][1], d2 = (uint32_t)t.k[h][2];
+    const uint32_t grp[4] = {d0, __builtin_amdgcn_alignbit(d1, d0, 24), __builtin_amdgcn_alignbit(d2, d1, 16),
+                             d2 >> 8};
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const uint32_t n = spread3to4(grp[w] ^ kBias3);  // c + 4 per nibble
-      a0[w] = (int)(n & 0x0f0f0f0fu);
-      a1[w] = (int)((n >> 4) & 0x0f0f0f0fu);
+      const uint32_t n = spread3to4(grp[w] & 0xffffffu);   // raw 3-bit fields per nibble
+      a0[w] = (int)((n << 5) & 0xe0e0e0e0u);               // 32 c
+      a1[w] = (int)((n << 1) & 0xe0e0e0e0u);
     }
   } else {  // turbo8: signed bytes as stored
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      a0[w] = (int)t.k[h][w];
-      a1[w] = (int)t.k[h][4 + w];
-    }
+    a0 = t.k[h][0];
+    a1 = t.k[h][1];
   }
 }
 
 // V codes of the eight token slots as bytes whose top bits hold (code + bias): byte i of e[j]
 // is dimension 8 c + 2 i (turbo8: 8 c + i), of o[j] dimension 8 c + 2 i + 1 (turbo8: 8 c + 4 + i).
 // Paired with a zero byte, such a byte is an fp16 subnormal, exactly (code + bias) * 2^-kVShift.
-// The matrix cores keep full precision only when that subnormal's mantissa has few leading
-// zeros, so the 4-bit (3-bit) codes are placed in the top bits of the byte.
 template <int DT>
 __device__ __forceinline__ void v_bytes(const Tile<DT>& t, uint32_t (&e)[8], uint32_t (&o)[8], int col) {
   if constexpr (DT == 4) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t u = t.v[j] ^ 0x88888888u;      // c + 8 per nibble
-      e[j] = (u << 4) & 0xf0f0f0f0u;                // even dims, (c + 8) << 4
-      o[j] = u & 0xf0f0f0f0u;                       // odd dims, already in the high nibble
+      const uint32_t u = (uint32_t)t.v[j] ^ 0x88888888u;   // c + 8 per nibble
+      e[j] = (u << 4) & 0xf0f0f0f0u;                       // even dims, (c + 8) << 4
+      o[j] = u & 0xf0f0f0f0u;                              // odd dims, already in the high nibble
     }
   } else if constexpr (DT == 3) {
     const uint32_t sh = (24u * col) & 31u;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t x = __builtin_amdgcn_alignbit(t.v[j][1], t.v[j][0], sh) & 0xffffffu;
+      const uint32_t x = __builtin_amdgcn_alignbit((uint32_t)t.v[j][1], (uint32_t)t.v[j][0], sh) & 0xffffffu;
       const uint32_t n = spread3to4(x ^ kBias3);    // c + 4 per nibble (0..7)
       e[j] = (n << 5) & 0xe0e0e0e0u;                // (c + 4) << 5
       o[j] = (n << 1) & 0xe0e0e0e0u;
@@ -332,27 +315,27 @@ __device__ __forceinline__ void v_bytes(const Tile<DT>& t, uint32_t (&e)[8], uin
   } else if constexpr (DT == 8) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      e[j] = t.v[j][0] ^ 0x80808080u;               // c + 128
-      o[j] = t.v[j][1] ^ 0x80808080u;
+      e[j] = (uint32_t)t.v[j][0] ^ 0x80808080u;     // c + 128
+      o[j] = (uint32_t)t.v[j][1] ^ 0x80808080u;
     }
   }
 }
 
-template <int DT>
 struct WaveState {
   v4f acc[8];          // PV accumulators: lane (g, c) reg r = head 4g + r, dimension 8c + tau
+  v4f accb;            // the same weights times the bias alone (every column equal)
   float m;             // reference of head c (log2 domain)
   float l;             // partial sum of p over this lane's tokens
-  float ps;            // partial sum of P' (bias removal)
 };
 
-// One 32-token tile: QK, online softmax, PV.
-template <int DT, bool kFull>
-__device__ __forceinline__ void process_tile(const Tile<DT>& t, WaveState<DT>& st,
+// One 32-token tile: QK, online softmax, PV. When `full` is false (the last tile of a split),
+// token slots 16 h + r >= lim are masked.
+template <int DT>
+__device__ __forceinline__ void process_tile(const Tile<DT>& t, WaveState& st,
                                              const v4i (&qi)[2][2], const v8bf (&qb)[4],
-                                             float qs, int qoff, int lim, int col, int g) {
-  // ---- scores: y = log2-domain score, w = y + log2(s_v) ------------------------------------
-  float y[8], w[8];
+                                             float qs, int lim, bool full, int col, int g) {
+  // ---- scores: y = log2-domain score; w = y + exponent field of s_v (turbo) --------------------
+  float y[8], w[8], sv[8];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     if constexpr (DT != 0) {
@@ -363,44 +346,42 @@ __device__ __forceinline__ void process_tile(const Tile<DT>& t, WaveState<DT>& s
       s0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, qi[1][0], s0, 0, 0, 0);
       v4i s1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, qi[0][1], z, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, qi[1][1], s1, 0, 0, 0);
-      const uint32_t ks[4] = {t.ks[h].x, t.ks[h].x >> 16, t.ks[h].y, t.ks[h].y >> 16};
-      const uint32_t vs[4] = {t.vs[h].x, t.vs[h].x >> 16, t.vs[h].y, t.vs[h].y >> 16};
+      const uint32_t ks[4] = {(uint32_t)t.ks[h][0], (uint32_t)t.ks[h][0] >> 16, (uint32_t)t.ks[h][1],
+                              (uint32_t)t.ks[h][1] >> 16};
+      const uint32_t vs[4] = {(uint32_t)t.vs[h][0], (uint32_t)t.vs[h][0] >> 16, (uint32_t)t.vs[h][1],
+                              (uint32_t)t.vs[h][1] >> 16};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int zi = (s1[r] << 8) + s0[r] - qoff;
-        const float sk = half_lo(ks[r]);
-        const float sv = half_lo(vs[r]);
-        y[4 * h + r] = (float)zi * (qs * sk);
-        w[4 * h + r] = y[4 * h + r] + __builtin_amdgcn_logf(fmaxf(sv, kTinyScale));
+        const int zi = (s1[r] << 8) + s0[r];
+        y[4 * h + r] = (float)zi * (qs * half_lo(ks[r]));
+        sv[4 * h + r] = half_lo(vs[r]);
+        w[4 * h + r] = y[4 * h + r] + (float)((vs[r] >> 10) & 31u);
       }
     } else {
       v4f s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const v8bf a = __builtin_bit_cast(v8bf, make_uint4(t.k[h][4 * m], t.k[h][4 * m + 1],
-                                                           t.k[h][4 * m + 2], t.k[h][4 * m + 3]));
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[m], s, 0, 0, 0);
-      }
+      for (int m = 0; m < 4; ++m)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, t.k[h][m]), qb[m], s, 0, 0, 0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         y[4 * h + r] = s[r] * qs;
         w[4 * h + r] = y[4 * h + r];
+        sv[4 * h + r] = 1.f;
       }
     }
   }
-  if constexpr (!kFull) {
+  if (!full) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const bool ok = 16 * (j >> 2) + (j & 3) < lim;
       y[j] = ok ? y[j] : -INFINITY;
       w[j] = ok ? w[j] : -INFINITY;
+      sv[j] = ok ? sv[j] : 0.f;   // unwritten slots may hold NaN patterns
     }
   }
 
   // ---- lazily moved reference -------------------------------------------------------------
-  float mx = w[0];
-#pragma unroll
-  for (int j = 1; j < 8; ++j) mx = fmaxf(mx, w[j]);
+  float mx = fmaxf(fmaxf(fmaxf(w[0], w[1]), fmaxf(w[2], w[3])), fmaxf(fmaxf(w[4], w[5]), fmaxf(w[6], w[7])));
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   const bool up = mx > st.m + kLazy;
@@ -408,34 +389,34 @@ __device__ __forceinline__ void process_tile(const Tile<DT>& t, WaveState<DT>& s
     const float f = up ? __builtin_amdgcn_exp2f(st.m - mx) : 1.f;
     st.m = up ? mx : st.m;
     st.l *= f;
-    st.ps *= f;
     float fr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) fr[r] = __shfl(f, 4 * g + r);
 #pragma unroll
-    for (int tau = 0; tau < 8; ++tau)
+    for (int r = 0; r < 4; ++r) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) st.acc[tau][r] *= fr[r];
+      for (int tau = 0; tau < 8; ++tau) st.acc[tau][r] *= fr[r];
+      st.accb[r] *= fr[r];
+    }
   }
 
-  // ---- weights --------------------------------------------------------------------------------
+  // ---- weights: p = 2^(y - m + 21) for the normaliser, P' = p * s_v for the MFMA ---------------
+  const float mref = (DT != 0) ? st.m - kWeightExp : st.m;
   float pw[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    pw[j] = __builtin_amdgcn_exp2f(w[j] - st.m);
-    st.l += (DT != 0) ? __builtin_amdgcn_exp2f(y[j] - st.m) : pw[j];
+    const float p = __builtin_amdgcn_exp2f(y[j] - mref);
+    st.l += p;
+    pw[j] = p * sv[j];
   }
   uint32_t ahi[4], alo[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     if constexpr (DT != 0) {
       const auto hi2 = __builtin_amdgcn_cvt_pkrtz(pw[2 * k], pw[2 * k + 1]);
-      const float h0 = (float)hi2[0], h1 = (float)hi2[1];
-      const auto lo2 = __builtin_amdgcn_cvt_pkrtz(pw[2 * k] - h0, pw[2 * k + 1] - h1);
+      const auto lo2 = __builtin_amdgcn_cvt_pkrtz(pw[2 * k] - (float)hi2[0], pw[2 * k + 1] - (float)hi2[1]);
       ahi[k] = __builtin_bit_cast(uint32_t, hi2);
       alo[k] = __builtin_bit_cast(uint32_t, lo2);
-      // the bias is removed with the weights exactly as the MFMAs see them
-      st.ps += (h0 + (float)lo2[0]) + (h1 + (float)lo2[1]);
     } else {
       const uint32_t b0 = __float_as_uint(pw[2 * k]), b1 = __float_as_uint(pw[2 * k + 1]);
       const float r0 = pw[2 * k] - __uint_as_float(b0 & 0xffff0000u);
@@ -449,6 +430,10 @@ __device__ __forceinline__ void process_tile(const Tile<DT>& t, WaveState<DT>& s
   if constexpr (DT != 0) {
     const v8h Ahi = __builtin_bit_cast(v8h, make_uint4(ahi[0], ahi[1], ahi[2], ahi[3]));
     const v8h Alo = __builtin_bit_cast(v8h, make_uint4(alo[0], alo[1], alo[2], alo[3]));
+    // the bias alone, (bias << (8 - bits)) in every slot: the byte 0x80 for all three types
+    const v8h Bb = __builtin_bit_cast(v8h, make_uint4(0x00800080u, 0x00800080u, 0x00800080u, 0x00800080u));
+    st.accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, Bb, st.accb, 0, 0, 0);
+    st.accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, Bb, st.accb, 0, 0, 0);
     uint32_t e[8], o[8];
     v_bytes<DT>(t, e, o, col);
 #pragma unroll
@@ -474,9 +459,9 @@ __device__ __forceinline__ void process_tile(const Tile<DT>& t, WaveState<DT>& s
     uint32_t vv[8][4];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const bool ok = kFull || (16 * (j >> 2) + (j & 3) < lim);   // unwritten slots may be NaN
+      const bool ok = full || (16 * (j >> 2) + (j & 3) < lim);   // unwritten slots may be NaN
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vv[j][i] = ok ? t.v[j][i] : 0u;
+      for (int i = 0; i < 4; ++i) vv[j][i] = ok ? (uint32_t)t.v[j][i] : 0u;
     }
 #pragma unroll
     for (int tau = 0; tau < 8; ++tau) {
@@ -506,7 +491,8 @@ __device__ void fwht_lds(float (*x)[D + 4], int rows, int tid) {
 }
 
 template <int DT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DT == 0 ? 1 : 2)))
+void decode_split_kernel(DecodeParams p) {
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int G = p.group;
@@ -535,14 +521,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   v4i qi[2][2] = {};
   v8bf qb[4] = {};
   float qs = 0.f;
-  int qoff = 0;
   if (col < G) {
     const int64_t row = (int64_t)b * p.hq + qh0 + col;
     if constexpr (DT != 0) {
       const v4i* s = reinterpret_cast<const v4i*>(p.qdig + (row * 4 + g) * 64);
       qi[0][0] = s[0]; qi[0][1] = s[1]; qi[1][0] = s[2]; qi[1][1] = s[3];
       qs = p.qscale[row];
-      qoff = p.qoff[row];
     } else {
       const v8bf* s = reinterpret_cast<const v8bf*>(p.q + row * D + 32 * g);
       qb[0] = s[0]; qb[1] = s[1]; qb[2] = s[2]; qb[3] = s[3];
@@ -550,23 +534,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
   }
 
-  WaveState<DT> st;
+  WaveState st;
 #pragma unroll
   for (int tau = 0; tau < 8; ++tau) st.acc[tau] = v4f{0.f, 0.f, 0.f, 0.f};
+  st.accb = v4f{0.f, 0.f, 0.f, 0.f};
   st.m = -INFINITY;
   st.l = 0.f;
-  st.ps = 0.f;
 
   // ---- main loop: wave w takes tiles w, w + 4, ...; two tiles in flight -------------------
+  constexpr int R = Codec<DT>::kRow;
   const int ntiles = (tok_end - tok_begin + 31) >> 5;
   const int ps = p.page_size;
   const int last_page = (L - 1) >> p.page_shift;
   const int64_t head_off = (int64_t)kvh * p.block_bytes;
   const int32_t* bt = p.block_tables + (int64_t)b * p.maxp;
-  const LaneOffsets lo = lane_offsets<DT>(col, g, ps);
-  constexpr int R = Codec<DT>::kRow;
-  // row bases (a) and scale bases (sc) of the two halves of the tile starting at t0
-  auto addr = [&](int t0, TileAddr& a, TileAddr& sc) {
+  const int nrec = (int)p.block_bytes;          // reads past the page block return zero
+  const LaneOffsets lo = lane_offsets<DT>(col, g);
+  auto addr = [&](int t0, HalfAddr (&a)[2]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int th = t0 + 16 * h;
@@ -574,57 +558,50 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       const int phys = __builtin_amdgcn_readfirstlane(bt[lp]);
       const int slot = th & (ps - 1);
       const int64_t off = (int64_t)phys * p.page_stride + head_off;
-      a.k[h] = p.k_pool + off + slot * R;
-      a.v[h] = p.v_pool + off + slot * R;
-      sc.k[h] = p.k_pool + off + ps * R + 2 * slot;
-      sc.v[h] = p.v_pool + off + ps * R + 2 * slot;
+      a[h].k = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.k_pool + off), (short)0, nrec, kBufferConfig);
+      a[h].v = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.v_pool + off), (short)0, nrec, kBufferConfig);
+      a[h].row = slot * R;
+      a[h].scale = ps * R + 2 * slot;
     }
   };
   auto fetch = [&](Tile<DT>& t, int i) {
-    TileAddr a, sc;
-    addr(tok_begin + 32 * i, a, sc);
-    load_tile<DT>(t, a, sc, lo);
+    HalfAddr a[2];
+    addr(tok_begin + 32 * i, a);
+    load_tile<DT>(t, a, lo);
   };
-  auto run = [&](const Tile<DT>& t, int t0) {
-    const int lim = tok_end - t0 - 4 * g;
-    if (t0 + 32 <= tok_end)
-      process_tile<DT, true>(t, st, qi, qb, qs, qoff, lim, col, g);
-    else
-      process_tile<DT, false>(t, st, qi, qb, qs, qoff, lim, col, g);
+  auto run = [&](const Tile<DT>& t, int i) {
+    const int t0 = tok_begin + 32 * i;
+    process_tile<DT>(t, st, qi, qb, qs, tok_end - t0 - 4 * g, t0 + 32 <= tok_end, col, g);
   };
   Tile<DT> ta, tb;
   int it = wave;
   if (it < ntiles) fetch(ta, it);
   while (it < ntiles) {
     if (it + kWaves < ntiles) fetch(tb, it + kWaves);
-    run(ta, tok_begin + 32 * it);
+    run(ta, it);
     it += kWaves;
     if (it >= ntiles) break;
     if (it + kWaves < ntiles) fetch(ta, it + kWaves);
-    run(tb, tok_begin + 32 * it);
+    run(tb, it);
     it += kWaves;
   }
 
   // ---- merge: lanes of a head, then the four waves -------------------------------------------
   st.l += __shfl_xor(st.l, 16);
   st.l += __shfl_xor(st.l, 32);
-  st.ps += __shfl_xor(st.ps, 16);
-  st.ps += __shfl_xor(st.ps, 32);
+  const float unit = (float)(1 << Codec<DT>::kVShift);
 #pragma unroll
   for (int tau = 0; tau < 8; ++tau)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (4 * g + r < G) red[wave][4 * g + r][8 * col + tau] = st.acc[tau][r];
+      if (4 * g + r < G) red[wave][4 * g + r][8 * col + tau] = (st.acc[tau][r] - st.accb[r]) * unit;
   if (g == 0 && col < G) {
     red[wave][col][D] = st.m;
     red[wave][col][D + 1] = st.l;
-    red[wave][col][D + 2] = st.ps;
   }
   __syncthreads();
 
   const bool single = nsplit_b == 1;
-  const float unit = (float)(1 << Codec<DT>::kVShift);
-  constexpr float bias = (float)Codec<DT>::kVBias;
   for (int k = tid; k < G * D; k += kThreads) {
     const int j = k >> 7, d = k & 127;
     float mx = -INFINITY;
@@ -635,7 +612,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int wv = 0; wv < kWaves; ++wv) {
       const float mw = red[wv][j][D];
       const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - mx);
-      num += (red[wv][j][d] * unit - bias * red[wv][j][D + 2]) * f;
+      num += red[wv][j][d] * f;
       l += red[wv][j][D + 1] * f;
     }
     if (single) {
@@ -659,50 +636,86 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 }
 
-// Merge split partials of one (sequence, q head) and rotate back. 128 threads, one per dim.
+// Merge split partials of one (sequence, q head) and rotate back. 256 threads: thread
+// (s0 = t / 32, d4 = t % 32) sums dimensions 4 d4 .. 4 d4 + 3 over splits s0, s0 + 8, ...
+constexpr int kCombThreads = 256;
+
 template <int DT>
-__global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodeParams p) {
   const int qh = blockIdx.x, b = blockIdx.y;
-  const int d = threadIdx.x;
+  const int t = threadIdx.x;
   const int L = min(p.context_lens[b], p.max_context_len);
-  const int nsplit_b = (L + p.tokens_per_split - 1) / p.tokens_per_split;
-  if (nsplit_b <= 1) return;  // written by the split kernel
+  const int ns = (L + p.tokens_per_split - 1) / p.tokens_per_split;
+  if (ns <= 1) return;  // written by the split kernel
   const float* part = p.partials + ((int64_t)b * p.hq + qh) * p.nsplits * kPartialStride;
-  float mx = -INFINITY;
-  for (int s = 0; s < nsplit_b; ++s) mx = fmaxf(mx, part[s * kPartialStride]);
-  float acc = 0.f, l = 0.f;
-  for (int s = 0; s < nsplit_b; ++s) {
-    const float ms = part[s * kPartialStride];
-    const float f = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - mx);
-    acc += part[s * kPartialStride + 4 + d] * f;
-    l += part[s * kPartialStride + 1] * f;
-  }
+  __shared__ float red[kCombThreads / 64];
+  __shared__ float4 accs[8][32];
+  __shared__ float lsum[8];
   __shared__ float o[D];
-  o[d] = acc / l;
+
+  // global reference M = max_s m_s
+  float mx = -INFINITY;
+  for (int s = t; s < ns; s += kCombThreads) mx = fmaxf(mx, part[(int64_t)s * kPartialStride]);
+  for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
+  if ((t & 63) == 0) red[t >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+
+  // weighted sums of l and acc
+  const int s0 = t >> 5, d4 = t & 31;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float l = 0.f;
+  for (int s = s0; s < ns; s += 8) {
+    const float* ps = part + (int64_t)s * kPartialStride;
+    const float ms = ps[0];
+    const float f = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - mx);
+    const float4 a = reinterpret_cast<const float4*>(ps + 4)[d4];
+    acc.x += a.x * f; acc.y += a.y * f; acc.z += a.z * f; acc.w += a.w * f;
+    l += ps[1] * f;   // the same for all 32 lanes of the group
+  }
+  accs[s0][d4] = acc;
+  if (d4 == 0) lsum[s0] = l;
+  __syncthreads();
+  if (t < D) {
+    float a = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float4 v = accs[k][t >> 2];
+      a += (t & 3) == 0 ? v.x : (t & 3) == 1 ? v.y : (t & 3) == 2 ? v.z : v.w;
+    }
+    float lt = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) lt += lsum[k];
+    o[t] = a / lt;
+  }
   float* outp = p.out + ((int64_t)b * p.hq + qh) * D;
   if constexpr (DT != 0) {
     for (int h = 1; h < D; h <<= 1) {
       __syncthreads();
       float a = 0.f, c = 0.f;
-      const bool lower = (d & h) == 0;
-      if (lower) { a = o[d]; c = o[d + h]; }
+      const bool lower = t < D && (t & h) == 0;
+      if (lower) { a = o[t]; c = o[t + h]; }
       __syncthreads();
-      if (lower) { o[d] = a + c; o[d + h] = a - c; }
+      if (lower) { o[t] = a + c; o[t + h] = a - c; }
     }
     __syncthreads();
-    outp[d] = o[d] * kRotC;
+    if (t < D) outp[t] = o[t] * kRotC;
   } else {
-    outp[d] = o[d];
+    __syncthreads();
+    if (t < D) outp[t] = o[t];
   }
 }
 
 template <int DT>
 hipError_t launch_dt(const DecodeParams& p, hipStream_t stream) {
-  if constexpr (DT != 0)
-    hipLaunchKernelGGL((q_prep_kernel<DT>), dim3(p.hkv, p.batch), dim3(64), 0, stream, p);
+  if constexpr (DT != 0) {
+    const int64_t lanes = (int64_t)p.batch * p.hq * 4;
+    hipLaunchKernelGGL((q_prep_kernel<DT>), dim3((unsigned)((lanes + kPrepThreads - 1) / kPrepThreads)),
+                       dim3(kPrepThreads), 0, stream, p);
+  }
   hipLaunchKernelGGL((decode_split_kernel<DT>), dim3(p.nsplits, p.hkv, p.batch), dim3(kThreads), 0, stream, p);
   if (p.nsplits > 1)
-    hipLaunchKernelGGL((decode_combine_kernel<DT>), dim3(p.hq, p.batch), dim3(128), 0, stream, p);
+    hipLaunchKernelGGL((decode_combine_kernel<DT>), dim3(p.hq, p.batch), dim3(kCombThreads), 0, stream, p);
   return hipGetLastError();
 }
 
