@@ -48,7 +48,8 @@
 // QK MFMA exactly where the PV MFMA wants its weights (lane l: head c, tokens 4 g + r), so no
 // data moves between the two products. Loads are buffer loads against a per-page resource
 // descriptor (scalar base and bound, constant lane offsets: no per-tile address arithmetic in
-// the vector unit, and a read past the page block returns zero); tiles are double-buffered.
+// the vector unit, and a read past the page block returns zero); each wave keeps three tiles
+// in flight in registers (two for bf16).
 //
 // The query digits are prepared once per (sequence, query head) by q_prep_kernel (rotation by
 // an in-register FWHT, scaling, digit split, packing in the operand layout) into the workspace.
@@ -69,6 +70,37 @@ constexpr float kLazy = 8.0f;             // rescale only when a score beats m b
 constexpr float kQiMax = 32000.f;         // |q| bound for two signed 8-bit digits
 constexpr float kWeightExp = 21.f;        // P' < 2^(w - m + 7): at most 2^15 in fp16
 constexpr int kBufferConfig = 0x00020000;   // gfx9 buffer descriptor word 3
+// Tiles in flight per wave (register path; bf16 tiles are four times larger).
+template <int DT> constexpr int kDepthOf = DT == 0 ? 2 : 3;
+
+// LDS staging of code bytes (turbo4, turbo8). Per 16-token half, the K and V code rows of the
+// half arrive by DMA (buffer_load_dwordx4 ... lds: 64 lanes x 16 B, lane i written at
+// LDS + 16 i) with per-lane source offsets chosen so that every operand read is linear in the
+// lane index (no LDS bank conflicts) and V comes out transposed. A slot holds one tile:
+// [K half 0][K half 1][V half 0][V half 1][scales: K h0, K h1, V h0, V h1, 32 B each, moved
+// by eight lanes of a dword DMA]; each wave owns kDepth slots. With everything staged, the
+// loop issues no vector loads into registers, so the only vector-memory waits in it are the
+// explicit ones below. kOps is the vector-memory instruction count of one tile (exact: those
+// waits count them).
+template <int DT> struct Stage {
+  static constexpr bool kOn = false;
+  static constexpr int kDepth = 0, kHalf = 0, kDma = 0, kOps = 0, kSlot = 0;
+};
+template <> struct Stage<4> {
+  static constexpr bool kOn = true;
+  static constexpr int kDepth = 3, kHalf = 1024, kDma = 1, kOps = 4 * kDma + 4, kSlot = 4 * kHalf + 128;
+};
+template <> struct Stage<8> {
+  static constexpr bool kOn = true;
+  static constexpr int kDepth = 2, kHalf = 2048, kDma = 2, kOps = 4 * kDma + 4, kSlot = 4 * kHalf + 128;
+};
+
+// Wait until at most N vector-memory instructions of this wave are outstanding. The memory
+// clobber keeps the compiler from moving LDS reads of a staged slot above the wait.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v3i __attribute__((ext_vector_type(3)));
@@ -265,6 +297,82 @@ __device__ __forceinline__ void load_tile(Tile<DT>& t, const HalfAddr (&a)[2], c
   }
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Per-lane source offsets of the staging DMAs (bytes from a half's first row).
+struct DmaOffsets {
+  int k[2];   // K chunk m: row c = i % 16, bytes of dimension group g = i / 16
+  int v[2];   // V chunk m: rows 4 g + r, the 16 bytes each lane of a row group needs
+};
+
+template <int DT>
+__device__ __forceinline__ DmaOffsets dma_offsets(int lane) {
+  DmaOffsets o{};
+  if constexpr (DT == 4) {
+    o.k[0] = (lane & 15) * 64 + 16 * (lane >> 4);
+    o.v[0] = (4 * ((lane >> 2) & 3) + (lane >> 4)) * 64 + 16 * (lane & 3);
+  } else if constexpr (DT == 8) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      o.k[m] = (lane & 15) * 128 + 32 * (lane >> 4) + 16 * m;
+      o.v[m] = (4 * ((lane >> 3) & 3) + 2 * m + (lane >> 5)) * 128 + 16 * (lane & 7);
+    }
+  }
+  return o;
+}
+
+// Issue the staging DMAs of one tile into `slot`.
+template <int DT>
+__device__ __forceinline__ void stage_tile(uint8_t* slot, const HalfAddr (&a)[2], const DmaOffsets& d,
+                                           int lane) {
+  using S = Stage<DT>;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int m = 0; m < S::kDma; ++m) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a[h].k, (lds_void*)(slot + h * S::kHalf + 1024 * m), 16,
+                                               d.k[m], a[h].row, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a[h].v, (lds_void*)(slot + (2 + h) * S::kHalf + 1024 * m), 16,
+                                               d.v[m], a[h].row, 0, 0);
+    }
+  }
+  // the 16 scales of each half: eight lanes, one dword each (always executed: lanes 0..7)
+  if (lane < 8) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a[h].k, (lds_void*)(slot + 4 * S::kHalf + 32 * h), 4, 4 * lane,
+                                               a[h].scale, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a[h].v, (lds_void*)(slot + 4 * S::kHalf + 64 + 32 * h), 4,
+                                               4 * lane, a[h].scale, 0, 0);
+    }
+  }
+}
+
+// Operand bytes of a staged tile, read from its slot.
+template <int DT>
+__device__ __forceinline__ void read_slot(Tile<DT>& t, const uint8_t* slot, int lane) {
+  using S = Stage<DT>;
+  const int g = lane >> 4;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    t.ks[h] = *reinterpret_cast<const v2i*>(slot + 4 * S::kHalf + 32 * h + 8 * g);
+    t.vs[h] = *reinterpret_cast<const v2i*>(slot + 4 * S::kHalf + 64 + 32 * h + 8 * g);
+    if constexpr (DT == 4) {
+      t.k[h] = *reinterpret_cast<const v4i*>(slot + h * S::kHalf + 16 * lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        t.v[4 * h + r] = *reinterpret_cast<const int*>(slot + (2 + h) * S::kHalf + 256 * r + 4 * lane);
+    } else if constexpr (DT == 8) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        t.k[h][m] = *reinterpret_cast<const v4i*>(slot + h * S::kHalf + 1024 * m + 16 * lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        t.v[4 * h + r] = *reinterpret_cast<const v2i*>(slot + (2 + h) * S::kHalf + 512 * r + 8 * lane);
+    }
+  }
+}
+
 // K codes of one half as QK operand bytes c * kKMul, for the two k-chunks of the MFMA.
 template <int DT>
 __device__ __forceinline__ void k_operands(const Tile<DT>& t, int h, v4i& a0, v4i& a1) {
@@ -335,7 +443,8 @@ __device__ __forceinline__ void process_tile(const Tile<DT>& t, WaveState& st,
                                              const v4i (&qi)[2][2], const v8bf (&qb)[4],
                                              float qs, int lim, bool full, int col, int g) {
   // ---- scores: y = log2-domain score; w = y + exponent field of s_v (turbo) --------------------
-  float y[8], w[8], sv[8];
+  float y[8], w[8];
+  uint32_t sv[8];   // fp16 value scale in the low half (1.0 for bf16)
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     if constexpr (DT != 0) {
@@ -353,8 +462,9 @@ __device__ __forceinline__ void process_tile(const Tile<DT>& t, WaveState& st,
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int zi = (s1[r] << 8) + s0[r];
-        y[4 * h + r] = (float)zi * (qs * half_lo(ks[r]));
-        sv[4 * h + r] = half_lo(vs[r]);
+        // fma with a zero addend keeps the fp16 operand in a mixed-precision fma
+        y[4 * h + r] = __builtin_fmaf(half_lo(ks[r]), (float)zi * qs, 0.f);
+        sv[4 * h + r] = vs[r];
         w[4 * h + r] = y[4 * h + r] + (float)((vs[r] >> 10) & 31u);
       }
     } else {
@@ -366,7 +476,7 @@ __device__ __forceinline__ void process_tile(const Tile<DT>& t, WaveState& st,
       for (int r = 0; r < 4; ++r) {
         y[4 * h + r] = s[r] * qs;
         w[4 * h + r] = y[4 * h + r];
-        sv[4 * h + r] = 1.f;
+        sv[4 * h + r] = 0x3c00u;
       }
     }
   }
@@ -376,16 +486,17 @@ __device__ __forceinline__ void process_tile(const Tile<DT>& t, WaveState& st,
       const bool ok = 16 * (j >> 2) + (j & 3) < lim;
       y[j] = ok ? y[j] : -INFINITY;
       w[j] = ok ? w[j] : -INFINITY;
-      sv[j] = ok ? sv[j] : 0.f;   // unwritten slots may hold NaN patterns
+      sv[j] = ok ? sv[j] : 0u;    // unwritten slots may hold NaN patterns
     }
   }
 
-  // ---- lazily moved reference -------------------------------------------------------------
+  // ---- lazily moved reference: each lane tests its own scores; only when some lane of the
+  // wave is past the threshold is the head maximum taken across the four lanes of a head ----
   float mx = fmaxf(fmaxf(fmaxf(w[0], w[1]), fmaxf(w[2], w[3])), fmaxf(fmaxf(w[4], w[5]), fmaxf(w[6], w[7])));
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const bool up = mx > st.m + kLazy;
-  if (__builtin_expect(__any(up), 0)) {
+  if (__builtin_expect(__any(mx > st.m + kLazy), 0)) {
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool up = mx > st.m + kLazy;
     const float f = up ? __builtin_amdgcn_exp2f(st.m - mx) : 1.f;
     st.m = up ? mx : st.m;
     st.l *= f;
@@ -407,14 +518,15 @@ __device__ __forceinline__ void process_tile(const Tile<DT>& t, WaveState& st,
   for (int j = 0; j < 8; ++j) {
     const float p = __builtin_amdgcn_exp2f(y[j] - mref);
     st.l += p;
-    pw[j] = p * sv[j];
+    pw[j] = __builtin_fmaf(half_lo(sv[j]), p, 0.f);
   }
   uint32_t ahi[4], alo[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     if constexpr (DT != 0) {
       const auto hi2 = __builtin_amdgcn_cvt_pkrtz(pw[2 * k], pw[2 * k + 1]);
-      const auto lo2 = __builtin_amdgcn_cvt_pkrtz(pw[2 * k] - (float)hi2[0], pw[2 * k + 1] - (float)hi2[1]);
+      const auto lo2 = __builtin_amdgcn_cvt_pkrtz(__builtin_fmaf((float)hi2[0], -1.f, pw[2 * k]),
+                                                  __builtin_fmaf((float)hi2[1], -1.f, pw[2 * k + 1]));
       ahi[k] = __builtin_bit_cast(uint32_t, hi2);
       alo[k] = __builtin_bit_cast(uint32_t, lo2);
     } else {
@@ -510,8 +622,13 @@ void decode_split_kernel(DecodeParams p) {
   const int tok_end = min(L, tok_begin + tps);
   const int nsplit_b = (L + tps - 1) / tps;
 
-  __shared__ float red[kWaves][kMaxGroup][D + 4];
-  __shared__ float ob[kMaxGroup][D + 4];
+  // the staging ring and the epilogue's merge arrays share one LDS buffer
+  constexpr int kMergeBytes = (kWaves + 1) * kMaxGroup * (D + 4) * 4;
+  constexpr int kRingBytes = kWaves * Stage<DT>::kDepth * Stage<DT>::kSlot;
+  constexpr int kSmemBytes = kMergeBytes > kRingBytes ? kMergeBytes : kRingBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+  auto red = reinterpret_cast<float (*)[kMaxGroup][D + 4]>(smem);
+  auto ob = reinterpret_cast<float (*)[D + 4]>(smem + kWaves * kMaxGroup * (D + 4) * 4);
 
   const int lane = tid & 63;
   const int col = lane & 15, g = lane >> 4;
@@ -541,13 +658,18 @@ void decode_split_kernel(DecodeParams p) {
   st.m = -INFINITY;
   st.l = 0.f;
 
-  // ---- main loop: wave w takes tiles w, w + 4, ...; two tiles in flight -------------------
+  // ---- main loop: wave w takes tiles w, w + 4, ...; kDepth tiles in flight ---------------
   constexpr int R = Codec<DT>::kRow;
+  constexpr int kDepth = kDepthOf<DT>;
   const int ntiles = (tok_end - tok_begin + 31) >> 5;
   const int ps = p.page_size;
   const int last_page = (L - 1) >> p.page_shift;
   const int64_t head_off = (int64_t)kvh * p.block_bytes;
-  const int32_t* bt = p.block_tables + (int64_t)b * p.maxp;
+  // the block table is read-only here: reading it through the constant address space keeps the
+  // per-tile page lookups on the scalar unit (a vector load would make the wave wait for every
+  // outstanding tile load before the lookup could be used)
+  const __attribute__((address_space(4))) int32_t* bt =
+      (const __attribute__((address_space(4))) int32_t*)(p.block_tables + (int64_t)b * p.maxp);
   const int nrec = (int)p.block_bytes;          // reads past the page block return zero
   const LaneOffsets lo = lane_offsets<DT>(col, g);
   auto addr = [&](int t0, HalfAddr (&a)[2]) {
@@ -555,7 +677,7 @@ void decode_split_kernel(DecodeParams p) {
     for (int h = 0; h < 2; ++h) {
       const int th = t0 + 16 * h;
       const int lp = min(th >> p.page_shift, last_page);   // never read a table entry past the context
-      const int phys = __builtin_amdgcn_readfirstlane(bt[lp]);
+      const int phys = bt[lp];
       const int slot = th & (ps - 1);
       const int64_t off = (int64_t)phys * p.page_stride + head_off;
       a[h].k = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.k_pool + off), (short)0, nrec, kBufferConfig);
@@ -573,22 +695,60 @@ void decode_split_kernel(DecodeParams p) {
     const int t0 = tok_begin + 32 * i;
     process_tile<DT>(t, st, qi, qb, qs, tok_end - t0 - 4 * g, t0 + 32 <= tok_end, col, g);
   };
-  Tile<DT> ta, tb;
-  int it = wave;
-  if (it < ntiles) fetch(ta, it);
-  while (it < ntiles) {
-    if (it + kWaves < ntiles) fetch(tb, it + kWaves);
-    run(ta, it);
-    it += kWaves;
-    if (it >= ntiles) break;
-    if (it + kWaves < ntiles) fetch(ta, it + kWaves);
-    run(tb, it);
-    it += kWaves;
+  if constexpr (Stage<DT>::kOn) {
+    // kDepth tiles in flight per wave, staged in LDS slots; slot d of this wave holds the
+    // wave's tiles d, d + kDepth, ...
+    using S = Stage<DT>;
+    const DmaOffsets dof = dma_offsets<DT>(lane);
+    uint8_t* ring = smem + wave * S::kDepth * S::kSlot;
+    auto stage = [&](int d, int i) {
+      HalfAddr a[2];
+      addr(tok_begin + 32 * i, a);
+      stage_tile<DT>(ring + d * S::kSlot, a, dof, lane);
+    };
+    Tile<DT> tile;
+#pragma unroll
+    for (int d = 0; d < S::kDepth - 1; ++d)
+      if (wave + d * kWaves < ntiles) stage(d, wave + d * kWaves);
+    for (int it = wave; it < ntiles;) {
+#pragma unroll
+      for (int d = 0; d < S::kDepth; ++d) {
+        const int ahead = it + (S::kDepth - 1) * kWaves;
+        if (ahead < ntiles) stage((d + S::kDepth - 1) % S::kDepth, ahead);
+        // this tile's instructions are complete once at most those of the tiles staged after
+        // it are outstanding
+        const int after = min(S::kDepth - 1, (ntiles - 1 - it) / kWaves);
+        if (after == 0) wait_vm<0>();
+        else if (after == 1) wait_vm<S::kOps>();
+        else wait_vm<2 * S::kOps>();
+        read_slot<DT>(tile, ring + d * S::kSlot, lane);
+        run(tile, it);
+        it += kWaves;
+        if (it >= ntiles) break;
+      }
+    }
+  } else {
+    // kDepth tiles in flight per wave: buffer (i / kWaves) % kDepth holds tile i
+    Tile<DT> tb[kDepth];
+#pragma unroll
+    for (int d = 0; d < kDepth - 1; ++d)
+      if (wave + d * kWaves < ntiles) fetch(tb[d], wave + d * kWaves);
+    for (int it = wave; it < ntiles;) {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) {
+        const int ahead = it + (kDepth - 1) * kWaves;
+        if (ahead < ntiles) fetch(tb[(d + kDepth - 1) % kDepth], ahead);
+        run(tb[d], it);
+        it += kWaves;
+        if (it >= ntiles) break;
+      }
+    }
   }
 
   // ---- merge: lanes of a head, then the four waves -------------------------------------------
   st.l += __shfl_xor(st.l, 16);
   st.l += __shfl_xor(st.l, 32);
+  __syncthreads();   // every wave is done with its staging slots, which the merge arrays reuse
   const float unit = (float)(1 << Codec<DT>::kVShift);
 #pragma unroll
   for (int tau = 0; tau < 8; ++tau)
