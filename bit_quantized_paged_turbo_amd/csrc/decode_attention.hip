@@ -39,37 +39,42 @@
 // fp16 exponent field of the value scale, so every fp16 weight P' stays below 2^15 whatever
 // the scales are, while the normaliser sum(p) is kept in fp32.
 //
-// Work split: one workgroup of four waves per (split, kv head, sequence); wave w takes the
-// 32-token tiles w, w+4, ... of the split and keeps its own softmax state; a tile is two
-// 16-token halves (two pages at page size 16). Lane l = 16 g + c loads, per half, token c's
-// K code bytes for dimensions [32 g, 32 g + 32) (a 16-lane group reads whole rows: one
-// coalesced 1 KB block at turbo4 / page size 16), and for V the c-th 4-byte group of the rows
-// of tokens 4 g + r, which is the transposed operand the PV MFMA needs. Scores come out of the
-// QK MFMA exactly where the PV MFMA wants its weights (lane l: head c, tokens 4 g + r), so no
-// data moves between the two products. Loads are buffer loads against a per-page resource
-// descriptor (scalar base and bound, constant lane offsets: no per-tile address arithmetic in
-// the vector unit, and a read past the page block returns zero); each wave keeps three tiles
-// in flight in registers (two for bf16).
+// Work split: one wave per (split, kv head, sequence), walking the split's 32-token tiles in
+// order with one softmax state; a tile is two 16-token halves (two pages at page size 16).
+// Scores come out of the QK MFMA exactly where the PV MFMA wants its weights (lane l = 16 g + c:
+// head c, tokens 4 g + r), so no data moves between the two products. Code bytes are read with
+// buffer loads against a per-page resource descriptor (scalar base and bound from a scalar
+// block-table lookup, constant lane offsets, a read past the page block returns zero). For
+// turbo4 and turbo8 the loads go straight to LDS (a ring of DEPTH tile slots per wave, DEPTH
+// picked at launch from how many waves share a compute unit), with lane offsets that leave
+// every operand read linear in the lane index and V transposed; turbo3 and bf16 load into
+// registers, three tiles (two for bf16) in flight.
 //
 // The query digits are prepared once per (sequence, query head) by q_prep_kernel (rotation by
 // an in-register FWHT, scaling, digit split, packing in the operand layout) into the workspace.
-// At the end the four waves are merged by log-sum-exp in LDS; a sequence that fits one split is
-// normalised, rotated back and stored, otherwise (m, l, acc) partials go to the workspace and
-// decode_combine_kernel merges them.
+// A sequence that fits one split is normalised, rotated back and stored by its wave; otherwise
+// (m, l, acc) partials go to the workspace and decode_combine_kernel merges them by
+// log-sum-exp, rotates back and stores.
 #include "xq_internal.h"
+
+#include <algorithm>
+#include <type_traits>
 
 namespace xq {
 namespace {
 
 constexpr int D = kHeadDim;
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kThreads = 64;              // one wave per work unit
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRotC = 0x1.6a09e6p-4f;   // fp32 nearest to 1/sqrt(128)
 constexpr float kLazy = 8.0f;             // rescale only when a score beats m by > 2^8
 constexpr float kQiMax = 32000.f;         // |q| bound for two signed 8-bit digits
 constexpr float kWeightExp = 21.f;        // P' < 2^(w - m + 7): at most 2^15 in fp16
 constexpr int kBufferConfig = 0x00020000;   // gfx9 buffer descriptor word 3
+// Cache policy of every cache read: non-temporal. Each code byte is read once per decode step,
+// so there is nothing to keep; measured on MI355X, random 1 KB page blocks stream at about
+// 6.5 TB/s with the bit and 5.5-5.8 TB/s without it.
+constexpr int kStream = 2;
 // Tiles in flight per wave (register path; bf16 tiles are four times larger).
 template <int DT> constexpr int kDepthOf = DT == 0 ? 2 : 3;
 
@@ -84,22 +89,38 @@ template <int DT> constexpr int kDepthOf = DT == 0 ? 2 : 3;
 // waits count them).
 template <int DT> struct Stage {
   static constexpr bool kOn = false;
-  static constexpr int kDepth = 0, kHalf = 0, kDma = 0, kOps = 0, kSlot = 0;
+  static constexpr int kHalf = 0, kDma = 0, kOps = 0, kSlot = 0;
 };
+// kOps: vector-memory instructions per staged tile with a pool-wide descriptor (the per-page
+// descriptor path issues two more; waiting on the smaller count is then merely conservative,
+// since loads complete in issue order).
 template <> struct Stage<4> {
   static constexpr bool kOn = true;
-  static constexpr int kDepth = 3, kHalf = 1024, kDma = 1, kOps = 4 * kDma + 4, kSlot = 4 * kHalf + 128;
+  static constexpr int kHalf = 1024, kDma = 1, kOps = 4 * kDma + 2, kSlot = 4 * kHalf + 128;
 };
 template <> struct Stage<8> {
   static constexpr bool kOn = true;
-  static constexpr int kDepth = 2, kHalf = 2048, kDma = 2, kOps = 4 * kDma + 4, kSlot = 4 * kHalf + 128;
+  static constexpr int kHalf = 2048, kDma = 2, kOps = 4 * kDma + 2, kSlot = 4 * kHalf + 128;
 };
+constexpr int kLdsPerCu = 160 * 1024;
+constexpr int kMaxVmcnt = 63;
 
 // Wait until at most N vector-memory instructions of this wave are outstanding. The memory
 // clobber keeps the compiler from moving LDS reads of a staged slot above the wait.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait for the tile that has `after` tiles (of OPS instructions each) staged behind it.
+template <int OPS, int A, int MAXA>
+__device__ __forceinline__ void wait_tiles(int after) {
+  if constexpr (A == MAXA) {
+    wait_vm<A * OPS>();
+  } else {
+    if (after == A) wait_vm<A * OPS>();
+    else wait_tiles<OPS, A + 1, MAXA>(after);
+  }
 }
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -266,32 +287,32 @@ __device__ __forceinline__ void load_tile(Tile<DT>& t, const HalfAddr (&a)[2], c
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     if constexpr (DT == 4) {
-      t.k[h] = __builtin_amdgcn_raw_buffer_load_b128(a[h].k, o.k, a[h].row, 0);
+      t.k[h] = __builtin_amdgcn_raw_buffer_load_b128(a[h].k, o.k, a[h].row, kStream);
     } else if constexpr (DT == 3) {
-      t.k[h] = __builtin_amdgcn_raw_buffer_load_b96(a[h].k, o.k, a[h].row, 0);
+      t.k[h] = __builtin_amdgcn_raw_buffer_load_b96(a[h].k, o.k, a[h].row, kStream);
     } else if constexpr (DT == 8) {
-      t.k[h][0] = __builtin_amdgcn_raw_buffer_load_b128(a[h].k, o.k, a[h].row, 0);
-      t.k[h][1] = __builtin_amdgcn_raw_buffer_load_b128(a[h].k, o.k + 16, a[h].row, 0);
+      t.k[h][0] = __builtin_amdgcn_raw_buffer_load_b128(a[h].k, o.k, a[h].row, kStream);
+      t.k[h][1] = __builtin_amdgcn_raw_buffer_load_b128(a[h].k, o.k + 16, a[h].row, kStream);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        t.k[h][i] = __builtin_amdgcn_raw_buffer_load_b128(a[h].k, o.k + 16 * i, a[h].row, 0);
+        t.k[h][i] = __builtin_amdgcn_raw_buffer_load_b128(a[h].k, o.k + 16 * i, a[h].row, kStream);
     }
     if constexpr (DT != 0) {
-      t.ks[h] = __builtin_amdgcn_raw_buffer_load_b64(a[h].k, o.s, a[h].scale, 0);
-      t.vs[h] = __builtin_amdgcn_raw_buffer_load_b64(a[h].v, o.s, a[h].scale, 0);
+      t.ks[h] = __builtin_amdgcn_raw_buffer_load_b64(a[h].k, o.s, a[h].scale, kStream);
+      t.vs[h] = __builtin_amdgcn_raw_buffer_load_b64(a[h].v, o.s, a[h].scale, kStream);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = 4 * h + r;
       if constexpr (DT == 4) {
-        t.v[j] = __builtin_amdgcn_raw_buffer_load_b32(a[h].v, o.v + r * R, a[h].row, 0);
+        t.v[j] = __builtin_amdgcn_raw_buffer_load_b32(a[h].v, o.v + r * R, a[h].row, kStream);
       } else if constexpr (DT == 3 || DT == 8) {
         // turbo3: dims 8c..8c+7 are bits [24c, 24c+24) of the row; the second dword of the
         // last group lies in the next row or the block's scale area, both inside the block
-        t.v[j] = __builtin_amdgcn_raw_buffer_load_b64(a[h].v, o.v + r * R, a[h].row, 0);
+        t.v[j] = __builtin_amdgcn_raw_buffer_load_b64(a[h].v, o.v + r * R, a[h].row, kStream);
       } else {
-        t.v[j] = __builtin_amdgcn_raw_buffer_load_b128(a[h].v, o.v + r * R, a[h].row, 0);
+        t.v[j] = __builtin_amdgcn_raw_buffer_load_b128(a[h].v, o.v + r * R, a[h].row, kStream);
       }
     }
   }
@@ -322,7 +343,7 @@ __device__ __forceinline__ DmaOffsets dma_offsets(int lane) {
 }
 
 // Issue the staging DMAs of one tile into `slot`.
-template <int DT>
+template <int DT, bool FLAT>
 __device__ __forceinline__ void stage_tile(uint8_t* slot, const HalfAddr (&a)[2], const DmaOffsets& d,
                                            int lane) {
   using S = Stage<DT>;
@@ -331,19 +352,26 @@ __device__ __forceinline__ void stage_tile(uint8_t* slot, const HalfAddr (&a)[2]
 #pragma unroll
     for (int m = 0; m < S::kDma; ++m) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(a[h].k, (lds_void*)(slot + h * S::kHalf + 1024 * m), 16,
-                                               d.k[m], a[h].row, 0, 0);
+                                               d.k[m], a[h].row, 0, kStream);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(a[h].v, (lds_void*)(slot + (2 + h) * S::kHalf + 1024 * m), 16,
-                                               d.v[m], a[h].row, 0, 0);
+                                               d.v[m], a[h].row, 0, kStream);
     }
   }
-  // the 16 scales of each half: eight lanes, one dword each (always executed: lanes 0..7)
-  if (lane < 8) {
+  // the 16 scales of each half: eight lanes per half, one dword each. With one descriptor for
+  // the whole pool both halves go in one instruction (lanes 0..7: half 0, 8..15: half 1).
+  if constexpr (FLAT) {
+    if (lane < 16) {
+      const int off = (lane < 8 ? a[0].scale : a[1].scale) + 4 * (lane & 7);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a[0].k, (lds_void*)(slot + 4 * S::kHalf), 4, off, 0, 0, kStream);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a[0].v, (lds_void*)(slot + 4 * S::kHalf + 64), 4, off, 0, 0, kStream);
+    }
+  } else if (lane < 8) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(a[h].k, (lds_void*)(slot + 4 * S::kHalf + 32 * h), 4, 4 * lane,
-                                               a[h].scale, 0, 0);
+                                               a[h].scale, 0, kStream);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(a[h].v, (lds_void*)(slot + 4 * S::kHalf + 64 + 32 * h), 4,
-                                               4 * lane, a[h].scale, 0, 0);
+                                               4 * lane, a[h].scale, 0, kStream);
     }
   }
 }
@@ -587,11 +615,11 @@ __device__ __forceinline__ void process_tile(const Tile<DT>& t, WaveState& st,
   }
 }
 
-__device__ void fwht_lds(float (*x)[D + 4], int rows, int tid) {
-  // in-place unnormalized FWHT of `rows` rows of 128 floats; ends with a barrier
+// In-place unnormalized FWHT of `rows` rows of 128 floats in LDS, by one wave.
+__device__ __forceinline__ void fwht_wave(float (*x)[D + 4], int rows, int lane) {
   for (int h = 1; h < D; h <<= 1) {
-    __syncthreads();
-    for (int k = tid; k < rows * 64; k += kThreads) {
+    __syncthreads();   // one wave per workgroup: orders the LDS stages
+    for (int k = lane; k < rows * 64; k += 64) {
       const int j = k >> 6, r = k & 63;
       const int i = ((r / h) * 2 * h) + (r % h);
       const float a = x[j][i], b = x[j][i + h];
@@ -602,18 +630,46 @@ __device__ void fwht_lds(float (*x)[D + 4], int rows, int tid) {
   __syncthreads();
 }
 
-template <int DT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DT == 0 ? 1 : 2)))
+// One wave per work unit (split, kv head, sequence): the wave walks the unit's 32-token tiles
+// in order, keeping kDepth of them in flight, and finishes the unit alone (no cross-wave merge,
+// no barrier in the loop).
+template <int DT> constexpr int kWavesPerEu = DT == 0 ? 1 : (DT == 3 ? 2 : 3);
+
+// DEPTH: tiles in flight per wave on the staged path (LDS slots); chosen at launch from how
+// many waves share a compute unit, so that the LDS of the resident waves holds as many tiles
+// in flight as it can.
+template <int DT, int DEPTH>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEu<DT>)))
 void decode_split_kernel(DecodeParams p) {
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x;
+  // Work unit of this wave. Workgroups go to the eight XCDs round-robin by id, so the ids of the
+  // kv heads of one (split, sequence) are spaced by 8: they run on one XCD, whose L2 then fetches
+  // each line of a page once for all of them (a page's kv-head blocks are adjacent and need not
+  // be line aligned). A tail that does not fill whole sets maps straight.
+  int split, kvh, b;
+  {
+    const uint32_t id = blockIdx.x, hkv = (uint32_t)p.hkv;
+    const uint32_t units = (uint32_t)p.nsplits * hkv * (uint32_t)p.batch;
+    const uint32_t full = units / (8u * hkv) * (8u * hkv);
+    uint32_t group;
+    if (id < full) {
+      const uint32_t slot = id >> 3;
+      kvh = (int)(slot % hkv);
+      group = slot / hkv * 8u + (id & 7u);
+    } else {
+      kvh = (int)(id % hkv);
+      group = id / hkv;
+    }
+    split = (int)(group % (uint32_t)p.nsplits);
+    b = (int)(group / (uint32_t)p.nsplits);
+  }
+  const int lane = threadIdx.x;
   const int G = p.group;
   const int qh0 = kvh * G;
   const int L = min(p.context_lens[b], p.max_context_len);
   float* outp = p.out + ((int64_t)b * p.hq + qh0) * D;
   if (L <= 0) {
     if (split == 0)
-      for (int i = tid; i < G * D; i += kThreads) outp[i] = 0.f;
+      for (int i = lane; i < G * D; i += kThreads) outp[i] = 0.f;
     return;
   }
   const int tps = p.tokens_per_split;
@@ -622,17 +678,14 @@ void decode_split_kernel(DecodeParams p) {
   const int tok_end = min(L, tok_begin + tps);
   const int nsplit_b = (L + tps - 1) / tps;
 
-  // the staging ring and the epilogue's merge arrays share one LDS buffer
-  constexpr int kMergeBytes = (kWaves + 1) * kMaxGroup * (D + 4) * 4;
-  constexpr int kRingBytes = kWaves * Stage<DT>::kDepth * Stage<DT>::kSlot;
-  constexpr int kSmemBytes = kMergeBytes > kRingBytes ? kMergeBytes : kRingBytes;
+  // the staging ring and the epilogue's output rows share one LDS buffer
+  constexpr int kOutBytes = kMaxGroup * (D + 4) * 4;
+  constexpr int kRingBytes = DEPTH * Stage<DT>::kSlot;
+  constexpr int kSmemBytes = kOutBytes > kRingBytes ? kOutBytes : kRingBytes;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
-  auto red = reinterpret_cast<float (*)[kMaxGroup][D + 4]>(smem);
-  auto ob = reinterpret_cast<float (*)[D + 4]>(smem + kWaves * kMaxGroup * (D + 4) * 4);
+  auto ob = reinterpret_cast<float (*)[D + 4]>(smem);
 
-  const int lane = tid & 63;
   const int col = lane & 15, g = lane >> 4;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // ---- query operands ---------------------------------------------------------------------
   v4i qi[2][2] = {};
@@ -658,141 +711,154 @@ void decode_split_kernel(DecodeParams p) {
   st.m = -INFINITY;
   st.l = 0.f;
 
-  // ---- main loop: wave w takes tiles w, w + 4, ...; kDepth tiles in flight ---------------
+  // ---- main loop: tiles 0 .. ntiles-1 of the unit, kDepth in flight --------------------------
   constexpr int R = Codec<DT>::kRow;
-  constexpr int kDepth = kDepthOf<DT>;
   const int ntiles = (tok_end - tok_begin + 31) >> 5;
   const int ps = p.page_size;
   const int last_page = (L - 1) >> p.page_shift;
   const int64_t head_off = (int64_t)kvh * p.block_bytes;
+  const LaneOffsets lo = lane_offsets<DT>(col, g);
+  const int lp0 = tok_begin >> p.page_shift;     // tok_begin is page aligned
+
+  // Page lookup and descriptors. Fast form (pools below 4 GiB, splits of at most 128 pages): one
+  // descriptor per pool, based at this kv head's block of page 0, serves the whole unit and the
+  // page's byte offset rides in the instructions' offsets; the unit's block-table entries sit in
+  // two VGPRs (entry lp0 + i in lane i % 64 of register i / 64) and come back with readlane, so a
+  // page costs no memory round trip and one scalar multiply. General form: a scalar load of the
+  // entry and a descriptor per page block (reads past the block return zero).
+  const bool fast = p.pool_bytes <= (int64_t)0xFFFFFFFF && last_page - lp0 < 128;
+  const uint32_t pool_rec = (uint32_t)(p.pool_bytes - head_off);
+  const __amdgpu_buffer_rsrc_t k_pool_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.k_pool + head_off), (short)0, (int)pool_rec, kBufferConfig);
+  const __amdgpu_buffer_rsrc_t v_pool_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.v_pool + head_off), (short)0, (int)pool_rec, kBufferConfig);
+  int btw0 = 0, btw1 = 0;
+  if (fast) {
+    const int32_t* row = p.block_tables + (int64_t)b * p.maxp + lp0;
+    const int nwin = last_page - lp0 + 1;
+    if (lane < nwin) btw0 = row[lane];
+    if (lane + 64 < nwin) btw1 = row[lane + 64];
+  }
   // the block table is read-only here: reading it through the constant address space keeps the
-  // per-tile page lookups on the scalar unit (a vector load would make the wave wait for every
-  // outstanding tile load before the lookup could be used)
+  // general form's lookups on the scalar unit
   const __attribute__((address_space(4))) int32_t* bt =
       (const __attribute__((address_space(4))) int32_t*)(p.block_tables + (int64_t)b * p.maxp);
-  const int nrec = (int)p.block_bytes;          // reads past the page block return zero
-  const LaneOffsets lo = lane_offsets<DT>(col, g);
-  auto addr = [&](int t0, HalfAddr (&a)[2]) {
+  const int nrec = (int)p.block_bytes;
+  auto addr = [&](auto kFast, int t0, HalfAddr (&a)[2]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int th = t0 + 16 * h;
       const int lp = min(th >> p.page_shift, last_page);   // never read a table entry past the context
-      const int phys = bt[lp];
       const int slot = th & (ps - 1);
-      const int64_t off = (int64_t)phys * p.page_stride + head_off;
-      a[h].k = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.k_pool + off), (short)0, nrec, kBufferConfig);
-      a[h].v = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.v_pool + off), (short)0, nrec, kBufferConfig);
-      a[h].row = slot * R;
-      a[h].scale = ps * R + 2 * slot;
+      if constexpr (decltype(kFast)::value) {
+        const int i = lp - lp0;
+        const int phys = i < 64 ? __builtin_amdgcn_readlane(btw0, i) : __builtin_amdgcn_readlane(btw1, i - 64);
+        const uint32_t base = (uint32_t)phys * (uint32_t)p.page_stride;
+        a[h].k = k_pool_rsrc;
+        a[h].v = v_pool_rsrc;
+        a[h].row = (int)(base + (uint32_t)(slot * R));
+        a[h].scale = (int)(base + (uint32_t)(ps * R + 2 * slot));
+      } else {
+        const int64_t off = (int64_t)bt[lp] * p.page_stride + head_off;
+        a[h].k = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.k_pool + off), (short)0, nrec, kBufferConfig);
+        a[h].v = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.v_pool + off), (short)0, nrec, kBufferConfig);
+        a[h].row = slot * R;
+        a[h].scale = ps * R + 2 * slot;
+      }
     }
-  };
-  auto fetch = [&](Tile<DT>& t, int i) {
-    HalfAddr a[2];
-    addr(tok_begin + 32 * i, a);
-    load_tile<DT>(t, a, lo);
   };
   auto run = [&](const Tile<DT>& t, int i) {
     const int t0 = tok_begin + 32 * i;
     process_tile<DT>(t, st, qi, qb, qs, tok_end - t0 - 4 * g, t0 + 32 <= tok_end, col, g);
   };
-  if constexpr (Stage<DT>::kOn) {
-    // kDepth tiles in flight per wave, staged in LDS slots; slot d of this wave holds the
-    // wave's tiles d, d + kDepth, ...
-    using S = Stage<DT>;
-    const DmaOffsets dof = dma_offsets<DT>(lane);
-    uint8_t* ring = smem + wave * S::kDepth * S::kSlot;
-    auto stage = [&](int d, int i) {
-      HalfAddr a[2];
-      addr(tok_begin + 32 * i, a);
-      stage_tile<DT>(ring + d * S::kSlot, a, dof, lane);
-    };
-    Tile<DT> tile;
-#pragma unroll
-    for (int d = 0; d < S::kDepth - 1; ++d)
-      if (wave + d * kWaves < ntiles) stage(d, wave + d * kWaves);
-    for (int it = wave; it < ntiles;) {
-#pragma unroll
-      for (int d = 0; d < S::kDepth; ++d) {
-        const int ahead = it + (S::kDepth - 1) * kWaves;
-        if (ahead < ntiles) stage((d + S::kDepth - 1) % S::kDepth, ahead);
-        // this tile's instructions are complete once at most those of the tiles staged after
-        // it are outstanding
-        const int after = min(S::kDepth - 1, (ntiles - 1 - it) / kWaves);
-        if (after == 0) wait_vm<0>();
-        else if (after == 1) wait_vm<S::kOps>();
-        else wait_vm<2 * S::kOps>();
-        read_slot<DT>(tile, ring + d * S::kSlot, lane);
+  auto main_loop = [&](auto kFast) {
+    if constexpr (Stage<DT>::kOn) {
+      // slot i % DEPTH holds tile i
+      using S = Stage<DT>;
+      static_assert((DEPTH - 1) * S::kOps <= kMaxVmcnt, "vmcnt field is 6 bits");
+      const DmaOffsets dof = dma_offsets<DT>(lane);
+      auto stage = [&](int i) {
+        HalfAddr a[2];
+        addr(kFast, tok_begin + 32 * i, a);
+        stage_tile<DT, decltype(kFast)::value>(smem + (i % DEPTH) * S::kSlot, a, dof, lane);
+      };
+      Tile<DT> tile;
+      for (int i = 0; i < DEPTH - 1 && i < ntiles; ++i) stage(i);
+      for (int it = 0; it < ntiles; ++it) {
+        if (it + DEPTH - 1 < ntiles) stage(it + DEPTH - 1);
+        // this tile's instructions are complete once at most those of the tiles staged after it
+        // are outstanding
+        wait_tiles<S::kOps, 0, DEPTH - 1>(min(DEPTH - 1, ntiles - 1 - it));
+        read_slot<DT>(tile, smem + (it % DEPTH) * S::kSlot, lane);
         run(tile, it);
-        it += kWaves;
-        if (it >= ntiles) break;
+      }
+    } else {
+      constexpr int kDepth = kDepthOf<DT>;
+      auto fetch = [&](Tile<DT>& t, int i) {
+        HalfAddr a[2];
+        addr(kFast, tok_begin + 32 * i, a);
+        load_tile<DT>(t, a, lo);
+      };
+      // buffer i % kDepth holds tile i
+      Tile<DT> tb[kDepth];
+#pragma unroll
+      for (int d = 0; d < kDepth - 1; ++d)
+        if (d < ntiles) fetch(tb[d], d);
+      for (int it = 0; it < ntiles;) {
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+          const int ahead = it + kDepth - 1;
+          if (ahead < ntiles) fetch(tb[(d + kDepth - 1) % kDepth], ahead);
+          run(tb[d], it);
+          if (++it >= ntiles) break;
+        }
       }
     }
-  } else {
-    // kDepth tiles in flight per wave: buffer (i / kWaves) % kDepth holds tile i
-    Tile<DT> tb[kDepth];
-#pragma unroll
-    for (int d = 0; d < kDepth - 1; ++d)
-      if (wave + d * kWaves < ntiles) fetch(tb[d], wave + d * kWaves);
-    for (int it = wave; it < ntiles;) {
-#pragma unroll
-      for (int d = 0; d < kDepth; ++d) {
-        const int ahead = it + (kDepth - 1) * kWaves;
-        if (ahead < ntiles) fetch(tb[(d + kDepth - 1) % kDepth], ahead);
-        run(tb[d], it);
-        it += kWaves;
-        if (it >= ntiles) break;
-      }
-    }
-  }
+  };
+  if (fast) main_loop(std::true_type{});
+  else main_loop(std::false_type{});
 
-  // ---- merge: lanes of a head, then the four waves -------------------------------------------
+  // ---- finish the unit: combine the four lanes of each head ------------------------------
   st.l += __shfl_xor(st.l, 16);
   st.l += __shfl_xor(st.l, 32);
-  __syncthreads();   // every wave is done with its staging slots, which the merge arrays reuse
   const float unit = (float)(1 << Codec<DT>::kVShift);
+  if (nsplit_b == 1) {
+    // out = H (acc / l); lane (g, c) holds heads 4g + r, dimensions 8c + tau
+    float lh[4];
 #pragma unroll
-  for (int tau = 0; tau < 8; ++tau)
+    for (int r = 0; r < 4; ++r) lh[r] = __shfl(st.l, 4 * g + r);
+    __syncthreads();   // the ring is drained (the last tile waited for everything): reuse it
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (4 * g + r < G) red[wave][4 * g + r][8 * col + tau] = (st.acc[tau][r] - st.accb[r]) * unit;
-  if (g == 0 && col < G) {
-    red[wave][col][D] = st.m;
-    red[wave][col][D + 1] = st.l;
-  }
-  __syncthreads();
-
-  const bool single = nsplit_b == 1;
-  for (int k = tid; k < G * D; k += kThreads) {
-    const int j = k >> 7, d = k & 127;
-    float mx = -INFINITY;
+      if (4 * g + r < G) {
+        const float inv = 1.f / lh[r];
 #pragma unroll
-    for (int wv = 0; wv < kWaves; ++wv) mx = fmaxf(mx, red[wv][j][D]);
-    float num = 0.f, l = 0.f;
-#pragma unroll
-    for (int wv = 0; wv < kWaves; ++wv) {
-      const float mw = red[wv][j][D];
-      const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - mx);
-      num += red[wv][j][d] * f;
-      l += red[wv][j][D + 1] * f;
-    }
-    if (single) {
-      ob[j][d] = num / l;
-    } else {
-      float* part = p.partials + (((int64_t)b * p.hq + qh0 + j) * p.nsplits + split) * kPartialStride;
-      part[4 + d] = num;
-      if (d == 0) {
-        part[0] = mx;
-        part[1] = l;
+        for (int tau = 0; tau < 8; ++tau) ob[4 * g + r][8 * col + tau] = (st.acc[tau][r] - st.accb[r]) * unit * inv;
       }
+    if constexpr (DT != 0) {
+      fwht_wave(ob, G, lane);
+      for (int k = lane; k < G * D; k += kThreads) outp[k] = ob[k >> 7][k & 127] * kRotC;
+    } else {
+      __syncthreads();
+      for (int k = lane; k < G * D; k += kThreads) outp[k] = ob[k >> 7][k & 127];
     }
-  }
-  if (!single) return;
-  if constexpr (DT != 0) {
-    fwht_lds(ob, G, tid);
-    for (int k = tid; k < G * D; k += kThreads) outp[k] = ob[k >> 7][k & 127] * kRotC;
   } else {
-    __syncthreads();
-    for (int k = tid; k < G * D; k += kThreads) outp[k] = ob[k >> 7][k & 127];
+    // partials (m, l, acc) of this split, in the rotated space
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * g + r < G) {
+        float* part = p.partials + (((int64_t)b * p.hq + qh0 + 4 * g + r) * p.nsplits + split) * kPartialStride;
+        float v[8];
+#pragma unroll
+        for (int tau = 0; tau < 8; ++tau) v[tau] = (st.acc[tau][r] - st.accb[r]) * unit;
+        reinterpret_cast<float4*>(part + 4 + 8 * col)[0] = make_float4(v[0], v[1], v[2], v[3]);
+        reinterpret_cast<float4*>(part + 4 + 8 * col)[1] = make_float4(v[4], v[5], v[6], v[7]);
+      }
+    if (g == 0 && col < G) {
+      float* part = p.partials + (((int64_t)b * p.hq + qh0 + col) * p.nsplits + split) * kPartialStride;
+      part[0] = st.m;
+      part[1] = st.l;
+    }
   }
 }
 
@@ -866,6 +932,28 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodePara
   }
 }
 
+// Ring depth for the staged path: the units are spread over 256 compute units; with w of them
+// resident per CU (at most 12: three waves per SIMD), the LDS holds 160 KB / (w * slot) slots.
+template <int DT>
+int pick_depth(const DecodeParams& p) {
+  if constexpr (!Stage<DT>::kOn) {
+    return 3;
+  } else {
+    const int64_t units = (int64_t)p.nsplits * p.hkv * p.batch;
+    const int64_t per_cu = std::min<int64_t>(12, std::max<int64_t>(1, (units + 255) / 256));
+    const int64_t slots = kLdsPerCu / (per_cu * Stage<DT>::kSlot);
+    const int64_t cap = kMaxVmcnt / Stage<DT>::kOps + 1;
+    const int64_t d = std::min<int64_t>(slots, cap);
+    return d >= 8 ? 8 : d >= 6 ? 6 : d >= 4 ? 4 : d >= 3 ? 3 : 2;
+  }
+}
+
+template <int DT, int DEPTH>
+void launch_split(const DecodeParams& p, hipStream_t stream) {
+  const int64_t units = (int64_t)p.nsplits * p.hkv * p.batch;
+  hipLaunchKernelGGL((decode_split_kernel<DT, DEPTH>), dim3((unsigned)units), dim3(kThreads), 0, stream, p);
+}
+
 template <int DT>
 hipError_t launch_dt(const DecodeParams& p, hipStream_t stream) {
   if constexpr (DT != 0) {
@@ -873,7 +961,17 @@ hipError_t launch_dt(const DecodeParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((q_prep_kernel<DT>), dim3((unsigned)((lanes + kPrepThreads - 1) / kPrepThreads)),
                        dim3(kPrepThreads), 0, stream, p);
   }
-  hipLaunchKernelGGL((decode_split_kernel<DT>), dim3(p.nsplits, p.hkv, p.batch), dim3(kThreads), 0, stream, p);
+  if constexpr (Stage<DT>::kOn) {
+    switch (pick_depth<DT>(p)) {
+      case 8: launch_split<DT, (Stage<DT>::kOps * 7 <= kMaxVmcnt ? 8 : 6)>(p, stream); break;
+      case 6: launch_split<DT, 6>(p, stream); break;
+      case 4: launch_split<DT, 4>(p, stream); break;
+      case 3: launch_split<DT, 3>(p, stream); break;
+      default: launch_split<DT, 2>(p, stream); break;
+    }
+  } else {
+    launch_split<DT, 3>(p, stream);
+  }
   if (p.nsplits > 1)
     hipLaunchKernelGGL((decode_combine_kernel<DT>), dim3(p.hq, p.batch), dim3(kCombThreads), 0, stream, p);
   return hipGetLastError();

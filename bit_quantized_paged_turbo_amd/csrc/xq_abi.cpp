@@ -46,19 +46,22 @@ int64_t block_bytes_of(const xq_cache_layout* L) {
   return (bytes + 15) & ~int64_t(15);
 }
 
-// Tokens per split: page aligned and a multiple of 32 (one tile of the decode kernel). hint > 0 asks for that many splits of
-// the longest sequence; 0 sizes splits so that the grid has about 2048 workgroups
-// (8 per compute unit on 256 CUs), with 64..1024 tokens per split.
+// Tokens per split: page aligned and a multiple of 32 (one tile of the decode kernel). hint > 0
+// asks for that many splits of the longest sequence; 0 lets the library choose from the shape.
 int32_t plan_tokens_per_split(const xq_cache_layout* L, int32_t batch, int32_t max_ctx, int32_t hint) {
   const int32_t ps = L->page_size;
   int64_t tps;
   if (hint > 0) {
     tps = (max_ctx + hint - 1) / hint;
   } else {
-    const int64_t units = (int64_t)batch * L->num_kv_heads;
-    int64_t want = (int64_t)max_ctx * units / 2048;
-    tps = 64;
-    while (tps < want && tps < 1024) tps <<= 1;
+    // One wave per (split, kv head, sequence). Long splits amortise each wave's set-up and
+    // epilogue; enough of them keep every compute unit busy: the longest power of two up to
+    // 2048 tokens that still gives 4 waves per CU (8 for the dtypes that read tiles straight
+    // into registers and rely on occupancy to hide latency), at least 64 tokens.
+    const int64_t heads = (int64_t)batch * L->num_kv_heads;
+    const int64_t target = (L->kv_dtype == 4 || L->kv_dtype == 8) ? 1024 : 2048;
+    tps = 2048;
+    while (tps > 64 && heads * ((max_ctx + tps - 1) / tps) < target) tps >>= 1;
   }
   const int64_t unit = ps > 32 ? ps : 32;   // whole pages and whole 32-token tiles
   tps = ((tps + unit - 1) / unit) * unit;
@@ -177,6 +180,10 @@ xq_status xq_paged_decode_attention(const xq_cache_layout* layout, const void* q
   const int32_t tps = plan_tokens_per_split(layout, batch, ctx, num_splits_hint);
   const int32_t nsplits = (ctx + tps - 1) / tps;
   if (nsplits > 65535) return fail(XQ_EUNSUPPORTED, "%d splits > 65535", nsplits);
+  // one 64-lane workgroup per (split, kv head, sequence) on a one-dimensional grid
+  const int64_t units = (int64_t)nsplits * layout->num_kv_heads * batch;
+  if (units >= ((int64_t)1 << 26))
+    return fail(XQ_EUNSUPPORTED, "%lld work units (splits x kv heads x batch) >= 2^26", (long long)units);
   const xq::WorkspaceLayout ws = xq::workspace_layout(layout->kv_dtype, batch, num_q_heads, nsplits);
   if (ws.total > 0) {
     if (!workspace || workspace_bytes < ws.total)
@@ -199,6 +206,7 @@ xq_status xq_paged_decode_attention(const xq_cache_layout* layout, const void* q
   p.partials = ws.part_bytes ? reinterpret_cast<float*>(wsp + ws.part_off) : nullptr;
   p.block_bytes = block_bytes_of(layout);
   p.page_stride = p.block_bytes * layout->num_kv_heads;
+  p.pool_bytes = p.page_stride * layout->num_pages;
   p.batch = batch;
   p.hq = num_q_heads;
   p.hkv = layout->num_kv_heads;

@@ -66,6 +66,7 @@ struct DecodeParams {
   float* partials;              // workspace: [batch][hq][nsplits][kPartialStride] (nsplits > 1)
   int64_t page_stride;
   int64_t block_bytes;
+  int64_t pool_bytes;           // bytes of each pool (num_pages * page_stride)
   int32_t batch;
   int32_t hq;
   int32_t hkv;

@@ -155,7 +155,10 @@ xq_status xq_quantize_append(const xq_cache_layout* layout,
  *                      aligned; may be NULL when that size is 0. Its contents on entry do
  *                      not matter; calls that share a workspace must not overlap.
  *   out                fp32 [batch][num_q_heads][128]
- * num_q_heads must be a multiple of num_kv_heads with a group size of at most 8.
+ * num_q_heads must be a multiple of num_kv_heads (XQ_EINVAL otherwise); a group size above 16,
+ * a batch above 65535, more than 65535 splits or 2^26 or more (split, kv head, sequence) units
+ * give XQ_EUNSUPPORTED. Block-table entries read for positions below context_lens[b] must be
+ * pages of the pool (not checked on the device).
  */
 xq_status xq_paged_decode_attention(const xq_cache_layout* layout,
                                     const void* q, int32_t batch, int32_t num_q_heads,

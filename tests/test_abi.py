@@ -55,14 +55,21 @@ def test_split_planning(lib):
     qdig, qaux = 40 * 256, 512
     assert xq.xq_decode_workspace_bytes(L, 1, 40, 262144, 256) == qdig + qaux + 40 * 256 * 132 * 4
     L = xq.CacheLayout(4, 8, 16, 9000)
-    assert xq.xq_decode_num_splits(L, 256, 16, 1022, 0) == 1
-    assert xq.xq_decode_workspace_bytes(L, 256, 16, 1022, 0) == 256 * 16 * 256 + 256 * 16 * 8
+    # library policy: whole pages / 32-token tiles per split, partials only when split
+    n = xq.xq_decode_num_splits(L, 256, 16, 1022, 0)
+    assert 1 <= n <= 16
+    tps = -(-1022 // n)
+    assert xq.xq_decode_num_splits(L, 256, 16, 1022, n) == n
+    part = 256 * 16 * n * 132 * 4 if n > 1 else 0
+    assert xq.xq_decode_workspace_bytes(L, 256, 16, 1022, 0) == 256 * 16 * 256 + 256 * 16 * 8 + part
+    assert xq.xq_decode_num_splits(L, 256, 16, 1022, 1) == 1
+    assert xq.xq_decode_workspace_bytes(L, 256, 16, 1022, 1) == 256 * 16 * 256 + 256 * 16 * 8
     assert xq.xq_decode_num_splits(L, 4, 16, 1000, 7) == 7
     assert xq.xq_decode_num_splits(L, 4, 16, 0, 0) == 1
     assert xq.xq_decode_num_splits(L, 4, 16, 100, -1) == -1
     # bf16 needs no query preparation: no workspace for a single split
     L = xq.CacheLayout(0, 8, 16, 9000)
-    assert xq.xq_decode_workspace_bytes(L, 256, 16, 1022, 0) == 0
+    assert xq.xq_decode_workspace_bytes(L, 256, 16, 1022, 1) == 0
 
 
 def _decode_status(lib, L, **kw):
