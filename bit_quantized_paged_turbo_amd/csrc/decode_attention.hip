@@ -103,6 +103,9 @@ template <> struct Stage<8> {
   static constexpr int kHalf = 2048, kDma = 2, kOps = 4 * kDma + 2, kSlot = 4 * kHalf + 128;
 };
 constexpr int kLdsPerCu = 160 * 1024;
+// Paired-block QK (turbo4, turbo8): with at most this many query heads per kv head, the 16
+// columns of the QK tile hold two 16-token blocks of the tile side by side.
+constexpr int kPairMaxGroup = 8;
 constexpr int kMaxVmcnt = 63;
 
 // Wait until at most N vector-memory instructions of this wave are outstanding. The memory
@@ -212,8 +215,18 @@ __global__ __launch_bounds__(kPrepThreads) void q_prep_kernel(DecodeParams p) {
   int qi[32];
 #pragma unroll
   for (int e = 0; e < 32; ++e) qi[e] = (int)rintf(x[e] * inv);
-  // operand m (k-chunk), digit dg, dword w, byte b holds dimension
-  //   turbo4/3: 32 g + 8 w + 2 b + m      turbo8: 32 g + 16 m + 4 w + b
+  // The score scale is made positive (the sign goes into the digits) and nonzero (a zero
+  // query or scale gives zero digits), so a maximum over unscaled scores is the maximum of the
+  // scores.
+  float sc = am > 0.f ? (am / kQiMax) * p.softmax_scale * kLog2e / (float)Codec<DT>::kKMul : 0.f;
+  const int sgn = sc < 0.f ? -1 : 1;
+  const bool zero = !(sc != 0.f);
+  sc = zero ? 1.f : fabsf(sc);
+  // operand m, digit dg, dword w, byte b holds dimension (relative to 32 g)
+  //   paired-block layout (turbo4/turbo8 with at most 8 heads per kv head), m = half p of the
+  //   32 dimensions:  turbo4: 16 m + 8 (w >> 1) + 2 b + (w & 1)   turbo8: 16 m + 4 w + b
+  //   one-block layout, m = k-chunk:  turbo4/3: 8 w + 2 b + m      turbo8: 16 m + 4 w + b
+  const bool paired = (DT == 4 || DT == 8) && p.group <= kPairMaxGroup;
   uint32_t word[2][2][4];
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
@@ -222,8 +235,9 @@ __global__ __launch_bounds__(kPrepThreads) void q_prep_kernel(DecodeParams p) {
       uint32_t lo = 0, hi = 0;
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
-        const int e = (DT == 8) ? (16 * m + 4 * w + bb) : (8 * w + 2 * bb + m);
-        const int q = qi[e];
+        const int e = (DT == 8) ? (16 * m + 4 * w + bb)
+                                : (paired ? 16 * m + 8 * (w >> 1) + 2 * bb + (w & 1) : 8 * w + 2 * bb + m);
+        const int q = zero ? 0 : sgn * qi[e];
         const int d0 = ((q + 128) & 255) - 128;
         const int d1 = (q - d0) >> 8;
         lo |= (uint32_t)(d0 & 255) << (8 * bb);
@@ -240,7 +254,7 @@ __global__ __launch_bounds__(kPrepThreads) void q_prep_kernel(DecodeParams p) {
   dst[3] = make_uint4(word[1][1][0], word[1][1][1], word[1][1][2], word[1][1][3]);
   if (g == 0) {
     // a K byte is c * kKMul, so the integer dot product is kKMul times q.c
-    p.qscale[row] = am > 0.f ? (am / kQiMax) * p.softmax_scale * kLog2e / (float)Codec<DT>::kKMul : 0.f;
+    p.qscale[row] = sc;
     p.qoff[row] = 0;
   }
 }
@@ -615,6 +629,206 @@ __device__ __forceinline__ void process_tile(const Tile<DT>& t, WaveState& st,
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Paired-block tile (turbo4 and turbo8 with G <= 8 query heads per kv head).
+//
+// The QK tile has 16 columns but a kv head has only G query heads, so column n = G j + h
+// (j = 0, 1; n >= 2 G repeats column n mod 2 G) holds head h against token block j (the 16
+// tokens of half j of the tile). The query operand is block diagonal over the four k-groups of
+// lanes: lane group gg (lanes 16 gg .. 16 gg + 15) carries block gg >> 1, so a column sees its
+// own block's keys only. The K operand of lane (gg, t) is token t of block gg >> 1,
+// dimensions 32 m + 16 (gg & 1) + [0, 16) in MFMA m (m = 0..3): four MFMAs per digit cover
+// 128 dimensions of both blocks, as many as one block takes in the one-block layout. Lane
+// (gg, n) then holds the scores of tokens 4 gg + r of block j(n) for head h(n): four values
+// where the one-block layout has eight, so the softmax work per tile halves. For PV the same
+// values go to k slots r (block 0) or 4 + r (block 1) of the A operand, zeros in the other
+// four, matching the V operand of the one-block layout; rows n and G + n of the product are
+// the two blocks' partial sums for head n and are added at the end of the unit.
+// ---------------------------------------------------------------------------------------
+template <int DT> struct PairTile;
+template <> struct PairTile<4> {
+  v2i k[4];            // raw K code bytes: 8 bytes (16 dims) per MFMA
+  int v[8];            // V as in Tile<4>
+  v2i ks, vs;          // fp16 scales of tokens 4 gg + r of block j(n)
+};
+template <> struct PairTile<8> {
+  v4i k[4];            // raw K code bytes: 16 bytes (16 dims) per MFMA
+  v2i v[8];
+  v2i ks, vs;
+};
+
+// Lane roles of the paired layout.
+struct PairLane {
+  int jn;      // token block of this lane's column (0, 1)
+  int hn;      // query head of this lane's column (0 .. G-1)
+  int kb;      // token block of this lane's K operand (lane group >> 1)
+  int kp;      // which 16 of each 32 dimensions this lane's K operand holds (lane group & 1)
+};
+
+__device__ __forceinline__ PairLane pair_lane(int lane, int G) {
+  const int n = lane & 15, gg = lane >> 4;
+  const int ne = n < 2 * G ? n : n % (2 * G);
+  return PairLane{ne / G, ne % G, gg >> 1, gg & 1};
+}
+
+template <int DT>
+__device__ __forceinline__ void read_slot_pair(PairTile<DT>& t, const uint8_t* slot, int lane, const PairLane& pl) {
+  using S = Stage<DT>;
+  const int gg = lane >> 4, tk = lane & 15;
+  // scales of tokens 4 gg + r of block jn
+  t.ks = *reinterpret_cast<const v2i*>(slot + 4 * S::kHalf + 32 * pl.jn + 8 * gg);
+  t.vs = *reinterpret_cast<const v2i*>(slot + 4 * S::kHalf + 64 + 32 * pl.jn + 8 * gg);
+  const uint8_t* kh = slot + pl.kb * S::kHalf;
+  if constexpr (DT == 4) {
+    // half layout: row t, 16-byte chunk c (32 dims) at 16 (t + 16 c)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) t.k[m] = *reinterpret_cast<const v2i*>(kh + 16 * (tk + 16 * m) + 8 * pl.kp);
+  } else {
+    // half layout: row t, bytes 32 c + 16 q at 1024 q + 16 (t + 16 c)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) t.k[m] = *reinterpret_cast<const v4i*>(kh + 1024 * pl.kp + 16 * (tk + 16 * m));
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (DT == 4)
+        t.v[4 * h + r] = *reinterpret_cast<const int*>(slot + (2 + h) * S::kHalf + 256 * r + 4 * lane);
+      else
+        t.v[4 * h + r] = *reinterpret_cast<const v2i*>(slot + (2 + h) * S::kHalf + 512 * r + 8 * lane);
+    }
+  }
+}
+
+// K operand of MFMA m: 16 codes as bytes c * kKMul; byte 4 w + b is dimension
+// 8 (w >> 1) + 2 b + (w & 1) (turbo4) or 4 w + b (turbo8) of the lane's 16.
+template <int DT>
+__device__ __forceinline__ v4i pair_k_operand(const PairTile<DT>& t, int m) {
+  if constexpr (DT == 4) {
+    const uint32_t x0 = (uint32_t)t.k[m][0], x1 = (uint32_t)t.k[m][1];
+    return v4i{(int)((x0 << 4) & 0xf0f0f0f0u), (int)(x0 & 0xf0f0f0f0u), (int)((x1 << 4) & 0xf0f0f0f0u),
+               (int)(x1 & 0xf0f0f0f0u)};
+  } else {
+    return t.k[m];
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void process_pair_tile(const PairTile<DT>& t, WaveState& st, const v4i (&qj)[4][2],
+                                                  float qs, int lim, bool full, const PairLane& pl, int G,
+                                                  int lane) {
+  // ---- scores: y' = s_k * (q.c) in integer-digit units; the log2-domain score is y' * qs ------
+  v4i s0 = {0, 0, 0, 0}, s1 = {0, 0, 0, 0};
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const v4i a = pair_k_operand<DT>(t, m);
+    s0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qj[m][0], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qj[m][1], s1, 0, 0, 0);
+  }
+  const uint32_t ks[4] = {(uint32_t)t.ks[0], (uint32_t)t.ks[0] >> 16, (uint32_t)t.ks[1], (uint32_t)t.ks[1] >> 16};
+  uint32_t sv[4] = {(uint32_t)t.vs[0] & 0xffffu, (uint32_t)t.vs[0] >> 16, (uint32_t)t.vs[1] & 0xffffu,
+                    (uint32_t)t.vs[1] >> 16};
+  float y[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int zi = (s1[r] << 8) + s0[r];
+    y[r] = __builtin_fmaf(half_lo(ks[r]), (float)zi, 0.f);
+  }
+  if (!full) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool ok = 16 * pl.jn + r < lim;
+      y[r] = ok ? y[r] : -INFINITY;
+      sv[r] = ok ? sv[r] : 0u;    // unwritten slots may hold NaN patterns
+    }
+  }
+  // lane bound of w = y + e(s_v): the largest score plus the largest exponent field of the
+  // lane's value scales (raw fp16 bits of positive scales order like their values)
+  const uint32_t smax = max(max(sv[0], sv[1]), max(sv[2], sv[3]));
+  const float ymax = fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3]));
+  float mx = __builtin_fmaf(ymax, qs, (float)(smax >> 10));
+  if (__builtin_expect(__any(mx > st.m + kLazy), 0)) {
+    // head maximum over the lanes of head hn: columns hn and G + hn, all four lane groups
+    const int pn = pl.jn ? pl.hn : pl.hn + G;
+    mx = fmaxf(mx, __shfl(mx, (lane & 48) | pn));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool up = mx > st.m + kLazy;
+    const float f = up ? __builtin_amdgcn_exp2f(st.m - mx) : 1.f;
+    st.m = up ? mx : st.m;
+    st.l *= f;
+    // PV row 4 gg + r is column n = 4 gg + r: head (n mod 2G) mod G, whose factor lane n has
+    const int g4 = (lane >> 4) * 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int nr = g4 + r;
+      const int ner = nr < 2 * G ? nr : nr % (2 * G);
+      const float fr = __shfl(f, ner % G);
+#pragma unroll
+      for (int tau = 0; tau < 8; ++tau) st.acc[tau][r] *= fr;
+      st.accb[r] *= fr;
+    }
+  }
+
+  // ---- weights: p = 2^(y - m + 21), P' = p * s_v --------------------------------------------
+  const float nref = kWeightExp - st.m;
+  float pw[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(y[r], qs, nref));
+    st.l += pr;
+    pw[r] = __builtin_fmaf(half_lo(sv[r]), pr, 0.f);
+  }
+  const auto h01 = __builtin_amdgcn_cvt_pkrtz(pw[0], pw[1]);
+  const auto h23 = __builtin_amdgcn_cvt_pkrtz(pw[2], pw[3]);
+  const auto l01 = __builtin_amdgcn_cvt_pkrtz(__builtin_fmaf((float)h01[0], -1.f, pw[0]),
+                                              __builtin_fmaf((float)h01[1], -1.f, pw[1]));
+  const auto l23 = __builtin_amdgcn_cvt_pkrtz(__builtin_fmaf((float)h23[0], -1.f, pw[2]),
+                                              __builtin_fmaf((float)h23[1], -1.f, pw[3]));
+  const uint32_t hi01 = __builtin_bit_cast(uint32_t, h01), hi23 = __builtin_bit_cast(uint32_t, h23);
+  const uint32_t lo01 = __builtin_bit_cast(uint32_t, l01), lo23 = __builtin_bit_cast(uint32_t, l23);
+  const bool b1 = pl.jn != 0;
+  const v8h Ahi = __builtin_bit_cast(v8h, make_uint4(b1 ? 0u : hi01, b1 ? 0u : hi23, b1 ? hi01 : 0u, b1 ? hi23 : 0u));
+  const v8h Alo = __builtin_bit_cast(v8h, make_uint4(b1 ? 0u : lo01, b1 ? 0u : lo23, b1 ? lo01 : 0u, b1 ? lo23 : 0u));
+
+  // ---- PV (as the one-block layout) -----------------------------------------------------------
+  const v8h Bb = __builtin_bit_cast(v8h, make_uint4(0x00800080u, 0x00800080u, 0x00800080u, 0x00800080u));
+  st.accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, Bb, st.accb, 0, 0, 0);
+  st.accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, Bb, st.accb, 0, 0, 0);
+  uint32_t e[8], o[8];
+  if constexpr (DT == 4) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t x = (uint32_t)t.v[j];
+      e[j] = ((x << 4) & 0xf0f0f0f0u) ^ 0x80808080u;   // even dims, (c + 8) << 4
+      o[j] = (x & 0xf0f0f0f0u) ^ 0x80808080u;          // odd dims
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      e[j] = (uint32_t)t.v[j][0] ^ 0x80808080u;     // c + 128
+      o[j] = (uint32_t)t.v[j][1] ^ 0x80808080u;
+    }
+  }
+#pragma unroll
+  for (int tau = 0; tau < 8; ++tau) {
+    const uint32_t* src;
+    int i;
+    if constexpr (DT == 8) {
+      src = tau < 4 ? e : o;
+      i = tau & 3;
+    } else {
+      src = (tau & 1) ? o : e;
+      i = tau >> 1;
+    }
+    const uint32_t sel = (uint32_t)i | (0x0cu << 8) | ((uint32_t)(4 + i) << 16) | (0x0cu << 24);
+    const v8h B = __builtin_bit_cast(v8h, make_uint4(perm(src[1], src[0], sel), perm(src[3], src[2], sel),
+                                                     perm(src[5], src[4], sel), perm(src[7], src[6], sel)));
+    st.acc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, B, st.acc[tau], 0, 0, 0);
+    st.acc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, B, st.acc[tau], 0, 0, 0);
+  }
+}
+
 // In-place unnormalized FWHT of `rows` rows of 128 floats in LDS, by one wave.
 __device__ __forceinline__ void fwht_wave(float (*x)[D + 4], int rows, int lane) {
   for (int h = 1; h < D; h <<= 1) {
@@ -678,8 +892,8 @@ void decode_split_kernel(DecodeParams p) {
   const int tok_end = min(L, tok_begin + tps);
   const int nsplit_b = (L + tps - 1) / tps;
 
-  // the staging ring and the epilogue's output rows share one LDS buffer
-  constexpr int kOutBytes = kMaxGroup * (D + 4) * 4;
+  // the staging ring and the epilogue's output rows (plus 64 per-lane sums) share one LDS buffer
+  constexpr int kOutBytes = kMaxGroup * (D + 4) * 4 + kThreads * 4;
   constexpr int kRingBytes = DEPTH * Stage<DT>::kSlot;
   constexpr int kSmemBytes = kOutBytes > kRingBytes ? kOutBytes : kRingBytes;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
@@ -688,10 +902,25 @@ void decode_split_kernel(DecodeParams p) {
   const int col = lane & 15, g = lane >> 4;
 
   // ---- query operands ---------------------------------------------------------------------
+  const bool pair = Stage<DT>::kOn && G <= kPairMaxGroup;
+  const PairLane pl = pair_lane(lane, G);
   v4i qi[2][2] = {};
+  v4i qj[4][2] = {};
   v8bf qb[4] = {};
   float qs = 0.f;
-  if (col < G) {
+  if (pair) {
+    // block-diagonal query operand: lane group g carries token block g >> 1
+    const int64_t row = (int64_t)b * p.hq + qh0 + pl.hn;
+    if (pl.jn == pl.kb) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const v4i* s = reinterpret_cast<const v4i*>(p.qdig + (row * 4 + m) * 64 + 32 * pl.kp);
+        qj[m][0] = s[0];
+        qj[m][1] = s[1];
+      }
+    }
+    qs = p.qscale[row];
+  } else if (col < G) {
     const int64_t row = (int64_t)b * p.hq + qh0 + col;
     if constexpr (DT != 0) {
       const v4i* s = reinterpret_cast<const v4i*>(p.qdig + (row * 4 + g) * 64);
@@ -771,7 +1000,7 @@ void decode_split_kernel(DecodeParams p) {
     const int t0 = tok_begin + 32 * i;
     process_tile<DT>(t, st, qi, qb, qs, tok_end - t0 - 4 * g, t0 + 32 <= tok_end, col, g);
   };
-  auto main_loop = [&](auto kFast) {
+  auto main_loop = [&](auto kFast, auto kPair) {
     if constexpr (Stage<DT>::kOn) {
       // slot i % DEPTH holds tile i
       using S = Stage<DT>;
@@ -782,15 +1011,21 @@ void decode_split_kernel(DecodeParams p) {
         addr(kFast, tok_begin + 32 * i, a);
         stage_tile<DT, decltype(kFast)::value>(smem + (i % DEPTH) * S::kSlot, a, dof, lane);
       };
-      Tile<DT> tile;
+      std::conditional_t<decltype(kPair)::value, PairTile<DT>, Tile<DT>> tile;
       for (int i = 0; i < DEPTH - 1 && i < ntiles; ++i) stage(i);
       for (int it = 0; it < ntiles; ++it) {
         if (it + DEPTH - 1 < ntiles) stage(it + DEPTH - 1);
         // this tile's instructions are complete once at most those of the tiles staged after it
         // are outstanding
         wait_tiles<S::kOps, 0, DEPTH - 1>(min(DEPTH - 1, ntiles - 1 - it));
-        read_slot<DT>(tile, smem + (it % DEPTH) * S::kSlot, lane);
-        run(tile, it);
+        if constexpr (decltype(kPair)::value) {
+          read_slot_pair<DT>(tile, smem + (it % DEPTH) * S::kSlot, lane, pl);
+          const int t0 = tok_begin + 32 * it;
+          process_pair_tile<DT>(tile, st, qj, qs, tok_end - t0 - 4 * g, t0 + 32 <= tok_end, pl, G, lane);
+        } else {
+          read_slot<DT>(tile, smem + (it % DEPTH) * S::kSlot, lane);
+          run(tile, it);
+        }
       }
     } else {
       constexpr int kDepth = kDepthOf<DT>;
@@ -815,13 +1050,64 @@ void decode_split_kernel(DecodeParams p) {
       }
     }
   };
-  if (fast) main_loop(std::true_type{});
-  else main_loop(std::false_type{});
+  if constexpr (Stage<DT>::kOn) {
+    if (pair) {
+      if (fast) main_loop(std::true_type{}, std::true_type{});
+      else main_loop(std::false_type{}, std::true_type{});
+    } else {
+      if (fast) main_loop(std::true_type{}, std::false_type{});
+      else main_loop(std::false_type{}, std::false_type{});
+    }
+  } else {
+    if (fast) main_loop(std::true_type{}, std::false_type{});
+    else main_loop(std::false_type{}, std::false_type{});
+  }
+
+  const float unit = (float)(1 << Codec<DT>::kVShift);
+  if (pair) {
+    // ---- finish a paired-block unit: rows n and G + n of the product are head n's two block
+    // sums; the normaliser of head n is the sum over the lanes of columns n and G + n ---------
+    float* lsum = reinterpret_cast<float*>(smem + kMaxGroup * (D + 4) * 4);
+    __syncthreads();   // the ring is drained (the last tile waited for everything): reuse it
+    lsum[lane] = st.l;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * g + r < 2 * G) {
+#pragma unroll
+        for (int tau = 0; tau < 8; ++tau) ob[4 * g + r][8 * col + tau] = (st.acc[tau][r] - st.accb[r]) * unit;
+      }
+    __syncthreads();
+    auto head_l = [&](int h) {
+      float l = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) l += lsum[16 * q + h] + lsum[16 * q + G + h];
+      return l;
+    };
+    if (nsplit_b == 1) {
+      for (int k = lane; k < G * D; k += kThreads) {
+        const int h = k >> 7, d = k & 127;
+        ob[h][d] = (ob[h][d] + ob[G + h][d]) / head_l(h);
+      }
+      fwht_wave(ob, G, lane);
+      for (int k = lane; k < G * D; k += kThreads) outp[k] = ob[k >> 7][k & 127] * kRotC;
+    } else {
+      for (int k = lane; k < G * D; k += kThreads) {
+        const int h = k >> 7, d = k & 127;
+        float* part = p.partials + (((int64_t)b * p.hq + qh0 + h) * p.nsplits + split) * kPartialStride;
+        part[4 + d] = ob[h][d] + ob[G + h][d];
+      }
+      if (lane < G) {   // lane n < G: column n is head n, block 0
+        float* part = p.partials + (((int64_t)b * p.hq + qh0 + lane) * p.nsplits + split) * kPartialStride;
+        part[0] = st.m;
+        part[1] = head_l(lane);
+      }
+    }
+    return;
+  }
 
   // ---- finish the unit: combine the four lanes of each head ------------------------------
   st.l += __shfl_xor(st.l, 16);
   st.l += __shfl_xor(st.l, 32);
-  const float unit = (float)(1 << Codec<DT>::kVShift);
   if (nsplit_b == 1) {
     // out = H (acc / l); lane (g, c) holds heads 4g + r, dimensions 8c + tau
     float lh[4];

@@ -174,9 +174,11 @@ def test_full_size_sampled(name, cfg, dtype, sample):
 # ------------------------------------------------------------------------------------
 # edge cases and properties
 # ------------------------------------------------------------------------------------
+# group sizes 1..8 take the paired-block QK layout for turbo4/turbo8, 9..16 the one-block one
 @pytest.mark.parametrize("dtype,ps,hq,hkv", [(4, 16, 8, 8), (4, 32, 24, 8), (4, 128, 16, 2),
                                              (4, 256, 8, 1), (3, 64, 6, 2), (8, 64, 14, 2),
-                                             (0, 32, 8, 1), (8, 16, 7, 7)])
+                                             (0, 32, 8, 1), (8, 16, 7, 7), (4, 16, 32, 2),
+                                             (8, 32, 12, 1), (4, 64, 10, 1)])
 def test_decode_shapes_and_ragged(dtype, ps, hq, hkv):
     _print_case("shapes", dtype, ps, hq, hkv)
     lens = [0, 1, 15, 17, ps + 3, 3 * ps - 1, 700]
@@ -193,6 +195,29 @@ def test_decode_shapes_and_ragged(dtype, ps, hq, hkv):
             want = _oracle_out(W, b, qb, kv[b])
             err = np.max(np.abs(got[b] - want))
             assert err <= TOL, f"splits {splits} seq {b} (L={lens[b]}): {err:.3e}"
+
+
+@pytest.mark.parametrize("dtype,hq", [(4, 4), (8, 4), (4, 16), (3, 4), (0, 4)])
+def test_query_and_scale_edge_cases(dtype, hq):
+    """A zero query gives uniform weights (the mean of the values); a negative softmax scale
+    flips the scores; both against the oracle."""
+    _print_case("qedge", dtype, hq)
+    W = workloads.make(f"qedge-{dtype}-{hq}", 500 + dtype, dtype, [45, 300], hq, 1, 16)
+    cache = make_cache(W)
+    bt, cl = upload_tables(W)
+    kv = {b: W.kv_bits(b) for b in range(W.batch)}
+    fill(cache, W, bt, kv=kv)
+    qb = W.q_bits()
+    qb[0, :] = 0                       # sequence 0: all-zero query
+    for scale in (W.softmax_scale, -W.softmax_scale, 0.0):
+        out = cache.decode(to_dev(qb), bt[: W.batch], cl, W.max_context_len, scale, 0)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        for b in range(W.batch):
+            k, v = kv[b]
+            want, _ = oracle.decode_sequence(W.dtype, qb[b], k, v, scale)
+            err = np.max(np.abs(got[b] - want))
+            assert err <= TOL, f"scale {scale} seq {b}: {err:.3e}"
 
 
 def test_splits_agree_and_repeat_is_deterministic():
