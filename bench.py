@@ -15,8 +15,11 @@ Infinity Cache cannot serve the KV reads of one step from the previous ones.
 
 Prints ONE JSON line. `value` is KV GB/s: the algorithmic KV bytes the decode reads per
 step (sum_b L_b * Hkv * 2 * row_bytes) over the whole step time. `roofline` is for the
-dominant kernel (the split-K decode kernel), timed with HIP events around each decode
-call inside the timed region; `cpu_baseline` is the oracle on the host cores.
+decode call, which is the dominant work of the step: q_prep_kernel, decode_split_kernel and,
+when a sequence spans several partitions, decode_combine_kernel, timed together with HIP
+events around each decode call on its stream inside the timed region (the rocprofv3 summary
+under profiles/ lists the three kernels separately); `traffic` is the measured HBM bytes of
+those kernels per call. `cpu_baseline` is the oracle on the host cores.
 """
 from __future__ import annotations
 
@@ -296,7 +299,7 @@ def main():
     nsplits = xq.xq_decode_num_splits(base.layout, B, hq, W.max_context_len, splits)
     value = kv_bytes / (step_ms * 1e-3) / 1e9
     achieved = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
-    tag = f"decode_split_{workloads.DTYPE_NAMES[W.dtype]}_{W.name}"
+    tag = f"decode_call_{workloads.DTYPE_NAMES[W.dtype]}_{W.name}"
     traffic = committed_traffic(tag)
 
     result = {
@@ -329,7 +332,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "decode_split_kernel",
+                     "kernel": "xq_paged_decode_attention call (q_prep_kernel + decode_split_kernel"
+                               + (" + decode_combine_kernel)" if nsplits > 1 else ")"),
                      "bytes_per_launch": kv_bytes},
     }
     log(f"GPU: {step_ms * 1e3:.1f} us/step, decode call {dec_avg_ms * 1e3:.1f} us")

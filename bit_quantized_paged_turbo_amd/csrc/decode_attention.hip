@@ -949,29 +949,26 @@ void decode_split_kernel(DecodeParams p) {
   const LaneOffsets lo = lane_offsets<DT>(col, g);
   const int lp0 = tok_begin >> p.page_shift;     // tok_begin is page aligned
 
-  // Page lookup and descriptors. Fast form (pools below 4 GiB, splits of at most 128 pages): one
-  // descriptor per pool, based at this kv head's block of page 0, serves the whole unit and the
-  // page's byte offset rides in the instructions' offsets; the unit's block-table entries sit in
-  // two VGPRs (entry lp0 + i in lane i % 64 of register i / 64) and come back with readlane, so a
-  // page costs no memory round trip and one scalar multiply. General form: a scalar load of the
-  // entry and a descriptor per page block (reads past the block return zero).
-  const bool fast = p.pool_bytes <= (int64_t)0xFFFFFFFF && last_page - lp0 < 128;
+  // Page lookup and descriptors. The unit's block-table entries (a split spans at most
+  // kMaxSplitPages = 128 pages) sit in two VGPRs, entry lp0 + i in lane i % 64 of register
+  // i / 64, and come back with readlane: a page costs no memory round trip. Pools below 4 GiB
+  // (fast form): one descriptor per pool, based at this kv head's block of page 0, serves the
+  // whole unit and the page's byte offset rides in the instructions' offsets. Larger pools: a
+  // descriptor per page block (reads past the block return zero).
+  static_assert(kMaxSplitPages <= 128, "two registers of block-table entries");
+  const bool fast = p.pool_bytes <= (int64_t)0xFFFFFFFF;
   const uint32_t pool_rec = (uint32_t)(p.pool_bytes - head_off);
   const __amdgpu_buffer_rsrc_t k_pool_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.k_pool + head_off), (short)0, (int)pool_rec, kBufferConfig);
   const __amdgpu_buffer_rsrc_t v_pool_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.v_pool + head_off), (short)0, (int)pool_rec, kBufferConfig);
   int btw0 = 0, btw1 = 0;
-  if (fast) {
+  {
     const int32_t* row = p.block_tables + (int64_t)b * p.maxp + lp0;
     const int nwin = last_page - lp0 + 1;
     if (lane < nwin) btw0 = row[lane];
     if (lane + 64 < nwin) btw1 = row[lane + 64];
   }
-  // the block table is read-only here: reading it through the constant address space keeps the
-  // general form's lookups on the scalar unit
-  const __attribute__((address_space(4))) int32_t* bt =
-      (const __attribute__((address_space(4))) int32_t*)(p.block_tables + (int64_t)b * p.maxp);
   const int nrec = (int)p.block_bytes;
   auto addr = [&](auto kFast, int t0, HalfAddr (&a)[2]) {
 #pragma unroll
@@ -979,16 +976,16 @@ void decode_split_kernel(DecodeParams p) {
       const int th = t0 + 16 * h;
       const int lp = min(th >> p.page_shift, last_page);   // never read a table entry past the context
       const int slot = th & (ps - 1);
+      const int i = lp - lp0;
+      const int phys = i < 64 ? __builtin_amdgcn_readlane(btw0, i) : __builtin_amdgcn_readlane(btw1, i - 64);
       if constexpr (decltype(kFast)::value) {
-        const int i = lp - lp0;
-        const int phys = i < 64 ? __builtin_amdgcn_readlane(btw0, i) : __builtin_amdgcn_readlane(btw1, i - 64);
         const uint32_t base = (uint32_t)phys * (uint32_t)p.page_stride;
         a[h].k = k_pool_rsrc;
         a[h].v = v_pool_rsrc;
         a[h].row = (int)(base + (uint32_t)(slot * R));
         a[h].scale = (int)(base + (uint32_t)(ps * R + 2 * slot));
       } else {
-        const int64_t off = (int64_t)bt[lp] * p.page_stride + head_off;
+        const int64_t off = (int64_t)phys * p.page_stride + head_off;
         a[h].k = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.k_pool + off), (short)0, nrec, kBufferConfig);
         a[h].v = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.v_pool + off), (short)0, nrec, kBufferConfig);
         a[h].row = slot * R;

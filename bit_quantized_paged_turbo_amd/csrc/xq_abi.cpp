@@ -65,7 +65,10 @@ int32_t plan_tokens_per_split(const xq_cache_layout* L, int32_t batch, int32_t m
   }
   const int64_t unit = ps > 32 ? ps : 32;   // whole pages and whole 32-token tiles
   tps = ((tps + unit - 1) / unit) * unit;
-  if (tps > (int64_t)1 << 30) tps = (int64_t)1 << 30;
+  // a split spans at most kMaxSplitPages pages: the decode kernel keeps a split's block-table
+  // entries in registers
+  const int64_t cap = (int64_t)xq::kMaxSplitPages * ps;
+  if (tps > cap) tps = cap;
   return (int32_t)tps;
 }
 

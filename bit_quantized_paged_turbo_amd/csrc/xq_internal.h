@@ -10,6 +10,7 @@ constexpr int kHeadDim = 128;
 constexpr int kMaxGroup = 16;         // query heads per kv head: the 16 columns of one MFMA tile
 constexpr int kPartialStride = 132;   // floats per (seq, q head, split) partial: m, l, pad, acc[128]
 constexpr int kQDigitBytes = 256;     // per (seq, q head): 4 lanes x (2 k-chunks x 2 digits x 16 B)
+constexpr int kMaxSplitPages = 128;   // pages per split: the block-table window of a decode wave
 
 // Bytes of one stored code row for a dtype (bf16: 256).
 inline constexpr int row_code_bytes(int dtype) { return dtype == 0 ? 256 : 16 * dtype; }

@@ -89,16 +89,18 @@ int64_t xq_pool_bytes(const xq_cache_layout* layout);
 /*
  * Number of sequence partitions ("splits") the decode uses for a sequence of up to
  * max_context_len tokens. num_splits_hint = 0 lets the library choose from the batch
- * shape; a positive hint asks for that many page-aligned partitions (capped so that every
- * partition holds at least one page). Returns -1 on invalid arguments.
+ * shape; a positive hint asks for that many partitions. Partitions are whole pages and
+ * whole 32-token tiles, and span at most 128 pages, so the count returned can be smaller
+ * (short contexts) or larger (long contexts) than the hint. Returns -1 on invalid arguments.
  */
 int32_t xq_decode_num_splits(const xq_cache_layout* layout, int32_t batch,
                              int32_t num_q_heads, int32_t max_context_len,
                              int32_t num_splits_hint);
 
 /*
- * Workspace bytes xq_paged_decode_attention needs for these arguments (0 when every
- * sequence fits one partition). Returns -1 on invalid arguments.
+ * Workspace bytes xq_paged_decode_attention needs for these arguments: the prepared query
+ * (turbo types) and, with more than one partition, the partition partials. Returns -1 on
+ * invalid arguments.
  */
 int64_t xq_decode_workspace_bytes(const xq_cache_layout* layout, int32_t batch,
                                   int32_t num_q_heads, int32_t max_context_len,

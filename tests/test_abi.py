@@ -67,6 +67,9 @@ def test_split_planning(lib):
     assert xq.xq_decode_num_splits(L, 4, 16, 1000, 7) == 7
     assert xq.xq_decode_num_splits(L, 4, 16, 0, 0) == 1
     assert xq.xq_decode_num_splits(L, 4, 16, 100, -1) == -1
+    # a split spans at most 128 pages, whatever the hint
+    assert xq.xq_decode_num_splits(xq.CacheLayout(4, 8, 16, 9000), 1, 8, 65536, 1) == 32
+    assert xq.xq_decode_num_splits(xq.CacheLayout(3, 8, 64, 9000), 1, 8, 262144, 4) == 32
     # bf16 needs no query preparation: no workspace for a single split
     L = xq.CacheLayout(0, 8, 16, 9000)
     assert xq.xq_decode_workspace_bytes(L, 256, 16, 1022, 1) == 0
