@@ -50,8 +50,9 @@
 // every operand read linear in the lane index and V transposed; turbo3 and bf16 load into
 // registers, three tiles (two for bf16) in flight.
 //
-// The query digits are prepared once per (sequence, query head) by q_prep_kernel (rotation by
-// an in-register FWHT, scaling, digit split, packing in the operand layout) into the workspace.
+// Each wave prepares the query digits of its kv head's query heads itself (rotation by an
+// in-register FWHT, scaling, digit split, packing in the operand layout), from rows fetched by
+// LDS DMA ahead of its first tiles.
 // A sequence that fits one split is normalised, rotated back and stored by its wave; otherwise
 // (m, l, acc) partials go to the workspace and decode_combine_kernel merges them by
 // log-sum-exp, rotates back and stores.
@@ -103,6 +104,9 @@ template <> struct Stage<8> {
   static constexpr int kHalf = 2048, kDma = 2, kOps = 4 * kDma + 2, kSlot = 4 * kHalf + 128;
 };
 constexpr int kLdsPerCu = 160 * 1024;
+// LDS for the wave's query preparation: kMaxGroup rows of 256 B, then their fp32 scales
+constexpr int kQueryLds = kMaxGroup * 256 + kMaxGroup * 4;
+static_assert(Stage<4>::kSlot >= kQueryLds && Stage<8>::kSlot >= kQueryLds, "query rows fit one ring slot");
 // Paired-block QK (turbo4, turbo8): with at most this many query heads per kv head, the 16
 // columns of the QK tile hold two 16-token blocks of the tile side by side.
 constexpr int kPairMaxGroup = 8;
@@ -160,19 +164,15 @@ __device__ __forceinline__ uint32_t spread3to4(uint32_t x) {
 constexpr uint32_t kBias3 = 0x924924u;   // bit 2 of every 3-bit field: c -> c + 4
 
 // ---------------------------------------------------------------------------------------
-// Query preparation: q' = H q, q = rint(q' * 32000 / max|q'|), two signed digits, packed in
-// the QK operand layout. Four lanes per (sequence, query head) row, lane g owning dimensions
-// [32 g, 32 g + 32); sixteen rows per wave.
+// Query preparation, done by the decode wave itself: q' = H q, q = rint(q' * 32000 / max|q'|),
+// two signed digits, packed in the QK operand layout. The G query rows of the kv head arrive in
+// LDS (row h at 256 h, bf16); lane 4 h + g (h < G) owns dimensions [32 g, 32 g + 32) of head h,
+// reads them from bytes [256 h + 64 g, +64) and writes its 64 operand bytes over the same
+// range, so no lane touches another lane's bytes. The score scale of head h goes to sc[h].
 // ---------------------------------------------------------------------------------------
-constexpr int kPrepThreads = 256;
-
-template <int DT>
-__global__ __launch_bounds__(kPrepThreads) void q_prep_kernel(DecodeParams p) {
-  const int64_t t = (int64_t)blockIdx.x * kPrepThreads + threadIdx.x;
-  const int64_t row = t >> 2;                      // b * hq + j
-  const int g = (int)(t & 3);
-  if (row >= (int64_t)p.batch * p.hq) return;      // the four lanes of a row exit together
-  const uint4* src = reinterpret_cast<const uint4*>(p.q + row * D + 32 * g);
+template <int DT, bool PAIRED>
+__device__ __forceinline__ void prep_query_lane(uint8_t* qa, float* sc_out, int h, int g, float softmax_scale) {
+  const uint4* src = reinterpret_cast<const uint4*>(qa + 256 * h + 64 * g);
   float x[32];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -183,17 +183,17 @@ __global__ __launch_bounds__(kPrepThreads) void q_prep_kernel(DecodeParams p) {
     x[8 * i + 6] = bf16_lo(w.w); x[8 * i + 7] = bf16_hi(w.w);
   }
 #pragma unroll
-  for (int h = 1; h < 32; h <<= 1) {
+  for (int hh = 1; hh < 32; hh <<= 1) {
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
-      if ((e & h) == 0) {
-        const float a = x[e], c = x[e + h];
+      if ((e & hh) == 0) {
+        const float a = x[e], c = x[e + hh];
         x[e] = a + c;
-        x[e + h] = a - c;
+        x[e + hh] = a - c;
       }
     }
   }
-  // stages h = 32, 64: the partner of dimension 32 g + e is lane ^ 1, lane ^ 2
+  // stages 32, 64: the partner of dimension 32 g + e is lane ^ 1, lane ^ 2
 #pragma unroll
   for (int m = 1; m <= 2; m <<= 1) {
     const bool upper = (g & m) != 0;
@@ -211,22 +211,17 @@ __global__ __launch_bounds__(kPrepThreads) void q_prep_kernel(DecodeParams p) {
   }
   am = fmaxf(am, __shfl_xor(am, 1));
   am = fmaxf(am, __shfl_xor(am, 2));
-  const float inv = am > 0.f ? kQiMax / am : 0.f;
-  int qi[32];
-#pragma unroll
-  for (int e = 0; e < 32; ++e) qi[e] = (int)rintf(x[e] * inv);
   // The score scale is made positive (the sign goes into the digits) and nonzero (a zero
   // query or scale gives zero digits), so a maximum over unscaled scores is the maximum of the
-  // scores.
-  float sc = am > 0.f ? (am / kQiMax) * p.softmax_scale * kLog2e / (float)Codec<DT>::kKMul : 0.f;
-  const int sgn = sc < 0.f ? -1 : 1;
+  // scores. A K byte is c * kKMul, so the integer dot product is kKMul times q.c.
+  float sc = am > 0.f ? (am / kQiMax) * softmax_scale * kLog2e / (float)Codec<DT>::kKMul : 0.f;
   const bool zero = !(sc != 0.f);
+  const float inv = zero ? 0.f : (sc < 0.f ? -kQiMax : kQiMax) / am;
   sc = zero ? 1.f : fabsf(sc);
   // operand m, digit dg, dword w, byte b holds dimension (relative to 32 g)
   //   paired-block layout (turbo4/turbo8 with at most 8 heads per kv head), m = half p of the
   //   32 dimensions:  turbo4: 16 m + 8 (w >> 1) + 2 b + (w & 1)   turbo8: 16 m + 4 w + b
   //   one-block layout, m = k-chunk:  turbo4/3: 8 w + 2 b + m      turbo8: 16 m + 4 w + b
-  const bool paired = (DT == 4 || DT == 8) && p.group <= kPairMaxGroup;
   uint32_t word[2][2][4];
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
@@ -236,8 +231,8 @@ __global__ __launch_bounds__(kPrepThreads) void q_prep_kernel(DecodeParams p) {
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
         const int e = (DT == 8) ? (16 * m + 4 * w + bb)
-                                : (paired ? 16 * m + 8 * (w >> 1) + 2 * bb + (w & 1) : 8 * w + 2 * bb + m);
-        const int q = zero ? 0 : sgn * qi[e];
+                                : (PAIRED ? 16 * m + 8 * (w >> 1) + 2 * bb + (w & 1) : 8 * w + 2 * bb + m);
+        const int q = (int)rintf(x[e] * inv);
         const int d0 = ((q + 128) & 255) - 128;
         const int d1 = (q - d0) >> 8;
         lo |= (uint32_t)(d0 & 255) << (8 * bb);
@@ -247,16 +242,12 @@ __global__ __launch_bounds__(kPrepThreads) void q_prep_kernel(DecodeParams p) {
       word[m][1][w] = hi;
     }
   }
-  uint4* dst = reinterpret_cast<uint4*>(p.qdig + (row * 4 + g) * 64);
+  uint4* dst = reinterpret_cast<uint4*>(qa + 256 * h + 64 * g);
   dst[0] = make_uint4(word[0][0][0], word[0][0][1], word[0][0][2], word[0][0][3]);
   dst[1] = make_uint4(word[0][1][0], word[0][1][1], word[0][1][2], word[0][1][3]);
   dst[2] = make_uint4(word[1][0][0], word[1][0][1], word[1][0][2], word[1][0][3]);
   dst[3] = make_uint4(word[1][1][0], word[1][1][1], word[1][1][2], word[1][1][3]);
-  if (g == 0) {
-    // a K byte is c * kKMul, so the integer dot product is kKMul times q.c
-    p.qscale[row] = sc;
-    p.qoff[row] = 0;
-  }
+  if (g == 0) sc_out[h] = sc;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -896,41 +887,64 @@ void decode_split_kernel(DecodeParams p) {
   constexpr int kOutBytes = kMaxGroup * (D + 4) * 4 + kThreads * 4;
   constexpr int kRingBytes = DEPTH * Stage<DT>::kSlot;
   constexpr int kSmemBytes = kOutBytes > kRingBytes ? kOutBytes : kRingBytes;
+  static_assert(kOutBytes >= kQueryLds, "query rows fit the output rows' LDS");
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
   auto ob = reinterpret_cast<float (*)[D + 4]>(smem);
 
   const int col = lane & 15, g = lane >> 4;
 
   // ---- query operands ---------------------------------------------------------------------
+  // turbo types: the wave rotates and quantizes its G query rows itself (prep_query_lane); the
+  // rows arrive by LDS DMA ahead of the first tiles, so the work overlaps their latency
   const bool pair = Stage<DT>::kOn && G <= kPairMaxGroup;
   const PairLane pl = pair_lane(lane, G);
   v4i qi[2][2] = {};
   v4i qj[4][2] = {};
   v8bf qb[4] = {};
   float qs = 0.f;
-  if (pair) {
-    // block-diagonal query operand: lane group g carries token block g >> 1
-    const int64_t row = (int64_t)b * p.hq + qh0 + pl.hn;
-    if (pl.jn == pl.kb) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const v4i* s = reinterpret_cast<const v4i*>(p.qdig + (row * 4 + m) * 64 + 32 * pl.kp);
-        qj[m][0] = s[0];
-        qj[m][1] = s[1];
-      }
+  auto issue_query = [&](uint8_t* qa) __attribute__((always_inline)) {   // G rows of 256 B to qa, 1 KB per instruction
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(p.q + ((int64_t)b * p.hq + qh0) * D), (short)0, G * 256, kBufferConfig);
+    for (int i = 0; i < (G + 3) >> 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(qa + 1024 * i), 16, 16 * lane, 1024 * i, 0, 0);
+  };
+  auto load_query = [&](uint8_t* qa) __attribute__((always_inline)) {    // after the rows have landed in qa
+    float* qsc = reinterpret_cast<float*>(qa + kMaxGroup * 256);
+    if (lane < 4 * G) {
+      if (pair) prep_query_lane<DT, true>(qa, qsc, lane >> 2, lane & 3, p.softmax_scale);
+      else prep_query_lane<DT, false>(qa, qsc, lane >> 2, lane & 3, p.softmax_scale);
     }
-    qs = p.qscale[row];
-  } else if (col < G) {
-    const int64_t row = (int64_t)b * p.hq + qh0 + col;
-    if constexpr (DT != 0) {
-      const v4i* s = reinterpret_cast<const v4i*>(p.qdig + (row * 4 + g) * 64);
+    __syncthreads();
+    if (pair) {
+      // block-diagonal query operand: lane group g carries token block g >> 1
+      if (pl.jn == pl.kb) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const v4i* s = reinterpret_cast<const v4i*>(qa + (pl.hn * 4 + m) * 64 + 32 * pl.kp);
+          qj[m][0] = s[0];
+          qj[m][1] = s[1];
+        }
+      }
+      qs = qsc[pl.hn];
+    } else if (col < G) {
+      const v4i* s = reinterpret_cast<const v4i*>(qa + (col * 4 + g) * 64);
       qi[0][0] = s[0]; qi[0][1] = s[1]; qi[1][0] = s[2]; qi[1][1] = s[3];
-      qs = p.qscale[row];
-    } else {
+      qs = qsc[col];
+    }
+    // the operand reads complete before a later DMA may refill this LDS
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+  if constexpr (DT == 0) {
+    if (col < G) {
+      const int64_t row = (int64_t)b * p.hq + qh0 + col;
       const v8bf* s = reinterpret_cast<const v8bf*>(p.q + row * D + 32 * g);
       qb[0] = s[0]; qb[1] = s[1]; qb[2] = s[2]; qb[3] = s[3];
       qs = p.softmax_scale * kLog2e;
     }
+  } else if constexpr (!Stage<DT>::kOn) {
+    issue_query(smem);
+    wait_vm<0>();
+    load_query(smem);
   }
 
   WaveState st;
@@ -993,23 +1007,29 @@ void decode_split_kernel(DecodeParams p) {
       }
     }
   };
-  auto run = [&](const Tile<DT>& t, int i) {
+  auto run = [&](const Tile<DT>& t, int i) __attribute__((always_inline)) {
     const int t0 = tok_begin + 32 * i;
     process_tile<DT>(t, st, qi, qb, qs, tok_end - t0 - 4 * g, t0 + 32 <= tok_end, col, g);
   };
-  auto main_loop = [&](auto kFast, auto kPair) {
+  auto main_loop = [&](auto kFast, auto kPair) __attribute__((always_inline)) {
     if constexpr (Stage<DT>::kOn) {
       // slot i % DEPTH holds tile i
       using S = Stage<DT>;
       static_assert((DEPTH - 1) * S::kOps <= kMaxVmcnt, "vmcnt field is 6 bits");
       const DmaOffsets dof = dma_offsets<DT>(lane);
-      auto stage = [&](int i) {
+      auto stage = [&](int i) __attribute__((always_inline)) {
         HalfAddr a[2];
         addr(kFast, tok_begin + 32 * i, a);
         stage_tile<DT, decltype(kFast)::value>(smem + (i % DEPTH) * S::kSlot, a, dof, lane);
       };
       std::conditional_t<decltype(kPair)::value, PairTile<DT>, Tile<DT>> tile;
+      // the query rows go to the last ring slot, which the loop first fills with tile DEPTH - 1
+      uint8_t* qa = smem + (DEPTH - 1) * S::kSlot;
+      issue_query(qa);
       for (int i = 0; i < DEPTH - 1 && i < ntiles; ++i) stage(i);
+      // loads complete in issue order: the rows are in once at most the staged tiles' are pending
+      wait_tiles<S::kOps, 0, DEPTH - 1>(min(DEPTH - 1, ntiles));
+      load_query(qa);
       for (int it = 0; it < ntiles; ++it) {
         if (it + DEPTH - 1 < ntiles) stage(it + DEPTH - 1);
         // this tile's instructions are complete once at most those of the tiles staged after it
@@ -1026,7 +1046,7 @@ void decode_split_kernel(DecodeParams p) {
       }
     } else {
       constexpr int kDepth = kDepthOf<DT>;
-      auto fetch = [&](Tile<DT>& t, int i) {
+      auto fetch = [&](Tile<DT>& t, int i) __attribute__((always_inline)) {
         HalfAddr a[2];
         addr(kFast, tok_begin + 32 * i, a);
         load_tile<DT>(t, a, lo);
@@ -1239,11 +1259,6 @@ void launch_split(const DecodeParams& p, hipStream_t stream) {
 
 template <int DT>
 hipError_t launch_dt(const DecodeParams& p, hipStream_t stream) {
-  if constexpr (DT != 0) {
-    const int64_t lanes = (int64_t)p.batch * p.hq * 4;
-    hipLaunchKernelGGL((q_prep_kernel<DT>), dim3((unsigned)((lanes + kPrepThreads - 1) / kPrepThreads)),
-                       dim3(kPrepThreads), 0, stream, p);
-  }
   if constexpr (Stage<DT>::kOn) {
     switch (pick_depth<DT>(p)) {
       case 8: launch_split<DT, (Stage<DT>::kOps * 7 <= kMaxVmcnt ? 8 : 6)>(p, stream); break;

@@ -203,9 +203,6 @@ xq_status xq_paged_decode_attention(const xq_cache_layout* layout, const void* q
   p.block_tables = block_tables;
   p.context_lens = context_lens;
   p.out = out;
-  p.qdig = ws.qdig_bytes ? wsp + ws.qdig_off : nullptr;
-  p.qscale = ws.qaux_bytes ? reinterpret_cast<float*>(wsp + ws.qaux_off) : nullptr;
-  p.qoff = ws.qaux_bytes ? reinterpret_cast<int32_t*>(wsp + ws.qaux_off) + (int64_t)batch * num_q_heads : nullptr;
   p.partials = ws.part_bytes ? reinterpret_cast<float*>(wsp + ws.part_off) : nullptr;
   p.block_bytes = block_bytes_of(layout);
   p.page_stride = p.block_bytes * layout->num_kv_heads;

@@ -9,7 +9,6 @@ namespace xq {
 constexpr int kHeadDim = 128;
 constexpr int kMaxGroup = 16;         // query heads per kv head: the 16 columns of one MFMA tile
 constexpr int kPartialStride = 132;   // floats per (seq, q head, split) partial: m, l, pad, acc[128]
-constexpr int kQDigitBytes = 256;     // per (seq, q head): 4 lanes x (2 k-chunks x 2 digits x 16 B)
 constexpr int kMaxSplitPages = 128;   // pages per split: the block-table window of a decode wave
 
 // Bytes of one stored code row for a dtype (bf16: 256).
@@ -17,22 +16,16 @@ inline constexpr int row_code_bytes(int dtype) { return dtype == 0 ? 256 : 16 * 
 
 inline constexpr int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
-// Workspace of one decode call: [query digits][query scale, offset][split partials].
+// Workspace of one decode call: the split partials (only with more than one split).
 struct WorkspaceLayout {
-  int64_t qdig_off, qdig_bytes;      // uint8 [batch][hq][kQDigitBytes]  (turbo types)
-  int64_t qaux_off, qaux_bytes;      // {float scale, int32 offset} [batch][hq]  (turbo types)
   int64_t part_off, part_bytes;      // float [batch][hq][nsplits][kPartialStride]  (nsplits > 1)
   int64_t total;
 };
 
 inline WorkspaceLayout workspace_layout(int dtype, int64_t batch, int64_t hq, int64_t nsplits) {
+  (void)dtype;
   WorkspaceLayout w{};
-  const bool turbo = dtype != 0;
-  w.qdig_off = 0;
-  w.qdig_bytes = turbo ? align256(batch * hq * kQDigitBytes) : 0;
-  w.qaux_off = w.qdig_off + w.qdig_bytes;
-  w.qaux_bytes = turbo ? align256(batch * hq * 8) : 0;
-  w.part_off = w.qaux_off + w.qaux_bytes;
+  w.part_off = 0;
   w.part_bytes = nsplits > 1 ? align256(batch * hq * nsplits * kPartialStride * 4) : 0;
   w.total = w.part_off + w.part_bytes;
   return w;
@@ -61,9 +54,6 @@ struct DecodeParams {
   const int32_t* block_tables;  // [batch][maxp]
   const int32_t* context_lens;  // [batch]
   float* out;                   // [batch][hq][128]
-  uint8_t* qdig;                // workspace: query digits (turbo types)
-  float* qscale;                // workspace: per (seq, q head) score scale (log2 domain)
-  int32_t* qoff;                // workspace: per (seq, q head) integer offset of the code bias
   float* partials;              // workspace: [batch][hq][nsplits][kPartialStride] (nsplits > 1)
   int64_t page_stride;
   int64_t block_bytes;

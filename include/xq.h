@@ -98,9 +98,8 @@ int32_t xq_decode_num_splits(const xq_cache_layout* layout, int32_t batch,
                              int32_t num_splits_hint);
 
 /*
- * Workspace bytes xq_paged_decode_attention needs for these arguments: the prepared query
- * (turbo types) and, with more than one partition, the partition partials. Returns -1 on
- * invalid arguments.
+ * Workspace bytes xq_paged_decode_attention needs for these arguments: the partition
+ * partials, 0 when every sequence fits one partition. Returns -1 on invalid arguments.
  */
 int64_t xq_decode_workspace_bytes(const xq_cache_layout* layout, int32_t batch,
                                   int32_t num_q_heads, int32_t max_context_len,

@@ -51,9 +51,8 @@ def test_invalid_layouts(lib, bad):
 def test_split_planning(lib):
     L = xq.CacheLayout(3, 8, 64, 4096)
     assert xq.xq_decode_num_splits(L, 1, 40, 262144, 256) == 256
-    # query digits (256 B) and scale/offset (8 B) per (sequence, q head), then the partials
-    qdig, qaux = 40 * 256, 512
-    assert xq.xq_decode_workspace_bytes(L, 1, 40, 262144, 256) == qdig + qaux + 40 * 256 * 132 * 4
+    # the partials: (m, l, pad, acc[128]) per (sequence, q head, split)
+    assert xq.xq_decode_workspace_bytes(L, 1, 40, 262144, 256) == 40 * 256 * 132 * 4
     L = xq.CacheLayout(4, 8, 16, 9000)
     # library policy: whole pages / 32-token tiles per split, partials only when split
     n = xq.xq_decode_num_splits(L, 256, 16, 1022, 0)
@@ -61,9 +60,9 @@ def test_split_planning(lib):
     tps = -(-1022 // n)
     assert xq.xq_decode_num_splits(L, 256, 16, 1022, n) == n
     part = 256 * 16 * n * 132 * 4 if n > 1 else 0
-    assert xq.xq_decode_workspace_bytes(L, 256, 16, 1022, 0) == 256 * 16 * 256 + 256 * 16 * 8 + part
+    assert xq.xq_decode_workspace_bytes(L, 256, 16, 1022, 0) == part
     assert xq.xq_decode_num_splits(L, 256, 16, 1022, 1) == 1
-    assert xq.xq_decode_workspace_bytes(L, 256, 16, 1022, 1) == 256 * 16 * 256 + 256 * 16 * 8
+    assert xq.xq_decode_workspace_bytes(L, 256, 16, 1022, 1) == 0
     assert xq.xq_decode_num_splits(L, 4, 16, 1000, 7) == 7
     assert xq.xq_decode_num_splits(L, 4, 16, 0, 0) == 1
     assert xq.xq_decode_num_splits(L, 4, 16, 100, -1) == -1
@@ -92,7 +91,7 @@ def test_decode_argument_errors(lib):
     assert _decode_status(lib, L, q=None) == xq.EINVAL
     assert _decode_status(lib, L, k=8) == xq.EINVAL            # misaligned pool
     assert _decode_status(lib, L, maxctx=65) == xq.EINVAL      # > maxp * page_size
-    assert _decode_status(lib, L, splits=2) == xq.EWORKSPACE   # query digits and partials
+    assert _decode_status(lib, L, splits=2) == xq.EWORKSPACE   # partials of two splits
     assert b"workspace" in lib.xq_last_error()
     assert _decode_status(lib, L, batch=0) == xq.OK            # nothing to do
     bad = xq.CacheLayout(4, 2, 20, 10)
