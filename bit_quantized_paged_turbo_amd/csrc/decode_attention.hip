@@ -820,6 +820,201 @@ __device__ __forceinline__ void process_pair_tile(const PairTile<DT>& t, WaveSta
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Quad-block tile (turbo4 and turbo8 with G <= 4, a ring of at least four slots): the pairing
+// above taken to four 16-token blocks, the halves of two consecutive tiles. Column n = G j + h
+// (j = 0..3; n >= 4 G repeats column n mod 4 G); lane group gg carries block gg in the query
+// operand; MFMA m (0..7) covers dimensions [16 m, 16 m + 16) of all four blocks, so eight MFMAs
+// per digit cover 64 tokens, as in the paired layout, while a lane holds 4 scores per 64 tokens.
+// PV runs per tile, block j's weights in the k slots of tile j >> 1, half j & 1.
+// ---------------------------------------------------------------------------------------
+struct QuadLane {
+  int jn;      // token block of this lane's column (0..3)
+  int hn;      // query head of this lane's column
+  int ne;      // the lane's effective column, G jn + hn
+};
+
+__device__ __forceinline__ QuadLane quad_lane(int lane, int G) {
+  const int n = lane & 15;
+  const int ne = n < 4 * G ? n : n % (4 * G);
+  return QuadLane{ne / G, ne % G, ne};
+}
+
+template <int DT> struct QuadK;
+template <> struct QuadK<4> { v4i k[4]; };   // the lane's token row: 16 B per 32 dims
+template <> struct QuadK<8> { v4i k[8]; };   // 16 B per 16 dims
+
+template <int DT>
+__device__ __forceinline__ void read_quad_k(QuadK<DT>& t, const uint8_t* slot0, const uint8_t* slot1, int lane) {
+  using S = Stage<DT>;
+  const int gg = lane >> 4, tk = lane & 15;
+  const uint8_t* kh = ((gg >> 1) ? slot1 : slot0) + (gg & 1) * S::kHalf;   // block gg, token tk
+  if constexpr (DT == 4) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) t.k[c] = *reinterpret_cast<const v4i*>(kh + 16 * (tk + 16 * c));
+  } else {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) t.k[m] = *reinterpret_cast<const v4i*>(kh + 1024 * (m & 1) + 16 * (tk + 16 * (m >> 1)));
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void quad_qk(const QuadK<DT>& t, const v4i (&qq)[8][2], v4i& s0, v4i& s1) {
+  s0 = v4i{0, 0, 0, 0};
+  s1 = v4i{0, 0, 0, 0};
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    v4i a;
+    if constexpr (DT == 4) {
+      const uint32_t x0 = (uint32_t)t.k[m >> 1][2 * (m & 1)], x1 = (uint32_t)t.k[m >> 1][2 * (m & 1) + 1];
+      a = v4i{(int)((x0 << 4) & 0xf0f0f0f0u), (int)(x0 & 0xf0f0f0f0u), (int)((x1 << 4) & 0xf0f0f0f0u),
+              (int)(x1 & 0xf0f0f0f0u)};
+    } else {
+      a = t.k[m];
+    }
+    s0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qq[m][0], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qq[m][1], s1, 0, 0, 0);
+  }
+}
+
+// V operand of one tile as fp16 subnormals and the PV MFMAs of that tile against A = (Ahi, Alo).
+template <int DT>
+__device__ __forceinline__ void tile_pv(const uint8_t* slot, int lane, v8h Ahi, v8h Alo, WaveState& st) {
+  using S = Stage<DT>;
+  struct {
+    std::conditional_t<DT == 4, int, v2i> v[8];
+  } t;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (DT == 4)
+        t.v[4 * h + r] = *reinterpret_cast<const int*>(slot + (2 + h) * S::kHalf + 256 * r + 4 * lane);
+      else
+        t.v[4 * h + r] = *reinterpret_cast<const v2i*>(slot + (2 + h) * S::kHalf + 512 * r + 8 * lane);
+    }
+  }
+  const v8h Bb = __builtin_bit_cast(v8h, make_uint4(0x00800080u, 0x00800080u, 0x00800080u, 0x00800080u));
+  st.accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, Bb, st.accb, 0, 0, 0);
+  st.accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, Bb, st.accb, 0, 0, 0);
+  uint32_t e[8], o[8];
+  if constexpr (DT == 4) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t x = (uint32_t)t.v[j];
+      e[j] = ((x << 4) & 0xf0f0f0f0u) ^ 0x80808080u;   // even dims, (c + 8) << 4
+      o[j] = (x & 0xf0f0f0f0u) ^ 0x80808080u;          // odd dims
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      e[j] = (uint32_t)t.v[j][0] ^ 0x80808080u;     // c + 128
+      o[j] = (uint32_t)t.v[j][1] ^ 0x80808080u;
+    }
+  }
+#pragma unroll
+  for (int tau = 0; tau < 8; ++tau) {
+    const uint32_t* src;
+    int i;
+    if constexpr (DT == 8) {
+      src = tau < 4 ? e : o;
+      i = tau & 3;
+    } else {
+      src = (tau & 1) ? o : e;
+      i = tau >> 1;
+    }
+    const uint32_t sel = (uint32_t)i | (0x0cu << 8) | ((uint32_t)(4 + i) << 16) | (0x0cu << 24);
+    const v8h B = __builtin_bit_cast(v8h, make_uint4(perm(src[1], src[0], sel), perm(src[3], src[2], sel),
+                                                     perm(src[5], src[4], sel), perm(src[7], src[6], sel)));
+    st.acc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, B, st.acc[tau], 0, 0, 0);
+    st.acc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, B, st.acc[tau], 0, 0, 0);
+  }
+}
+
+// One 64-token group: tiles in slot0 (tokens 0..31) and slot1 (32..63; all masked when absent).
+template <int DT>
+__device__ __forceinline__ void process_quad(const uint8_t* slot0, const uint8_t* slot1, WaveState& st,
+                                             const v4i (&qq)[8][2], float qs, int lim, bool full,
+                                             const QuadLane& ql, int G, int lane) {
+  using S = Stage<DT>;
+  const int gg = lane >> 4;
+  v4i s0, s1;
+  {
+    QuadK<DT> t;
+    read_quad_k<DT>(t, slot0, slot1, lane);
+    quad_qk<DT>(t, qq, s0, s1);
+  }
+  // scales of tokens 4 gg + r of block jn
+  const uint8_t* ss = ((ql.jn >> 1) ? slot1 : slot0) + 4 * S::kHalf + 32 * (ql.jn & 1) + 8 * gg;
+  const v2i ksw = *reinterpret_cast<const v2i*>(ss);
+  const v2i vsw = *reinterpret_cast<const v2i*>(ss + 64);
+  const uint32_t ks[4] = {(uint32_t)ksw[0], (uint32_t)ksw[0] >> 16, (uint32_t)ksw[1], (uint32_t)ksw[1] >> 16};
+  uint32_t sv[4] = {(uint32_t)vsw[0] & 0xffffu, (uint32_t)vsw[0] >> 16, (uint32_t)vsw[1] & 0xffffu,
+                    (uint32_t)vsw[1] >> 16};
+  float y[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int zi = (s1[r] << 8) + s0[r];
+    y[r] = __builtin_fmaf(half_lo(ks[r]), (float)zi, 0.f);
+  }
+  if (!full) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool ok = 16 * ql.jn + r < lim;
+      y[r] = ok ? y[r] : -INFINITY;
+      sv[r] = ok ? sv[r] : 0u;    // unwritten or absent slots may hold anything
+    }
+  }
+  const uint32_t smax = max(max(sv[0], sv[1]), max(sv[2], sv[3]));
+  const float ymax = fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3]));
+  float mx = __builtin_fmaf(ymax, qs, (float)(smax >> 10));
+  if (__builtin_expect(__any(mx > st.m + kLazy), 0)) {
+    // head maximum over the lanes of head hn: columns hn + G j (j = 0..3), all lane groups
+    const int base = lane & 48, J4 = 4 * G;
+    mx = fmaxf(mx, __shfl(mx, base | ((ql.ne + G) % J4)));
+    mx = fmaxf(mx, __shfl(mx, base | ((ql.ne + 2 * G) % J4)));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool up = mx > st.m + kLazy;
+    const float f = up ? __builtin_amdgcn_exp2f(st.m - mx) : 1.f;
+    st.m = up ? mx : st.m;
+    st.l *= f;
+    const int g4 = gg * 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int nr = g4 + r;
+      const int ner = nr < J4 ? nr : nr % J4;
+      const float fr = __shfl(f, ner % G);
+#pragma unroll
+      for (int tau = 0; tau < 8; ++tau) st.acc[tau][r] *= fr;
+      st.accb[r] *= fr;
+    }
+  }
+  const float nref = kWeightExp - st.m;
+  float pw[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(y[r], qs, nref));
+    st.l += pr;
+    pw[r] = __builtin_fmaf(half_lo(sv[r]), pr, 0.f);
+  }
+  const auto h01 = __builtin_amdgcn_cvt_pkrtz(pw[0], pw[1]);
+  const auto h23 = __builtin_amdgcn_cvt_pkrtz(pw[2], pw[3]);
+  const auto l01 = __builtin_amdgcn_cvt_pkrtz(__builtin_fmaf((float)h01[0], -1.f, pw[0]),
+                                              __builtin_fmaf((float)h01[1], -1.f, pw[1]));
+  const auto l23 = __builtin_amdgcn_cvt_pkrtz(__builtin_fmaf((float)h23[0], -1.f, pw[2]),
+                                              __builtin_fmaf((float)h23[1], -1.f, pw[3]));
+  const uint32_t hi01 = __builtin_bit_cast(uint32_t, h01), hi23 = __builtin_bit_cast(uint32_t, h23);
+  const uint32_t lo01 = __builtin_bit_cast(uint32_t, l01), lo23 = __builtin_bit_cast(uint32_t, l23);
+#pragma unroll
+  for (int tl = 0; tl < 2; ++tl) {
+    const bool a = ql.jn == 2 * tl, c = ql.jn == 2 * tl + 1;
+    const v8h Ahi = __builtin_bit_cast(v8h, make_uint4(a ? hi01 : 0u, a ? hi23 : 0u, c ? hi01 : 0u, c ? hi23 : 0u));
+    const v8h Alo = __builtin_bit_cast(v8h, make_uint4(a ? lo01 : 0u, a ? lo23 : 0u, c ? lo01 : 0u, c ? lo23 : 0u));
+    tile_pv<DT>(tl ? slot1 : slot0, lane, Ahi, Alo, st);
+  }
+}
+
 // In-place unnormalized FWHT of `rows` rows of 128 floats in LDS, by one wave.
 __device__ __forceinline__ void fwht_wave(float (*x)[D + 4], int rows, int lane) {
   for (int h = 1; h < D; h <<= 1) {
@@ -838,34 +1033,47 @@ __device__ __forceinline__ void fwht_wave(float (*x)[D + 4], int rows, int lane)
 // One wave per work unit (split, kv head, sequence): the wave walks the unit's 32-token tiles
 // in order, keeping kDepth of them in flight, and finishes the unit alone (no cross-wave merge,
 // no barrier in the loop).
-template <int DT> constexpr int kWavesPerEu = DT == 0 ? 1 : (DT == 3 ? 2 : 3);
+// Waves per SIMD the register budget is sized for: deep rings (4+ slots) are only picked when
+// at most two waves share a SIMD.
+template <int DT, int DEPTH> constexpr int kWavesPerEu = DT == 0 ? 1 : (DT == 3 ? 2 : (DEPTH >= 4 ? 2 : 3));
 
 // DEPTH: tiles in flight per wave on the staged path (LDS slots); chosen at launch from how
 // many waves share a compute unit, so that the LDS of the resident waves holds as many tiles
 // in flight as it can.
 template <int DT, int DEPTH>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEu<DT>)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEu<DT, DEPTH>)))
 void decode_split_kernel(DecodeParams p) {
-  // Work unit of this wave. Workgroups go to the eight XCDs round-robin by id, so the ids of the
-  // kv heads of one (split, sequence) are spaced by 8: they run on one XCD, whose L2 then fetches
-  // each line of a page once for all of them (a page's kv-head blocks are adjacent and need not
-  // be line aligned). A tail that does not fill whole sets maps straight.
+  // Work unit of this wave. Workgroups go to the eight XCDs round-robin by id (XCD = id mod 8).
+  // The kv heads of one (split, sequence) share an XCD, whose L2 then fetches each line of a
+  // page once for all of them (a page's kv-head blocks are adjacent but not line aligned).
+  // With a batch that is a multiple of 8, split s of sequence b goes to XCD (b + s) mod 8, and
+  // within an XCD first splits come first: every sequence is spread over all XCDs, every XCD
+  // gets the same number of (long) first splits, and those start first. Otherwise (the
+  // leftover ids too) units map in (sequence, split) order.
   int split, kvh, b;
   {
     const uint32_t id = blockIdx.x, hkv = (uint32_t)p.hkv;
     const uint32_t units = (uint32_t)p.nsplits * hkv * (uint32_t)p.batch;
     const uint32_t full = units / (8u * hkv) * (8u * hkv);
-    uint32_t group;
-    if (id < full) {
-      const uint32_t slot = id >> 3;
+    if ((p.batch & 7) == 0) {
+      const uint32_t xcd = id & 7u, slot = id >> 3;
       kvh = (int)(slot % hkv);
-      group = slot / hkv * 8u + (id & 7u);
+      const uint32_t r = slot / hkv, per = (uint32_t)p.batch >> 3;
+      split = (int)(r / per);
+      b = (int)(8u * (r % per) + ((xcd - (uint32_t)split) & 7u));
     } else {
-      kvh = (int)(id % hkv);
-      group = id / hkv;
+      uint32_t group;
+      if (id < full) {
+        const uint32_t slot = id >> 3;
+        kvh = (int)(slot % hkv);
+        group = slot / hkv * 8u + (id & 7u);
+      } else {
+        kvh = (int)(id % hkv);
+        group = id / hkv;
+      }
+      split = (int)(group % (uint32_t)p.nsplits);
+      b = (int)(group / (uint32_t)p.nsplits);
     }
-    split = (int)(group % (uint32_t)p.nsplits);
-    b = (int)(group / (uint32_t)p.nsplits);
   }
   const int lane = threadIdx.x;
   const int G = p.group;
@@ -897,9 +1105,12 @@ void decode_split_kernel(DecodeParams p) {
   // turbo types: the wave rotates and quantizes its G query rows itself (prep_query_lane); the
   // rows arrive by LDS DMA ahead of the first tiles, so the work overlaps their latency
   const bool pair = Stage<DT>::kOn && G <= kPairMaxGroup;
+  const bool quad = Stage<DT>::kOn && DEPTH >= 4 && G <= 4;   // the quad-block layout (pair too)
   const PairLane pl = pair_lane(lane, G);
+  const QuadLane ql = quad_lane(lane, G);
   v4i qi[2][2] = {};
   v4i qj[4][2] = {};
+  v4i qq[8][2] = {};
   v8bf qb[4] = {};
   float qs = 0.f;
   auto issue_query = [&](uint8_t* qa) __attribute__((always_inline)) {   // G rows of 256 B to qa, 1 KB per instruction
@@ -915,7 +1126,18 @@ void decode_split_kernel(DecodeParams p) {
       else prep_query_lane<DT, false>(qa, qsc, lane >> 2, lane & 3, p.softmax_scale);
     }
     __syncthreads();
-    if (pair) {
+    if (quad) {
+      // block-diagonal query operand: lane group g carries token block g
+      if (ql.jn == g) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const v4i* s = reinterpret_cast<const v4i*>(qa + (ql.hn * 4 + (m >> 1)) * 64 + 32 * (m & 1));
+          qq[m][0] = s[0];
+          qq[m][1] = s[1];
+        }
+      }
+      qs = qsc[ql.hn];
+    } else if (pair) {
       // block-diagonal query operand: lane group g carries token block g >> 1
       if (pl.jn == pl.kb) {
 #pragma unroll
@@ -1026,6 +1248,24 @@ void decode_split_kernel(DecodeParams p) {
       // the query rows go to the last ring slot, which the loop first fills with tile DEPTH - 1
       uint8_t* qa = smem + (DEPTH - 1) * S::kSlot;
       issue_query(qa);
+      if constexpr (decltype(kPair)::value && DEPTH >= 4) {
+        if (quad) {
+          // two tiles per step; the step stages the two tiles whose slots the previous step freed
+          for (int i = 0; i < DEPTH - 2 && i < ntiles; ++i) stage(i);
+          wait_tiles<S::kOps, 0, DEPTH - 1>(min(DEPTH - 2, ntiles));
+          load_query(qa);
+          for (int it = 0; it < ntiles; it += 2) {
+            if (it + DEPTH - 2 < ntiles) stage(it + DEPTH - 2);
+            if (it + DEPTH - 1 < ntiles) stage(it + DEPTH - 1);
+            // tiles it, it + 1 are in once at most the tiles staged after them are outstanding
+            wait_tiles<S::kOps, 0, DEPTH - 1>(max(0, min(DEPTH - 2, ntiles - 2 - it)));
+            const int t0 = tok_begin + 32 * it;
+            process_quad<DT>(smem + (it % DEPTH) * S::kSlot, smem + ((it + 1) % DEPTH) * S::kSlot, st, qq, qs,
+                             tok_end - t0 - 4 * g, t0 + 64 <= tok_end, ql, G, lane);
+          }
+          return;
+        }
+      }
       for (int i = 0; i < DEPTH - 1 && i < ntiles; ++i) stage(i);
       // loads complete in issue order: the rows are in once at most the staged tiles' are pending
       wait_tiles<S::kOps, 0, DEPTH - 1>(min(DEPTH - 1, ntiles));
@@ -1082,14 +1322,15 @@ void decode_split_kernel(DecodeParams p) {
 
   const float unit = (float)(1 << Codec<DT>::kVShift);
   if (pair) {
-    // ---- finish a paired-block unit: rows n and G + n of the product are head n's two block
-    // sums; the normaliser of head n is the sum over the lanes of columns n and G + n ---------
+    // ---- finish a paired (J = 2) or quad (J = 4) block unit: rows n + G j of the product are
+    // head n's block sums; the normaliser of head n is the sum over the lanes of those columns --
+    const int J = quad ? 4 : 2;
     float* lsum = reinterpret_cast<float*>(smem + kMaxGroup * (D + 4) * 4);
     __syncthreads();   // the ring is drained (the last tile waited for everything): reuse it
     lsum[lane] = st.l;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (4 * g + r < 2 * G) {
+      if (4 * g + r < J * G) {
 #pragma unroll
         for (int tau = 0; tau < 8; ++tau) ob[4 * g + r][8 * col + tau] = (st.acc[tau][r] - st.accb[r]) * unit;
       }
@@ -1097,13 +1338,19 @@ void decode_split_kernel(DecodeParams p) {
     auto head_l = [&](int h) {
       float l = 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) l += lsum[16 * q + h] + lsum[16 * q + G + h];
+      for (int q = 0; q < 4; ++q)
+        for (int j = 0; j < J; ++j) l += lsum[16 * q + G * j + h];
       return l;
+    };
+    auto head_acc = [&](int h, int d) {
+      float a = 0.f;
+      for (int j = 0; j < J; ++j) a += ob[G * j + h][d];
+      return a;
     };
     if (nsplit_b == 1) {
       for (int k = lane; k < G * D; k += kThreads) {
         const int h = k >> 7, d = k & 127;
-        ob[h][d] = (ob[h][d] + ob[G + h][d]) / head_l(h);
+        ob[h][d] = head_acc(h, d) / head_l(h);
       }
       fwht_wave(ob, G, lane);
       for (int k = lane; k < G * D; k += kThreads) outp[k] = ob[k >> 7][k & 127] * kRotC;
@@ -1111,7 +1358,7 @@ void decode_split_kernel(DecodeParams p) {
       for (int k = lane; k < G * D; k += kThreads) {
         const int h = k >> 7, d = k & 127;
         float* part = p.partials + (((int64_t)b * p.hq + qh0 + h) * p.nsplits + split) * kPartialStride;
-        part[4 + d] = ob[h][d] + ob[G + h][d];
+        part[4 + d] = head_acc(h, d);
       }
       if (lane < G) {   // lane n < G: column n is head n, block 0
         float* part = p.partials + (((int64_t)b * p.hq + qh0 + lane) * p.nsplits + split) * kPartialStride;
@@ -1165,21 +1412,22 @@ void decode_split_kernel(DecodeParams p) {
   }
 }
 
-// Merge split partials of one (sequence, q head) and rotate back. 256 threads: thread
-// (s0 = t / 32, d4 = t % 32) sums dimensions 4 d4 .. 4 d4 + 3 over splits s0, s0 + 8, ...
-constexpr int kCombThreads = 256;
-
-template <int DT>
+// Merge split partials of one (sequence, q head) and rotate back. THREADS = 32 * groups:
+// thread (s0 = t / 32, d4 = t % 32) sums dimensions 4 d4 .. 4 d4 + 3 over splits s0,
+// s0 + groups, ..., four splits per step with their loads issued together (128 threads for a
+// few splits, 512 for many).
+template <int DT, int kCombThreads>
 __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodeParams p) {
+  constexpr int kCombGroups = kCombThreads / 32;
   const int qh = blockIdx.x, b = blockIdx.y;
   const int t = threadIdx.x;
   const int L = min(p.context_lens[b], p.max_context_len);
   const int ns = (L + p.tokens_per_split - 1) / p.tokens_per_split;
   if (ns <= 1) return;  // written by the split kernel
   const float* part = p.partials + ((int64_t)b * p.hq + qh) * p.nsplits * kPartialStride;
-  __shared__ float red[kCombThreads / 64];
-  __shared__ float4 accs[8][32];
-  __shared__ float lsum[8];
+  __shared__ float red[kCombThreads / 64 > 0 ? kCombThreads / 64 : 1];
+  __shared__ float4 accs[kCombGroups][32];
+  __shared__ float lsum[kCombGroups];
   __shared__ float o[D];
 
   // global reference M = max_s m_s
@@ -1188,19 +1436,30 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodePara
   for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
   if ((t & 63) == 0) red[t >> 6] = mx;
   __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+#pragma unroll
+  for (int k = 0; k < kCombThreads / 64; ++k) mx = fmaxf(mx, red[k]);
 
   // weighted sums of l and acc
   const int s0 = t >> 5, d4 = t & 31;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float l = 0.f;
-  for (int s = s0; s < ns; s += 8) {
-    const float* ps = part + (int64_t)s * kPartialStride;
-    const float ms = ps[0];
-    const float f = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - mx);
-    const float4 a = reinterpret_cast<const float4*>(ps + 4)[d4];
-    acc.x += a.x * f; acc.y += a.y * f; acc.z += a.z * f; acc.w += a.w * f;
-    l += ps[1] * f;   // the same for all 32 lanes of the group
+  for (int sb = s0; sb < ns; sb += 4 * kCombGroups) {
+    float ms[4], ls[4];
+    float4 a[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int s = sb + u * kCombGroups;
+      const float* ps = part + (int64_t)(s < ns ? s : sb) * kPartialStride;
+      ms[u] = s < ns ? ps[0] : -INFINITY;
+      ls[u] = ps[1];
+      a[u] = reinterpret_cast<const float4*>(ps + 4)[d4];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float f = (ms[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[u] - mx);
+      acc.x += a[u].x * f; acc.y += a[u].y * f; acc.z += a[u].z * f; acc.w += a[u].w * f;
+      l += ls[u] * f;   // the same for all 32 lanes of the group
+    }
   }
   accs[s0][d4] = acc;
   if (d4 == 0) lsum[s0] = l;
@@ -1208,13 +1467,13 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodePara
   if (t < D) {
     float a = 0.f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < kCombGroups; ++k) {
       const float4 v = accs[k][t >> 2];
       a += (t & 3) == 0 ? v.x : (t & 3) == 1 ? v.y : (t & 3) == 2 ? v.z : v.w;
     }
     float lt = 0.f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) lt += lsum[k];
+    for (int k = 0; k < kCombGroups; ++k) lt += lsum[k];
     o[t] = a / lt;
   }
   float* outp = p.out + ((int64_t)b * p.hq + qh) * D;
@@ -1247,7 +1506,8 @@ int pick_depth(const DecodeParams& p) {
     const int64_t slots = kLdsPerCu / (per_cu * Stage<DT>::kSlot);
     const int64_t cap = kMaxVmcnt / Stage<DT>::kOps + 1;
     const int64_t d = std::min<int64_t>(slots, cap);
-    return d >= 8 ? 8 : d >= 6 ? 6 : d >= 4 ? 4 : d >= 3 ? 3 : 2;
+    if (per_cu <= 8 && d >= 4) return d >= 8 ? 8 : d >= 6 ? 6 : 4;   // two waves per SIMD at most
+    return d >= 3 ? 3 : 2;
   }
 }
 
@@ -1271,7 +1531,12 @@ hipError_t launch_dt(const DecodeParams& p, hipStream_t stream) {
     launch_split<DT, 3>(p, stream);
   }
   if (p.nsplits > 1)
-    hipLaunchKernelGGL((decode_combine_kernel<DT>), dim3(p.hq, p.batch), dim3(kCombThreads), 0, stream, p);
+  {
+    if (p.nsplits > 32)
+      hipLaunchKernelGGL((decode_combine_kernel<DT, 512>), dim3(p.hq, p.batch), dim3(512), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_combine_kernel<DT, 128>), dim3(p.hq, p.batch), dim3(128), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
