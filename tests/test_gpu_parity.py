@@ -10,6 +10,7 @@ import torch
 
 import oracle
 import workloads
+import bit_quantized_paged_turbo_amd as xq
 from bit_quantized_paged_turbo_amd import xq_block_bytes
 from tests.gpu_util import fill, gather, make_cache, to_dev, upload_tables
 
@@ -218,6 +219,34 @@ def test_query_and_scale_edge_cases(dtype, hq):
             want, _ = oracle.decode_sequence(W.dtype, qb[b], k, v, scale)
             err = np.max(np.abs(got[b] - want))
             assert err <= TOL, f"scale {scale} seq {b}: {err:.3e}"
+
+
+@pytest.mark.parametrize("dtype,hq", [(4, 16), (4, 96), (3, 40), (0, 16)])
+def test_pool_beyond_4gib(dtype, hq):
+    """Pools larger than 4 GiB take per-page buffer descriptors and 64-bit page offsets; the
+    sequences here live in the pages above the 4 GiB mark."""
+    _print_case("bigpool", dtype, hq)
+    lens = [300, 45, 1]
+    hkv, ps = 8, 16
+    block = xq_block_bytes(xq.CacheLayout(dtype, hkv, ps, 1))
+    pages = (1 << 32) // (block * hkv) + 64
+    W = workloads.make(f"bigpool-{dtype}", 600 + dtype, dtype, lens, hq, hkv, ps, pool_pages=pages)
+    top = pages - 1 - np.arange(W.block_tables.size, dtype=np.int64)
+    W.block_tables[:] = top.reshape(W.block_tables.shape).astype(W.block_tables.dtype)
+    cache = make_cache(W, fill_byte=None)
+    assert cache.pool_bytes > (1 << 32)
+    bt, cl = upload_tables(W)
+    kv = {b: W.kv_bits(b) for b in range(W.batch)}
+    fill(cache, W, bt, kv=kv)
+    qb = W.q_bits()
+    for splits in (0, 5):
+        got = _decode(W, cache, bt, cl, splits, to_dev(qb))
+        for b in range(W.batch):
+            want = _oracle_out(W, b, qb, kv[b])
+            err = np.max(np.abs(got[b] - want))
+            assert err <= TOL, f"splits {splits} seq {b}: {err:.3e}"
+    del cache
+    torch.cuda.empty_cache()
 
 
 def test_splits_agree_and_repeat_is_deterministic():
