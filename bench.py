@@ -15,10 +15,10 @@ Infinity Cache cannot serve the KV reads of one step from the previous ones.
 
 Prints ONE JSON line. `value` is KV GB/s: the algorithmic KV bytes the decode reads per
 step (sum_b L_b * Hkv * 2 * row_bytes) over the whole step time. `roofline` is for the
-decode call, which is the dominant work of the step: q_prep_kernel, decode_split_kernel and,
-when a sequence spans several partitions, decode_combine_kernel, timed together with HIP
-events around each decode call on its stream inside the timed region (the rocprofv3 summary
-under profiles/ lists the three kernels separately); `traffic` is the measured HBM bytes of
+decode call, which is the dominant work of the step: decode_split_kernel and, when a
+sequence spans several partitions, decode_combine_kernel, timed together with HIP events
+around each decode call on its stream inside the timed region (the rocprofv3 summary under
+profiles/ lists the kernels separately); `traffic` is the measured HBM bytes of
 those kernels per call. `cpu_baseline` is the oracle on the host cores.
 """
 from __future__ import annotations
@@ -332,7 +332,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "xq_paged_decode_attention call (q_prep_kernel + decode_split_kernel"
+                     "kernel": "xq_paged_decode_attention call (decode_split_kernel"
                                + (" + decode_combine_kernel)" if nsplits > 1 else ")"),
                      "bytes_per_launch": kv_bytes},
     }
