@@ -166,16 +166,67 @@ constexpr uint32_t kBias3 = 0x924924u;   // bit 2 of every 3-bit field: c -> c +
 // ---------------------------------------------------------------------------------------
 // Query preparation, done by the decode wave itself: q' = H q, q = rint(q' * 32000 / max|q'|),
 // two signed digits, packed in the QK operand layout. The G query rows of the kv head arrive in
-// LDS (row h at 256 h, bf16); lane 4 h + g (h < G) owns dimensions [32 g, 32 g + 32) of head h,
-// reads them from bytes [256 h + 64 g, +64) and writes its 64 operand bytes over the same
-// range, so no lane touches another lane's bytes. The score scale of head h goes to sc[h].
+// LDS (row h at 256 h, bf16). The whole wave takes part: head h < G owns the aligned group of
+// 128 / NPL lanes starting at lane (128 / NPL) h, and lane r of the group holds the NPL
+// consecutive dimensions [NPL r, NPL r + NPL) (NPL = 8 for G <= 4, 16 for G <= 8, else 32).
+// The FWHT stages below NPL run in-lane, the others exchange with lane r ^ (stage / NPL). The
+// digits of dimension d go to operand byte 64 (d >> 5) + lin(d & 31) of the row (low digit; the
+// high digit 16 bytes on), which other lanes read from: the wave's LDS reads all precede its
+// writes. The score scale of head h goes to sc[h].
 // ---------------------------------------------------------------------------------------
-template <int DT, bool PAIRED>
-__device__ __forceinline__ void prep_query_lane(uint8_t* qa, float* sc_out, int h, int g, float softmax_scale) {
-  const uint4* src = reinterpret_cast<const uint4*>(qa + 256 * h + 64 * g);
-  float x[32];
+// Value held by lane (lane ^ M), M = 1, 2, 4 or 8: DPP quad_perm (M = 1, 2) and row_ror:8
+// (M = 8) are VALU operand modifiers; M = 4 is a ds_swizzle in bit-mask mode (no memory access).
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  if constexpr (M == 1 || M == 2) {
+    constexpr int kCtrl = M == 1 ? 0xB1 : 0x4E;   // quad_perm [1,0,3,2] and [2,3,0,1]
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, true));
+  } else if constexpr (M == 8) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, true));
+  } else {
+    static_assert(M == 4, "lane exchanges within 16 lanes");
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (M << 10)));
+  }
+}
+
+// One cross-lane FWHT stage: the lane whose bit M is clear holds the lower dimension a and gets
+// a + b; its partner gets a - b.
+template <int M, int N>
+__device__ __forceinline__ void fwht_cross(float (&x)[N], int r) {
+  const bool upper = (r & M) != 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int e = 0; e < N; ++e) {
+    const float other = lane_xor<M>(x[e]);
+    x[e] = upper ? other - x[e] : x[e] + other;
+  }
+}
+
+// Operand byte (low digit) of dimension e (0..31) of a 32-dimension group: 32 m + 4 w + b for
+// operand half/chunk m, dword w, byte b. The map is linear in the bits of e.
+//   turbo8 (both layouts):              e = 16 m + 4 w + b
+//   paired-block turbo4:                e = 16 m + 8 (w >> 1) + 2 b + (w & 1)
+//   one-block turbo4/turbo3 (m = chunk): e = 8 w + 2 b + m
+template <int DT, bool PAIRED>
+__device__ __forceinline__ int operand_byte(int e) {
+  int m, w, b;
+  if constexpr (DT == 8) {
+    m = e >> 4; w = (e >> 2) & 3; b = e & 3;
+  } else if constexpr (PAIRED) {
+    m = e >> 4; w = 2 * ((e >> 3) & 1) + (e & 1); b = (e >> 1) & 3;
+  } else {
+    m = e & 1; w = e >> 3; b = (e >> 1) & 3;
+  }
+  return 32 * m + 4 * w + b;
+}
+
+template <int DT, bool PAIRED, int NPL>
+__device__ __forceinline__ void prep_query_lanes(uint8_t* qa, float* sc_out, int h, int r, float softmax_scale) {
+  static_assert(NPL == 8 || NPL == 16 || NPL == 32, "8..32 dimensions per lane");
+  constexpr int kLanes = 128 / NPL;
+  float x[NPL];
+  const uint4* src = reinterpret_cast<const uint4*>(qa + 256 * h + 2 * NPL * r);
+#pragma unroll
+  for (int i = 0; i < NPL / 8; ++i) {
     const uint4 w = src[i];
     x[8 * i + 0] = bf16_lo(w.x); x[8 * i + 1] = bf16_hi(w.x);
     x[8 * i + 2] = bf16_lo(w.y); x[8 * i + 3] = bf16_hi(w.y);
@@ -183,9 +234,9 @@ __device__ __forceinline__ void prep_query_lane(uint8_t* qa, float* sc_out, int 
     x[8 * i + 6] = bf16_lo(w.w); x[8 * i + 7] = bf16_hi(w.w);
   }
 #pragma unroll
-  for (int hh = 1; hh < 32; hh <<= 1) {
+  for (int hh = 1; hh < NPL; hh <<= 1) {
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
+    for (int e = 0; e < NPL; ++e) {
       if ((e & hh) == 0) {
         const float a = x[e], c = x[e + hh];
         x[e] = a + c;
@@ -193,24 +244,20 @@ __device__ __forceinline__ void prep_query_lane(uint8_t* qa, float* sc_out, int 
       }
     }
   }
-  // stages 32, 64: the partner of dimension 32 g + e is lane ^ 1, lane ^ 2
-#pragma unroll
-  for (int m = 1; m <= 2; m <<= 1) {
-    const bool upper = (g & m) != 0;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const float other = __shfl_xor(x[e], m);
-      x[e] = upper ? other - x[e] : x[e] + other;
-    }
-  }
+  fwht_cross<1>(x, r);
+  fwht_cross<2>(x, r);
+  if constexpr (kLanes > 4) fwht_cross<4>(x, r);
+  if constexpr (kLanes > 8) fwht_cross<8>(x, r);
   float am = 0.f;
 #pragma unroll
-  for (int e = 0; e < 32; ++e) {
+  for (int e = 0; e < NPL; ++e) {
     x[e] *= kRotC;
     am = fmaxf(am, fabsf(x[e]));
   }
-  am = fmaxf(am, __shfl_xor(am, 1));
-  am = fmaxf(am, __shfl_xor(am, 2));
+  am = fmaxf(am, lane_xor<1>(am));
+  am = fmaxf(am, lane_xor<2>(am));
+  if constexpr (kLanes > 4) am = fmaxf(am, lane_xor<4>(am));
+  if constexpr (kLanes > 8) am = fmaxf(am, lane_xor<8>(am));
   // The score scale is made positive (the sign goes into the digits) and nonzero (a zero
   // query or scale gives zero digits), so a maximum over unscaled scores is the maximum of the
   // scores. A K byte is c * kKMul, so the integer dot product is kKMul times q.c.
@@ -218,36 +265,18 @@ __device__ __forceinline__ void prep_query_lane(uint8_t* qa, float* sc_out, int 
   const bool zero = !(sc != 0.f);
   const float inv = zero ? 0.f : (sc < 0.f ? -kQiMax : kQiMax) / am;
   sc = zero ? 1.f : fabsf(sc);
-  // operand m, digit dg, dword w, byte b holds dimension (relative to 32 g)
-  //   paired-block layout (turbo4/turbo8 with at most 8 heads per kv head), m = half p of the
-  //   32 dimensions:  turbo4: 16 m + 8 (w >> 1) + 2 b + (w & 1)   turbo8: 16 m + 4 w + b
-  //   one-block layout, m = k-chunk:  turbo4/3: 8 w + 2 b + m      turbo8: 16 m + 4 w + b
-  uint32_t word[2][2][4];
+  const int d0 = NPL * r;   // the lane's dimensions are d0 + e, e < NPL, with d0 a multiple of NPL
+  uint8_t* row = qa + 256 * h + 64 * (d0 >> 5) + operand_byte<DT, PAIRED>(d0 & 31);
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const int e = (DT == 8) ? (16 * m + 4 * w + bb)
-                                : (PAIRED ? 16 * m + 8 * (w >> 1) + 2 * bb + (w & 1) : 8 * w + 2 * bb + m);
-        const int q = (int)rintf(x[e] * inv);
-        const int d0 = ((q + 128) & 255) - 128;
-        const int d1 = (q - d0) >> 8;
-        lo |= (uint32_t)(d0 & 255) << (8 * bb);
-        hi |= (uint32_t)(d1 & 255) << (8 * bb);
-      }
-      word[m][0][w] = lo;
-      word[m][1][w] = hi;
-    }
+  for (int e = 0; e < NPL; ++e) {
+    const int q = (int)rintf(x[e] * inv);
+    const int lo = ((q + 128) & 255) - 128;
+    const int hi = (q - lo) >> 8;
+    const int off = operand_byte<DT, PAIRED>(e);
+    row[off] = (uint8_t)lo;
+    row[off + 16] = (uint8_t)hi;
   }
-  uint4* dst = reinterpret_cast<uint4*>(qa + 256 * h + 64 * g);
-  dst[0] = make_uint4(word[0][0][0], word[0][0][1], word[0][0][2], word[0][0][3]);
-  dst[1] = make_uint4(word[0][1][0], word[0][1][1], word[0][1][2], word[0][1][3]);
-  dst[2] = make_uint4(word[1][0][0], word[1][0][1], word[1][0][2], word[1][0][3]);
-  dst[3] = make_uint4(word[1][1][0], word[1][1][1], word[1][1][2], word[1][1][3]);
-  if (g == 0) sc_out[h] = sc;
+  if (r == 0) sc_out[h] = sc;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -877,23 +906,32 @@ __device__ __forceinline__ void quad_qk(const QuadK<DT>& t, const v4i (&qq)[8][2
   }
 }
 
-// V operand of one tile as fp16 subnormals and the PV MFMAs of that tile against A = (Ahi, Alo).
+// The lane's V words of one tile (as laid out in the slot: transposed, dimension-major).
+template <int DT> using QuadV = std::conditional_t<DT == 4, int, v2i>[8];
+
 template <int DT>
-__device__ __forceinline__ void tile_pv(const uint8_t* slot, int lane, v8h Ahi, v8h Alo, WaveState& st) {
+__device__ __forceinline__ void read_tile_v(QuadV<DT>& v, const uint8_t* slot, int lane) {
   using S = Stage<DT>;
-  struct {
-    std::conditional_t<DT == 4, int, v2i> v[8];
-  } t;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if constexpr (DT == 4)
-        t.v[4 * h + r] = *reinterpret_cast<const int*>(slot + (2 + h) * S::kHalf + 256 * r + 4 * lane);
+        v[4 * h + r] = *reinterpret_cast<const int*>(slot + (2 + h) * S::kHalf + 256 * r + 4 * lane);
       else
-        t.v[4 * h + r] = *reinterpret_cast<const v2i*>(slot + (2 + h) * S::kHalf + 512 * r + 8 * lane);
+        v[4 * h + r] = *reinterpret_cast<const v2i*>(slot + (2 + h) * S::kHalf + 512 * r + 8 * lane);
     }
   }
+}
+
+// V operand of one tile as fp16 subnormals and the PV MFMAs of that tile against A = (Ahi, Alo).
+template <int DT>
+__device__ __forceinline__ void tile_pv(const QuadV<DT>& tv, v8h Ahi, v8h Alo, WaveState& st) {
+  struct {
+    std::conditional_t<DT == 4, int, v2i> v[8];
+  } t;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) t.v[j] = tv[j];
   const v8h Bb = __builtin_bit_cast(v8h, make_uint4(0x00800080u, 0x00800080u, 0x00800080u, 0x00800080u));
   st.accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, Bb, st.accb, 0, 0, 0);
   st.accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, Bb, st.accb, 0, 0, 0);
@@ -931,23 +969,36 @@ __device__ __forceinline__ void tile_pv(const uint8_t* slot, int lane, v8h Ahi, 
   }
 }
 
-// One 64-token group: tiles in slot0 (tokens 0..31) and slot1 (32..63; all masked when absent).
+// Everything a lane reads from the two slots of a 64-token group, so that the slots can be
+// refilled before the group is processed.
+template <int DT> struct QuadData {
+  QuadK<DT> k;
+  QuadV<DT> v[2];   // per tile
+  v2i ksw, vsw;     // K and V scales of tokens 4 gg + r of block jn
+};
+
+// Tiles in slot0 (tokens 0..31) and slot1 (32..63; all masked when absent).
 template <int DT>
-__device__ __forceinline__ void process_quad(const uint8_t* slot0, const uint8_t* slot1, WaveState& st,
-                                             const v4i (&qq)[8][2], float qs, int lim, bool full,
-                                             const QuadLane& ql, int G, int lane) {
+__device__ __forceinline__ void read_quad(QuadData<DT>& d, const uint8_t* slot0, const uint8_t* slot1,
+                                          const QuadLane& ql, int lane) {
   using S = Stage<DT>;
+  read_quad_k<DT>(d.k, slot0, slot1, lane);
+  const uint8_t* ss = ((ql.jn >> 1) ? slot1 : slot0) + 4 * S::kHalf + 32 * (ql.jn & 1) + 8 * (lane >> 4);
+  d.ksw = *reinterpret_cast<const v2i*>(ss);
+  d.vsw = *reinterpret_cast<const v2i*>(ss + 64);
+  read_tile_v<DT>(d.v[0], slot0, lane);
+  read_tile_v<DT>(d.v[1], slot1, lane);
+}
+
+// One 64-token group, from registers.
+template <int DT>
+__device__ __forceinline__ void process_quad(const QuadData<DT>& d, WaveState& st, const v4i (&qq)[8][2],
+                                             float qs, int lim, bool full, const QuadLane& ql, int G,
+                                             int lane) {
   const int gg = lane >> 4;
   v4i s0, s1;
-  {
-    QuadK<DT> t;
-    read_quad_k<DT>(t, slot0, slot1, lane);
-    quad_qk<DT>(t, qq, s0, s1);
-  }
-  // scales of tokens 4 gg + r of block jn
-  const uint8_t* ss = ((ql.jn >> 1) ? slot1 : slot0) + 4 * S::kHalf + 32 * (ql.jn & 1) + 8 * gg;
-  const v2i ksw = *reinterpret_cast<const v2i*>(ss);
-  const v2i vsw = *reinterpret_cast<const v2i*>(ss + 64);
+  quad_qk<DT>(d.k, qq, s0, s1);
+  const v2i ksw = d.ksw, vsw = d.vsw;
   const uint32_t ks[4] = {(uint32_t)ksw[0], (uint32_t)ksw[0] >> 16, (uint32_t)ksw[1], (uint32_t)ksw[1] >> 16};
   uint32_t sv[4] = {(uint32_t)vsw[0] & 0xffffu, (uint32_t)vsw[0] >> 16, (uint32_t)vsw[1] & 0xffffu,
                     (uint32_t)vsw[1] >> 16};
@@ -1011,7 +1062,7 @@ __device__ __forceinline__ void process_quad(const uint8_t* slot0, const uint8_t
     const bool a = ql.jn == 2 * tl, c = ql.jn == 2 * tl + 1;
     const v8h Ahi = __builtin_bit_cast(v8h, make_uint4(a ? hi01 : 0u, a ? hi23 : 0u, c ? hi01 : 0u, c ? hi23 : 0u));
     const v8h Alo = __builtin_bit_cast(v8h, make_uint4(a ? lo01 : 0u, a ? lo23 : 0u, c ? lo01 : 0u, c ? lo23 : 0u));
-    tile_pv<DT>(tl ? slot1 : slot0, lane, Ahi, Alo, st);
+    tile_pv<DT>(d.v[tl], Ahi, Alo, st);
   }
 }
 
@@ -1102,7 +1153,7 @@ void decode_split_kernel(DecodeParams p) {
   const int col = lane & 15, g = lane >> 4;
 
   // ---- query operands ---------------------------------------------------------------------
-  // turbo types: the wave rotates and quantizes its G query rows itself (prep_query_lane); the
+  // turbo types: the wave rotates and quantizes its G query rows itself (prep_query_lanes); the
   // rows arrive by LDS DMA ahead of the first tiles, so the work overlaps their latency
   const bool pair = Stage<DT>::kOn && G <= kPairMaxGroup;
   const bool quad = Stage<DT>::kOn && DEPTH >= 4 && G <= 4;   // the quad-block layout (pair too)
@@ -1121,9 +1172,18 @@ void decode_split_kernel(DecodeParams p) {
   };
   auto load_query = [&](uint8_t* qa) __attribute__((always_inline)) {    // after the rows have landed in qa
     float* qsc = reinterpret_cast<float*>(qa + kMaxGroup * 256);
-    if (lane < 4 * G) {
-      if (pair) prep_query_lane<DT, true>(qa, qsc, lane >> 2, lane & 3, p.softmax_scale);
-      else prep_query_lane<DT, false>(qa, qsc, lane >> 2, lane & 3, p.softmax_scale);
+    if (G <= 4) {
+      if (lane < 16 * G) {
+        if (pair) prep_query_lanes<DT, true, 8>(qa, qsc, lane >> 4, lane & 15, p.softmax_scale);
+        else prep_query_lanes<DT, false, 8>(qa, qsc, lane >> 4, lane & 15, p.softmax_scale);
+      }
+    } else if (G <= 8) {
+      if (lane < 8 * G) {
+        if (pair) prep_query_lanes<DT, true, 16>(qa, qsc, lane >> 3, lane & 7, p.softmax_scale);
+        else prep_query_lanes<DT, false, 16>(qa, qsc, lane >> 3, lane & 7, p.softmax_scale);
+      }
+    } else if (lane < 4 * G) {
+      prep_query_lanes<DT, false, 32>(qa, qsc, lane >> 2, lane & 3, p.softmax_scale);
     }
     __syncthreads();
     if (quad) {
@@ -1248,39 +1308,48 @@ void decode_split_kernel(DecodeParams p) {
       // the query rows go to the last ring slot, which the loop first fills with tile DEPTH - 1
       uint8_t* qa = smem + (DEPTH - 1) * S::kSlot;
       issue_query(qa);
+      // Tiles 0 .. DEPTH - 2 go to their slots beside the query rows (last slot); loads complete
+      // in issue order, so the rows are in once at most the staged tiles' loads are pending.
+      // After the query is prepared its slot takes tile DEPTH - 1. A step reads its tiles from
+      // LDS into registers, waits for those reads and refills the freed slots before the math,
+      // so DEPTH tiles are in flight while it computes.
+      for (int i = 0; i < DEPTH - 1 && i < ntiles; ++i) stage(i);
+      wait_tiles<S::kOps, 0, DEPTH - 1>(min(DEPTH - 1, ntiles));
+      load_query(qa);   // ends with its LDS reads complete
+      if (DEPTH - 1 < ntiles) stage(DEPTH - 1);
       if constexpr (decltype(kPair)::value && DEPTH >= 4) {
         if (quad) {
-          // two tiles per step; the step stages the two tiles whose slots the previous step freed
-          for (int i = 0; i < DEPTH - 2 && i < ntiles; ++i) stage(i);
-          wait_tiles<S::kOps, 0, DEPTH - 1>(min(DEPTH - 2, ntiles));
-          load_query(qa);
+          // two tiles per step
           for (int it = 0; it < ntiles; it += 2) {
-            if (it + DEPTH - 2 < ntiles) stage(it + DEPTH - 2);
-            if (it + DEPTH - 1 < ntiles) stage(it + DEPTH - 1);
-            // tiles it, it + 1 are in once at most the tiles staged after them are outstanding
+            // tiles it, it + 1 are in once at most the tiles staged after them (it + 2 ..
+            // it + DEPTH - 1) are outstanding
             wait_tiles<S::kOps, 0, DEPTH - 1>(max(0, min(DEPTH - 2, ntiles - 2 - it)));
+            QuadData<DT> qd;
+            read_quad<DT>(qd, smem + (it % DEPTH) * S::kSlot, smem + ((it + 1) % DEPTH) * S::kSlot, ql, lane);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (it + DEPTH < ntiles) stage(it + DEPTH);
+            if (it + DEPTH + 1 < ntiles) stage(it + DEPTH + 1);
             const int t0 = tok_begin + 32 * it;
-            process_quad<DT>(smem + (it % DEPTH) * S::kSlot, smem + ((it + 1) % DEPTH) * S::kSlot, st, qq, qs,
-                             tok_end - t0 - 4 * g, t0 + 64 <= tok_end, ql, G, lane);
+            process_quad<DT>(qd, st, qq, qs, tok_end - t0 - 4 * g, t0 + 64 <= tok_end, ql, G, lane);
           }
           return;
         }
       }
-      for (int i = 0; i < DEPTH - 1 && i < ntiles; ++i) stage(i);
-      // loads complete in issue order: the rows are in once at most the staged tiles' are pending
-      wait_tiles<S::kOps, 0, DEPTH - 1>(min(DEPTH - 1, ntiles));
-      load_query(qa);
       for (int it = 0; it < ntiles; ++it) {
-        if (it + DEPTH - 1 < ntiles) stage(it + DEPTH - 1);
-        // this tile's instructions are complete once at most those of the tiles staged after it
-        // are outstanding
+        // this tile is in once at most the tiles staged after it (it + 1 .. it + DEPTH - 1) are
+        // outstanding
         wait_tiles<S::kOps, 0, DEPTH - 1>(min(DEPTH - 1, ntiles - 1 - it));
         if constexpr (decltype(kPair)::value) {
           read_slot_pair<DT>(tile, smem + (it % DEPTH) * S::kSlot, lane, pl);
+        } else {
+          read_slot<DT>(tile, smem + (it % DEPTH) * S::kSlot, lane);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (it + DEPTH < ntiles) stage(it + DEPTH);
+        if constexpr (decltype(kPair)::value) {
           const int t0 = tok_begin + 32 * it;
           process_pair_tile<DT>(tile, st, qj, qs, tok_end - t0 - 4 * g, t0 + 32 <= tok_end, pl, G, lane);
         } else {
-          read_slot<DT>(tile, smem + (it % DEPTH) * S::kSlot, lane);
           run(tile, it);
         }
       }
