@@ -6,8 +6,11 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
+#include <unordered_set>
+#include <vector>
 
 #include "xq_internal.h"
 
@@ -37,6 +40,78 @@ xq_status check_layout(const xq_cache_layout* L) {
   if (!pow2(L->page_size) || L->page_size < 16 || L->page_size > 256)
     return fail(XQ_EINVAL, "page_size %d is not a power of two in [16, 256]", L->page_size);
   if (L->num_pages < 1) return fail(XQ_EINVAL, "num_pages %lld < 1", (long long)L->num_pages);
+  return XQ_OK;
+}
+
+// ---- XQ_DEBUG: checks of device-array contents -------------------------------------------
+// On when the environment variable XQ_DEBUG is set to anything but "" or "0" (read at every
+// call). The arrays are copied to host memory on the caller's stream, which the call then
+// waits for; a violation of the contract returns XQ_EINVAL and launches nothing.
+bool debug_on() {
+  const char* e = std::getenv("XQ_DEBUG");
+  return e && *e && std::strcmp(e, "0") != 0;
+}
+
+xq_status fetch(std::vector<int32_t>& h, const int32_t* d, int64_t n, hipStream_t s) {
+  h.resize((size_t)n);
+  hipError_t e = hipMemcpyAsync(h.data(), d, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(XQ_EHIP, "XQ_DEBUG copy of a device array: %s", hipGetErrorString(e));
+  return XQ_OK;
+}
+
+// decode: 0 <= context_lens[b] <= max_context_len, and the block-table entries of the pages
+// holding positions below context_lens[b] are page ids in [0, num_pages)
+xq_status debug_check_decode(const xq_cache_layout* L, int32_t batch, const int32_t* block_tables,
+                             int32_t maxp, const int32_t* context_lens, int32_t max_ctx, hipStream_t s) {
+  std::vector<int32_t> cl, bt;
+  if (xq_status st = fetch(cl, context_lens, batch, s)) return st;
+  if (xq_status st = fetch(bt, block_tables, (int64_t)batch * maxp, s)) return st;
+  for (int32_t b = 0; b < batch; ++b) {
+    if (cl[b] < 0 || cl[b] > max_ctx)
+      return fail(XQ_EINVAL, "XQ_DEBUG: context_lens[%d] = %d is outside [0, max_context_len = %d]", b, cl[b],
+                  max_ctx);
+    const int32_t pages = (cl[b] + L->page_size - 1) / L->page_size;
+    for (int32_t i = 0; i < pages; ++i) {
+      const int32_t pg = bt[(size_t)b * maxp + i];
+      if (pg < 0 || pg >= L->num_pages)
+        return fail(XQ_EINVAL, "XQ_DEBUG: block_tables[%d][%d] = %d is not a page id below num_pages = %lld", b,
+                    i, pg, (long long)L->num_pages);
+    }
+  }
+  return XQ_OK;
+}
+
+// append: token_seq >= 0, 0 <= token_pos < max_pages_per_seq * page_size, the page of every
+// token is a page id in [0, num_pages), and no two tokens write the same (page, slot). The
+// block table is read for rows 0 .. max(token_seq), the rows the kernel reads.
+xq_status debug_check_append(const xq_cache_layout* L, int32_t n, const int32_t* token_seq,
+                             const int32_t* token_pos, const int32_t* block_tables, int32_t maxp,
+                             hipStream_t s) {
+  std::vector<int32_t> seq, pos, bt;
+  if (xq_status st = fetch(seq, token_seq, n, s)) return st;
+  if (xq_status st = fetch(pos, token_pos, n, s)) return st;
+  const int64_t cap = (int64_t)maxp * L->page_size;
+  int32_t max_seq = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (seq[i] < 0) return fail(XQ_EINVAL, "XQ_DEBUG: token_seq[%d] = %d < 0", i, seq[i]);
+    if (pos[i] < 0 || pos[i] >= cap)
+      return fail(XQ_EINVAL, "XQ_DEBUG: token_pos[%d] = %d is outside [0, max_pages_per_seq * page_size = %lld)", i,
+                  pos[i], (long long)cap);
+    if (seq[i] > max_seq) max_seq = seq[i];
+  }
+  if (xq_status st = fetch(bt, block_tables, ((int64_t)max_seq + 1) * maxp, s)) return st;
+  std::unordered_set<int64_t> slots;
+  slots.reserve((size_t)n * 2);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t pg = bt[(size_t)seq[i] * maxp + pos[i] / L->page_size];
+    if (pg < 0 || pg >= L->num_pages)
+      return fail(XQ_EINVAL, "XQ_DEBUG: token %d (sequence %d, position %d) maps to page %d, not below num_pages = %lld",
+                  i, seq[i], pos[i], pg, (long long)L->num_pages);
+    if (!slots.insert((int64_t)pg * L->page_size + pos[i] % L->page_size).second)
+      return fail(XQ_EINVAL, "XQ_DEBUG: token %d writes page %d slot %d, already written by an earlier token", i, pg,
+                  pos[i] % L->page_size);
+  }
   return XQ_OK;
 }
 
@@ -134,6 +209,10 @@ xq_status xq_quantize_append(const xq_cache_layout* layout, const void* k_new, c
   if (max_pages_per_seq < 1) return fail(XQ_EINVAL, "max_pages_per_seq %d < 1", max_pages_per_seq);
   if ((int64_t)n_tokens * layout->num_kv_heads > ((int64_t)1 << 31) * 16)
     return fail(XQ_EINVAL, "n_tokens * num_kv_heads too large for one launch");
+  if (debug_on())
+    if (xq_status st = debug_check_append(layout, n_tokens, token_seq, token_pos, block_tables, max_pages_per_seq,
+                                          static_cast<hipStream_t>(stream)))
+      return st;
   xq::AppendParams p{};
   p.k_new = static_cast<const uint16_t*>(k_new);
   p.v_new = static_cast<const uint16_t*>(v_new);
@@ -195,6 +274,10 @@ xq_status xq_paged_decode_attention(const xq_cache_layout* layout, const void* q
     if (!aligned16(workspace)) return fail(XQ_EINVAL, "workspace must be 16-byte aligned");
   }
   uint8_t* wsp = static_cast<uint8_t*>(workspace);
+  if (debug_on())
+    if (xq_status st = debug_check_decode(layout, batch, block_tables, max_pages_per_seq, context_lens,
+                                          max_context_len, static_cast<hipStream_t>(stream)))
+      return st;
 
   xq::DecodeParams p{};
   p.q = static_cast<const uint16_t*>(q);

@@ -43,7 +43,13 @@
  * workspace size); a failed check launches nothing. A failed launch returns XQ_EHIP.
  * The contents of device arrays are the caller's contract: page ids < num_pages,
  * context_lens[b] <= max_pages_per_seq * page_size and <= max_context_len, and no two
- * tokens of one append writing the same slot. Nothing throws across this boundary.
+ * tokens of one append writing the same slot. With the environment variable XQ_DEBUG set
+ * (to anything but "0") both calls also check those contents before launching: they copy
+ * the index arrays (context_lens and the block table rows a decode reads; token_seq,
+ * token_pos and block-table rows 0 .. max(token_seq) of an append) to host memory on the
+ * caller's stream, wait for it, and return XQ_EINVAL with xq_last_error naming the first
+ * bad entry. That mode is synchronous and allocates host memory; it is for debugging.
+ * Nothing throws across this boundary.
  */
 #ifndef XQ_H
 #define XQ_H
