@@ -10,7 +10,8 @@ Sources (the pages):
     - section "What actually sits between the request and the tokens": TurboQuant rotates
       each K/V head vector with a Walsh-Hadamard transform, then quantizes it with a
       per-head absmax scale; the rotation spreads outlier channels across the head
-      dimension before the absmax is taken.
+      dimension before the absmax is taken. The cache it produces is 2 to 4 bits wide, so
+      a 2-bit width (turbo2, codes -1..1) is read as the same recipe with qmax = 1.
     - section "Getting a server up: the commands in the README": cache types fp8, turbo8,
       turbo4, turbo3; BF16 when none is given.
     - section "TurboQuant is a memory trade, and the README does not price it fully":
@@ -37,7 +38,7 @@ from __future__ import annotations
 import numpy as np
 
 HEAD_DIM = 128
-QMAX = {8: 127, 4: 7, 3: 3}
+QMAX = {8: 127, 4: 7, 3: 3, 2: 1}
 # fp32 round-to-nearest of 1/sqrt(128); its bit pattern is 0x3DB504F3.
 C_F32 = np.float32(1.0 / np.sqrt(np.float64(HEAD_DIM)))
 FP16_MAX = np.float32(65504.0)
@@ -242,7 +243,7 @@ def decode_sequence(dtype_bits: int, q_bits: np.ndarray, k_bits: np.ndarray,
                     v_bits: np.ndarray, softmax_scale: float):
     """Quantize one sequence's K/V rows (if turbo) and run decode attention.
 
-    dtype_bits 0 = bf16, else 8/4/3. Returns (out [Hq,128] float64, codec) where codec is
+    dtype_bits 0 = bf16, else 8/4/3/2. Returns (out [Hq,128] float64, codec) where codec is
     None for bf16 or (k_codes, k_scales, v_codes, v_scales) for turbo types.
     """
     if dtype_bits == 0:

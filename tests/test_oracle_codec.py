@@ -153,7 +153,7 @@ def test_quantizer_hand_worked(row):
     assert np.all(codes[0, len(want):] == 0)
 
 
-@pytest.mark.parametrize("bits", [8, 4, 3])
+@pytest.mark.parametrize("bits", [8, 4, 3, 2])
 def test_quantizer_round_trip_on_grid(bits):
     g = np.random.default_rng(10 + bits)
     qmax = oracle.QMAX[bits]
@@ -167,7 +167,7 @@ def test_quantizer_round_trip_on_grid(bits):
         assert np.array_equal(codes[0], c.astype(np.int8))
 
 
-@pytest.mark.parametrize("bits", [8, 4, 3])
+@pytest.mark.parametrize("bits", [8, 4, 3, 2])
 def test_quantizer_error_bound_and_full_range(bits):
     g = np.random.default_rng(20 + bits)
     x = (g.standard_normal((500, 128)) * g.uniform(0.01, 50, size=(500, 1))).astype(np.float32)
@@ -231,7 +231,7 @@ def test_pack_hand_worked(row):
     assert np.all(packed[len(want):] == 0)
 
 
-@pytest.mark.parametrize("bits", [8, 4, 3])
+@pytest.mark.parametrize("bits", [8, 4, 3, 2])
 def test_pack_matches_bigint_bitstream(bits):
     g = np.random.default_rng(40 + bits)
     q = oracle.QMAX[bits]
@@ -244,7 +244,7 @@ def test_pack_matches_bigint_bitstream(bits):
         assert int.from_bytes(bytes(p), "little") == stream
 
 
-@pytest.mark.parametrize("bits", [8, 4, 3])
+@pytest.mark.parametrize("bits", [8, 4, 3, 2])
 def test_pack_unpack_exhaustive(bits):
     vals = np.arange(-(1 << (bits - 1)), 1 << (bits - 1))
     for shift in range(len(vals)):

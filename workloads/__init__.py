@@ -28,7 +28,8 @@ BF16 = 0
 TURBO8 = 8
 TURBO4 = 4
 TURBO3 = 3
-DTYPE_NAMES = {BF16: "bf16", TURBO8: "turbo8", TURBO4: "turbo4", TURBO3: "turbo3"}
+TURBO2 = 2
+DTYPE_NAMES = {BF16: "bf16", TURBO8: "turbo8", TURBO4: "turbo4", TURBO3: "turbo3", TURBO2: "turbo2"}
 
 
 def rng(cfg: int, stream: int, *extra: int) -> np.random.Generator:
