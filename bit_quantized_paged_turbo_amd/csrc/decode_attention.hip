@@ -143,6 +143,7 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 template <int DT> struct Codec;
 template <> struct Codec<4> { static constexpr int kRow = 64, kKMul = 16, kVBias = 8, kVShift = 20; };
 template <> struct Codec<3> { static constexpr int kRow = 48, kKMul = 32, kVBias = 4, kVShift = 19; };
+template <> struct Codec<2> { static constexpr int kRow = 32, kKMul = 64, kVBias = 2, kVShift = 18; };
 template <> struct Codec<8> { static constexpr int kRow = 128, kKMul = 1, kVBias = 128, kVShift = 24; };
 template <> struct Codec<0> { static constexpr int kRow = 256, kKMul = 1, kVBias = 0, kVShift = 0; };
 
@@ -206,11 +207,14 @@ __device__ __forceinline__ void fwht_cross(float (&x)[N], int r) {
 //   turbo8 (both layouts):              e = 16 m + 4 w + b
 //   paired-block turbo4:                e = 16 m + 8 (w >> 1) + 2 b + (w & 1)
 //   one-block turbo4/turbo3 (m = chunk): e = 8 w + 2 b + m
+//   turbo2 (one-block):                 e = 16 m + 4 b + w
 template <int DT, bool PAIRED>
 __device__ __forceinline__ int operand_byte(int e) {
   int m, w, b;
   if constexpr (DT == 8) {
     m = e >> 4; w = (e >> 2) & 3; b = e & 3;
+  } else if constexpr (DT == 2) {
+    m = e >> 4; w = e & 3; b = (e >> 2) & 3;
   } else if constexpr (PAIRED) {
     m = e >> 4; w = 2 * ((e >> 3) & 1) + (e & 1); b = (e >> 1) & 3;
   } else {
@@ -285,6 +289,7 @@ __device__ __forceinline__ void prep_query_lanes(uint8_t* qa, float* sc_out, int
 template <int DT> struct Tile;
 template <> struct Tile<4> { v4i k[2]; int v[8]; v2i ks[2], vs[2]; };
 template <> struct Tile<3> { v3i k[2]; v2i v[8]; v2i ks[2], vs[2]; };
+template <> struct Tile<2> { v2i k[2]; int v[8]; v2i ks[2], vs[2]; };
 template <> struct Tile<8> { v4i k[2][2]; v2i v[8]; v2i ks[2], vs[2]; };
 template <> struct Tile<0> { v4i k[2][4]; v4i v[8]; };
 
@@ -309,6 +314,7 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int col, int g) {
   o.k = col * R + g * (R / 4);
   if constexpr (DT == 4) o.v = 4 * g * R + 4 * col;
   else if constexpr (DT == 3) o.v = 4 * g * R + 4 * ((3 * col) >> 2);
+  else if constexpr (DT == 2) o.v = 4 * g * R + 4 * (col >> 1);   // dims 16 (c >> 1) .. + 15
   else if constexpr (DT == 8) o.v = 4 * g * R + 8 * col;
   else o.v = 4 * g * R + 16 * col;
   o.s = 8 * g;
@@ -324,6 +330,8 @@ __device__ __forceinline__ void load_tile(Tile<DT>& t, const HalfAddr (&a)[2], c
       t.k[h] = __builtin_amdgcn_raw_buffer_load_b128(a[h].k, o.k, a[h].row, kStream);
     } else if constexpr (DT == 3) {
       t.k[h] = __builtin_amdgcn_raw_buffer_load_b96(a[h].k, o.k, a[h].row, kStream);
+    } else if constexpr (DT == 2) {
+      t.k[h] = __builtin_amdgcn_raw_buffer_load_b64(a[h].k, o.k, a[h].row, kStream);
     } else if constexpr (DT == 8) {
       t.k[h][0] = __builtin_amdgcn_raw_buffer_load_b128(a[h].k, o.k, a[h].row, kStream);
       t.k[h][1] = __builtin_amdgcn_raw_buffer_load_b128(a[h].k, o.k + 16, a[h].row, kStream);
@@ -339,7 +347,7 @@ __device__ __forceinline__ void load_tile(Tile<DT>& t, const HalfAddr (&a)[2], c
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = 4 * h + r;
-      if constexpr (DT == 4) {
+      if constexpr (DT == 4 || DT == 2) {
         t.v[j] = __builtin_amdgcn_raw_buffer_load_b32(a[h].v, o.v + r * R, a[h].row, kStream);
       } else if constexpr (DT == 3 || DT == 8) {
         // turbo3: dims 8c..8c+7 are bits [24c, 24c+24) of the row; the second dword of the
@@ -455,6 +463,15 @@ __device__ __forceinline__ void k_operands(const Tile<DT>& t, int h, v4i& a0, v4
       a0[w] = (int)((n << 5) & 0xe0e0e0e0u);               // 32 c
       a1[w] = (int)((n << 1) & 0xe0e0e0e0u);
     }
+  } else if constexpr (DT == 2) {
+    // dword i holds dims 16 i .. 16 i + 15 of the lane's 32, code 4 b + w in bits 2 w of byte b;
+    // shifting field w to the top of each byte gives 64 c: chunk m, dword w, byte b is dim
+    // 16 m + 4 b + w
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      a0[w] = (int)(((uint32_t)t.k[h][0] << (6 - 2 * w)) & 0xc0c0c0c0u);
+      a1[w] = (int)(((uint32_t)t.k[h][1] << (6 - 2 * w)) & 0xc0c0c0c0u);
+    }
   } else {  // turbo8: signed bytes as stored
     a0 = t.k[h][0];
     a1 = t.k[h][1];
@@ -487,6 +504,17 @@ __device__ __forceinline__ void v_bytes(const Tile<DT>& t, uint32_t (&e)[8], uin
     for (int j = 0; j < 8; ++j) {
       e[j] = (uint32_t)t.v[j][0] ^ 0x80808080u;     // c + 128
       o[j] = (uint32_t)t.v[j][1] ^ 0x80808080u;
+    }
+  } else if constexpr (DT == 2) {
+    // the lane's 8 dims are the low or high 16 bits of the loaded dword; their bytes go to
+    // bytes 0 and 2, then nibble i (dims 8 c + 2 i, 8 c + 2 i + 1) to byte i
+    const uint32_t sel = (col & 1) ? 0x0c030c02u : 0x0c010c00u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t u = perm(0u, (uint32_t)t.v[j] ^ 0xaaaaaaaau, sel);   // c + 2 per field
+      const uint32_t n = (u & 0x000f000fu) | ((u << 4) & 0x0f000f00u);
+      e[j] = (n << 6) & 0xc0c0c0c0u;                // (c + 2) << 6
+      o[j] = (n << 4) & 0xc0c0c0c0u;
     }
   }
 }
@@ -1086,7 +1114,7 @@ __device__ __forceinline__ void fwht_wave(float (*x)[D + 4], int rows, int lane)
 // no barrier in the loop).
 // Waves per SIMD the register budget is sized for: deep rings (4+ slots) are only picked when
 // at most two waves share a SIMD.
-template <int DT, int DEPTH> constexpr int kWavesPerEu = DT == 0 ? 1 : (DT == 3 ? 2 : (DEPTH >= 4 ? 2 : 3));
+template <int DT, int DEPTH> constexpr int kWavesPerEu = DT == 0 ? 1 : ((DT == 3 || DT == 2) ? 2 : (DEPTH >= 4 ? 2 : 3));
 
 // DEPTH: tiles in flight per wave on the staged path (LDS slots); chosen at launch from how
 // many waves share a compute unit, so that the LDS of the resident waves holds as many tiles
@@ -1617,6 +1645,7 @@ hipError_t launch_decode(int dtype, const DecodeParams& p, hipStream_t stream) {
     case 8: return launch_dt<8>(p, stream);
     case 4: return launch_dt<4>(p, stream);
     case 3: return launch_dt<3>(p, stream);
+    case 2: return launch_dt<2>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -119,6 +119,11 @@ __global__ __launch_bounds__(kThreads) void quantize_append_kernel(AppendParams 
         w1 |= (uint32_t)(code[e + 4] & 0xff) << (8 * e);
       }
       *reinterpret_cast<uint2*>(dst + 8 * lane16) = make_uint2(w0, w1);
+    } else if constexpr (BITS == 2) {   // 16 bits per lane, two bytes
+      uint32_t w = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w |= (uint32_t)(code[e] & 0x3) << (2 * e);
+      *reinterpret_cast<uint16_t*>(dst + 2 * lane16) = (uint16_t)w;
     } else {  // BITS == 3: 24 bits per lane at bit offset 24*lane16; 12 dwords per row
       uint32_t v = 0;
 #pragma unroll
@@ -151,6 +156,7 @@ hipError_t launch_quantize_append(int dtype, const AppendParams& p, hipStream_t 
     case 8: hipLaunchKernelGGL(quantize_append_kernel<8>, grid, dim3(kThreads), 0, stream, p); break;
     case 4: hipLaunchKernelGGL(quantize_append_kernel<4>, grid, dim3(kThreads), 0, stream, p); break;
     case 3: hipLaunchKernelGGL(quantize_append_kernel<3>, grid, dim3(kThreads), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL(quantize_append_kernel<2>, grid, dim3(kThreads), 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

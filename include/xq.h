@@ -5,7 +5,8 @@
  *   - "xInfer: Pure-Rust LLM Inference Without a Python Runtime" (hysenlabs.com),
  *     section "What actually sits between the request and the tokens": each K/V head
  *     vector is rotated by a Walsh-Hadamard transform, then quantized with one absmax
- *     scale per head, so that the rotation spreads outlier channels before the absmax.
+ *     scale per head, so that the rotation spreads outlier channels before the absmax;
+ *     the resulting cache is 2 to 4 bits wide (turbo2 is its 2-bit end).
  *   - same page, section "Getting a server up: the commands in the README": the KV cache
  *     type is one of fp8, turbo8, turbo4, turbo3, and BF16 when no type is given.
  *   - same page, section "TurboQuant is a memory trade, and the README does not price it
@@ -18,7 +19,7 @@
  *     (Sylvester) order, no random signs; stages h = 1, 2, 4, ..., 64 of (a+b, a-b) in
  *     fp32, then one multiply by C = fp32(1/sqrt(128)) = 0x3DB504F3;
  *   - scale: one fp16 per (token, kv_head), s = fp16_rne(min(absmax / qmax, 65504)),
- *     qmax = 2^(bits-1) - 1 (127, 7, 3), division in fp32;
+ *     qmax = 2^(bits-1) - 1 (127, 7, 3, 1), division in fp32;
  *   - codes: c = clamp(rint_half_even(x / s), -qmax, qmax) in fp32; all zero when s == 0;
  *   - packing: code d of a row occupies bits [bits*d, bits*d + bits) of the row's
  *     little-endian bitstream, as a bits-wide two's complement field.
@@ -65,7 +66,8 @@ typedef enum {
   XQ_KV_BF16 = 0,   /* unquantized: the cache type used when none is given */
   XQ_KV_TURBO8 = 8, /* 8-bit codes, 130 bytes per row (128 codes + fp16 scale) */
   XQ_KV_TURBO4 = 4, /* 4-bit codes, 66 bytes per row */
-  XQ_KV_TURBO3 = 3  /* 3-bit codes in a dense bitstream, 50 bytes per row */
+  XQ_KV_TURBO3 = 3, /* 3-bit codes in a dense bitstream, 50 bytes per row */
+  XQ_KV_TURBO2 = 2  /* 2-bit codes (-1, 0, 1), 34 bytes per row */
 } xq_kv_dtype;
 
 typedef enum {

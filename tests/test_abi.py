@@ -28,7 +28,8 @@ def test_exports_match_header(lib):
 
 
 @pytest.mark.parametrize("dtype,ps,block", [(4, 16, 1056), (8, 16, 2080), (3, 64, 3200),
-                                            (0, 16, 4096), (3, 16, 800), (4, 256, 16896)])
+                                            (0, 16, 4096), (3, 16, 800), (4, 256, 16896),
+                                            (2, 16, 544), (2, 64, 2176)])
 def test_block_geometry(lib, dtype, ps, block):
     L = xq.CacheLayout(dtype, 8, ps, 10)
     assert xq.xq_block_bytes(L) == block

@@ -64,7 +64,8 @@ def _oracle_out(W, b, q_bits, kv=None):
 # ------------------------------------------------------------------------------------
 # codec
 # ------------------------------------------------------------------------------------
-@pytest.mark.parametrize("dtype,ps", [(4, 16), (4, 64), (8, 16), (8, 32), (3, 64), (3, 16), (0, 16)])
+@pytest.mark.parametrize("dtype,ps", [(4, 16), (4, 64), (8, 16), (8, 32), (3, 64), (3, 16), (0, 16),
+                                      (2, 16), (2, 64)])
 def test_append_codes_bit_exact(dtype, ps):
     _print_case("append", dtype, ps)
     W = workloads.make(f"codec-{dtype}-{ps}", 100 + dtype, dtype, [1, 37, 130, 16], 8, 2, ps)
@@ -84,7 +85,7 @@ def test_append_codes_bit_exact(dtype, ps):
             assert np.all(kp[page, :, (L % ps) * rowb: ps * rowb] == 0xFF)
 
 
-@pytest.mark.parametrize("dtype", [8, 4, 3])
+@pytest.mark.parametrize("dtype", [8, 4, 3, 2])
 def test_append_edge_rows(dtype):
     """Zero rows, rows whose scale underflows or saturates, subnormal bf16 inputs, rows
     already on the quantization grid, and ties."""
@@ -123,6 +124,8 @@ SMALL = [
     ("c2-bf16-b2", 2, 0, 2, 1 / 8),
     ("c3-1/64", 3, None, None, 1 / 64),
     ("c4-b6-1/8", 4, None, 6, 1 / 8),
+    ("c1-turbo2-b24", 1, 2, 24, 1.0),
+    ("c3-turbo2-1/64", 3, 2, None, 1 / 64),
 ]
 
 
@@ -150,7 +153,8 @@ def test_decode_matches_oracle(name, cfg, dtype, batch, scale):
 # recomputes a sample of sequences
 # ------------------------------------------------------------------------------------
 FULL = [("c1", 1, None, list(range(0, 256, 17))), ("c2-turbo8", 2, 8, [0, 31]),
-        ("c2-bf16", 2, 0, [5]), ("c3", 3, None, [0]), ("c4", 4, None, [0, 13, 63])]
+        ("c2-bf16", 2, 0, [5]), ("c3", 3, None, [0]), ("c4", 4, None, [0, 13, 63]),
+        ("c1-turbo2", 1, 2, [0, 100, 255])]
 
 
 @pytest.mark.parametrize("name,cfg,dtype,sample", FULL, ids=[f[0] for f in FULL])
@@ -179,7 +183,8 @@ def test_full_size_sampled(name, cfg, dtype, sample):
 @pytest.mark.parametrize("dtype,ps,hq,hkv", [(4, 16, 8, 8), (4, 32, 24, 8), (4, 128, 16, 2),
                                              (4, 256, 8, 1), (3, 64, 6, 2), (8, 64, 14, 2),
                                              (0, 32, 8, 1), (8, 16, 7, 7), (4, 16, 32, 2),
-                                             (8, 32, 12, 1), (4, 64, 10, 1)])
+                                             (8, 32, 12, 1), (4, 64, 10, 1), (2, 16, 8, 8),
+                                             (2, 64, 40, 8), (2, 32, 32, 2)])
 def test_decode_shapes_and_ragged(dtype, ps, hq, hkv):
     _print_case("shapes", dtype, ps, hq, hkv)
     lens = [0, 1, 15, 17, ps + 3, 3 * ps - 1, 700]
@@ -198,7 +203,7 @@ def test_decode_shapes_and_ragged(dtype, ps, hq, hkv):
             assert err <= TOL, f"splits {splits} seq {b} (L={lens[b]}): {err:.3e}"
 
 
-@pytest.mark.parametrize("dtype,hq", [(4, 4), (8, 4), (4, 16), (3, 4), (0, 4)])
+@pytest.mark.parametrize("dtype,hq", [(4, 4), (8, 4), (4, 16), (3, 4), (0, 4), (2, 4)])
 def test_query_and_scale_edge_cases(dtype, hq):
     """A zero query gives uniform weights (the mean of the values); a negative softmax scale
     flips the scores; both against the oracle."""
@@ -221,7 +226,7 @@ def test_query_and_scale_edge_cases(dtype, hq):
             assert err <= TOL, f"scale {scale} seq {b}: {err:.3e}"
 
 
-@pytest.mark.parametrize("dtype,hq", [(4, 16), (4, 96), (3, 40), (0, 16)])
+@pytest.mark.parametrize("dtype,hq", [(4, 16), (4, 96), (3, 40), (0, 16), (2, 16)])
 def test_pool_beyond_4gib(dtype, hq):
     """Pools larger than 4 GiB take per-page buffer descriptors and 64-bit page offsets; the
     sequences here live in the pages above the 4 GiB mark."""
