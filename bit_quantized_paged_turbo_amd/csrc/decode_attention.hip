@@ -1301,7 +1301,9 @@ void decode_split_kernel(DecodeParams p) {
       const int lp = min(th >> p.page_shift, last_page);   // never read a table entry past the context
       const int slot = th & (ps - 1);
       const int i = lp - lp0;
-      const int phys = i < 64 ? __builtin_amdgcn_readlane(btw0, i) : __builtin_amdgcn_readlane(btw1, i - 64);
+      // both registers read, one kept: no branch
+      const int p0 = __builtin_amdgcn_readlane(btw0, i & 63), p1 = __builtin_amdgcn_readlane(btw1, i & 63);
+      const int phys = i < 64 ? p0 : p1;
       if constexpr (decltype(kFast)::value) {
         const uint32_t base = (uint32_t)phys * (uint32_t)p.page_stride;
         a[h].k = k_pool_rsrc;
@@ -1327,11 +1329,12 @@ void decode_split_kernel(DecodeParams p) {
       using S = Stage<DT>;
       static_assert((DEPTH - 1) * S::kOps <= kMaxVmcnt, "vmcnt field is 6 bits");
       const DmaOffsets dof = dma_offsets<DT>(lane);
-      auto stage = [&](int i) __attribute__((always_inline)) {
+      auto stage = [&](int i, int slot) __attribute__((always_inline)) {   // slot = i % DEPTH
         HalfAddr a[2];
         addr(kFast, tok_begin + 32 * i, a);
-        stage_tile<DT, decltype(kFast)::value>(smem + (i % DEPTH) * S::kSlot, a, dof, lane);
+        stage_tile<DT, decltype(kFast)::value>(smem + slot * S::kSlot, a, dof, lane);
       };
+      auto next_slot = [](int slot) { return slot + 1 == DEPTH ? 0 : slot + 1; };
       std::conditional_t<decltype(kPair)::value, PairTile<DT>, Tile<DT>> tile;
       // the query rows go to the last ring slot, which the loop first fills with tile DEPTH - 1
       uint8_t* qa = smem + (DEPTH - 1) * S::kSlot;
@@ -1341,39 +1344,48 @@ void decode_split_kernel(DecodeParams p) {
       // After the query is prepared its slot takes tile DEPTH - 1. A step reads its tiles from
       // LDS into registers, waits for those reads and refills the freed slots before the math,
       // so DEPTH tiles are in flight while it computes.
-      for (int i = 0; i < DEPTH - 1 && i < ntiles; ++i) stage(i);
+      for (int i = 0; i < DEPTH - 1 && i < ntiles; ++i) stage(i, i);
       wait_tiles<S::kOps, 0, DEPTH - 1>(min(DEPTH - 1, ntiles));
       load_query(qa);   // ends with its LDS reads complete
-      if (DEPTH - 1 < ntiles) stage(DEPTH - 1);
+      if (DEPTH - 1 < ntiles) stage(DEPTH - 1, DEPTH - 1);
+      // While tiles it .. it + DEPTH - 1 all exist, the number of tiles staged after the ones a
+      // step reads is fixed and the wait takes a constant; only the last steps count down.
       if constexpr (decltype(kPair)::value && DEPTH >= 4) {
         if (quad) {
-          // two tiles per step
+          // two tiles per step, in slots cur and next_slot(cur)
+          int cur = 0;
           for (int it = 0; it < ntiles; it += 2) {
             // tiles it, it + 1 are in once at most the tiles staged after them (it + 2 ..
             // it + DEPTH - 1) are outstanding
-            wait_tiles<S::kOps, 0, DEPTH - 1>(max(0, min(DEPTH - 2, ntiles - 2 - it)));
+            if (it + DEPTH - 1 < ntiles) wait_vm<(DEPTH - 2) * S::kOps>();
+            else wait_tiles<S::kOps, 0, DEPTH - 1>(max(0, ntiles - 2 - it));
+            const int nxt = next_slot(cur);
             QuadData<DT> qd;
-            read_quad<DT>(qd, smem + (it % DEPTH) * S::kSlot, smem + ((it + 1) % DEPTH) * S::kSlot, ql, lane);
+            read_quad<DT>(qd, smem + cur * S::kSlot, smem + nxt * S::kSlot, ql, lane);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            if (it + DEPTH < ntiles) stage(it + DEPTH);
-            if (it + DEPTH + 1 < ntiles) stage(it + DEPTH + 1);
+            if (it + DEPTH < ntiles) stage(it + DEPTH, cur);
+            if (it + DEPTH + 1 < ntiles) stage(it + DEPTH + 1, nxt);
             const int t0 = tok_begin + 32 * it;
             process_quad<DT>(qd, st, qq, qs, tok_end - t0 - 4 * g, t0 + 64 <= tok_end, ql, G, lane);
+            cur = next_slot(nxt);
           }
           return;
         }
       }
+      int cur = 0;   // slot of tile it
       for (int it = 0; it < ntiles; ++it) {
         // this tile is in once at most the tiles staged after it (it + 1 .. it + DEPTH - 1) are
         // outstanding
-        wait_tiles<S::kOps, 0, DEPTH - 1>(min(DEPTH - 1, ntiles - 1 - it));
+        if (it + DEPTH - 1 < ntiles) wait_vm<(DEPTH - 1) * S::kOps>();
+        else wait_tiles<S::kOps, 0, DEPTH - 1>(ntiles - 1 - it);
         if constexpr (decltype(kPair)::value) {
-          read_slot_pair<DT>(tile, smem + (it % DEPTH) * S::kSlot, lane, pl);
+          read_slot_pair<DT>(tile, smem + cur * S::kSlot, lane, pl);
         } else {
-          read_slot<DT>(tile, smem + (it % DEPTH) * S::kSlot, lane);
+          read_slot<DT>(tile, smem + cur * S::kSlot, lane);
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if (it + DEPTH < ntiles) stage(it + DEPTH);
+        if (it + DEPTH < ntiles) stage(it + DEPTH, cur);
+        cur = next_slot(cur);
         if constexpr (decltype(kPair)::value) {
           const int t0 = tok_begin + 32 * it;
           process_pair_tile<DT>(tile, st, qj, qs, tok_end - t0 - 4 * g, t0 + 32 <= tok_end, pl, G, lane);
