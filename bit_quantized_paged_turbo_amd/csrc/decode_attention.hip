@@ -1626,10 +1626,14 @@ void launch_split(const DecodeParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((decode_split_kernel<DT, DEPTH>), dim3((unsigned)units), dim3(kThreads), 0, stream, p);
 }
 
+// With fixed partitions (batch-invariant mode) the kernel variants do not depend on the batch:
+// a three-slot ring (the paired/one-block layouts, never the quad one, whose blocking of the
+// softmax differs) and the 128-thread combine, so a sequence's output depends only on its own
+// inputs and the partition size.
 template <int DT>
 hipError_t launch_dt(const DecodeParams& p, hipStream_t stream) {
   if constexpr (Stage<DT>::kOn) {
-    switch (pick_depth<DT>(p)) {
+    switch (p.fixed_splits ? 3 : pick_depth<DT>(p)) {
       case 8: launch_split<DT, (Stage<DT>::kOps * 7 <= kMaxVmcnt ? 8 : 6)>(p, stream); break;
       case 6: launch_split<DT, 6>(p, stream); break;
       case 4: launch_split<DT, 4>(p, stream); break;
@@ -1641,7 +1645,7 @@ hipError_t launch_dt(const DecodeParams& p, hipStream_t stream) {
   }
   if (p.nsplits > 1)
   {
-    if (p.nsplits > 32)
+    if (p.nsplits > 32 && !p.fixed_splits)
       hipLaunchKernelGGL((decode_combine_kernel<DT, 512>), dim3(p.hq, p.batch), dim3(512), 0, stream, p);
     else
       hipLaunchKernelGGL((decode_combine_kernel<DT, 128>), dim3(p.hq, p.batch), dim3(128), 0, stream, p);

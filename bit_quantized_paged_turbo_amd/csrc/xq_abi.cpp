@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -123,9 +124,19 @@ int64_t block_bytes_of(const xq_cache_layout* L) {
   return (bytes + 15) & ~int64_t(15);
 }
 
+// A negative hint asks for fixed partitions of -hint tokens: whole pages, whole 32-token tiles and
+// at most kMaxSplitPages pages.
+bool fixed_split_ok(const xq_cache_layout* L, int32_t hint) {
+  if (hint >= 0 || hint == INT32_MIN) return false;
+  const int64_t tps = -(int64_t)hint, unit = L->page_size > 32 ? L->page_size : 32;
+  return tps % unit == 0 && tps <= (int64_t)xq::kMaxSplitPages * L->page_size;
+}
+
 // Tokens per split: page aligned and a multiple of 32 (one tile of the decode kernel). hint > 0
-// asks for that many splits of the longest sequence; 0 lets the library choose from the shape.
+// asks for that many splits of the longest sequence; 0 lets the library choose from the shape;
+// hint < 0 (checked by fixed_split_ok) fixes the partition at -hint tokens.
 int32_t plan_tokens_per_split(const xq_cache_layout* L, int32_t batch, int32_t max_ctx, int32_t hint) {
+  if (hint < 0) return -hint;
   const int32_t ps = L->page_size;
   int64_t tps;
   if (hint > 0) {
@@ -171,7 +182,8 @@ int64_t xq_pool_bytes(const xq_cache_layout* layout) {
 int32_t xq_decode_num_splits(const xq_cache_layout* layout, int32_t batch, int32_t num_q_heads,
                              int32_t max_context_len, int32_t num_splits_hint) {
   if (check_layout(layout) != XQ_OK) return -1;
-  if (batch < 0 || num_q_heads < 1 || max_context_len < 0 || num_splits_hint < 0) return -1;
+  if (batch < 0 || num_q_heads < 1 || max_context_len < 0) return -1;
+  if (num_splits_hint < 0 && !fixed_split_ok(layout, num_splits_hint)) return -1;
   if (max_context_len == 0) return 1;
   const int32_t tps = plan_tokens_per_split(layout, batch, max_context_len, num_splits_hint);
   return (max_context_len + tps - 1) / tps;
@@ -257,7 +269,10 @@ xq_status xq_paged_decode_attention(const xq_cache_layout* layout, const void* q
   if (max_pages_per_seq < 1) return fail(XQ_EINVAL, "max_pages_per_seq %d < 1", max_pages_per_seq);
   if ((int64_t)max_context_len > (int64_t)max_pages_per_seq * layout->page_size)
     return fail(XQ_EINVAL, "max_context_len %d exceeds max_pages_per_seq * page_size", max_context_len);
-  if (num_splits_hint < 0) return fail(XQ_EINVAL, "num_splits_hint %d < 0", num_splits_hint);
+  if (num_splits_hint < 0 && !fixed_split_ok(layout, num_splits_hint))
+    return fail(XQ_EINVAL,
+                "num_splits_hint %d: a fixed partition must be a multiple of 32 tokens and of the page size, "
+                "at most 128 pages", num_splits_hint);
   if (!(softmax_scale == softmax_scale)) return fail(XQ_EINVAL, "softmax_scale is NaN");
 
   const int32_t ctx = max_context_len > 0 ? max_context_len : 1;
@@ -303,6 +318,7 @@ xq_status xq_paged_decode_attention(const xq_cache_layout* layout, const void* q
   p.nsplits = nsplits;
   p.max_context_len = max_context_len;
   p.softmax_scale = softmax_scale;
+  p.fixed_splits = num_splits_hint < 0 ? 1 : 0;
   const hipError_t e = xq::launch_decode(layout->kv_dtype, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(XQ_EHIP, "decode launch: %s", hipGetErrorString(e));
   return XQ_OK;

@@ -69,6 +69,8 @@ struct DecodeParams {
   int32_t nsplits;              // splits of the longest sequence (grid x)
   int32_t max_context_len;      // context_lens are clamped to this
   float softmax_scale;
+  int32_t fixed_splits;         // 1: partitions fixed by the caller; kernel variants chosen
+                                // independently of the batch, so results are batch invariant
 };
 
 hipError_t launch_quantize_append(int dtype, const AppendParams& p, hipStream_t stream);

@@ -99,7 +99,13 @@ int64_t xq_pool_bytes(const xq_cache_layout* layout);
  * max_context_len tokens. num_splits_hint = 0 lets the library choose from the batch
  * shape; a positive hint asks for that many partitions. Partitions are whole pages and
  * whole 32-token tiles, and span at most 128 pages, so the count returned can be smaller
- * (short contexts) or larger (long contexts) than the hint. Returns -1 on invalid arguments.
+ * (short contexts) or larger (long contexts) than the hint. A negative hint fixes every
+ * partition at -num_splits_hint tokens, which must be a multiple of 32 and of page_size and
+ * at most 128 pages: the batch-invariant mode, in which a sequence's decode output is
+ * bitwise the same whatever else is in the batch and whatever max_context_len is (the
+ * xInfer page's decode step is replayed as a captured graph, section "What actually sits
+ * between the request and the tokens", which wants shapes that do not change the results).
+ * Returns -1 on invalid arguments.
  */
 int32_t xq_decode_num_splits(const xq_cache_layout* layout, int32_t batch,
                              int32_t num_q_heads, int32_t max_context_len,
@@ -159,7 +165,8 @@ xq_status xq_quantize_append(const xq_cache_layout* layout,
  *   context_lens       int32 [batch] (device)
  *   max_context_len    host upper bound of context_lens (sizes the launch)
  *   softmax_scale      multiplies q . k (e.g. 1/sqrt(128))
- *   num_splits_hint    0 = library policy, else as for xq_decode_num_splits
+ *   num_splits_hint    0 = library policy, > 0 a split count, < 0 fixed partitions of
+ *                      -num_splits_hint tokens (batch invariant); as for xq_decode_num_splits
  *   workspace          device scratch of >= xq_decode_workspace_bytes(...) bytes, 16-byte
  *                      aligned; may be NULL when that size is 0. Its contents on entry do
  *                      not matter; calls that share a workspace must not overlap.

@@ -70,6 +70,17 @@ def test_split_planning(lib):
     # a split spans at most 128 pages, whatever the hint
     assert xq.xq_decode_num_splits(xq.CacheLayout(4, 8, 16, 9000), 1, 8, 65536, 1) == 32
     assert xq.xq_decode_num_splits(xq.CacheLayout(3, 8, 64, 9000), 1, 8, 262144, 4) == 32
+    # fixed partitions (negative hint): -hint tokens each, independent of the batch
+    L = xq.CacheLayout(4, 8, 16, 9000)
+    assert xq.xq_decode_num_splits(L, 256, 16, 9000, -1024) == 9
+    assert xq.xq_decode_num_splits(L, 1, 16, 9000, -1024) == 9
+    assert xq.xq_decode_num_splits(L, 3, 16, 9000, -2048) == 5
+    assert xq.xq_decode_num_splits(L, 3, 16, 9000, -1000) == -1     # not a multiple of 32
+    assert xq.xq_decode_num_splits(L, 3, 16, 9000, -2080) == -1     # more than 128 pages
+    assert xq.xq_decode_workspace_bytes(L, 4, 16, 1000, -256) == 4 * 16 * 4 * 132 * 4
+    L = xq.CacheLayout(3, 8, 64, 4096)
+    assert xq.xq_decode_num_splits(L, 1, 40, 262144, -32) == -1      # not whole pages
+    assert xq.xq_decode_num_splits(L, 1, 40, 262144, -1024) == 256
     # bf16 needs no query preparation: no workspace for a single split
     L = xq.CacheLayout(0, 8, 16, 9000)
     assert xq.xq_decode_workspace_bytes(L, 256, 16, 1022, 1) == 0
@@ -94,6 +105,8 @@ def test_decode_argument_errors(lib):
     assert _decode_status(lib, L, maxctx=65) == xq.EINVAL      # > maxp * page_size
     assert _decode_status(lib, L, splits=2) == xq.EWORKSPACE   # partials of two splits
     assert b"workspace" in lib.xq_last_error()
+    assert _decode_status(lib, L, splits=-48) == xq.EINVAL      # fixed partition not whole tiles
+    assert b"fixed partition" in lib.xq_last_error()
     assert _decode_status(lib, L, batch=0) == xq.OK            # nothing to do
     bad = xq.CacheLayout(4, 2, 20, 10)
     assert _decode_status(lib, bad) == xq.EINVAL

@@ -254,6 +254,41 @@ def test_pool_beyond_4gib(dtype, hq):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("dtype,hq", [(4, 16), (4, 32), (8, 32), (3, 40), (0, 16), (2, 16)])
+def test_fixed_partitions_are_batch_invariant(dtype, hq):
+    """A negative split hint fixes the partitions: a sequence's output is then bitwise the
+    same alone, in the full batch and in a reordered batch with another max_context_len."""
+    _print_case("fixed", dtype, hq)
+    lens = [700, 33, 1500, 0, 256, 1029, 64, 900]
+    W = workloads.make(f"fixed-{dtype}", 700 + dtype, dtype, lens, hq, 8, 16)
+    cache = make_cache(W)
+    bt, cl = upload_tables(W)
+    kv = {b: W.kv_bits(b) for b in range(W.batch)}
+    fill(cache, W, bt, kv=kv)
+    qb = W.q_bits()
+    q = to_dev(qb)
+    hint = -256
+    # 64 more table columns (page 0, never read) allow a max_context_len up to 2528
+    bt = torch.cat([bt, torch.zeros((bt.shape[0], 64), dtype=bt.dtype, device=bt.device)], 1)
+
+    def run(rows, max_ctx):
+        idx = torch.tensor(rows, dtype=torch.long, device="cuda")
+        out = cache.decode(q[idx].contiguous(), bt[idx].contiguous(), cl[idx].contiguous(), max_ctx,
+                           W.softmax_scale, hint)
+        torch.cuda.synchronize()
+        return out.cpu()
+
+    full = run(list(range(W.batch)), 2048)
+    for b in range(W.batch):
+        if lens[b]:
+            want = _oracle_out(W, b, qb, kv[b])
+            assert np.max(np.abs(full[b].numpy().astype(np.float64) - want)) <= TOL
+    for rows, max_ctx in (([2], 1500), ([5, 0, 7, 2], 1536), ([7, 6, 5, 4, 3, 2, 1, 0], 2496)):
+        part = run(rows, max_ctx)
+        for i, b in enumerate(rows):
+            assert torch.equal(part[i], full[b]), f"seq {b} differs in batch {rows}"
+
+
 def test_splits_agree_and_repeat_is_deterministic():
     _print_case("splits")
     W = workloads.config(1, batch=16)
