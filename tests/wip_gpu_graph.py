@@ -1,0 +1,64 @@
+"""The decode step (append of every sequence's newest row, then the decode with fixed
+partitions) captured once into a HIP graph and replayed: the library allocates nothing, clears
+nothing with memset and never waits on the host, so the captured launches are the whole step.
+The xInfer page replays its decode step as a captured graph (section "What actually sits
+between the request and the tokens"). Every replay, with eager work and synchronisations in
+between, must reproduce the eager step bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from tests.gpu_util import fill, make_cache, to_dev, upload_tables
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dtype,hq", [(4, 16), (8, 32), (3, 40)])
+def test_step_replays_from_a_captured_graph(dtype, hq):
+    print("CASE graph", dtype, hq, flush=True)
+    lens = [300, 45, 700, 1, 1029, 64]
+    W = workloads.make(f"graph-{dtype}", 900 + dtype, dtype, lens, hq, 8, 16)
+    cache = make_cache(W)
+    bt, cl = upload_tables(W)
+    kv = {b: W.kv_bits(b) for b in range(W.batch)}
+    fill(cache, W, bt, kv=kv)
+    q = to_dev(W.q_bits())
+    # the step's new rows: each sequence's last position again (same data, so every replay
+    # leaves the cache as it was)
+    k_new = to_dev(np.stack([kv[b][0][-1] for b in range(W.batch)]))
+    v_new = to_dev(np.stack([kv[b][1][-1] for b in range(W.batch)]))
+    seq = to_dev(np.arange(W.batch, dtype=np.int32))
+    pos = to_dev(np.array([L - 1 for L in lens], np.int32))
+    hint, max_ctx = -256, W.max_context_len
+    out = torch.empty((W.batch, hq, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty((max(16, cache.workspace_bytes(W.batch, hq, max_ctx, hint)),), dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        cache.append(k_new, v_new, seq, pos, bt)
+        cache.decode(q, bt, cl, max_ctx, W.softmax_scale, hint, out=out, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    want = out.clone()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for r in range(4):
+        out.fill_(float("nan"))
+        scratch = torch.randn(1 << 20, device="cuda").sum()     # unrelated eager work
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), f"replay {r} differs from the eager step"
+        assert bool(torch.isfinite(scratch))
+    del graph
