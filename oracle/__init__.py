@@ -13,7 +13,10 @@ Sources (the pages):
       dimension before the absmax is taken. The cache it produces is 2 to 4 bits wide, so
       a 2-bit width (turbo2, codes -1..1) is read as the same recipe with qmax = 1.
     - section "Getting a server up: the commands in the README": cache types fp8, turbo8,
-      turbo4, turbo3; BF16 when none is given.
+      turbo4, turbo3; BF16 when none is given. The compression table of the same page puts
+      fp8 at 2x against BF16, so an fp8 row is 128 one-byte elements with nothing beside
+      them: each bf16 element cast to OCP FP8 E4M3 (round to nearest, ties to even,
+      saturating at +-448), with no rotation and no scale.
     - section "TurboQuant is a memory trade, and the README does not price it fully":
       attention dequantizes the cache on every step.
   [infero]  infero landing page, section "Beyond plain text decode", item "Continuous
@@ -27,7 +30,9 @@ The pages do not fix the number format. The readings used here (one per function
   - codes packed little-endian, `bits`-wide two's complement fields, 16*bits bytes a row;
   - attention per (sequence, query head) in float64 over the dequantized rows in the
     rotated space, then rotated back with H (H is symmetric and orthonormal);
-  - query head j reads kv head j // (Hq // Hkv); all positions < context length attend.
+  - query head j reads kv head j // (Hq // Hkv); all positions < context length attend;
+  - fp8: the nearest finite OCP E4M3 value of each bf16 element, ties to the even code,
+    magnitudes past 448 saturating to 448, the sign kept (also on zero).
 
 Every function here is pinned by tests/test_oracle_*.py against something other than
 itself (dense Hadamard matrices, closed forms, hand-worked values, brute force,
@@ -39,6 +44,7 @@ import numpy as np
 
 HEAD_DIM = 128
 QMAX = {8: 127, 4: 7, 3: 3, 2: 1}
+FP8 = 16          # cache-type value of the fp8 (E4M3) cache; 0 is bf16, 2..8 the turbo widths
 # fp32 round-to-nearest of 1/sqrt(128); its bit pattern is 0x3DB504F3.
 C_F32 = np.float32(1.0 / np.sqrt(np.float64(HEAD_DIM)))
 FP16_MAX = np.float32(65504.0)
@@ -101,6 +107,52 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 def f32_to_f16_saturating(x: np.ndarray) -> np.ndarray:
     """fp32 -> binary16 with round-half-even, saturating at 65504, subnormals kept."""
     return np.minimum(np.asarray(x, dtype=np.float32), FP16_MAX).astype(np.float16)
+
+
+# --------------------------------------------------------------------------------------
+# fp8 cache: OCP FP8 E4M3 elements
+# --------------------------------------------------------------------------------------
+def fp8_e4m3_value(code) -> np.ndarray:
+    """Value of OCP FP8 E4M3 bit patterns, float64 (NaN for S.1111.111).
+
+    Fields: sign (bit 7), exponent E (bits 6..3, bias 7), mantissa M (bits 2..0).
+    E = 0: M * 2^-9 (subnormal); otherwise (1 + M/8) * 2^(E-7). E = 15 with M = 7 is NaN;
+    there is no infinity, so the largest finite magnitude is 1.75 * 2^8 = 448.
+    """
+    c = np.asarray(code, dtype=np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def fp8_e4m3_encode(x) -> np.ndarray:
+    """Round finite values to OCP FP8 E4M3 bit patterns (uint8).
+
+    The result is the finite E4M3 value nearest to |x| (codes 0x00..0x7E, which increase
+    with the value), the even code on a tie, with x's sign bit on top (so -0.0 -> 0x80).
+    Anything beyond 448 has 448 as its nearest finite value: the cast saturates.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("non-finite input is outside the fp8 cast's contract")
+    mags = fp8_e4m3_value(np.arange(0x7F))             # 0 .. 448, strictly increasing
+    a = np.abs(x)
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 0, 0x7E)   # first magnitude >= a
+    lo = np.clip(hi - 1, 0, 0x7E)
+    d_lo = a - mags[lo]
+    d_hi = mags[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(a >= mags[0x7E], 0x7E, np.where(pick_hi, hi, lo))
+    neg = np.signbit(x)
+    return (code | np.where(neg, 0x80, 0)).astype(np.uint8)
+
+
+def fp8_encode_rows_bf16(bits_u16: np.ndarray) -> np.ndarray:
+    """The fp8 cache row of bf16 rows [..., 128]: one E4M3 byte per element, nothing else."""
+    return fp8_e4m3_encode(bf16_bits_to_f32(bits_u16))
 
 
 # --------------------------------------------------------------------------------------
@@ -239,15 +291,40 @@ def decode_attention_bf16(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.nda
     return out
 
 
+def decode_attention_fp8(q_bits: np.ndarray, k_fp8: np.ndarray, v_fp8: np.ndarray,
+                         softmax_scale: float) -> np.ndarray:
+    """Decode attention of one sequence over an fp8 (E4M3) cache, in float64.
+
+    q_bits bf16 bit patterns [Hq, 128]; k_fp8 / v_fp8 E4M3 bytes [L, Hkv, 128]. The cached
+    rows are the elements' E4M3 values, unrotated and unscaled, so this is textbook softmax
+    attention over those values.
+    """
+    q = bf16_bits_to_f32(q_bits).astype(np.float64)
+    k = fp8_e4m3_value(k_fp8)
+    v = fp8_e4m3_value(v_fp8)
+    hq = q.shape[0]
+    hkv = k.shape[1]
+    g = hq // hkv
+    out = np.zeros((hq, HEAD_DIM), dtype=np.float64)
+    for j in range(hq):
+        kvh = j // g
+        out[j] = _attend(q[j], k[:, kvh, :], v[:, kvh, :], softmax_scale)
+    return out
+
+
 def decode_sequence(dtype_bits: int, q_bits: np.ndarray, k_bits: np.ndarray,
                     v_bits: np.ndarray, softmax_scale: float):
-    """Quantize one sequence's K/V rows (if turbo) and run decode attention.
+    """Quantize one sequence's K/V rows (if turbo or fp8) and run decode attention.
 
-    dtype_bits 0 = bf16, else 8/4/3/2. Returns (out [Hq,128] float64, codec) where codec is
-    None for bf16 or (k_codes, k_scales, v_codes, v_scales) for turbo types.
+    dtype_bits 0 = bf16, FP8 (16) = E4M3, else 8/4/3/2. Returns (out [Hq,128] float64, codec)
+    where codec is None for bf16, (k_fp8, v_fp8) for fp8 or (k_codes, k_scales, v_codes,
+    v_scales) for turbo types.
     """
     if dtype_bits == 0:
         return decode_attention_bf16(q_bits, k_bits, v_bits, softmax_scale), None
+    if dtype_bits == FP8:
+        kf, vf = fp8_encode_rows_bf16(k_bits), fp8_encode_rows_bf16(v_bits)
+        return decode_attention_fp8(q_bits, kf, vf, softmax_scale), (kf, vf)
     kc, ks = quantize_rows_bf16(k_bits, dtype_bits)
     vc, vs = quantize_rows_bf16(v_bits, dtype_bits)
     out = decode_attention_turbo(q_bits, kc, ks, vc, vs, softmax_scale)

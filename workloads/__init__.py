@@ -29,7 +29,9 @@ TURBO8 = 8
 TURBO4 = 4
 TURBO3 = 3
 TURBO2 = 2
-DTYPE_NAMES = {BF16: "bf16", TURBO8: "turbo8", TURBO4: "turbo4", TURBO3: "turbo3", TURBO2: "turbo2"}
+FP8 = 16        # OCP FP8 E4M3 elements, no rotation, no scale
+DTYPE_NAMES = {BF16: "bf16", TURBO8: "turbo8", TURBO4: "turbo4", TURBO3: "turbo3", TURBO2: "turbo2",
+               FP8: "fp8"}
 
 
 def rng(cfg: int, stream: int, *extra: int) -> np.random.Generator:
