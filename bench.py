@@ -37,6 +37,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+import workloads  # noqa: E402  (seeded inputs; no arithmetic of the method)
+
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 PROFILES = os.path.join(ROOT, "profiles")
 DECODE_SRC = os.path.join(ROOT, "bit_quantized_paged_turbo_amd", "csrc", "decode_attention.hip")
@@ -64,7 +66,7 @@ def log(msg: str):
 
 
 def row_bytes(dtype: int) -> int:
-    return 256 if dtype == 0 else 16 * dtype + 2
+    return 256 if dtype == 0 else 128 if dtype == workloads.FP8 else 16 * dtype + 2
 
 
 def source_digest(path: str) -> str:
@@ -138,13 +140,21 @@ def _cpu_baseline(oracle, W, seconds: float):
     while elapsed < seconds:
         if b not in prepared:
             k, v = W.kv_bits(b)
-            if W.dtype:
+            if W.dtype == workloads.FP8:
+                prepared[b] = (k[-1:], v[-1:], oracle.fp8_encode_rows_bf16(k[:-1]),
+                               oracle.fp8_encode_rows_bf16(v[:-1]))
+            elif W.dtype:
                 prepared[b] = (k[-1:], v[-1:], oracle.quantize_rows_bf16(k[:-1], W.dtype),
                                oracle.quantize_rows_bf16(v[:-1], W.dtype))
             else:
                 prepared[b] = (k, v)
         t0 = time.perf_counter()
-        if W.dtype:
+        if W.dtype == workloads.FP8:
+            k1, v1, kf, vf = prepared[b]
+            kf2 = np.concatenate([kf, oracle.fp8_encode_rows_bf16(k1)])
+            vf2 = np.concatenate([vf, oracle.fp8_encode_rows_bf16(v1)])
+            oracle.decode_attention_fp8(qb[b], kf2, vf2, W.softmax_scale)
+        elif W.dtype:
             k1, v1, (kc, ks), (vc, vs) = prepared[b]
             nk = oracle.quantize_rows_bf16(k1, W.dtype)
             nv = oracle.quantize_rows_bf16(v1, W.dtype)
@@ -313,8 +323,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i4xi16->i32 QK, f32 softmax/PV" if W.dtype in (4, 3) else
-                 ("i8xi24->i32 QK, f32 softmax/PV" if W.dtype == 8 else "bf16xbf16->f32"),
+        "dtype": {4: "i4xi16->i32 QK, f32 softmax/PV", 3: "i3xi16->i32 QK, f32 softmax/PV",
+                  2: "i2xi16->i32 QK, f32 softmax/PV", 8: "i8xi16->i32 QK, f32 softmax/PV",
+                  0: "bf16xbf16->f32", workloads.FP8: "e4m3->bf16, bf16xbf16->f32"}[W.dtype],
         "data": "synthetic",
         "config": {
             "workload": W.name, "description": W.note, "cache": workloads.DTYPE_NAMES[W.dtype],

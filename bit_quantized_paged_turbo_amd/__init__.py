@@ -13,7 +13,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libxq.so")
 
-KV_BF16, KV_TURBO8, KV_TURBO4, KV_TURBO3, KV_TURBO2 = 0, 8, 4, 3, 2
+KV_BF16, KV_TURBO8, KV_TURBO4, KV_TURBO3, KV_TURBO2, KV_FP8 = 0, 8, 4, 3, 2, 16
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
 
 # Every symbol include/xq.h declares.

@@ -33,6 +33,12 @@
 //       MFMA loses up to 2^-13 of a code step; in the top bits of the low byte below 2^-18.)
 //   bf16 cache: q and K are bf16 operands of v_mfma_f32_16x16x32_bf16 (exact products), the
 //       weights are split into bf16 high and low parts against bf16 V.
+//   fp8 (E4M3) cache: the bf16 path, with every K and V byte pair widened to two bf16 values by
+//       v_cvt_scalef32_pk_bf16_fp8 (unit scale; every E4M3 value, subnormals included, is a bf16
+//       normal, so the widening is exact). The fp8 matrix-core instruction (16x16x128, E4M3 K
+//       bytes against the query as two E4M3 digits) was tried first: on keys with x30 outlier
+//       channels its scores drifted by about 2^-13 of their size, which is more than the 2e-3
+//       output tolerance allows.
 //
 // Online softmax runs in the log2 domain against a per-head reference that moves only when a
 // score beats it by more than 2^8. For turbo caches the reference tracks score + e(s_v), e the
@@ -78,6 +84,11 @@ constexpr int kBufferConfig = 0x00020000;   // gfx9 buffer descriptor word 3
 constexpr int kStream = 2;
 // Tiles in flight per wave (register path; bf16 tiles are four times larger).
 template <int DT> constexpr int kDepthOf = DT == 0 ? 2 : 3;
+// Cache types whose rows are Walsh-Hadamard rotated (the turbo types): the output is rotated
+// back. bf16 and fp8 rows are stored unrotated.
+template <int DT> constexpr bool kRotated = DT >= 2 && DT <= 8;
+// Cache types whose products run on the bf16 matrix-core instructions (unscaled rows).
+template <int DT> constexpr bool kBf16Mma = DT == 0 || DT == kFp8;
 
 // LDS staging of code bytes (turbo4, turbo8). Per 16-token half, the K and V code rows of the
 // half arrive by DMA (buffer_load_dwordx4 ... lds: 64 lanes x 16 B, lane i written at
@@ -146,6 +157,7 @@ template <> struct Codec<3> { static constexpr int kRow = 48, kKMul = 32, kVBias
 template <> struct Codec<2> { static constexpr int kRow = 32, kKMul = 64, kVBias = 2, kVShift = 18; };
 template <> struct Codec<8> { static constexpr int kRow = 128, kKMul = 1, kVBias = 128, kVShift = 24; };
 template <> struct Codec<0> { static constexpr int kRow = 256, kKMul = 1, kVBias = 0, kVShift = 0; };
+template <> struct Codec<kFp8> { static constexpr int kRow = 128, kKMul = 1, kVBias = 0, kVShift = 0; };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -292,6 +304,7 @@ template <> struct Tile<3> { v3i k[2]; v2i v[8]; v2i ks[2], vs[2]; };
 template <> struct Tile<2> { v2i k[2]; int v[8]; v2i ks[2], vs[2]; };
 template <> struct Tile<8> { v4i k[2][2]; v2i v[8]; v2i ks[2], vs[2]; };
 template <> struct Tile<0> { v4i k[2][4]; v4i v[8]; };
+template <> struct Tile<kFp8> { v4i k[2][2]; v2i v[8]; };
 
 // Wave-uniform view of one 16-token half of a tile: buffer descriptors of the page's K and V
 // blocks, the byte offset of the half's first code row and of its first scale.
@@ -315,7 +328,7 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int col, int g) {
   if constexpr (DT == 4) o.v = 4 * g * R + 4 * col;
   else if constexpr (DT == 3) o.v = 4 * g * R + 4 * ((3 * col) >> 2);
   else if constexpr (DT == 2) o.v = 4 * g * R + 4 * (col >> 1);   // dims 16 (c >> 1) .. + 15
-  else if constexpr (DT == 8) o.v = 4 * g * R + 8 * col;
+  else if constexpr (DT == 8 || DT == kFp8) o.v = 4 * g * R + 8 * col;
   else o.v = 4 * g * R + 16 * col;
   o.s = 8 * g;
   return o;
@@ -332,7 +345,7 @@ __device__ __forceinline__ void load_tile(Tile<DT>& t, const HalfAddr (&a)[2], c
       t.k[h] = __builtin_amdgcn_raw_buffer_load_b96(a[h].k, o.k, a[h].row, kStream);
     } else if constexpr (DT == 2) {
       t.k[h] = __builtin_amdgcn_raw_buffer_load_b64(a[h].k, o.k, a[h].row, kStream);
-    } else if constexpr (DT == 8) {
+    } else if constexpr (DT == 8 || DT == kFp8) {
       t.k[h][0] = __builtin_amdgcn_raw_buffer_load_b128(a[h].k, o.k, a[h].row, kStream);
       t.k[h][1] = __builtin_amdgcn_raw_buffer_load_b128(a[h].k, o.k + 16, a[h].row, kStream);
     } else {
@@ -340,7 +353,7 @@ __device__ __forceinline__ void load_tile(Tile<DT>& t, const HalfAddr (&a)[2], c
       for (int i = 0; i < 4; ++i)
         t.k[h][i] = __builtin_amdgcn_raw_buffer_load_b128(a[h].k, o.k + 16 * i, a[h].row, kStream);
     }
-    if constexpr (DT != 0) {
+    if constexpr (has_scales(DT)) {
       t.ks[h] = __builtin_amdgcn_raw_buffer_load_b64(a[h].k, o.s, a[h].scale, kStream);
       t.vs[h] = __builtin_amdgcn_raw_buffer_load_b64(a[h].v, o.s, a[h].scale, kStream);
     }
@@ -349,7 +362,7 @@ __device__ __forceinline__ void load_tile(Tile<DT>& t, const HalfAddr (&a)[2], c
       const int j = 4 * h + r;
       if constexpr (DT == 4 || DT == 2) {
         t.v[j] = __builtin_amdgcn_raw_buffer_load_b32(a[h].v, o.v + r * R, a[h].row, kStream);
-      } else if constexpr (DT == 3 || DT == 8) {
+      } else if constexpr (DT == 3 || DT == 8 || DT == kFp8) {
         // turbo3: dims 8c..8c+7 are bits [24c, 24c+24) of the row; the second dword of the
         // last group lies in the next row or the block's scale area, both inside the block
         t.v[j] = __builtin_amdgcn_raw_buffer_load_b64(a[h].v, o.v + r * R, a[h].row, kStream);
@@ -505,6 +518,7 @@ __device__ __forceinline__ void v_bytes(const Tile<DT>& t, uint32_t (&e)[8], uin
       e[j] = (uint32_t)t.v[j][0] ^ 0x80808080u;     // c + 128
       o[j] = (uint32_t)t.v[j][1] ^ 0x80808080u;
     }
+
   } else if constexpr (DT == 2) {
     // the lane's 8 dims are the low or high 16 bits of the loaded dword; their bytes go to
     // bytes 0 and 2, then nibble i (dims 8 c + 2 i, 8 c + 2 i + 1) to byte i
@@ -516,6 +530,35 @@ __device__ __forceinline__ void v_bytes(const Tile<DT>& t, uint32_t (&e)[8], uin
       e[j] = (n << 6) & 0xc0c0c0c0u;                // (c + 2) << 6
       o[j] = (n << 4) & 0xc0c0c0c0u;
     }
+  }
+}
+
+// bf16 matrix-core operands. K: the 8 dimensions 32 g + 8 m .. + 7 of the lane's token; V: dword i
+// (dimensions 8 c + 2 i, 8 c + 2 i + 1) of token slot j. fp8 bytes are widened exactly.
+template <int DT>
+__device__ __forceinline__ v8bf bf16_k_operand(const Tile<DT>& t, int h, int m) {
+  if constexpr (DT == kFp8) {
+    const v4i& x = t.k[h][m >> 1];
+    const int w = 2 * (m & 1);
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)x[w], 1.f, false);
+    const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)x[w], 1.f, true);
+    const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)x[w + 1], 1.f, false);
+    const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)x[w + 1], 1.f, true);
+    return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  } else {
+    return __builtin_bit_cast(v8bf, t.k[h][m]);
+  }
+}
+template <int DT>
+__device__ __forceinline__ uint32_t bf16_v_dword(const Tile<DT>& t, int j, int i) {
+  if constexpr (DT == kFp8) {
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    const uint32_t x = (uint32_t)t.v[j][i >> 1];
+    return __builtin_bit_cast(uint32_t, (i & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.f, true)
+                                                : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.f, false));
+  } else {
+    return (uint32_t)t.v[j][i];
   }
 }
 
@@ -537,7 +580,7 @@ __device__ __forceinline__ void process_tile(const Tile<DT>& t, WaveState& st,
   uint32_t sv[8];   // fp16 value scale in the low half (1.0 for bf16)
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    if constexpr (DT != 0) {
+    if constexpr (!kBf16Mma<DT>) {
       v4i a0, a1;
       k_operands<DT>(t, h, a0, a1);
       const v4i z = {0, 0, 0, 0};
@@ -561,7 +604,7 @@ __device__ __forceinline__ void process_tile(const Tile<DT>& t, WaveState& st,
       v4f s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < 4; ++m)
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, t.k[h][m]), qb[m], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16_k_operand<DT>(t, h, m), qb[m], s, 0, 0, 0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         y[4 * h + r] = s[r] * qs;
@@ -602,7 +645,7 @@ __device__ __forceinline__ void process_tile(const Tile<DT>& t, WaveState& st,
   }
 
   // ---- weights: p = 2^(y - m + 21) for the normaliser, P' = p * s_v for the MFMA ---------------
-  const float mref = (DT != 0) ? st.m - kWeightExp : st.m;
+  const float mref = !kBf16Mma<DT> ? st.m - kWeightExp : st.m;
   float pw[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -613,7 +656,7 @@ __device__ __forceinline__ void process_tile(const Tile<DT>& t, WaveState& st,
   uint32_t ahi[4], alo[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    if constexpr (DT != 0) {
+    if constexpr (!kBf16Mma<DT>) {
       const auto hi2 = __builtin_amdgcn_cvt_pkrtz(pw[2 * k], pw[2 * k + 1]);
       const auto lo2 = __builtin_amdgcn_cvt_pkrtz(__builtin_fmaf((float)hi2[0], -1.f, pw[2 * k]),
                                                   __builtin_fmaf((float)hi2[1], -1.f, pw[2 * k + 1]));
@@ -629,13 +672,15 @@ __device__ __forceinline__ void process_tile(const Tile<DT>& t, WaveState& st,
   }
 
   // ---- PV -----------------------------------------------------------------------------------
-  if constexpr (DT != 0) {
+  if constexpr (!kBf16Mma<DT>) {
     const v8h Ahi = __builtin_bit_cast(v8h, make_uint4(ahi[0], ahi[1], ahi[2], ahi[3]));
     const v8h Alo = __builtin_bit_cast(v8h, make_uint4(alo[0], alo[1], alo[2], alo[3]));
     // the bias alone, (bias << (8 - bits)) in every slot: the byte 0x80 for all three types
-    const v8h Bb = __builtin_bit_cast(v8h, make_uint4(0x00800080u, 0x00800080u, 0x00800080u, 0x00800080u));
-    st.accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, Bb, st.accb, 0, 0, 0);
-    st.accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, Bb, st.accb, 0, 0, 0);
+    if constexpr (Codec<DT>::kVBias != 0) {
+      const v8h Bb = __builtin_bit_cast(v8h, make_uint4(0x00800080u, 0x00800080u, 0x00800080u, 0x00800080u));
+      st.accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, Bb, st.accb, 0, 0, 0);
+      st.accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, Bb, st.accb, 0, 0, 0);
+    }
     uint32_t e[8], o[8];
     v_bytes<DT>(t, e, o, col);
 #pragma unroll
@@ -663,7 +708,7 @@ __device__ __forceinline__ void process_tile(const Tile<DT>& t, WaveState& st,
     for (int j = 0; j < 8; ++j) {
       const bool ok = full || (16 * (j >> 2) + (j & 3) < lim);   // unwritten slots may be NaN
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vv[j][i] = ok ? (uint32_t)t.v[j][i] : 0u;
+      for (int i = 0; i < 4; ++i) vv[j][i] = ok ? bf16_v_dword<DT>(t, j, i) : 0u;
     }
 #pragma unroll
     for (int tau = 0; tau < 8; ++tau) {
@@ -1114,7 +1159,8 @@ __device__ __forceinline__ void fwht_wave(float (*x)[D + 4], int rows, int lane)
 // no barrier in the loop).
 // Waves per SIMD the register budget is sized for: deep rings (4+ slots) are only picked when
 // at most two waves share a SIMD.
-template <int DT, int DEPTH> constexpr int kWavesPerEu = DT == 0 ? 1 : ((DT == 3 || DT == 2) ? 2 : (DEPTH >= 4 ? 2 : 3));
+template <int DT, int DEPTH>
+constexpr int kWavesPerEu = DT == 0 ? 1 : ((DT == 3 || DT == 2 || DT == kFp8) ? 2 : (DEPTH >= 4 ? 2 : 3));
 
 // DEPTH: tiles in flight per wave on the staged path (LDS slots); chosen at launch from how
 // many waves share a compute unit, so that the LDS of the resident waves holds as many tiles
@@ -1244,7 +1290,7 @@ void decode_split_kernel(DecodeParams p) {
     // the operand reads complete before a later DMA may refill this LDS
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
-  if constexpr (DT == 0) {
+  if constexpr (kBf16Mma<DT>) {
     if (col < G) {
       const int64_t row = (int64_t)b * p.hq + qh0 + col;
       const v8bf* s = reinterpret_cast<const v8bf*>(p.q + row * D + 32 * g);
@@ -1494,7 +1540,7 @@ void decode_split_kernel(DecodeParams p) {
 #pragma unroll
         for (int tau = 0; tau < 8; ++tau) ob[4 * g + r][8 * col + tau] = (st.acc[tau][r] - st.accb[r]) * unit * inv;
       }
-    if constexpr (DT != 0) {
+    if constexpr (kRotated<DT>) {
       fwht_wave(ob, G, lane);
       for (int k = lane; k < G * D; k += kThreads) outp[k] = ob[k >> 7][k & 127] * kRotC;
     } else {
@@ -1586,7 +1632,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodePara
     o[t] = a / lt;
   }
   float* outp = p.out + ((int64_t)b * p.hq + qh) * D;
-  if constexpr (DT != 0) {
+  if constexpr (kRotated<DT>) {
     for (int h = 1; h < D; h <<= 1) {
       __syncthreads();
       float a = 0.f, c = 0.f;
@@ -1662,6 +1708,7 @@ hipError_t launch_decode(int dtype, const DecodeParams& p, hipStream_t stream) {
     case 4: return launch_dt<4>(p, stream);
     case 3: return launch_dt<3>(p, stream);
     case 2: return launch_dt<2>(p, stream);
+    case kFp8: return launch_dt<kFp8>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -14,6 +14,10 @@
 // run inside a lane, h = 8..64 across lanes (partner lane = lane ^ h/8). A 256-thread
 // workgroup handles 16 rows of K (blockIdx.y = 0) or V (blockIdx.y = 1); a row's 16 lanes
 // store its code bytes as one contiguous 16*bits-byte segment of the page block.
+//
+// The fp8 cache type (same page, section "Getting a server up: the commands in the README",
+// and its compression table: 2x against BF16) stores each bf16 element as the nearest finite
+// OCP FP8 E4M3 value, ties to even, saturating at 448: no rotation, no scale.
 #include "xq_internal.h"
 
 #pragma clang fp contract(off)
@@ -27,6 +31,25 @@ constexpr int kThreads = 256;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// OCP FP8 E4M3 byte of a finite fp32 value: sign kept; magnitudes from 448 on give 448 (0x7E);
+// normal results (from 2^-6) keep 3 mantissa bits rounded to nearest, ties to even, where a
+// carry moves into the exponent; below 2^-6 the result is the nearest multiple of 2^-9
+// (subnormal codes 0..7, or 8 = 2^-6), rounded half to even.
+__device__ __forceinline__ uint32_t fp8_e4m3(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  uint32_t c;
+  if (a >= 0x43e00000u) {              // 448
+    c = 0x7eu;
+  } else if (a >= 0x3c800000u) {       // 2^-6
+    c = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - ((127u - 7u) << 3);
+  } else {
+    c = (uint32_t)rintf(__uint_as_float(a) * 512.f);
+  }
+  return sign | c;
+}
 
 __device__ __forceinline__ float shfl_xor16(float v, int mask) {
   // exchange within the 16-lane group that owns a row
@@ -56,6 +79,19 @@ __global__ __launch_bounds__(kThreads) void quantize_append_kernel(AppendParams 
   if constexpr (BITS == 0) {
     // unquantized cache: copy the bf16 row into its slot
     *reinterpret_cast<uint4*>(block + (int64_t)slot * 256 + lane16 * 16) = raw;
+    return;
+  } else if constexpr (BITS == kFp8) {
+    // fp8 cache: eight E4M3 bytes per lane, elements 8 lane16 .. 8 lane16 + 7
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t b0 = fp8_e4m3(bf16_lo(w[e])), b1 = fp8_e4m3(bf16_hi(w[e]));
+      const uint32_t pair = b0 | (b1 << 8);
+      if (e < 2) lo |= pair << (16 * e);
+      else hi |= pair << (16 * (e - 2));
+    }
+    *reinterpret_cast<uint2*>(block + (int64_t)slot * 128 + lane16 * 8) = make_uint2(lo, hi);
     return;
   } else {
     constexpr int qmax = (1 << (BITS - 1)) - 1;
@@ -157,6 +193,7 @@ hipError_t launch_quantize_append(int dtype, const AppendParams& p, hipStream_t 
     case 4: hipLaunchKernelGGL(quantize_append_kernel<4>, grid, dim3(kThreads), 0, stream, p); break;
     case 3: hipLaunchKernelGGL(quantize_append_kernel<3>, grid, dim3(kThreads), 0, stream, p); break;
     case 2: hipLaunchKernelGGL(quantize_append_kernel<2>, grid, dim3(kThreads), 0, stream, p); break;
+    case kFp8: hipLaunchKernelGGL(quantize_append_kernel<kFp8>, grid, dim3(kThreads), 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

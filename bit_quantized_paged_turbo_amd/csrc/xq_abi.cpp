@@ -30,14 +30,15 @@ xq_status fail(xq_status st, const char* fmt, ...) {
 }
 
 bool is_dtype(int32_t d) {
-  return d == XQ_KV_BF16 || d == XQ_KV_TURBO8 || d == XQ_KV_TURBO4 || d == XQ_KV_TURBO3 || d == XQ_KV_TURBO2;
+  return d == XQ_KV_BF16 || d == XQ_KV_TURBO8 || d == XQ_KV_TURBO4 || d == XQ_KV_TURBO3 || d == XQ_KV_TURBO2 ||
+         d == XQ_KV_FP8;
 }
 bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 xq_status check_layout(const xq_cache_layout* L) {
   if (!L) return fail(XQ_EINVAL, "layout is NULL");
-  if (!is_dtype(L->kv_dtype)) return fail(XQ_EINVAL, "kv_dtype %d is not one of 0 (bf16), 8, 4, 3, 2", L->kv_dtype);
+  if (!is_dtype(L->kv_dtype)) return fail(XQ_EINVAL, "kv_dtype %d is not one of 0 (bf16), 8, 4, 3, 2, 16 (fp8)", L->kv_dtype);
   if (L->head_dim != 128) return fail(XQ_EUNSUPPORTED, "head_dim %d: only 128 is supported", L->head_dim);
   if (L->num_kv_heads < 1) return fail(XQ_EINVAL, "num_kv_heads %d < 1", L->num_kv_heads);
   if (!pow2(L->page_size) || L->page_size < 16 || L->page_size > 256)
@@ -120,7 +121,7 @@ xq_status debug_check_append(const xq_cache_layout* L, int32_t n, const int32_t*
 
 int64_t block_bytes_of(const xq_cache_layout* L) {
   const int64_t row = xq::row_code_bytes(L->kv_dtype);
-  const int64_t bytes = L->page_size * row + (L->kv_dtype == XQ_KV_BF16 ? 0 : 2 * L->page_size);
+  const int64_t bytes = L->page_size * row + (xq::has_scales(L->kv_dtype) ? 2 * L->page_size : 0);
   return (bytes + 15) & ~int64_t(15);
 }
 

@@ -11,8 +11,12 @@ constexpr int kMaxGroup = 16;         // query heads per kv head: the 16 columns
 constexpr int kPartialStride = 132;   // floats per (seq, q head, split) partial: m, l, pad, acc[128]
 constexpr int kMaxSplitPages = 128;   // pages per split: the block-table window of a decode wave
 
-// Bytes of one stored code row for a dtype (bf16: 256).
-inline constexpr int row_code_bytes(int dtype) { return dtype == 0 ? 256 : 16 * dtype; }
+constexpr int kFp8 = 16;              // cache-type value of the E4M3 cache (not a code width)
+
+// Bytes of one stored code row for a dtype (bf16: 256, fp8: 128).
+inline constexpr int row_code_bytes(int dtype) { return dtype == 0 ? 256 : dtype == kFp8 ? 128 : 16 * dtype; }
+// Whether rows carry an fp16 scale after the page's code rows (the turbo types).
+inline constexpr bool has_scales(int dtype) { return dtype != 0 && dtype != kFp8; }
 
 inline constexpr int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 

@@ -23,12 +23,17 @@
  *   - codes: c = clamp(rint_half_even(x / s), -qmax, qmax) in fp32; all zero when s == 0;
  *   - packing: code d of a row occupies bits [bits*d, bits*d + bits) of the row's
  *     little-endian bitstream, as a bits-wide two's complement field.
+ *   - fp8 (the page's compression table gives it 2x against BF16, so nothing is stored beside
+ *     the elements): each bf16 element becomes the nearest finite OCP FP8 E4M3 value (sign,
+ *     4 exponent bits with bias 7, 3 mantissa bits), ties to the even code, magnitudes past
+ *     448 saturating to 448, the sign kept on zero; no rotation, no scale.
  *
  * Memory layout (both pools, K and V, have the same layout):
  *   pool + page * page_stride + kv_head * block_bytes   is one (page, kv_head) block;
  *   a turbo block is page_size code rows of 16*bits bytes (slot s at s * 16 * bits),
  *   followed by page_size fp16 scales (slot s at page_size * 16 * bits + 2 * s);
- *   a bf16 block is page_size rows of 128 bf16 values (256 bytes per row).
+ *   a bf16 block is page_size rows of 128 bf16 values (256 bytes per row);
+ *   an fp8 block is page_size rows of 128 E4M3 bytes.
  *   block_bytes is a multiple of 16. Physical page ids come from a per-sequence block
  *   table: token position p of sequence b lives in page block_tables[b][p / page_size],
  *   slot p % page_size.
@@ -67,7 +72,9 @@ typedef enum {
   XQ_KV_TURBO8 = 8, /* 8-bit codes, 130 bytes per row (128 codes + fp16 scale) */
   XQ_KV_TURBO4 = 4, /* 4-bit codes, 66 bytes per row */
   XQ_KV_TURBO3 = 3, /* 3-bit codes in a dense bitstream, 50 bytes per row */
-  XQ_KV_TURBO2 = 2  /* 2-bit codes (-1, 0, 1), 34 bytes per row */
+  XQ_KV_TURBO2 = 2, /* 2-bit codes (-1, 0, 1), 34 bytes per row */
+  XQ_KV_FP8 = 16    /* OCP FP8 E4M3 elements, 128 bytes per row, no rotation and no scale
+                       (the value is not a code width) */
 } xq_kv_dtype;
 
 typedef enum {
@@ -138,7 +145,8 @@ const char* xq_last_error(void);
  *   stream             hipStream_t (NULL = default stream)
  * Each (token, kv_head) row of K and of V becomes one code row and one fp16 scale at
  * page block_tables[token_seq[i]][token_pos[i] / page_size], slot token_pos[i] % page_size.
- * In bf16 mode the row is copied unchanged. Bytes of other slots are not touched.
+ * In bf16 mode the row is copied unchanged; in fp8 mode it becomes 128 E4M3 bytes (no scale).
+ * Bytes of other slots are not touched.
  */
 xq_status xq_quantize_append(const xq_cache_layout* layout,
                              const void* k_new, const void* v_new, int32_t n_tokens,
@@ -155,7 +163,7 @@ xq_status xq_quantize_append(const xq_cache_layout* layout,
  * For sequence b and query head j (kv head j / (num_q_heads / num_kv_heads)):
  *   turbo types:  q' = H q;  k'_t = s_k[t] c_k[t];  v'_t = s_v[t] c_v[t]   (rotated space)
  *                 z_t = softmax_scale * (q' . k'_t);  o = sum_t softmax(z)_t v'_t;  out = H o
- *   bf16:         the same without H, over the stored bf16 rows.
+ *   bf16, fp8:    the same without H, over the stored bf16 or E4M3 values.
  * H is the orthonormal Walsh-Hadamard matrix (symmetric, its own inverse), t runs over
  * positions 0 .. context_lens[b]-1 with no mask, and context_lens[b] = 0 gives zeros.
  *

@@ -65,7 +65,7 @@ def fill(cache: PagedKVCache, W: workloads.Workload, bt: torch.Tensor, seqs=None
 def gather(pool: np.ndarray, W: workloads.Workload, block_bytes: int, b: int, positions):
     """Read (code bytes [n, Hkv, rowb], scale bits [n, Hkv]) of sequence b out of a pool."""
     ps, hkv = W.page_size, W.num_kv_heads
-    rowb = 256 if W.dtype == 0 else 16 * W.dtype
+    rowb = 256 if W.dtype == 0 else 128 if W.dtype == workloads.FP8 else 16 * W.dtype
     blocks = pool.reshape(W.num_pages, hkv, block_bytes)
     positions = np.asarray(positions)
     pages = W.block_tables[b, positions // ps]
@@ -73,7 +73,7 @@ def gather(pool: np.ndarray, W: workloads.Workload, block_bytes: int, b: int, po
     codes = np.stack([blocks[pages, h][np.arange(len(positions))[:, None],
                                       slots[:, None] * rowb + np.arange(rowb)[None, :]]
                       for h in range(hkv)], axis=1)
-    if W.dtype == 0:
+    if W.dtype in (0, workloads.FP8):
         return codes, None
     sc = np.stack([blocks[pages, h][np.arange(len(positions))[:, None],
                                    ps * rowb + 2 * slots[:, None] + np.arange(2)[None, :]]

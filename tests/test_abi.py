@@ -29,7 +29,7 @@ def test_exports_match_header(lib):
 
 @pytest.mark.parametrize("dtype,ps,block", [(4, 16, 1056), (8, 16, 2080), (3, 64, 3200),
                                             (0, 16, 4096), (3, 16, 800), (4, 256, 16896),
-                                            (2, 16, 544), (2, 64, 2176)])
+                                            (2, 16, 544), (2, 64, 2176), (16, 16, 2048), (16, 64, 8192)])
 def test_block_geometry(lib, dtype, ps, block):
     L = xq.CacheLayout(dtype, 8, ps, 10)
     assert xq.xq_block_bytes(L) == block
@@ -37,7 +37,7 @@ def test_block_geometry(lib, dtype, ps, block):
     assert xq.xq_pool_bytes(L) == 80 * block
 
 
-@pytest.mark.parametrize("bad", [dict(kv_dtype=5), dict(head_dim=64), dict(num_kv_heads=0),
+@pytest.mark.parametrize("bad", [dict(kv_dtype=5), dict(kv_dtype=1), dict(kv_dtype=17), dict(head_dim=64), dict(num_kv_heads=0),
                                  dict(page_size=24), dict(page_size=8), dict(page_size=512),
                                  dict(num_pages=0)])
 def test_invalid_layouts(lib, bad):

@@ -41,6 +41,11 @@ def _codec_check(W, cache, seqs):
             if W.dtype == 0:
                 assert np.array_equal(codes.view(np.uint16).reshape(rows.shape), rows)
                 continue
+            if W.dtype == workloads.FP8:
+                want = oracle.fp8_encode_rows_bf16(rows)
+                bad = np.argwhere(codes != want)
+                assert bad.size == 0, f"seq {b}: {len(bad)} fp8 bytes differ, first {bad[:3]}"
+                continue
             c, s = oracle.quantize_rows_bf16(rows, W.dtype)
             want = oracle.pack_codes(c, W.dtype)
             bad = np.argwhere(codes != want)
@@ -65,7 +70,7 @@ def _oracle_out(W, b, q_bits, kv=None):
 # codec
 # ------------------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype,ps", [(4, 16), (4, 64), (8, 16), (8, 32), (3, 64), (3, 16), (0, 16),
-                                      (2, 16), (2, 64)])
+                                      (2, 16), (2, 64), (16, 16), (16, 128)])
 def test_append_codes_bit_exact(dtype, ps):
     _print_case("append", dtype, ps)
     W = workloads.make(f"codec-{dtype}-{ps}", 100 + dtype, dtype, [1, 37, 130, 16], 8, 2, ps)
@@ -77,7 +82,7 @@ def test_append_codes_bit_exact(dtype, ps):
     # slots past each sequence's end keep the poison bytes
     bb = xq_block_bytes(cache.layout)
     kp = cache.k_pool.cpu().numpy().reshape(W.num_pages, W.num_kv_heads, bb)
-    rowb = 256 if dtype == 0 else 16 * dtype
+    rowb = 256 if dtype == 0 else 128 if dtype == workloads.FP8 else 16 * dtype
     for b in range(W.batch):
         L = int(W.context_lens[b])
         if L % ps:
@@ -114,6 +119,61 @@ def test_append_edge_rows(dtype):
     assert np.array_equal(scales, s.view(np.uint16))
 
 
+def test_fp8_append_every_bf16_value():
+    """Every finite bf16 bit pattern (65,280 of them, both signs, subnormals, values far past
+    the E4M3 range) through the fp8 append, against the oracle's nearest-value cast."""
+    _print_case("fp8-all-bf16")
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = (bits & 0x7F80) != 0x7F80
+    vals = bits[finite]
+    n = -(-vals.size // 128)
+    rows = np.zeros(n * 128, np.uint16)
+    rows[: vals.size] = vals
+    rows = rows.reshape(n, 1, 128)
+    W = workloads.make("fp8-all", 250, workloads.FP8, [n], 1, 1, 16)
+    cache = make_cache(W)
+    bt, _ = upload_tables(W)
+    k = to_dev(rows)
+    pos = to_dev(np.arange(n, dtype=np.int32))
+    seq = to_dev(np.zeros(n, np.int32))
+    cache.append(k, k, seq, pos, bt)
+    torch.cuda.synchronize()
+    for pool in (cache.k_pool, cache.v_pool):
+        codes, _ = gather(pool.cpu().numpy(), W, xq_block_bytes(cache.layout), 0, np.arange(n))
+        want = oracle.fp8_encode_rows_bf16(rows)
+        bad = np.argwhere(codes != want)
+        assert bad.size == 0, f"{len(bad)} bytes differ, first {bad[:3]}"
+
+
+def test_fp8_decode_over_every_code():
+    """K and V rows built from all 254 finite E4M3 values (subnormals, +-0, +-448), each
+    stored exactly, so the decode widens every code; a query scaled by 2^-6 keeps the scores
+    moderate."""
+    _print_case("fp8-every-code")
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F])
+    vals = oracle.fp8_e4m3_value(codes)
+    g = np.random.default_rng(17)
+    L = 300
+    k = g.choice(vals, size=(L, 2, 128))
+    v = g.choice(vals, size=(L, 2, 128))
+    for rows in (k, v):                                    # every code in both heads of both
+        rows[:2, 0, :127] = vals[:127]
+        rows[2:4, 1, :127] = vals[127:]
+    kb = workloads.round_to_bf16_bits(k.astype(np.float32))
+    vb = workloads.round_to_bf16_bits(v.astype(np.float32))
+    W = workloads.make("fp8-codes", 251, workloads.FP8, [L], 8, 2, 16)
+    cache = make_cache(W)
+    bt, cl = upload_tables(W)
+    fill(cache, W, bt, kv={0: (kb, vb)})
+    qb = workloads.round_to_bf16_bits(oracle.bf16_bits_to_f32(W.q_bits()) / np.float32(64.0))
+    for splits in (0, 3):
+        got = _decode(W, cache, bt, cl, splits, to_dev(qb))
+        want, (kf, vf) = oracle.decode_sequence(W.dtype, qb[0], kb, vb, W.softmax_scale)
+        assert np.array_equal(oracle.fp8_e4m3_value(kf), k)   # the rows were stored exactly
+        rel = np.max(np.abs(got[0] - want)) / max(1.0, np.max(np.abs(want)))
+        assert rel <= TOL / 4, f"splits {splits}: relative err {rel:.3e}"
+
+
 # ------------------------------------------------------------------------------------
 # decode on the presets (scaled-down versions run the oracle on every sequence)
 # ------------------------------------------------------------------------------------
@@ -126,6 +186,9 @@ SMALL = [
     ("c4-b6-1/8", 4, None, 6, 1 / 8),
     ("c1-turbo2-b24", 1, 2, 24, 1.0),
     ("c3-turbo2-1/64", 3, 2, None, 1 / 64),
+    ("c2-fp8-b2", 2, 16, 2, 1 / 8),
+    ("c1-fp8-b24", 1, 16, 24, 1.0),
+    ("c3-fp8-1/64", 3, 16, None, 1 / 64),
 ]
 
 
@@ -154,7 +217,7 @@ def test_decode_matches_oracle(name, cfg, dtype, batch, scale):
 # ------------------------------------------------------------------------------------
 FULL = [("c1", 1, None, list(range(0, 256, 17))), ("c2-turbo8", 2, 8, [0, 31]),
         ("c2-bf16", 2, 0, [5]), ("c3", 3, None, [0]), ("c4", 4, None, [0, 13, 63]),
-        ("c1-turbo2", 1, 2, [0, 100, 255])]
+        ("c1-turbo2", 1, 2, [0, 100, 255]), ("c2-fp8", 2, 16, [0, 31])]
 
 
 @pytest.mark.parametrize("name,cfg,dtype,sample", FULL, ids=[f[0] for f in FULL])
@@ -184,7 +247,8 @@ def test_full_size_sampled(name, cfg, dtype, sample):
                                              (4, 256, 8, 1), (3, 64, 6, 2), (8, 64, 14, 2),
                                              (0, 32, 8, 1), (8, 16, 7, 7), (4, 16, 32, 2),
                                              (8, 32, 12, 1), (4, 64, 10, 1), (2, 16, 8, 8),
-                                             (2, 64, 40, 8), (2, 32, 32, 2)])
+                                             (2, 64, 40, 8), (2, 32, 32, 2), (16, 16, 8, 8),
+                                             (16, 64, 40, 8), (16, 32, 32, 2), (16, 128, 3, 1)])
 def test_decode_shapes_and_ragged(dtype, ps, hq, hkv):
     _print_case("shapes", dtype, ps, hq, hkv)
     lens = [0, 1, 15, 17, ps + 3, 3 * ps - 1, 700]
@@ -203,7 +267,7 @@ def test_decode_shapes_and_ragged(dtype, ps, hq, hkv):
             assert err <= TOL, f"splits {splits} seq {b} (L={lens[b]}): {err:.3e}"
 
 
-@pytest.mark.parametrize("dtype,hq", [(4, 4), (8, 4), (4, 16), (3, 4), (0, 4), (2, 4)])
+@pytest.mark.parametrize("dtype,hq", [(4, 4), (8, 4), (4, 16), (3, 4), (0, 4), (2, 4), (16, 4), (16, 16)])
 def test_query_and_scale_edge_cases(dtype, hq):
     """A zero query gives uniform weights (the mean of the values); a negative softmax scale
     flips the scores; both against the oracle."""
@@ -226,7 +290,7 @@ def test_query_and_scale_edge_cases(dtype, hq):
             assert err <= TOL, f"scale {scale} seq {b}: {err:.3e}"
 
 
-@pytest.mark.parametrize("dtype,hq", [(4, 16), (4, 96), (3, 40), (0, 16), (2, 16)])
+@pytest.mark.parametrize("dtype,hq", [(4, 16), (4, 96), (3, 40), (0, 16), (2, 16), (16, 32)])
 def test_pool_beyond_4gib(dtype, hq):
     """Pools larger than 4 GiB take per-page buffer descriptors and 64-bit page offsets; the
     sequences here live in the pages above the 4 GiB mark."""
@@ -254,7 +318,7 @@ def test_pool_beyond_4gib(dtype, hq):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("dtype,hq", [(4, 16), (4, 32), (8, 32), (3, 40), (0, 16), (2, 16)])
+@pytest.mark.parametrize("dtype,hq", [(4, 16), (4, 32), (8, 32), (3, 40), (0, 16), (2, 16), (16, 32)])
 def test_fixed_partitions_are_batch_invariant(dtype, hq):
     """A negative split hint fixes the partitions: a sequence's output is then bitwise the
     same alone, in the full batch and in a reordered batch with another max_context_len."""
