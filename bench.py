@@ -54,6 +54,7 @@ def parse():
     ap.add_argument("--splits", type=int, default=None, help="override the split hint")
     ap.add_argument("--replica-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run plain 512 MiB device copies (a known byte count for "
@@ -303,6 +304,42 @@ def main():
     dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
     dec_avg_ms = float(dec_ms.mean())
 
+    # ---- the same steps replayed from captured HIP graphs (one per pool replica): the library
+    # allocates, clears and waits on nothing, so a step captures whole ---------------------------
+    graph = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for r in runners[:64]:
+                r.run(side.cuda_stream)
+                r.decode(side.cuda_stream)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for r in runners[:64]:         # tiny workloads have thousands of replicas: cap the graphs
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                cs = torch.cuda.current_stream().cuda_stream
+                r.run(cs)
+                r.decode(cs)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        NG = len(graphs)
+        for i in range(Wm):
+            graphs[i % NG].replay()
+        torch.cuda.synchronize()
+        gstart, gstop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gstart.record(stream)
+        for i in range(K):
+            graphs[(Wm + i) % NG].replay()
+        gstop.record(stream)
+        torch.cuda.synchronize()
+        g_ms = gstart.elapsed_time(gstop) / K
+        graph = {"ms_per_step": round(g_ms, 5), "replicas": NG}
+        log(f"graph replay: {g_ms * 1e3:.1f} us/step")
+        del graphs
+
     rb = row_bytes(W.dtype)
     kv_bytes = int(W.context_lens.astype(np.int64).sum()) * hkv * 2 * rb
     tokens = int(W.context_lens.astype(np.int64).sum())
@@ -347,6 +384,10 @@ def main():
                                + (" + decode_combine_kernel)" if nsplits > 1 else ")"),
                      "bytes_per_launch": kv_bytes},
     }
+    if graph is not None:
+        graph["value"] = round(kv_bytes / (graph["ms_per_step"] * 1e-3) / 1e9, 2)
+        graph["seq_tokens_per_s"] = round(tokens / (graph["ms_per_step"] * 1e-3), 1)
+        result["graph_replay"] = graph
     log(f"GPU: {step_ms * 1e3:.1f} us/step, decode call {dec_avg_ms * 1e3:.1f} us")
     if not args.no_cpu:
         log("oracle baseline on the host")

@@ -66,15 +66,17 @@ __global__ __launch_bounds__(kThreads) void quantize_append_kernel(AppendParams 
   const int tok = (int)(row / p.hkv);
   const int head = (int)(row - (int64_t)tok * p.hkv);
 
+  // the row's load does not depend on the page lookup: issue it first so the two overlap
+  const uint16_t* src = (is_v ? p.v_new : p.k_new) + row * kHeadDim + lane16 * 8;
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u rv = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(src));
+  const uint4 raw = make_uint4(rv[0], rv[1], rv[2], rv[3]);
   const int seq = p.token_seq[tok];
   const int pos = p.token_pos[tok];
   const int page = p.block_tables[(int64_t)seq * p.maxp + pos / p.page_size];
   const int slot = pos % p.page_size;
   uint8_t* block = (is_v ? p.v_pool : p.k_pool) + (int64_t)page * p.page_stride +
                    (int64_t)head * p.block_bytes;
-
-  const uint16_t* src = (is_v ? p.v_new : p.k_new) + row * kHeadDim + lane16 * 8;
-  const uint4 raw = *reinterpret_cast<const uint4*>(src);
 
   if constexpr (BITS == 0) {
     // unquantized cache: copy the bf16 row into its slot

@@ -32,7 +32,9 @@ The pages do not fix the number format. The readings used here (one per function
     rotated space, then rotated back with H (H is symmetric and orthonormal);
   - query head j reads kv head j // (Hq // Hkv); all positions < context length attend;
   - fp8: the nearest finite OCP E4M3 value of each bf16 element, ties to the even code,
-    magnitudes past 448 saturating to 448, the sign kept (also on zero).
+    magnitudes past 448 saturating to 448, the sign kept (also on zero);
+  - chunked prefill: query i of a chunk starting at position P attends to positions 0 .. P + i
+    of the cache as stored, the chunk's own rows included.
 
 Every function here is pinned by tests/test_oracle_*.py against something other than
 itself (dense Hadamard matrices, closed forms, hand-worked values, brute force,
@@ -329,3 +331,42 @@ def decode_sequence(dtype_bits: int, q_bits: np.ndarray, k_bits: np.ndarray,
     vc, vs = quantize_rows_bf16(v_bits, dtype_bits)
     out = decode_attention_turbo(q_bits, kc, ks, vc, vs, softmax_scale)
     return out, (kc, ks, vc, vs)
+
+
+# --------------------------------------------------------------------------------------
+# Chunked prefill over the quantized cache
+# --------------------------------------------------------------------------------------
+def prefill_sequence(dtype_bits: int, q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
+                     start: int, softmax_scale: float) -> np.ndarray:
+    """Attention of a prefill chunk over its sequence's cache, in float64.
+
+    q_bits     bf16 bits [C, Hq, 128]: the chunk's queries, query i at position start + i
+    k_bits     bf16 bits [start + C, Hkv, 128] (same for v): every row of the sequence up to the
+               chunk's end, the chunk's own rows included (appended before the attention)
+    Returns    float64 [C, Hq, 128]
+
+    Query i attends to positions 0 .. start + i (causal, nothing past itself), over the cache as
+    stored: quantized (turbo, fp8) or not (bf16) by the same definitions as decode. The infero
+    landing page, section "Beyond plain text decode", item "Continuous batching": decodes go
+    first and prefill fills what is left of a step, split across steps, so a chunk attends to
+    the cached prefix of earlier chunks plus itself.
+    """
+    c = q_bits.shape[0]
+    out = np.zeros((c,) + q_bits.shape[1:], dtype=np.float64)
+    if dtype_bits == 0:
+        for i in range(c):
+            n = start + i + 1
+            out[i] = decode_attention_bf16(q_bits[i], k_bits[:n], v_bits[:n], softmax_scale)
+        return out
+    if dtype_bits == FP8:
+        kf, vf = fp8_encode_rows_bf16(k_bits), fp8_encode_rows_bf16(v_bits)
+        for i in range(c):
+            n = start + i + 1
+            out[i] = decode_attention_fp8(q_bits[i], kf[:n], vf[:n], softmax_scale)
+        return out
+    kc, ks = quantize_rows_bf16(k_bits, dtype_bits)
+    vc, vs = quantize_rows_bf16(v_bits, dtype_bits)
+    for i in range(c):
+        n = start + i + 1
+        out[i] = decode_attention_turbo(q_bits[i], kc[:n], ks[:n], vc[:n], vs[:n], softmax_scale)
+    return out
