@@ -19,7 +19,7 @@ OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
 # Every symbol include/xq.h declares.
 EXPORTS = ("xq_block_bytes", "xq_page_stride_bytes", "xq_pool_bytes", "xq_decode_num_splits",
            "xq_decode_workspace_bytes", "xq_status_string", "xq_last_error",
-           "xq_quantize_append", "xq_paged_decode_attention")
+           "xq_quantize_append", "xq_paged_decode_attention", "xq_paged_prefill_attention")
 
 
 class XqError(RuntimeError):
@@ -64,6 +64,8 @@ def load() -> ctypes.CDLL:
         "xq_quantize_append": (I32, [LP, P, P, I32, P, P, P, I32, P, P, P]),
         "xq_paged_decode_attention": (I32, [LP, P, I32, I32, P, P, P, I32, P, I32, F32, I32,
                                             P, I64, P, P]),
+        "xq_paged_prefill_attention": (I32, [LP, P, I32, I32, P, P, P, I32, I32, F32, I32,
+                                             P, I64, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -136,3 +138,14 @@ def xq_paged_decode_attention(layout: CacheLayout, q, batch: int, num_q_heads: i
         _ptr(block_tables), max_pages_per_seq, _ptr(context_lens), max_context_len,
         float(softmax_scale), num_splits_hint, _ptr(workspace), int(workspace_bytes), _ptr(out),
         _stream(stream)))
+
+
+def xq_paged_prefill_attention(layout: CacheLayout, q, n_query: int, num_q_heads: int, k_pool,
+                               v_pool, block_table, max_pages: int, start_pos: int,
+                               softmax_scale: float, num_splits_hint: int, workspace,
+                               workspace_bytes: int, out, stream=None):
+    """See xq_paged_prefill_attention in include/xq.h. Tensors are passed by data_ptr()."""
+    _check(load().xq_paged_prefill_attention(
+        ctypes.byref(layout), _ptr(q), n_query, num_q_heads, _ptr(k_pool), _ptr(v_pool),
+        _ptr(block_table), max_pages, start_pos, float(softmax_scale), num_splits_hint,
+        _ptr(workspace), int(workspace_bytes), _ptr(out), _stream(stream)))

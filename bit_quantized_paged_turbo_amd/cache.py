@@ -8,6 +8,7 @@ from __future__ import annotations
 import torch
 
 from . import (CacheLayout, load, xq_decode_workspace_bytes, xq_paged_decode_attention,
+               xq_paged_prefill_attention,
                xq_pool_bytes, xq_quantize_append)
 
 
@@ -54,4 +55,24 @@ class PagedKVCache:
                                   block_tables, int(block_tables.shape[1]), context_lens,
                                   int(max_context_len), softmax_scale, num_splits, workspace,
                                   wbytes, out, stream)
+        return out
+
+    def prefill(self, q: torch.Tensor, block_table: torch.Tensor, start_pos: int,
+                softmax_scale: float, num_splits: int = 0, out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """Chunk queries q bf16 [C, Hq, 128] at positions start_pos .. start_pos + C - 1 of the
+        sequence whose block-table row is `block_table` (int32 [max_pages]); its rows up to the
+        chunk's end must already be appended. -> out fp32 [C, Hq, 128]."""
+        n, hq = int(q.shape[0]), int(q.shape[1])
+        if out is None:
+            out = torch.empty((n, hq, 128), dtype=torch.float32, device=q.device)
+        need = self.workspace_bytes(n, hq, start_pos + n, num_splits)
+        if workspace is None and need > 0:
+            if self._ws is None or self._ws.numel() < need:
+                self._ws = torch.empty((need,), dtype=torch.uint8, device=q.device)
+            workspace = self._ws
+        wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        xq_paged_prefill_attention(self.layout, q, n, hq, self.k_pool, self.v_pool, block_table,
+                                   int(block_table.shape[-1]), int(start_pos), softmax_scale,
+                                   num_splits, workspace, wbytes, out, stream)
         return out

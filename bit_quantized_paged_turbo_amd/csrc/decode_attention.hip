@@ -1139,6 +1139,12 @@ __device__ __forceinline__ void process_quad(const QuadData<DT>& d, WaveState& s
   }
 }
 
+// Tokens row b attends to: its context length (decode), or start + b + 1 for query b of a
+// prefill chunk (causal; every row reads the chunk's sequence's block-table row).
+__device__ __forceinline__ int row_context(const DecodeParams& p, int b) {
+  return p.ctx_base > 0 ? min(p.ctx_base + b, p.max_context_len) : min(p.context_lens[b], p.max_context_len);
+}
+
 // In-place unnormalized FWHT of `rows` rows of 128 floats in LDS, by one wave.
 __device__ __forceinline__ void fwht_wave(float (*x)[D + 4], int rows, int lane) {
   for (int h = 1; h < D; h <<= 1) {
@@ -1203,7 +1209,7 @@ void decode_split_kernel(DecodeParams p) {
   const int lane = threadIdx.x;
   const int G = p.group;
   const int qh0 = kvh * G;
-  const int L = min(p.context_lens[b], p.max_context_len);
+  const int L = row_context(p, b);
   float* outp = p.out + ((int64_t)b * p.hq + qh0) * D;
   if (L <= 0) {
     if (split == 0)
@@ -1334,7 +1340,7 @@ void decode_split_kernel(DecodeParams p) {
       const_cast<uint8_t*>(p.v_pool + head_off), (short)0, (int)pool_rec, kBufferConfig);
   int btw0 = 0, btw1 = 0;
   {
-    const int32_t* row = p.block_tables + (int64_t)b * p.maxp + lp0;
+    const int32_t* row = p.block_tables + (int64_t)b * p.bt_stride + lp0;
     const int nwin = last_page - lp0 + 1;
     if (lane < nwin) btw0 = row[lane];
     if (lane + 64 < nwin) btw1 = row[lane + 64];
@@ -1576,7 +1582,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodePara
   constexpr int kCombGroups = kCombThreads / 32;
   const int qh = blockIdx.x, b = blockIdx.y;
   const int t = threadIdx.x;
-  const int L = min(p.context_lens[b], p.max_context_len);
+  const int L = row_context(p, b);
   const int ns = (L + p.tokens_per_split - 1) / p.tokens_per_split;
   if (ns <= 1) return;  // written by the split kernel
   const float* part = p.partials + ((int64_t)b * p.hq + qh) * p.nsplits * kPartialStride;

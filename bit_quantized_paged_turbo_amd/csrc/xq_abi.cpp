@@ -86,6 +86,20 @@ xq_status debug_check_decode(const xq_cache_layout* L, int32_t batch, const int3
   return XQ_OK;
 }
 
+// prefill: the pages of positions 0 .. max_ctx - 1 in the chunk's block-table row are page ids
+// in [0, num_pages).
+xq_status debug_check_prefill(const xq_cache_layout* L, const int32_t* block_table, int32_t max_ctx,
+                              hipStream_t s) {
+  std::vector<int32_t> bt;
+  const int32_t pages = (max_ctx + L->page_size - 1) / L->page_size;
+  if (xq_status st = fetch(bt, block_table, pages, s)) return st;
+  for (int32_t i = 0; i < pages; ++i)
+    if (bt[i] < 0 || bt[i] >= L->num_pages)
+      return fail(XQ_EINVAL, "XQ_DEBUG: block_table[%d] = %d is not a page id below num_pages = %lld", i, bt[i],
+                  (long long)L->num_pages);
+  return XQ_OK;
+}
+
 // append: token_seq >= 0, 0 <= token_pos < max_pages_per_seq * page_size, the page of every
 // token is a page id in [0, num_pages), and no two tokens write the same (page, slot). The
 // block table is read for rows 0 .. max(token_seq), the rows the kernel reads.
@@ -159,6 +173,86 @@ int32_t plan_tokens_per_split(const xq_cache_layout* L, int32_t batch, int32_t m
   const int64_t cap = (int64_t)xq::kMaxSplitPages * ps;
   if (tps > cap) tps = cap;
   return (int32_t)tps;
+}
+
+// Shared by decode and prefill. Row b (a sequence, or a query token of a prefill chunk) reads
+// block_tables + b * bt_stride and attends to context_lens[b] tokens (ctx_base == 0) or to
+// ctx_base + b tokens (prefill: ctx_base = start_pos + 1, one shared table row).
+xq_status attention(const xq_cache_layout* layout, const void* q, int32_t batch, int32_t num_q_heads,
+                    const void* k_pool, const void* v_pool, const int32_t* block_tables, int32_t bt_stride,
+                    int32_t max_pages_per_seq, const int32_t* context_lens, int32_t ctx_base,
+                    int32_t max_context_len, float softmax_scale, int32_t num_splits_hint, void* workspace,
+                    int64_t workspace_bytes, float* out, hipStream_t stream) {
+  if (batch > 65535) return fail(XQ_EUNSUPPORTED, "batch %d > 65535", batch);
+  if (num_q_heads < 1 || num_q_heads % layout->num_kv_heads != 0)
+    return fail(XQ_EINVAL, "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads,
+                layout->num_kv_heads);
+  const int32_t g = num_q_heads / layout->num_kv_heads;
+  if (g > xq::kMaxGroup) return fail(XQ_EUNSUPPORTED, "group size %d > %d", g, xq::kMaxGroup);
+  if (!q || !k_pool || !v_pool || !block_tables || !out)
+    return fail(XQ_EINVAL, "a required pointer is NULL");
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(XQ_EINVAL, "q and the pools must be 16-byte aligned");
+  if (max_pages_per_seq < 1) return fail(XQ_EINVAL, "max_pages_per_seq %d < 1", max_pages_per_seq);
+  if ((int64_t)max_context_len > (int64_t)max_pages_per_seq * layout->page_size)
+    return fail(XQ_EINVAL, "context of %d tokens exceeds max_pages * page_size", max_context_len);
+  if (num_splits_hint < 0 && !fixed_split_ok(layout, num_splits_hint))
+    return fail(XQ_EINVAL,
+                "num_splits_hint %d: a fixed partition must be a multiple of 32 tokens and of the page size, "
+                "at most 128 pages", num_splits_hint);
+  if (!(softmax_scale == softmax_scale)) return fail(XQ_EINVAL, "softmax_scale is NaN");
+
+  const int32_t ctx = max_context_len > 0 ? max_context_len : 1;
+  const int32_t tps = plan_tokens_per_split(layout, batch, ctx, num_splits_hint);
+  const int32_t nsplits = (ctx + tps - 1) / tps;
+  if (nsplits > 65535) return fail(XQ_EUNSUPPORTED, "%d splits > 65535", nsplits);
+  // one 64-lane workgroup per (split, kv head, row) on a one-dimensional grid
+  const int64_t units = (int64_t)nsplits * layout->num_kv_heads * batch;
+  if (units >= ((int64_t)1 << 26))
+    return fail(XQ_EUNSUPPORTED, "%lld work units (splits x kv heads x rows) >= 2^26", (long long)units);
+  const xq::WorkspaceLayout ws = xq::workspace_layout(layout->kv_dtype, batch, num_q_heads, nsplits);
+  if (ws.total > 0) {
+    if (!workspace || workspace_bytes < ws.total)
+      return fail(XQ_EWORKSPACE, "workspace of %lld bytes needed, %lld given", (long long)ws.total,
+                  (long long)workspace_bytes);
+    if (!aligned16(workspace)) return fail(XQ_EINVAL, "workspace must be 16-byte aligned");
+  }
+  uint8_t* wsp = static_cast<uint8_t*>(workspace);
+  if (debug_on()) {
+    xq_status st = ctx_base > 0 ? debug_check_prefill(layout, block_tables, max_context_len, stream)
+                                : debug_check_decode(layout, batch, block_tables, max_pages_per_seq, context_lens,
+                                                     max_context_len, stream);
+    if (st) return st;
+  }
+
+  xq::DecodeParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_pool = static_cast<const uint8_t*>(k_pool);
+  p.v_pool = static_cast<const uint8_t*>(v_pool);
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.out = out;
+  p.partials = ws.part_bytes ? reinterpret_cast<float*>(wsp + ws.part_off) : nullptr;
+  p.block_bytes = block_bytes_of(layout);
+  p.page_stride = p.block_bytes * layout->num_kv_heads;
+  p.pool_bytes = p.page_stride * layout->num_pages;
+  p.batch = batch;
+  p.hq = num_q_heads;
+  p.hkv = layout->num_kv_heads;
+  p.group = g;
+  p.page_size = layout->page_size;
+  p.page_shift = __builtin_ctz((unsigned)layout->page_size);
+  p.maxp = max_pages_per_seq;
+  p.tokens_per_split = tps;
+  p.nsplits = nsplits;
+  p.max_context_len = max_context_len;
+  p.softmax_scale = softmax_scale;
+  p.fixed_splits = num_splits_hint < 0 ? 1 : 0;
+  p.bt_stride = bt_stride;
+  p.ctx_base = ctx_base;
+  const hipError_t e = xq::launch_decode(layout->kv_dtype, p, stream);
+  if (e != hipSuccess) return fail(XQ_EHIP, "attention launch: %s", hipGetErrorString(e));
+  return XQ_OK;
 }
 
 }  // namespace
@@ -256,73 +350,27 @@ xq_status xq_paged_decode_attention(const xq_cache_layout* layout, const void* q
   if (xq_status st = check_layout(layout)) return st;
   if (batch < 0) return fail(XQ_EINVAL, "batch %d < 0", batch);
   if (batch == 0) return XQ_OK;
-  if (batch > 65535) return fail(XQ_EUNSUPPORTED, "batch %d > 65535", batch);
-  if (num_q_heads < 1 || num_q_heads % layout->num_kv_heads != 0)
-    return fail(XQ_EINVAL, "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads,
-                layout->num_kv_heads);
-  const int32_t g = num_q_heads / layout->num_kv_heads;
-  if (g > xq::kMaxGroup) return fail(XQ_EUNSUPPORTED, "group size %d > %d", g, xq::kMaxGroup);
-  if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out)
-    return fail(XQ_EINVAL, "a required pointer is NULL");
-  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
-    return fail(XQ_EINVAL, "q and the pools must be 16-byte aligned");
+  if (!context_lens) return fail(XQ_EINVAL, "a required pointer is NULL");
   if (max_context_len < 0) return fail(XQ_EINVAL, "max_context_len %d < 0", max_context_len);
-  if (max_pages_per_seq < 1) return fail(XQ_EINVAL, "max_pages_per_seq %d < 1", max_pages_per_seq);
-  if ((int64_t)max_context_len > (int64_t)max_pages_per_seq * layout->page_size)
-    return fail(XQ_EINVAL, "max_context_len %d exceeds max_pages_per_seq * page_size", max_context_len);
-  if (num_splits_hint < 0 && !fixed_split_ok(layout, num_splits_hint))
-    return fail(XQ_EINVAL,
-                "num_splits_hint %d: a fixed partition must be a multiple of 32 tokens and of the page size, "
-                "at most 128 pages", num_splits_hint);
-  if (!(softmax_scale == softmax_scale)) return fail(XQ_EINVAL, "softmax_scale is NaN");
+  return attention(layout, q, batch, num_q_heads, k_pool, v_pool, block_tables, max_pages_per_seq,
+                   max_pages_per_seq, context_lens, 0, max_context_len, softmax_scale, num_splits_hint,
+                   workspace, workspace_bytes, out, static_cast<hipStream_t>(stream));
+}
 
-  const int32_t ctx = max_context_len > 0 ? max_context_len : 1;
-  const int32_t tps = plan_tokens_per_split(layout, batch, ctx, num_splits_hint);
-  const int32_t nsplits = (ctx + tps - 1) / tps;
-  if (nsplits > 65535) return fail(XQ_EUNSUPPORTED, "%d splits > 65535", nsplits);
-  // one 64-lane workgroup per (split, kv head, sequence) on a one-dimensional grid
-  const int64_t units = (int64_t)nsplits * layout->num_kv_heads * batch;
-  if (units >= ((int64_t)1 << 26))
-    return fail(XQ_EUNSUPPORTED, "%lld work units (splits x kv heads x batch) >= 2^26", (long long)units);
-  const xq::WorkspaceLayout ws = xq::workspace_layout(layout->kv_dtype, batch, num_q_heads, nsplits);
-  if (ws.total > 0) {
-    if (!workspace || workspace_bytes < ws.total)
-      return fail(XQ_EWORKSPACE, "workspace of %lld bytes needed, %lld given", (long long)ws.total,
-                  (long long)workspace_bytes);
-    if (!aligned16(workspace)) return fail(XQ_EINVAL, "workspace must be 16-byte aligned");
-  }
-  uint8_t* wsp = static_cast<uint8_t*>(workspace);
-  if (debug_on())
-    if (xq_status st = debug_check_decode(layout, batch, block_tables, max_pages_per_seq, context_lens,
-                                          max_context_len, static_cast<hipStream_t>(stream)))
-      return st;
-
-  xq::DecodeParams p{};
-  p.q = static_cast<const uint16_t*>(q);
-  p.k_pool = static_cast<const uint8_t*>(k_pool);
-  p.v_pool = static_cast<const uint8_t*>(v_pool);
-  p.block_tables = block_tables;
-  p.context_lens = context_lens;
-  p.out = out;
-  p.partials = ws.part_bytes ? reinterpret_cast<float*>(wsp + ws.part_off) : nullptr;
-  p.block_bytes = block_bytes_of(layout);
-  p.page_stride = p.block_bytes * layout->num_kv_heads;
-  p.pool_bytes = p.page_stride * layout->num_pages;
-  p.batch = batch;
-  p.hq = num_q_heads;
-  p.hkv = layout->num_kv_heads;
-  p.group = g;
-  p.page_size = layout->page_size;
-  p.page_shift = __builtin_ctz((unsigned)layout->page_size);
-  p.maxp = max_pages_per_seq;
-  p.tokens_per_split = tps;
-  p.nsplits = nsplits;
-  p.max_context_len = max_context_len;
-  p.softmax_scale = softmax_scale;
-  p.fixed_splits = num_splits_hint < 0 ? 1 : 0;
-  const hipError_t e = xq::launch_decode(layout->kv_dtype, p, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(XQ_EHIP, "decode launch: %s", hipGetErrorString(e));
-  return XQ_OK;
+xq_status xq_paged_prefill_attention(const xq_cache_layout* layout, const void* q, int32_t n_query,
+                                     int32_t num_q_heads, const void* k_pool, const void* v_pool,
+                                     const int32_t* block_table, int32_t max_pages, int32_t start_pos,
+                                     float softmax_scale, int32_t num_splits_hint, void* workspace,
+                                     int64_t workspace_bytes, float* out, void* stream) {
+  if (xq_status st = check_layout(layout)) return st;
+  if (n_query < 0) return fail(XQ_EINVAL, "n_query %d < 0", n_query);
+  if (start_pos < 0) return fail(XQ_EINVAL, "start_pos %d < 0", start_pos);
+  if (n_query == 0) return XQ_OK;
+  if ((int64_t)start_pos + n_query > INT32_MAX / 2)
+    return fail(XQ_EINVAL, "start_pos + n_query = %lld is too large", (long long)start_pos + n_query);
+  return attention(layout, q, n_query, num_q_heads, k_pool, v_pool, block_table, 0, max_pages, nullptr,
+                   start_pos + 1, start_pos + n_query, softmax_scale, num_splits_hint, workspace,
+                   workspace_bytes, out, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -75,6 +75,9 @@ struct DecodeParams {
   float softmax_scale;
   int32_t fixed_splits;         // 1: partitions fixed by the caller; kernel variants chosen
                                 // independently of the batch, so results are batch invariant
+  int32_t bt_stride;            // block-table entries between rows (maxp; 0: one shared row)
+  int32_t ctx_base;             // 0: row b attends to context_lens[b] tokens; > 0: to
+                                // ctx_base + b tokens (query b of a prefill chunk)
 };
 
 hipError_t launch_quantize_append(int dtype, const AppendParams& p, hipStream_t stream);

@@ -193,6 +193,42 @@ xq_status xq_paged_decode_attention(const xq_cache_layout* layout,
                                     void* workspace, int64_t workspace_bytes,
                                     float* out, void* stream);
 
+/*
+ * Chunked prefill attention over the paged (and, for turbo types, quantized) cache: the queries
+ * of one chunk of one sequence, each attending causally to the sequence's cached rows. Defined
+ * by the infero page, section "Beyond plain text decode", item "Continuous batching" (decodes
+ * go first, prefill fills the rest of a step and may be split across steps, so a chunk attends
+ * to the cached rows of earlier chunks and to its own), with each row read as the decode reads
+ * it (the xInfer page's TurboQuant rows, rotated and quantized).
+ *
+ * Query i sits at position start_pos + i and attends to positions 0 .. start_pos + i (no row
+ * after its own); the chunk's own K/V rows must have been appended (xq_quantize_append) before.
+ * Per query head j (kv head j / (num_q_heads / num_kv_heads)) the result is the decode's formula
+ * with context length start_pos + i + 1.
+ *
+ *   q                  bf16 [n_query][num_q_heads][128], 16-byte aligned
+ *   k_pool, v_pool     pools written by xq_quantize_append
+ *   block_table        int32 [max_pages]: the sequence's physical page per logical page
+ *   start_pos          position of query 0 (the number of rows cached before the chunk), >= 0
+ *   softmax_scale      multiplies q . k
+ *   num_splits_hint    as for xq_paged_decode_attention
+ *   workspace          device scratch of >= xq_decode_workspace_bytes(layout, n_query,
+ *                      num_q_heads, start_pos + n_query, num_splits_hint) bytes (may be NULL when
+ *                      that is 0); calls that share a workspace must not overlap
+ *   out                fp32 [n_query][num_q_heads][128]
+ * n_query = 0 is a no-op. start_pos + n_query must not exceed max_pages * page_size (XQ_EINVAL);
+ * more than 65535 queries, a group size above 16 or 2^26 or more (split, kv head, query) units
+ * give XQ_EUNSUPPORTED. The block-table entries of positions below start_pos + n_query must be
+ * pages of the pool (checked only under XQ_DEBUG).
+ */
+xq_status xq_paged_prefill_attention(const xq_cache_layout* layout,
+                                     const void* q, int32_t n_query, int32_t num_q_heads,
+                                     const void* k_pool, const void* v_pool,
+                                     const int32_t* block_table, int32_t max_pages,
+                                     int32_t start_pos, float softmax_scale, int32_t num_splits_hint,
+                                     void* workspace, int64_t workspace_bytes,
+                                     float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

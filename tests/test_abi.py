@@ -123,3 +123,27 @@ def test_append_argument_errors(lib):
     assert call(kp=24) == xq.EINVAL
     assert call(maxp=0) == xq.EINVAL
     assert lib.xq_status_string(xq.EHIP) == b"HIP runtime error"
+
+
+def _prefill_status(lib, L, **kw):
+    a = dict(q=16, n=8, hq=8, k=16, v=16, bt=16, maxp=4, start=10, scale=0.1, splits=0, ws=None,
+             wsb=0, out=16, stream=None)
+    a.update(kw)
+    return lib.xq_paged_prefill_attention(ctypes.byref(L), a["q"], a["n"], a["hq"], a["k"], a["v"],
+                                          a["bt"], a["maxp"], a["start"], a["scale"], a["splits"],
+                                          a["ws"], a["wsb"], a["out"], a["stream"])
+
+
+def test_prefill_argument_errors(lib):
+    """Argument checks of the chunked prefill; every case fails (or returns) before a launch."""
+    L = xq.CacheLayout(4, 2, 16, 10)
+    assert _prefill_status(lib, L, n=0) == xq.OK                # nothing to do
+    assert _prefill_status(lib, L, n=-1) == xq.EINVAL
+    assert _prefill_status(lib, L, start=-1) == xq.EINVAL
+    assert _prefill_status(lib, L, start=60, n=5) == xq.EINVAL  # 65 positions > 4 pages of 16
+    assert b"max_pages" in lib.xq_last_error()
+    assert _prefill_status(lib, L, hq=7) == xq.EINVAL
+    assert _prefill_status(lib, L, bt=None) == xq.EINVAL
+    assert _prefill_status(lib, L, n=70000, maxp=5000, start=0) == xq.EUNSUPPORTED
+    assert _prefill_status(lib, L, start=40, splits=2) == xq.EWORKSPACE  # 48 positions, 2 partitions
+    assert _prefill_status(lib, L, scale=float("nan")) == xq.EINVAL

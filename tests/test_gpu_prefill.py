@@ -1,0 +1,86 @@
+"""GPU parity of the chunked prefill (xq_paged_prefill_attention) against the oracle's
+prefill_sequence: a chunk's queries attending causally to the sequence's cache, its own rows
+included (infero landing page, section "Beyond plain text decode", item "Continuous batching").
+Bar: within 2e-3 max-abs of the float64 oracle; with fixed partitions, query i bitwise equals
+the decode of the same sequence cut at start + i + 1 tokens."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_util import fill, make_cache, to_dev, upload_tables
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def _case(*a):
+    print("CASE", *a, flush=True)
+
+
+def _setup(dtype, start, chunk, hq, hkv, ps, cfg):
+    W = workloads.make(f"prefill-{dtype}-{ps}", cfg, dtype, [start + chunk], hq, hkv, ps)
+    cache = make_cache(W)
+    bt, _ = upload_tables(W)
+    kv = {0: W.kv_bits(0)}
+    fill(cache, W, bt, kv=kv)                  # the prefix and the chunk's own rows
+    r = np.random.default_rng(cfg)
+    q = workloads.round_to_bf16_bits(r.standard_normal((chunk, hq, 128)).astype(np.float32))
+    return W, cache, bt, kv, q
+
+
+@pytest.mark.parametrize("dtype,start,chunk,hq,hkv,ps", [
+    (4, 0, 77, 8, 2, 16), (4, 100, 77, 16, 8, 16), (4, 333, 40, 32, 8, 64), (8, 50, 33, 32, 8, 16),
+    (3, 200, 65, 40, 8, 64), (2, 17, 50, 8, 8, 16), (0, 90, 45, 8, 2, 32), (16, 120, 60, 32, 8, 16),
+    (4, 700, 1, 8, 2, 16)])
+def test_prefill_matches_oracle(dtype, start, chunk, hq, hkv, ps):
+    _case("prefill", dtype, start, chunk, hq, hkv, ps)
+    W, cache, bt, kv, q = _setup(dtype, start, chunk, hq, hkv, ps, 800 + dtype)
+    k, v = kv[0]
+    want = oracle.prefill_sequence(dtype, q, k, v, start, W.softmax_scale)
+    for splits in (0, 3):
+        out = cache.prefill(to_dev(q), bt[0], start, W.softmax_scale, splits)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        err = np.max(np.abs(got - want), axis=(1, 2))
+        assert np.all(err <= TOL), f"splits {splits}: worst query {int(np.argmax(err))} err {err.max():.3e}"
+
+
+def test_prefill_rows_equal_decode_cut_at_their_position():
+    """With fixed partitions the kernel variants do not depend on the batch, so query i of a
+    chunk and a decode of the same sequence with context start + i + 1 compute the same sums."""
+    _case("prefill-vs-decode")
+    dtype, start, chunk = 4, 300, 40
+    W, cache, bt, kv, q = _setup(dtype, start, chunk, 16, 8, 16, 820)
+    qd = to_dev(q)
+    out = cache.prefill(qd, bt[0], start, W.softmax_scale, -256)
+    rows = [0, 1, 17, chunk - 1]
+    cl = to_dev(np.array([start + i + 1 for i in rows], np.int32))
+    btr = bt[0:1].repeat(len(rows), 1).contiguous()
+    dec = cache.decode(qd[rows].contiguous(), btr, cl, start + chunk, W.softmax_scale, -256)
+    torch.cuda.synchronize()
+    for j, i in enumerate(rows):
+        assert torch.equal(out[i].cpu(), dec[j].cpu()), f"query {i}"
+
+
+def test_prefill_full_chunk_of_the_mixed_step():
+    """The mixed step's 2,048-token chunk (32q/8kv, turbo4, page 16, pages shuffled over the
+    2M-token pool) attending to itself from position 0; sampled queries against the oracle."""
+    _case("prefill-c4-chunk")
+    W = workloads.config(4)
+    cache = make_cache(W, fill_byte=None)
+    bt, _ = upload_tables(W)
+    b = W.batch                                  # the chunk's sequence
+    k, v = W.kv_bits(b)
+    fill(cache, W, bt, seqs=[b], kv={b: (k, v)})
+    r = np.random.default_rng(4)
+    q = workloads.round_to_bf16_bits(r.standard_normal((W.chunk_tokens, W.num_q_heads, 128)).astype(np.float32))
+    out = cache.prefill(to_dev(q), bt[b], 0, W.softmax_scale, 0)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    for i in (0, 1, 15, 16, 1000, W.chunk_tokens - 1):
+        want = oracle.prefill_sequence(W.dtype, q[i:i + 1], k[: i + 1], v[: i + 1], i, W.softmax_scale)
+        err = np.max(np.abs(got[i] - want[0]))
+        assert err <= TOL, f"query {i}: {err:.3e}"
