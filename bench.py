@@ -55,6 +55,7 @@ def parse():
     ap.add_argument("--replica-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the chunk-prefill timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run plain 512 MiB device copies (a known byte count for "
@@ -120,6 +121,37 @@ class Step:
                                            splits, ws, wsb, out, stream)
         if st:
             raise RuntimeError(lib.xq_last_error().decode())
+
+
+def time_prefill(lib, cache, W, bt, to_dev, stream, K, Wm):
+    """The chunk's queries attending causally to the chunk (xq_paged_prefill_attention from
+    position 0 over the chunk's appended rows): HIP events around each call on its stream."""
+    import torch
+    n, hq = W.chunk_tokens, W.num_q_heads
+    g = np.random.default_rng(7)
+    q = to_dev(workloads.round_to_bf16_bits(g.standard_normal((n, hq, 128)).astype(np.float32)))
+    row = bt[W.batch]
+    for _ in range(Wm):
+        cache.prefill(q, row, 0, W.softmax_scale)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record(stream)
+        cache.prefill(q, row, 0, W.softmax_scale)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    pairs = n * (n + 1) // 2                      # (query, key) pairs of the causal chunk
+    flops = 4 * 128 * hq * pairs                  # QK and PV multiply-adds
+    rows_bytes = n * W.num_kv_heads * 2 * row_bytes(W.dtype)
+    log(f"prefill of the {n}-token chunk: {ms * 1e3:.1f} us")
+    return {"queries": n, "start": 0, "call_us": round(ms * 1e3, 2),
+            "query_tokens_per_s": round(n / (ms * 1e-3), 1),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 3), "flops_per_call": flops,
+            "kv_bytes_once": rows_bytes,
+            "note": "the decode kernel with 16/g query tokens x g heads in the 16 matrix-core "
+                    "columns of a unit; each unit reads its causal prefix (from L2/MALL for this "
+                    "chunk)"}
 
 
 def cpu_baseline(W, seconds: float):
@@ -384,6 +416,8 @@ def main():
                                + (" + decode_combine_kernel)" if nsplits > 1 else ")"),
                      "bytes_per_launch": kv_bytes},
     }
+    if chunk is not None and not args.no_prefill:
+        result["prefill"] = time_prefill(lib, base, W, bt, to_dev, stream, K, Wm)
     if graph is not None:
         graph["value"] = round(kv_bytes / (graph["ms_per_step"] * 1e-3) / 1e9, 2)
         graph["seq_tokens_per_s"] = round(tokens / (graph["ms_per_step"] * 1e-3), 1)

@@ -76,7 +76,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRotC = 0x1.6a09e6p-4f;   // fp32 nearest to 1/sqrt(128)
 constexpr float kLazy = 8.0f;             // rescale only when a score beats m by > 2^8
 constexpr float kQiMax = 32000.f;         // |q| bound for two signed 8-bit digits
-constexpr float kWeightExp = 21.f;        // P' < 2^(w - m + 7): at most 2^15 in fp16
+constexpr float kWeightExp = 21.f;
+// Initial softmax reference: finite, so that a column with no token in its split (a prefill
+// query whose position lies before the split) gets weights 2^(-inf - ref) = 0 rather than NaN;
+// the first real score always moves the reference (it beats kNoRef by far more than 2^8).
+constexpr float kNoRef = -1e30f;        // P' < 2^(w - m + 7): at most 2^15 in fp16
 constexpr int kBufferConfig = 0x00020000;   // gfx9 buffer descriptor word 3
 // Cache policy of every cache read: non-temporal. Each code byte is read once per decode step,
 // so there is nothing to keep; measured on MI355X, random 1 KB page blocks stream at about
@@ -574,7 +578,7 @@ struct WaveState {
 template <int DT>
 __device__ __forceinline__ void process_tile(const Tile<DT>& t, WaveState& st,
                                              const v4i (&qi)[2][2], const v8bf (&qb)[4],
-                                             float qs, int lim, bool full, int col, int g) {
+                                             float qs, int lim, int lim_rows, bool full, int col, int g) {
   // ---- scores: y = log2-domain score; w = y + exponent field of s_v (turbo) --------------------
   float y[8], w[8];
   uint32_t sv[8];   // fp16 value scale in the low half (1.0 for bf16)
@@ -706,7 +710,7 @@ __device__ __forceinline__ void process_tile(const Tile<DT>& t, WaveState& st,
     uint32_t vv[8][4];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const bool ok = full || (16 * (j >> 2) + (j & 3) < lim);   // unwritten slots may be NaN
+      const bool ok = full || (16 * (j >> 2) + (j & 3) < lim_rows);   // unwritten slots may be NaN
 #pragma unroll
       for (int i = 0; i < 4; ++i) vv[j][i] = ok ? bf16_v_dword<DT>(t, j, i) : 0u;
     }
@@ -1181,15 +1185,18 @@ void decode_split_kernel(DecodeParams p) {
   // within an XCD first splits come first: every sequence is spread over all XCDs, every XCD
   // gets the same number of (long) first splits, and those start first. Otherwise (the
   // leftover ids too) units map in (sequence, split) order.
+  // A unit's rows: row block b (p.qt consecutive rows: sequences of a decode, where qt = 1, or
+  // queries of a prefill chunk).
   int split, kvh, b;
+  const uint32_t nblocks = ((uint32_t)p.batch + (uint32_t)p.qt - 1u) / (uint32_t)p.qt;
   {
     const uint32_t id = blockIdx.x, hkv = (uint32_t)p.hkv;
-    const uint32_t units = (uint32_t)p.nsplits * hkv * (uint32_t)p.batch;
+    const uint32_t units = (uint32_t)p.nsplits * hkv * nblocks;
     const uint32_t full = units / (8u * hkv) * (8u * hkv);
-    if ((p.batch & 7) == 0) {
+    if ((nblocks & 7u) == 0) {
       const uint32_t xcd = id & 7u, slot = id >> 3;
       kvh = (int)(slot % hkv);
-      const uint32_t r = slot / hkv, per = (uint32_t)p.batch >> 3;
+      const uint32_t r = slot / hkv, per = nblocks >> 3;
       split = (int)(r / per);
       b = (int)(8u * (r % per) + ((xcd - (uint32_t)split) & 7u));
     } else {
@@ -1207,13 +1214,21 @@ void decode_split_kernel(DecodeParams p) {
     }
   }
   const int lane = threadIdx.x;
-  const int G = p.group;
-  const int qh0 = kvh * G;
-  const int L = row_context(p, b);
-  float* outp = p.out + ((int64_t)b * p.hq + qh0) * D;
+  // Columns of the unit's MFMA tiles: c = t Gq + h is head h (of the kv head's Gq) of row
+  // b0 + t. A decode has one row (G = Gq); a prefill packs 16 / Gq query tokens of the chunk.
+  const int Gq = p.group;
+  const int qh0 = kvh * Gq;
+  const int b0 = b * p.qt;
+  if (b0 >= p.batch) return;   // (the grid has no such unit)
+  const int nrow = min(p.qt, p.batch - b0);
+  const int G = nrow * Gq;
+  auto qrow = [&](int c) -> int64_t {   // row of column c in q, out and the partials
+    return (int64_t)(b0 + c / Gq) * p.hq + qh0 + c % Gq;
+  };
+  const int L = row_context(p, b0 + nrow - 1);   // the unit's longest row (its last)
   if (L <= 0) {
     if (split == 0)
-      for (int i = lane; i < G * D; i += kThreads) outp[i] = 0.f;
+      for (int i = lane; i < G * D; i += kThreads) p.out[qrow(i >> 7) * D + (i & 127)] = 0.f;
     return;
   }
   const int tps = p.tokens_per_split;
@@ -1221,6 +1236,11 @@ void decode_split_kernel(DecodeParams p) {
   if (tok_begin >= L) return;
   const int tok_end = min(L, tok_begin + tps);
   const int nsplit_b = (L + tps - 1) / tps;
+  // causal limits of a prefill: this lane's column attends to tok_end_c tokens of the split; every
+  // column of a tile ending by tok_end_min is full
+  const int col0 = threadIdx.x & 15;
+  const int tok_end_c = min(tok_end, row_context(p, b0 + min(col0, G - 1) / Gq));
+  const int tok_end_min = min(tok_end, row_context(p, b0));
 
   // the staging ring and the epilogue's output rows (plus 64 per-lane sums) share one LDS buffer
   constexpr int kOutBytes = kMaxGroup * (D + 4) * 4 + kThreads * 4;
@@ -1235,8 +1255,9 @@ void decode_split_kernel(DecodeParams p) {
   // ---- query operands ---------------------------------------------------------------------
   // turbo types: the wave rotates and quantizes its G query rows itself (prep_query_lanes); the
   // rows arrive by LDS DMA ahead of the first tiles, so the work overlaps their latency
-  const bool pair = Stage<DT>::kOn && G <= kPairMaxGroup;
-  const bool quad = Stage<DT>::kOn && DEPTH >= 4 && G <= 4;   // the quad-block layout (pair too)
+  // (paired and quad layouts: decode only, all columns sharing one row)
+  const bool pair = Stage<DT>::kOn && G <= kPairMaxGroup && p.qt == 1;
+  const bool quad = pair && DEPTH >= 4 && G <= 4;   // the quad-block layout (pair too)
   const PairLane pl = pair_lane(lane, G);
   const QuadLane ql = quad_lane(lane, G);
   v4i qi[2][2] = {};
@@ -1244,11 +1265,16 @@ void decode_split_kernel(DecodeParams p) {
   v4i qq[8][2] = {};
   v8bf qb[4] = {};
   float qs = 0.f;
-  auto issue_query = [&](uint8_t* qa) __attribute__((always_inline)) {   // G rows of 256 B to qa, 1 KB per instruction
-    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(p.q + ((int64_t)b * p.hq + qh0) * D), (short)0, G * 256, kBufferConfig);
-    for (int i = 0; i < (G + 3) >> 2; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(qa + 1024 * i), 16, 16 * lane, 1024 * i, 0, 0);
+  auto issue_query = [&](uint8_t* qa) __attribute__((always_inline)) {   // G rows of 256 B to qa
+    // row t of the unit: Gq rows of 256 B, contiguous in q, to qa + t Gq 256 (1 KB an instruction)
+    for (int t = 0; t < nrow; ++t) {
+      const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(p.q + qrow(t * Gq) * D), (short)0, Gq * 256, kBufferConfig);
+      for (int i = 0; i < (Gq + 3) >> 2; ++i)
+        if (16 * lane + 1024 * i < Gq * 256)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(qa + t * Gq * 256 + 1024 * i), 16, 16 * lane,
+                                                   1024 * i, 0, 0);
+    }
   };
   auto load_query = [&](uint8_t* qa) __attribute__((always_inline)) {    // after the rows have landed in qa
     float* qsc = reinterpret_cast<float*>(qa + kMaxGroup * 256);
@@ -1298,7 +1324,7 @@ void decode_split_kernel(DecodeParams p) {
   };
   if constexpr (kBf16Mma<DT>) {
     if (col < G) {
-      const int64_t row = (int64_t)b * p.hq + qh0 + col;
+      const int64_t row = qrow(col);
       const v8bf* s = reinterpret_cast<const v8bf*>(p.q + row * D + 32 * g);
       qb[0] = s[0]; qb[1] = s[1]; qb[2] = s[2]; qb[3] = s[3];
       qs = p.softmax_scale * kLog2e;
@@ -1313,7 +1339,7 @@ void decode_split_kernel(DecodeParams p) {
 #pragma unroll
   for (int tau = 0; tau < 8; ++tau) st.acc[tau] = v4f{0.f, 0.f, 0.f, 0.f};
   st.accb = v4f{0.f, 0.f, 0.f, 0.f};
-  st.m = -INFINITY;
+  st.m = kNoRef;
   st.l = 0.f;
 
   // ---- main loop: tiles 0 .. ntiles-1 of the unit, kDepth in flight --------------------------
@@ -1373,7 +1399,7 @@ void decode_split_kernel(DecodeParams p) {
   };
   auto run = [&](const Tile<DT>& t, int i) __attribute__((always_inline)) {
     const int t0 = tok_begin + 32 * i;
-    process_tile<DT>(t, st, qi, qb, qs, tok_end - t0 - 4 * g, t0 + 32 <= tok_end, col, g);
+    process_tile<DT>(t, st, qi, qb, qs, tok_end_c - t0 - 4 * g, tok_end - t0 - 4 * g, t0 + 32 <= tok_end_min, col, g);
   };
   auto main_loop = [&](auto kFast, auto kPair) __attribute__((always_inline)) {
     if constexpr (Stage<DT>::kOn) {
@@ -1514,15 +1540,15 @@ void decode_split_kernel(DecodeParams p) {
         ob[h][d] = head_acc(h, d) / head_l(h);
       }
       fwht_wave(ob, G, lane);
-      for (int k = lane; k < G * D; k += kThreads) outp[k] = ob[k >> 7][k & 127] * kRotC;
+      for (int k = lane; k < G * D; k += kThreads) p.out[qrow(k >> 7) * D + (k & 127)] = ob[k >> 7][k & 127] * kRotC;
     } else {
       for (int k = lane; k < G * D; k += kThreads) {
         const int h = k >> 7, d = k & 127;
-        float* part = p.partials + (((int64_t)b * p.hq + qh0 + h) * p.nsplits + split) * kPartialStride;
+        float* part = p.partials + (qrow(h) * p.nsplits + split) * kPartialStride;
         part[4 + d] = head_acc(h, d);
       }
       if (lane < G) {   // lane n < G: column n is head n, block 0
-        float* part = p.partials + (((int64_t)b * p.hq + qh0 + lane) * p.nsplits + split) * kPartialStride;
+        float* part = p.partials + (qrow(lane) * p.nsplits + split) * kPartialStride;
         part[0] = st.m;
         part[1] = head_l(lane);
       }
@@ -1548,17 +1574,17 @@ void decode_split_kernel(DecodeParams p) {
       }
     if constexpr (kRotated<DT>) {
       fwht_wave(ob, G, lane);
-      for (int k = lane; k < G * D; k += kThreads) outp[k] = ob[k >> 7][k & 127] * kRotC;
+      for (int k = lane; k < G * D; k += kThreads) p.out[qrow(k >> 7) * D + (k & 127)] = ob[k >> 7][k & 127] * kRotC;
     } else {
       __syncthreads();
-      for (int k = lane; k < G * D; k += kThreads) outp[k] = ob[k >> 7][k & 127];
+      for (int k = lane; k < G * D; k += kThreads) p.out[qrow(k >> 7) * D + (k & 127)] = ob[k >> 7][k & 127];
     }
   } else {
     // partials (m, l, acc) of this split, in the rotated space
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       if (4 * g + r < G) {
-        float* part = p.partials + (((int64_t)b * p.hq + qh0 + 4 * g + r) * p.nsplits + split) * kPartialStride;
+        float* part = p.partials + (qrow(4 * g + r) * p.nsplits + split) * kPartialStride;
         float v[8];
 #pragma unroll
         for (int tau = 0; tau < 8; ++tau) v[tau] = (st.acc[tau][r] - st.accb[r]) * unit;
@@ -1566,7 +1592,7 @@ void decode_split_kernel(DecodeParams p) {
         reinterpret_cast<float4*>(part + 4 + 8 * col)[1] = make_float4(v[4], v[5], v[6], v[7]);
       }
     if (g == 0 && col < G) {
-      float* part = p.partials + (((int64_t)b * p.hq + qh0 + col) * p.nsplits + split) * kPartialStride;
+      float* part = p.partials + (qrow(col) * p.nsplits + split) * kPartialStride;
       part[0] = st.m;
       part[1] = st.l;
     }
@@ -1582,7 +1608,8 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodePara
   constexpr int kCombGroups = kCombThreads / 32;
   const int qh = blockIdx.x, b = blockIdx.y;
   const int t = threadIdx.x;
-  const int L = row_context(p, b);
+  // the split count of b's unit (its last row's), which the split kernel used for every row
+  const int L = row_context(p, min(p.batch - 1, (b / p.qt) * p.qt + p.qt - 1));
   const int ns = (L + p.tokens_per_split - 1) / p.tokens_per_split;
   if (ns <= 1) return;  // written by the split kernel
   const float* part = p.partials + ((int64_t)b * p.hq + qh) * p.nsplits * kPartialStride;
@@ -1655,6 +1682,11 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodePara
   }
 }
 
+// Work units of a call: (split, kv head, block of qt rows).
+inline int64_t unit_count(const DecodeParams& p) {
+  return (int64_t)p.nsplits * p.hkv * (((int64_t)p.batch + p.qt - 1) / p.qt);
+}
+
 // Ring depth for the staged path: the units are spread over 256 compute units; with w of them
 // resident per CU (at most 12: three waves per SIMD), the LDS holds 160 KB / (w * slot) slots.
 template <int DT>
@@ -1662,7 +1694,7 @@ int pick_depth(const DecodeParams& p) {
   if constexpr (!Stage<DT>::kOn) {
     return 3;
   } else {
-    const int64_t units = (int64_t)p.nsplits * p.hkv * p.batch;
+    const int64_t units = unit_count(p);
     const int64_t per_cu = std::min<int64_t>(12, std::max<int64_t>(1, (units + 255) / 256));
     const int64_t slots = kLdsPerCu / (per_cu * Stage<DT>::kSlot);
     const int64_t cap = kMaxVmcnt / Stage<DT>::kOps + 1;
@@ -1674,7 +1706,7 @@ int pick_depth(const DecodeParams& p) {
 
 template <int DT, int DEPTH>
 void launch_split(const DecodeParams& p, hipStream_t stream) {
-  const int64_t units = (int64_t)p.nsplits * p.hkv * p.batch;
+  const int64_t units = unit_count(p);
   hipLaunchKernelGGL((decode_split_kernel<DT, DEPTH>), dim3((unsigned)units), dim3(kThreads), 0, stream, p);
 }
 

@@ -206,8 +206,10 @@ xq_status attention(const xq_cache_layout* layout, const void* q, int32_t batch,
   const int32_t tps = plan_tokens_per_split(layout, batch, ctx, num_splits_hint);
   const int32_t nsplits = (ctx + tps - 1) / tps;
   if (nsplits > 65535) return fail(XQ_EUNSUPPORTED, "%d splits > 65535", nsplits);
-  // one 64-lane workgroup per (split, kv head, row) on a one-dimensional grid
-  const int64_t units = (int64_t)nsplits * layout->num_kv_heads * batch;
+  // One 64-lane workgroup per (split, kv head, row block) on a one-dimensional grid. A prefill
+  // packs 16 / g query tokens (all g heads of each) into the 16 columns of a unit's MFMA tiles.
+  const int32_t qt = ctx_base > 0 ? std::max(1, xq::kMaxGroup / g) : 1;
+  const int64_t units = (int64_t)nsplits * layout->num_kv_heads * ((batch + qt - 1) / qt);
   if (units >= ((int64_t)1 << 26))
     return fail(XQ_EUNSUPPORTED, "%lld work units (splits x kv heads x rows) >= 2^26", (long long)units);
   const xq::WorkspaceLayout ws = xq::workspace_layout(layout->kv_dtype, batch, num_q_heads, nsplits);
@@ -250,6 +252,7 @@ xq_status attention(const xq_cache_layout* layout, const void* q, int32_t batch,
   p.fixed_splits = num_splits_hint < 0 ? 1 : 0;
   p.bt_stride = bt_stride;
   p.ctx_base = ctx_base;
+  p.qt = qt;
   const hipError_t e = xq::launch_decode(layout->kv_dtype, p, stream);
   if (e != hipSuccess) return fail(XQ_EHIP, "attention launch: %s", hipGetErrorString(e));
   return XQ_OK;

@@ -78,6 +78,7 @@ struct DecodeParams {
   int32_t bt_stride;            // block-table entries between rows (maxp; 0: one shared row)
   int32_t ctx_base;             // 0: row b attends to context_lens[b] tokens; > 0: to
                                 // ctx_base + b tokens (query b of a prefill chunk)
+  int32_t qt;                   // rows per work unit: 1 (decode) or 16 / group (prefill)
 };
 
 hipError_t launch_quantize_append(int dtype, const AppendParams& p, hipStream_t stream);

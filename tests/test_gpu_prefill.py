@@ -33,7 +33,8 @@ def _setup(dtype, start, chunk, hq, hkv, ps, cfg):
 @pytest.mark.parametrize("dtype,start,chunk,hq,hkv,ps", [
     (4, 0, 77, 8, 2, 16), (4, 100, 77, 16, 8, 16), (4, 333, 40, 32, 8, 64), (8, 50, 33, 32, 8, 16),
     (3, 200, 65, 40, 8, 64), (2, 17, 50, 8, 8, 16), (0, 90, 45, 8, 2, 32), (16, 120, 60, 32, 8, 16),
-    (4, 700, 1, 8, 2, 16)])
+    (4, 700, 1, 8, 2, 16), (4, 37, 50, 8, 8, 16), (3, 64, 29, 40, 8, 64), (8, 5, 70, 16, 1, 32),
+    (0, 30, 47, 24, 8, 16), (16, 3, 61, 8, 1, 16)])
 def test_prefill_matches_oracle(dtype, start, chunk, hq, hkv, ps):
     _case("prefill", dtype, start, chunk, hq, hkv, ps)
     W, cache, bt, kv, q = _setup(dtype, start, chunk, hq, hkv, ps, 800 + dtype)
@@ -47,12 +48,16 @@ def test_prefill_matches_oracle(dtype, start, chunk, hq, hkv, ps):
         assert np.all(err <= TOL), f"splits {splits}: worst query {int(np.argmax(err))} err {err.max():.3e}"
 
 
-def test_prefill_rows_equal_decode_cut_at_their_position():
-    """With fixed partitions the kernel variants do not depend on the batch, so query i of a
-    chunk and a decode of the same sequence with context start + i + 1 compute the same sums."""
-    _case("prefill-vs-decode")
+@pytest.mark.parametrize("hq,hkv,exact", [(16, 1, True), (16, 8, False), (32, 8, False)])
+def test_prefill_rows_equal_decode_cut_at_their_position(hq, hkv, exact):
+    """Query i of a chunk against a decode of the same sequence with context start + i + 1, both
+    with fixed partitions. With 16 query heads per kv head a prefill unit holds one query, in the
+    decode's layout, so the two are bitwise equal; with fewer, the prefill packs 16 / g queries
+    into a unit's 16 columns where the decode uses its paired layout, and the sums are rounded in
+    another order."""
+    _case("prefill-vs-decode", hq, hkv)
     dtype, start, chunk = 4, 300, 40
-    W, cache, bt, kv, q = _setup(dtype, start, chunk, 16, 8, 16, 820)
+    W, cache, bt, kv, q = _setup(dtype, start, chunk, hq, hkv, 16, 820)
     qd = to_dev(q)
     out = cache.prefill(qd, bt[0], start, W.softmax_scale, -256)
     rows = [0, 1, 17, chunk - 1]
@@ -61,7 +66,11 @@ def test_prefill_rows_equal_decode_cut_at_their_position():
     dec = cache.decode(qd[rows].contiguous(), btr, cl, start + chunk, W.softmax_scale, -256)
     torch.cuda.synchronize()
     for j, i in enumerate(rows):
-        assert torch.equal(out[i].cpu(), dec[j].cpu()), f"query {i}"
+        a, d = out[i].cpu(), dec[j].cpu()
+        if exact:
+            assert torch.equal(a, d), f"query {i}"
+        else:
+            assert float((a - d).abs().max()) < 1e-4, f"query {i}"
 
 
 def test_prefill_full_chunk_of_the_mixed_step():
