@@ -118,10 +118,19 @@ template <> struct Stage<8> {
   static constexpr bool kOn = true;
   static constexpr int kHalf = 2048, kDma = 2, kOps = 4 * kDma + 2, kSlot = 4 * kHalf + 128;
 };
+// turbo3: a half's 16 code rows (768 B, contiguous in the page block) are copied as they are by
+// one DMA of 16 B per lane; the last 16 lanes land in the 256 B of padding that follow.
+template <> struct Stage<3> {
+  static constexpr bool kOn = true;
+  static constexpr int kHalf = 1024, kDma = 1, kOps = 4 * kDma + 2, kSlot = 4 * kHalf + 128;
+};
+// Layouts that pair (or quad) token blocks in the QK tile; the others use the one-block layout.
+template <int DT> constexpr bool kPairOk = DT == 4 || DT == 8;
 constexpr int kLdsPerCu = 160 * 1024;
 // LDS for the wave's query preparation: kMaxGroup rows of 256 B, then their fp32 scales
 constexpr int kQueryLds = kMaxGroup * 256 + kMaxGroup * 4;
-static_assert(Stage<4>::kSlot >= kQueryLds && Stage<8>::kSlot >= kQueryLds, "query rows fit one ring slot");
+static_assert(Stage<4>::kSlot >= kQueryLds && Stage<8>::kSlot >= kQueryLds && Stage<3>::kSlot >= kQueryLds,
+              "query rows fit one ring slot");
 // Paired-block QK (turbo4, turbo8): with at most this many query heads per kv head, the 16
 // columns of the QK tile hold two 16-token blocks of the tile side by side.
 constexpr int kPairMaxGroup = 8;
@@ -391,6 +400,9 @@ __device__ __forceinline__ DmaOffsets dma_offsets(int lane) {
   if constexpr (DT == 4) {
     o.k[0] = (lane & 15) * 64 + 16 * (lane >> 4);
     o.v[0] = (4 * ((lane >> 2) & 3) + (lane >> 4)) * 64 + 16 * (lane & 3);
+  } else if constexpr (DT == 3) {
+    o.k[0] = 16 * lane;   // as stored: row c of the half at 48 c
+    o.v[0] = 16 * lane;
   } else if constexpr (DT == 8) {
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -444,7 +456,18 @@ __device__ __forceinline__ void read_slot(Tile<DT>& t, const uint8_t* slot, int 
   for (int h = 0; h < 2; ++h) {
     t.ks[h] = *reinterpret_cast<const v2i*>(slot + 4 * S::kHalf + 32 * h + 8 * g);
     t.vs[h] = *reinterpret_cast<const v2i*>(slot + 4 * S::kHalf + 64 + 32 * h + 8 * g);
-    if constexpr (DT == 4) {
+    if constexpr (DT == 3) {
+      // the bytes the register path loads: K row c, bytes 12 g .. 12 g + 11; V rows 4 g + r, the
+      // two dwords from byte 4 ((3 c) >> 2) (read as dwords: the offsets are 4-byte aligned)
+      const int col = lane & 15;
+      const int* kr = reinterpret_cast<const int*>(slot + h * S::kHalf + 48 * col + 12 * g);
+      t.k[h] = v3i{kr[0], kr[1], kr[2]};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int* vr = reinterpret_cast<const int*>(slot + (2 + h) * S::kHalf + 48 * (4 * g + r) + 4 * ((3 * col) >> 2));
+        t.v[4 * h + r] = v2i{vr[0], vr[1]};
+      }
+    } else if constexpr (DT == 4) {
       t.k[h] = *reinterpret_cast<const v4i*>(slot + h * S::kHalf + 16 * lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -949,6 +972,7 @@ __device__ __forceinline__ QuadLane quad_lane(int lane, int G) {
 template <int DT> struct QuadK;
 template <> struct QuadK<4> { v4i k[4]; };   // the lane's token row: 16 B per 32 dims
 template <> struct QuadK<8> { v4i k[8]; };   // 16 B per 16 dims
+template <> struct QuadK<3> { v4i k[1]; };   // never used: turbo3 has no quad layout (kPairOk)
 
 template <int DT>
 __device__ __forceinline__ void read_quad_k(QuadK<DT>& t, const uint8_t* slot0, const uint8_t* slot1, int lane) {
@@ -1170,7 +1194,7 @@ __device__ __forceinline__ void fwht_wave(float (*x)[D + 4], int rows, int lane)
 // Waves per SIMD the register budget is sized for: deep rings (4+ slots) are only picked when
 // at most two waves share a SIMD.
 template <int DT, int DEPTH>
-constexpr int kWavesPerEu = DT == 0 ? 1 : ((DT == 3 || DT == 2 || DT == kFp8) ? 2 : (DEPTH >= 4 ? 2 : 3));
+constexpr int kWavesPerEu = DT == 0 ? 1 : ((DT == 2 || DT == kFp8) ? 2 : (DEPTH >= 4 ? 2 : 3));
 
 // DEPTH: tiles in flight per wave on the staged path (LDS slots); chosen at launch from how
 // many waves share a compute unit, so that the LDS of the resident waves holds as many tiles
@@ -1256,7 +1280,7 @@ void decode_split_kernel(DecodeParams p) {
   // turbo types: the wave rotates and quantizes its G query rows itself (prep_query_lanes); the
   // rows arrive by LDS DMA ahead of the first tiles, so the work overlaps their latency
   // (paired and quad layouts: decode only, all columns sharing one row)
-  const bool pair = Stage<DT>::kOn && G <= kPairMaxGroup && p.qt == 1;
+  const bool pair = kPairOk<DT> && G <= kPairMaxGroup && p.qt == 1;
   const bool quad = pair && DEPTH >= 4 && G <= 4;   // the quad-block layout (pair too)
   const PairLane pl = pair_lane(lane, G);
   const QuadLane ql = quad_lane(lane, G);
@@ -1428,7 +1452,7 @@ void decode_split_kernel(DecodeParams p) {
       if (DEPTH - 1 < ntiles) stage(DEPTH - 1, DEPTH - 1);
       // While tiles it .. it + DEPTH - 1 all exist, the number of tiles staged after the ones a
       // step reads is fixed and the wait takes a constant; only the last steps count down.
-      if constexpr (decltype(kPair)::value && DEPTH >= 4) {
+      if constexpr (kPairOk<DT> && decltype(kPair)::value && DEPTH >= 4) {
         if (quad) {
           // two tiles per step, in slots cur and next_slot(cur)
           int cur = 0;
@@ -1494,7 +1518,7 @@ void decode_split_kernel(DecodeParams p) {
       }
     }
   };
-  if constexpr (Stage<DT>::kOn) {
+  if constexpr (kPairOk<DT>) {
     if (pair) {
       if (fast) main_loop(std::true_type{}, std::true_type{});
       else main_loop(std::false_type{}, std::true_type{});

@@ -162,7 +162,7 @@ int32_t plan_tokens_per_split(const xq_cache_layout* L, int32_t batch, int32_t m
     // 2048 tokens that still gives 4 waves per CU (8 for the dtypes that read tiles straight
     // into registers and rely on occupancy to hide latency), at least 64 tokens.
     const int64_t heads = (int64_t)batch * L->num_kv_heads;
-    const int64_t target = (L->kv_dtype == 4 || L->kv_dtype == 8) ? 1024 : 2048;
+    const int64_t target = (L->kv_dtype == 4 || L->kv_dtype == 8 || L->kv_dtype == 3) ? 1024 : 2048;
     tps = 2048;
     while (tps > 64 && heads * ((max_ctx + tps - 1) / tps) < target) tps >>= 1;
   }
