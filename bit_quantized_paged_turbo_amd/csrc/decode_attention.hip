@@ -1637,24 +1637,16 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodePara
   const int ns = (L + p.tokens_per_split - 1) / p.tokens_per_split;
   if (ns <= 1) return;  // written by the split kernel
   const float* part = p.partials + ((int64_t)b * p.hq + qh) * p.nsplits * kPartialStride;
-  __shared__ float red[kCombThreads / 64 > 0 ? kCombThreads / 64 : 1];
   __shared__ float4 accs[kCombGroups][32];
   __shared__ float lsum[kCombGroups];
+  __shared__ float msum[kCombGroups];
   __shared__ float o[D];
 
-  // global reference M = max_s m_s
-  float mx = -INFINITY;
-  for (int s = t; s < ns; s += kCombThreads) mx = fmaxf(mx, part[(int64_t)s * kPartialStride]);
-  for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
-  if ((t & 63) == 0) red[t >> 6] = mx;
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < kCombThreads / 64; ++k) mx = fmaxf(mx, red[k]);
-
-  // weighted sums of l and acc
+  // One pass: each group of 32 threads merges its splits into a running (m, l, acc) by
+  // log-sum-exp, four splits' partials loaded together; the groups are merged at the end.
   const int s0 = t >> 5, d4 = t & 31;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float l = 0.f;
+  float l = 0.f, mt = -INFINITY;
   for (int sb = s0; sb < ns; sb += 4 * kCombGroups) {
     float ms[4], ls[4];
     float4 a[4];
@@ -1666,26 +1658,37 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodePara
       ls[u] = ps[1];
       a[u] = reinterpret_cast<const float4*>(ps + 4)[d4];
     }
+    // split sb < ns is real, so mn is finite; the first step scales the empty state by 0
+    const float mn = fmaxf(fmaxf(mt, fmaxf(ms[0], ms[1])), fmaxf(ms[2], ms[3]));
+    const float fo = __builtin_amdgcn_exp2f(mt - mn);
+    acc.x *= fo; acc.y *= fo; acc.z *= fo; acc.w *= fo;
+    l *= fo;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const float f = (ms[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[u] - mx);
+      const float f = (ms[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[u] - mn);
       acc.x += a[u].x * f; acc.y += a[u].y * f; acc.z += a[u].z * f; acc.w += a[u].w * f;
       l += ls[u] * f;   // the same for all 32 lanes of the group
     }
+    mt = mn;
   }
   accs[s0][d4] = acc;
-  if (d4 == 0) lsum[s0] = l;
+  if (d4 == 0) {
+    lsum[s0] = l;
+    msum[s0] = mt;
+  }
   __syncthreads();
   if (t < D) {
-    float a = 0.f;
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kCombGroups; ++k) M = fmaxf(M, msum[k]);   // group 0 holds split 0
+    float a = 0.f, lt = 0.f;
 #pragma unroll
     for (int k = 0; k < kCombGroups; ++k) {
+      const float f = msum[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(msum[k] - M);
       const float4 v = accs[k][t >> 2];
-      a += (t & 3) == 0 ? v.x : (t & 3) == 1 ? v.y : (t & 3) == 2 ? v.z : v.w;
+      a += ((t & 3) == 0 ? v.x : (t & 3) == 1 ? v.y : (t & 3) == 2 ? v.z : v.w) * f;
+      lt += lsum[k] * f;
     }
-    float lt = 0.f;
-#pragma unroll
-    for (int k = 0; k < kCombGroups; ++k) lt += lsum[k];
     o[t] = a / lt;
   }
   float* outp = p.out + ((int64_t)b * p.hq + qh) * D;

@@ -51,9 +51,30 @@ __device__ __forceinline__ uint32_t fp8_e4m3(float x) {
   return sign | c;
 }
 
-__device__ __forceinline__ float shfl_xor16(float v, int mask) {
-  // exchange within the 16-lane group that owns a row
-  return __shfl_xor(v, mask, 16);
+// Value held by lane (lane ^ M) of the 16-lane group that owns a row: DPP quad_perm (M = 1, 2)
+// and row_ror:8 (M = 8, a row being 16 lanes) are VALU operand modifiers, M = 4 a ds_swizzle in
+// bit-mask mode (no memory access). Pure data movement: the arithmetic is unchanged.
+template <int M>
+__device__ __forceinline__ float shfl_xor16(float v) {
+  if constexpr (M == 1 || M == 2) {
+    constexpr int kCtrl = M == 1 ? 0xB1 : 0x4E;   // quad_perm [1,0,3,2] and [2,3,0,1]
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, true));
+  } else if constexpr (M == 8) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, true));
+  } else {
+    static_assert(M == 4, "exchanges within 16 lanes");
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (M << 10)));
+  }
+}
+
+template <int M>
+__device__ __forceinline__ void fwht_cross(float (&r)[8], int lane16) {
+  const bool upper = (lane16 & M) != 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float other = shfl_xor16<M>(r[e]);
+    r[e] = upper ? (other - r[e]) : (r[e] + other);
+  }
 }
 
 template <int BITS>
@@ -113,23 +134,20 @@ __global__ __launch_bounds__(kThreads) void quantize_append_kernel(AppendParams 
     }
     // cross-lane stages h = 8, 16, 32, 64: the lane with bit (h/8) clear holds the lower
     // element of every pair and keeps a + b; its partner keeps a - b.
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-      const bool upper = (lane16 & m) != 0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float other = shfl_xor16(r[e], m);
-        r[e] = upper ? (other - r[e]) : (r[e] + other);
-      }
-    }
+    fwht_cross<1>(r, lane16);
+    fwht_cross<2>(r, lane16);
+    fwht_cross<4>(r, lane16);
+    fwht_cross<8>(r, lane16);
     float amax = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       r[e] = r[e] * kRotC;
       amax = fmaxf(amax, fabsf(r[e]));
     }
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, shfl_xor16(amax, m));
+    amax = fmaxf(amax, shfl_xor16<1>(amax));
+    amax = fmaxf(amax, shfl_xor16<2>(amax));
+    amax = fmaxf(amax, shfl_xor16<4>(amax));
+    amax = fmaxf(amax, shfl_xor16<8>(amax));
 
     const float s32 = amax / (float)qmax;
     const _Float16 s16 = (_Float16)fminf(s32, 65504.f);
