@@ -181,11 +181,12 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// Eight 3-bit fields of a 24-bit value -> eight nibbles (fields in bits 0..2 of each).
-__device__ __forceinline__ uint32_t spread3to4(uint32_t x) {
+// Eight 3-bit fields in the low 24 bits of x (bits 24..31 are ignored) -> two fields per byte:
+// field 2i in bits 0..2 and field 2i+1 in bits 3..5 of byte i. A shift by 5 (by 2) then moves
+// the even (odd) fields to the top three bits of their bytes.
+__device__ __forceinline__ uint32_t spread3to6(uint32_t x) {
   x = (x & 0xfffu) | ((x & 0xfff000u) << 4);
-  x = (x & 0x003f003fu) | ((x & 0x0fc00fc0u) << 2);
-  return (x & 0x07070707u) | ((x & 0x38383838u) << 1);
+  return (x & 0x003f003fu) | ((x & 0x0fc00fc0u) << 2);
 }
 constexpr uint32_t kBias3 = 0x924924u;   // bit 2 of every 3-bit field: c -> c + 4
 
@@ -499,9 +500,9 @@ __device__ __forceinline__ void k_operands(const Tile<DT>& t, int h, v4i& a0, v4
                              d2 >> 8};
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const uint32_t n = spread3to4(grp[w] & 0xffffffu);   // raw 3-bit fields per nibble
+      const uint32_t n = spread3to6(grp[w]);              // raw 3-bit fields, two per byte
       a0[w] = (int)((n << 5) & 0xe0e0e0e0u);               // 32 c
-      a1[w] = (int)((n << 1) & 0xe0e0e0e0u);
+      a1[w] = (int)((n << 2) & 0xe0e0e0e0u);
     }
   } else if constexpr (DT == 2) {
     // dword i holds dims 16 i .. 16 i + 15 of the lane's 32, code 4 b + w in bits 2 w of byte b;
@@ -534,10 +535,10 @@ __device__ __forceinline__ void v_bytes(const Tile<DT>& t, uint32_t (&e)[8], uin
     const uint32_t sh = (24u * col) & 31u;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t x = __builtin_amdgcn_alignbit((uint32_t)t.v[j][1], (uint32_t)t.v[j][0], sh) & 0xffffffu;
-      const uint32_t n = spread3to4(x ^ kBias3);    // c + 4 per nibble (0..7)
+      const uint32_t x = __builtin_amdgcn_alignbit((uint32_t)t.v[j][1], (uint32_t)t.v[j][0], sh);
+      const uint32_t n = spread3to6(x ^ kBias3);    // c + 4 (0..7), two fields per byte
       e[j] = (n << 5) & 0xe0e0e0e0u;                // (c + 4) << 5
-      o[j] = (n << 1) & 0xe0e0e0e0u;
+      o[j] = (n << 2) & 0xe0e0e0e0u;
     }
   } else if constexpr (DT == 8) {
 #pragma unroll
@@ -1626,7 +1627,7 @@ void decode_split_kernel(DecodeParams p) {
 // Merge split partials of one (sequence, q head) and rotate back. THREADS = 32 * groups:
 // thread (s0 = t / 32, d4 = t % 32) sums dimensions 4 d4 .. 4 d4 + 3 over splits s0,
 // s0 + groups, ..., four splits per step with their loads issued together (128 threads for a
-// few splits, 512 for many).
+// few splits, 512 for many; 1024 threads measured slower on 256 splits).
 template <int DT, int kCombThreads>
 __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodeParams p) {
   constexpr int kCombGroups = kCombThreads / 32;
