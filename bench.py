@@ -3,8 +3,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1] [--no-cpu]
 
 A step is one pass of the whole hot path for one layer of a decode batch:
-  1. xq_quantize_append of the step's new K/V row of every sequence (rotate, quantize,
-     pack, scatter into its page), plus the prefill chunk where the workload has one;
+  1. one xq_quantize_append of the step's new K/V rows (rotate, quantize, pack, scatter into
+     their pages): every sequence's new row, plus the prefill chunk where the workload has one;
   2. xq_paged_decode_attention over every sequence's paged, quantized context.
 The new row of sequence b goes to position L_b - 1, so every step has the same shape and
 the cache content stays what the oracle computes.
@@ -93,21 +93,17 @@ def committed_traffic(kernel_tag: str):
 class Step:
     """Precomputed ctypes arguments for the two calls of one step on one replica."""
 
-    def __init__(self, lib, layout, cache, app, chunk, dec):
+    def __init__(self, lib, layout, cache, app, dec):
         import ctypes
         self.lib = lib
         self.L = ctypes.byref(layout)
         self.cache = cache
-        self.app, self.chunk, self.dec = app, chunk, dec
+        self.app, self.dec = app, dec
 
     def run(self, stream: int):
         lib = self.lib
         c = self.cache
         kp, vp = c.k_pool.data_ptr(), c.v_pool.data_ptr()
-        if self.chunk is not None:
-            st = lib.xq_quantize_append(self.L, *self.chunk, kp, vp, stream)
-            if st:
-                raise RuntimeError(lib.xq_last_error().decode())
         st = lib.xq_quantize_append(self.L, *self.app, kp, vp, stream)
         if st:
             raise RuntimeError(lib.xq_last_error().decode())
@@ -299,15 +295,19 @@ def main():
            bt.data_ptr(), maxp)
     chunk = None
     if chunk_kv is not None:
-        ck, cv = to_dev(chunk_kv[0]), to_dev(chunk_kv[1])
-        cs = to_dev(np.full(W.chunk_tokens, W.batch, np.int32))
-        cp = to_dev(np.arange(W.chunk_tokens, dtype=np.int32))
+        # one append per step takes every new row: the chunk's and the decode batch's own
+        ck = to_dev(np.concatenate([chunk_kv[0], np.stack(last_k)]))
+        cv = to_dev(np.concatenate([chunk_kv[1], np.stack(last_v)]))
+        cs = to_dev(np.concatenate([np.full(W.chunk_tokens, W.batch, np.int32), np.arange(B, dtype=np.int32)]))
+        cp = to_dev(np.concatenate([np.arange(W.chunk_tokens, dtype=np.int32),
+                                    (W.context_lens - 1).astype(np.int32)]))
         keep = (ck, cv, cs, cp)
-        chunk = (ck.data_ptr(), cv.data_ptr(), W.chunk_tokens, cs.data_ptr(), cp.data_ptr(),
-                 bt.data_ptr(), maxp)
+        app = (ck.data_ptr(), cv.data_ptr(), W.chunk_tokens + B, cs.data_ptr(), cp.data_ptr(),
+               bt.data_ptr(), maxp)
+        chunk = True
     dec = (q.data_ptr(), B, hq, bt.data_ptr(), maxp, cl.data_ptr(), W.max_context_len,
            W.softmax_scale, splits, ws.data_ptr(), wsb, out.data_ptr())
-    runners = [Step(lib, c.layout, c, app, chunk, dec) for c in caches]
+    runners = [Step(lib, c.layout, c, app, dec) for c in caches]
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 

@@ -124,3 +124,26 @@ def test_append_valid_batch_passes_the_checks(monkeypatch):
     k, v = _bf16(rng, 2, HKV, 128), _bf16(rng, 2, HKV, 128)
     xq.xq_quantize_append(L, k, v, 2, seq, pos, bt, bt.shape[1], kp, vp)
     torch.cuda.synchronize()
+
+
+def test_debug_prefill_rejects_a_page_past_the_pool(monkeypatch):
+    """A prefill reads the chunk's block-table row for every position below start + n: an entry
+    naming a page at or past num_pages is rejected under XQ_DEBUG before any launch, and the same
+    call with a good row gives the unchecked result."""
+    L, kp, vp, bt, cl, q, rng = _setup(num_pages=5, alloc_pages=12)
+    qp = _bf16(rng, 10, HQ, 128)
+    out = torch.zeros(10, HQ, 128, dtype=torch.float32, device="cuda")
+    row = bt[0].clone()
+    monkeypatch.setenv("XQ_DEBUG", "0")
+    xq.xq_paged_prefill_attention(L, qp, 10, HQ, kp, vp, row, row.shape[0], 30, 0.088, 1, None, 0, out)
+    torch.cuda.synchronize()
+    ref = out.cpu().clone()
+    monkeypatch.setenv("XQ_DEBUG", "1")
+    xq.xq_paged_prefill_attention(L, qp, 10, HQ, kp, vp, row, row.shape[0], 30, 0.088, 1, None, 0, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), ref)
+    bad = row.clone()
+    bad[2] = 7                                    # page 7 >= num_pages = 5 (the pools hold 12)
+    with pytest.raises(xq.XqError) as e:
+        xq.xq_paged_prefill_attention(L, qp, 10, HQ, kp, vp, bad, bad.shape[0], 30, 0.088, 1, None, 0, out)
+    assert e.value.status == xq.EINVAL and "block_table[2]" in str(e.value)
