@@ -56,6 +56,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunk-prefill timing")
+    ap.add_argument("--no-plan", action="store_true", help="decode without the host plan")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run plain 512 MiB device copies (a known byte count for "
@@ -111,10 +112,15 @@ class Step:
     def decode(self, stream: int):
         lib = self.lib
         c = self.cache
-        q, batch, hq, bt, maxp, cl, maxctx, scale, splits, ws, wsb, out = self.dec
-        st = lib.xq_paged_decode_attention(self.L, q, batch, hq, c.k_pool.data_ptr(),
-                                           c.v_pool.data_ptr(), bt, maxp, cl, maxctx, scale,
-                                           splits, ws, wsb, out, stream)
+        q, batch, hq, bt, maxp, cl, maxctx, scale, splits, ws, wsb, out, order = self.dec
+        if order is None:
+            st = lib.xq_paged_decode_attention(self.L, q, batch, hq, c.k_pool.data_ptr(),
+                                               c.v_pool.data_ptr(), bt, maxp, cl, maxctx, scale,
+                                               splits, ws, wsb, out, stream)
+        else:
+            st = lib.xq_paged_decode_attention_planned(self.L, q, batch, hq, c.k_pool.data_ptr(),
+                                                       c.v_pool.data_ptr(), bt, maxp, cl, maxctx,
+                                                       scale, splits, ws, wsb, out, order, stream)
         if st:
             raise RuntimeError(lib.xq_last_error().decode())
 
@@ -305,8 +311,13 @@ def main():
         app = (ck.data_ptr(), cv.data_ptr(), W.chunk_tokens + B, cs.data_ptr(), cp.data_ptr(),
                bt.data_ptr(), maxp)
         chunk = True
+    # the host plan: long and short sequences share SIMDs (identity where it cannot help)
+    order = None
+    if not args.no_plan:
+        order = base.plan([int(x) for x in W.context_lens], hq, W.max_context_len, splits, device=dev)
     dec = (q.data_ptr(), B, hq, bt.data_ptr(), maxp, cl.data_ptr(), W.max_context_len,
-           W.softmax_scale, splits, ws.data_ptr(), wsb, out.data_ptr())
+           W.softmax_scale, splits, ws.data_ptr(), wsb, out.data_ptr(),
+           None if order is None else order.data_ptr())
     runners = [Step(lib, c.layout, c, app, dec) for c in caches]
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
@@ -401,6 +412,7 @@ def main():
             "batch": B, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": 128,
             "page_size": W.page_size, "context_tokens": tokens, "max_context": W.max_context_len,
             "splits": nsplits, "chunk_append_tokens": W.chunk_tokens, "pool_replicas": R,
+            "plan": order is not None and order.cpu().tolist() != list(range(B)),
         },
         "seq_tokens_per_s": round(tokens / (step_ms * 1e-3), 1),
         "decode_seqs_per_s": round(B / (step_ms * 1e-3), 1),

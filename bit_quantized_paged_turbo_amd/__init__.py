@@ -19,7 +19,8 @@ OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
 # Every symbol include/xq.h declares.
 EXPORTS = ("xq_block_bytes", "xq_page_stride_bytes", "xq_pool_bytes", "xq_decode_num_splits",
            "xq_decode_workspace_bytes", "xq_status_string", "xq_last_error",
-           "xq_quantize_append", "xq_paged_decode_attention", "xq_paged_prefill_attention")
+           "xq_quantize_append", "xq_paged_decode_attention", "xq_paged_prefill_attention",
+           "xq_decode_plan", "xq_paged_decode_attention_planned")
 
 
 class XqError(RuntimeError):
@@ -66,6 +67,9 @@ def load() -> ctypes.CDLL:
                                             P, I64, P, P]),
         "xq_paged_prefill_attention": (I32, [LP, P, I32, I32, P, P, P, I32, I32, F32, I32,
                                              P, I64, P, P]),
+        "xq_decode_plan": (I32, [LP, I32, I32, I32, I32, P, P]),
+        "xq_paged_decode_attention_planned": (I32, [LP, P, I32, I32, P, P, P, I32, P, I32, F32, I32,
+                                                    P, I64, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -149,3 +153,26 @@ def xq_paged_prefill_attention(layout: CacheLayout, q, n_query: int, num_q_heads
         ctypes.byref(layout), _ptr(q), n_query, num_q_heads, _ptr(k_pool), _ptr(v_pool),
         _ptr(block_table), max_pages, start_pos, float(softmax_scale), num_splits_hint,
         _ptr(workspace), int(workspace_bytes), _ptr(out), _stream(stream)))
+
+
+def xq_decode_plan(layout: CacheLayout, batch: int, num_q_heads: int, max_context_len: int,
+                   num_splits_hint: int, context_lens) -> "list[int]":
+    """See xq_decode_plan in include/xq.h. context_lens: host sequence of ints; returns the order."""
+    lens = (ctypes.c_int32 * max(1, batch))(*[int(x) for x in context_lens])
+    order = (ctypes.c_int32 * max(1, batch))()
+    _check(load().xq_decode_plan(ctypes.byref(layout), batch, num_q_heads, max_context_len,
+                                 num_splits_hint, ctypes.cast(lens, ctypes.c_void_p),
+                                 ctypes.cast(order, ctypes.c_void_p)))
+    return list(order)[:batch]
+
+
+def xq_paged_decode_attention_planned(layout: CacheLayout, q, batch: int, num_q_heads: int, k_pool,
+                                      v_pool, block_tables, max_pages_per_seq: int, context_lens,
+                                      max_context_len: int, softmax_scale: float, num_splits_hint: int,
+                                      workspace, workspace_bytes: int, out, seq_order, stream=None):
+    """See xq_paged_decode_attention_planned in include/xq.h. Tensors are passed by data_ptr()."""
+    _check(load().xq_paged_decode_attention_planned(
+        ctypes.byref(layout), _ptr(q), batch, num_q_heads, _ptr(k_pool), _ptr(v_pool),
+        _ptr(block_tables), max_pages_per_seq, _ptr(context_lens), max_context_len,
+        float(softmax_scale), num_splits_hint, _ptr(workspace), int(workspace_bytes), _ptr(out),
+        _ptr(seq_order), _stream(stream)))

@@ -7,8 +7,8 @@ from __future__ import annotations
 
 import torch
 
-from . import (CacheLayout, load, xq_decode_workspace_bytes, xq_paged_decode_attention,
-               xq_paged_prefill_attention,
+from . import (CacheLayout, load, xq_decode_plan, xq_decode_workspace_bytes, xq_paged_decode_attention,
+               xq_paged_decode_attention_planned, xq_paged_prefill_attention,
                xq_pool_bytes, xq_quantize_append)
 
 
@@ -40,8 +40,9 @@ class PagedKVCache:
     def decode(self, q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
                max_context_len: int, softmax_scale: float, num_splits: int = 0,
                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-               stream=None) -> torch.Tensor:
-        """q bf16 [B, Hq, 128] -> out fp32 [B, Hq, 128]."""
+               stream=None, seq_order: torch.Tensor | None = None) -> torch.Tensor:
+        """q bf16 [B, Hq, 128] -> out fp32 [B, Hq, 128]. seq_order: a device int32 [B] plan
+        (see plan()), or None."""
         batch, hq = int(q.shape[0]), int(q.shape[1])
         if out is None:
             out = torch.empty((batch, hq, 128), dtype=torch.float32, device=q.device)
@@ -51,11 +52,24 @@ class PagedKVCache:
                 self._ws = torch.empty((need,), dtype=torch.uint8, device=q.device)
             workspace = self._ws
         wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-        xq_paged_decode_attention(self.layout, q, batch, hq, self.k_pool, self.v_pool,
-                                  block_tables, int(block_tables.shape[1]), context_lens,
-                                  int(max_context_len), softmax_scale, num_splits, workspace,
-                                  wbytes, out, stream)
+        if seq_order is None:
+            xq_paged_decode_attention(self.layout, q, batch, hq, self.k_pool, self.v_pool,
+                                      block_tables, int(block_tables.shape[1]), context_lens,
+                                      int(max_context_len), softmax_scale, num_splits, workspace,
+                                      wbytes, out, stream)
+        else:
+            xq_paged_decode_attention_planned(self.layout, q, batch, hq, self.k_pool, self.v_pool,
+                                              block_tables, int(block_tables.shape[1]), context_lens,
+                                              int(max_context_len), softmax_scale, num_splits,
+                                              workspace, wbytes, out, seq_order, stream)
         return out
+
+    def plan(self, host_context_lens, num_q_heads: int, max_context_len: int, num_splits: int = 0,
+             device="cuda") -> torch.Tensor:
+        """xq_decode_plan from host lengths, as a device int32 tensor for decode(seq_order=...)."""
+        order = xq_decode_plan(self.layout, len(host_context_lens), num_q_heads, int(max_context_len),
+                               num_splits, host_context_lens)
+        return torch.tensor(order, dtype=torch.int32, device=device)
 
     def prefill(self, q: torch.Tensor, block_table: torch.Tensor, start_pos: int,
                 softmax_scale: float, num_splits: int = 0, out: torch.Tensor | None = None,

@@ -1237,6 +1237,9 @@ void decode_split_kernel(DecodeParams p) {
       split = (int)(group % (uint32_t)p.nsplits);
       b = (int)(group / (uint32_t)p.nsplits);
     }
+    // a host plan may hand this slot another sequence (long and short ones sharing a SIMD)
+    // (clamped: an entry outside the batch, outside the contract, still indexes the batch's arrays)
+    if (p.seq_order) b = min(max(p.seq_order[b], 0), p.batch - 1);
   }
   const int lane = threadIdx.x;
   // Columns of the unit's MFMA tiles: c = t Gq + h is head h (of the kv head's Gq) of row

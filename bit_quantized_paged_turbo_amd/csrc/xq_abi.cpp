@@ -11,6 +11,7 @@
 #include <cstring>
 #include <string>
 #include <unordered_set>
+#include <algorithm>
 #include <vector>
 
 #include "xq_internal.h"
@@ -82,6 +83,19 @@ xq_status debug_check_decode(const xq_cache_layout* L, int32_t batch, const int3
         return fail(XQ_EINVAL, "XQ_DEBUG: block_tables[%d][%d] = %d is not a page id below num_pages = %lld", b,
                     i, pg, (long long)L->num_pages);
     }
+  }
+  return XQ_OK;
+}
+
+// planned decode: seq_order is a permutation of 0 .. batch - 1.
+xq_status debug_check_order(int32_t batch, const int32_t* seq_order, hipStream_t s) {
+  std::vector<int32_t> o;
+  if (xq_status st = fetch(o, seq_order, batch, s)) return st;
+  std::vector<char> seen((size_t)batch, 0);
+  for (int32_t i = 0; i < batch; ++i) {
+    if (o[i] < 0 || o[i] >= batch || seen[(size_t)o[i]])
+      return fail(XQ_EINVAL, "XQ_DEBUG: seq_order[%d] = %d: not a permutation of the batch", i, o[i]);
+    seen[(size_t)o[i]] = 1;
   }
   return XQ_OK;
 }
@@ -182,7 +196,7 @@ xq_status attention(const xq_cache_layout* layout, const void* q, int32_t batch,
                     const void* k_pool, const void* v_pool, const int32_t* block_tables, int32_t bt_stride,
                     int32_t max_pages_per_seq, const int32_t* context_lens, int32_t ctx_base,
                     int32_t max_context_len, float softmax_scale, int32_t num_splits_hint, void* workspace,
-                    int64_t workspace_bytes, float* out, hipStream_t stream) {
+                    int64_t workspace_bytes, float* out, hipStream_t stream, const int32_t* seq_order = nullptr) {
   if (batch > 65535) return fail(XQ_EUNSUPPORTED, "batch %d > 65535", batch);
   if (num_q_heads < 1 || num_q_heads % layout->num_kv_heads != 0)
     return fail(XQ_EINVAL, "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads,
@@ -224,6 +238,7 @@ xq_status attention(const xq_cache_layout* layout, const void* q, int32_t batch,
     xq_status st = ctx_base > 0 ? debug_check_prefill(layout, block_tables, max_context_len, stream)
                                 : debug_check_decode(layout, batch, block_tables, max_pages_per_seq, context_lens,
                                                      max_context_len, stream);
+    if (!st && seq_order) st = debug_check_order(batch, seq_order, stream);
     if (st) return st;
   }
 
@@ -253,6 +268,7 @@ xq_status attention(const xq_cache_layout* layout, const void* q, int32_t batch,
   p.bt_stride = bt_stride;
   p.ctx_base = ctx_base;
   p.qt = qt;
+  p.seq_order = seq_order;
   const hipError_t e = xq::launch_decode(layout->kv_dtype, p, stream);
   if (e != hipSuccess) return fail(XQ_EHIP, "attention launch: %s", hipGetErrorString(e));
   return XQ_OK;
@@ -358,6 +374,68 @@ xq_status xq_paged_decode_attention(const xq_cache_layout* layout, const void* q
   return attention(layout, q, batch, num_q_heads, k_pool, v_pool, block_tables, max_pages_per_seq,
                    max_pages_per_seq, context_lens, 0, max_context_len, softmax_scale, num_splits_hint,
                    workspace, workspace_bytes, out, static_cast<hipStream_t>(stream));
+}
+
+xq_status xq_paged_decode_attention_planned(const xq_cache_layout* layout, const void* q, int32_t batch,
+                                            int32_t num_q_heads, const void* k_pool, const void* v_pool,
+                                            const int32_t* block_tables, int32_t max_pages_per_seq,
+                                            const int32_t* context_lens, int32_t max_context_len,
+                                            float softmax_scale, int32_t num_splits_hint, void* workspace,
+                                            int64_t workspace_bytes, float* out, const int32_t* seq_order,
+                                            void* stream) {
+  if (xq_status st = check_layout(layout)) return st;
+  if (batch < 0) return fail(XQ_EINVAL, "batch %d < 0", batch);
+  if (batch == 0) return XQ_OK;
+  if (!context_lens || !seq_order) return fail(XQ_EINVAL, "a required pointer is NULL");
+  if (max_context_len < 0) return fail(XQ_EINVAL, "max_context_len %d < 0", max_context_len);
+  return attention(layout, q, batch, num_q_heads, k_pool, v_pool, block_tables, max_pages_per_seq,
+                   max_pages_per_seq, context_lens, 0, max_context_len, softmax_scale, num_splits_hint,
+                   workspace, workspace_bytes, out, static_cast<hipStream_t>(stream), seq_order);
+}
+
+xq_status xq_decode_plan(const xq_cache_layout* layout, int32_t batch, int32_t num_q_heads,
+                         int32_t max_context_len, int32_t num_splits_hint, const int32_t* host_context_lens,
+                         int32_t* host_seq_order) {
+  if (xq_status st = check_layout(layout)) return st;
+  if (batch < 0 || num_q_heads < 1 || max_context_len < 0) return fail(XQ_EINVAL, "invalid batch, heads or length");
+  if (batch > 0 && (!host_context_lens || !host_seq_order)) return fail(XQ_EINVAL, "a required pointer is NULL");
+  if (num_splits_hint < 0 && !fixed_split_ok(layout, num_splits_hint))
+    return fail(XQ_EINVAL, "num_splits_hint %d is not a valid fixed partition", num_splits_hint);
+  for (int32_t b = 0; b < batch; ++b) host_seq_order[b] = b;
+  if (batch == 0) return XQ_OK;
+  const int32_t ctx = max_context_len > 0 ? max_context_len : 1;
+  const int32_t nsplits = (ctx + plan_tokens_per_split(layout, batch, ctx, num_splits_hint) - 1) /
+                          plan_tokens_per_split(layout, batch, ctx, num_splits_hint);
+  // Waves fill the SIMDs round-robin: with every unit resident, workgroups i, i + S, i + 2S, ...
+  // (S = SIMDs of the device) share a SIMD. With one partition per sequence and a batch that is a
+  // multiple of 8, the decode's unit order puts sequence slots b, b + S / Hkv, b + 2 S / Hkv, ...
+  // on the same SIMDs (all their kv heads). Sorted by length, sequences are dealt to those slot
+  // groups in snake order, so a SIMD's units add up to about the same number of tiles.
+  const int64_t hkv = layout->num_kv_heads;
+  int simds = 1024;   // MI355X: 256 compute units x 4 SIMDs, if the device cannot be asked
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+    simds = 4 * cus;
+  else
+    (void)hipGetLastError();
+  if (nsplits != 1 || batch % 8 != 0 || simds % (8 * hkv) != 0) return XQ_OK;
+  const int64_t period = simds / hkv;   // slots b and b + period share SIMDs
+  if (period >= batch) return XQ_OK;
+  std::vector<int32_t> idx((size_t)batch);
+  for (int32_t b = 0; b < batch; ++b) idx[(size_t)b] = b;
+  std::stable_sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) {
+    return host_context_lens[a] > host_context_lens[b];
+  });
+  size_t next = 0;
+  for (int64_t k = 0; next < idx.size(); ++k) {       // pass k fills member k of every group
+    for (int64_t j = 0; j < period && next < idx.size(); ++j) {
+      const int64_t group = (k & 1) ? period - 1 - j : j;
+      const int64_t slot = group + k * period;
+      if (slot < batch) host_seq_order[slot] = idx[next++];
+    }
+  }
+  return XQ_OK;
 }
 
 xq_status xq_paged_prefill_attention(const xq_cache_layout* layout, const void* q, int32_t n_query,

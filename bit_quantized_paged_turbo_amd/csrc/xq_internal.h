@@ -79,6 +79,8 @@ struct DecodeParams {
   int32_t ctx_base;             // 0: row b attends to context_lens[b] tokens; > 0: to
                                 // ctx_base + b tokens (query b of a prefill chunk)
   int32_t qt;                   // rows per work unit: 1 (decode) or 16 / group (prefill)
+  const int32_t* seq_order;     // null, or a permutation of the batch from xq_decode_plan: the
+                                // slot of sequence b in the unit order runs sequence seq_order[b]
 };
 
 hipError_t launch_quantize_append(int dtype, const AppendParams& p, hipStream_t stream);

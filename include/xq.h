@@ -194,6 +194,42 @@ xq_status xq_paged_decode_attention(const xq_cache_layout* layout,
                                     float* out, void* stream);
 
 /*
+ * Optional host-side plan for a decode (the split into a host "plan" and a device "run" of
+ * batched-attention libraries): from the host's copy of the context lengths, a permutation of the
+ * batch that puts long and short sequences on the same SIMDs, so that the SIMDs finish together.
+ * With every work unit resident, the GPU fills its SIMDs round-robin by workgroup id, and with one
+ * partition per sequence the decode's unit order puts sequence slots b, b + S / num_kv_heads, ...
+ * (S SIMDs) on the same SIMDs; sequences sorted by length are dealt to those slot groups in snake
+ * order. Where the plan cannot help (several partitions, a batch that is not a multiple of 8) it
+ * returns the identity. The order changes where a sequence runs, never what it computes: outputs
+ * are bitwise those of xq_paged_decode_attention.
+ *
+ *   host_context_lens  int32 [batch], host memory: the lengths the decode will see
+ *   host_seq_order     int32 [batch], host memory, written: slot b runs sequence host_seq_order[b]
+ * Other arguments as for xq_decode_num_splits. The device is queried for its SIMD count (1024,
+ * MI355X's, if that fails). Nothing is launched; XQ_EINVAL on invalid arguments.
+ */
+xq_status xq_decode_plan(const xq_cache_layout* layout, int32_t batch, int32_t num_q_heads,
+                         int32_t max_context_len, int32_t num_splits_hint,
+                         const int32_t* host_context_lens, int32_t* host_seq_order);
+
+/*
+ * xq_paged_decode_attention with a plan: seq_order is device int32 [batch], a permutation of
+ * 0 .. batch-1 (the plan's host_seq_order, copied to the device by the caller); the result is
+ * bitwise that of xq_paged_decode_attention with the same arguments. A seq_order that is not a
+ * permutation is outside the contract (rejected under XQ_DEBUG; otherwise some sequences are
+ * computed twice and others not at all).
+ */
+xq_status xq_paged_decode_attention_planned(const xq_cache_layout* layout,
+                                            const void* q, int32_t batch, int32_t num_q_heads,
+                                            const void* k_pool, const void* v_pool,
+                                            const int32_t* block_tables, int32_t max_pages_per_seq,
+                                            const int32_t* context_lens, int32_t max_context_len,
+                                            float softmax_scale, int32_t num_splits_hint,
+                                            void* workspace, int64_t workspace_bytes,
+                                            float* out, const int32_t* seq_order, void* stream);
+
+/*
  * Chunked prefill attention over the paged (and, for turbo types, quantized) cache: the queries
  * of one chunk of one sequence, each attending causally to the sequence's cached rows. Defined
  * by the infero page, section "Beyond plain text decode", item "Continuous batching" (decodes

@@ -147,3 +147,25 @@ def test_prefill_argument_errors(lib):
     assert _prefill_status(lib, L, n=70000, maxp=5000, start=0) == xq.EUNSUPPORTED
     assert _prefill_status(lib, L, start=40, splits=2) == xq.EWORKSPACE  # 48 positions, 2 partitions
     assert _prefill_status(lib, L, scale=float("nan")) == xq.EINVAL
+
+
+def test_decode_plan_pairs_long_with_short(lib):
+    """The host plan (no launch): a permutation of the batch; with one partition per sequence the
+    slots b and b + 1024 / Hkv (which share SIMDs) get lengths that add up evenly; otherwise the
+    identity."""
+    import numpy as np
+    L = xq.CacheLayout(4, 8, 16, 10000)
+    lens = list(np.random.default_rng(1).integers(64, 1025, 256))
+    order = xq.xq_decode_plan(L, 256, 16, max(lens), 0, lens)
+    assert sorted(order) == list(range(256))
+    period = 1024 // 8
+    planned = [lens[order[b]] + lens[order[b + period]] for b in range(period)]
+    plain = [lens[b] + lens[b + period] for b in range(period)]
+    assert max(planned) - min(planned) < (max(plain) - min(plain)) / 4
+    # the k-th longest shares its SIMDs with the k-th shortest
+    srt = sorted(lens, reverse=True)
+    assert lens[order[0]] == srt[0] and lens[order[period]] == srt[-1]
+    # several partitions, or a batch that is not a multiple of 8: the identity
+    assert xq.xq_decode_plan(L, 256, 16, max(lens), 4, lens) == list(range(256))
+    assert xq.xq_decode_plan(L, 255, 16, max(lens), 0, lens[:255]) == list(range(255))
+    assert xq.xq_decode_plan(L, 0, 16, 0, 0, []) == []

@@ -147,3 +147,19 @@ def test_debug_prefill_rejects_a_page_past_the_pool(monkeypatch):
     with pytest.raises(xq.XqError) as e:
         xq.xq_paged_prefill_attention(L, qp, 10, HQ, kp, vp, bad, bad.shape[0], 30, 0.088, 1, None, 0, out)
     assert e.value.status == xq.EINVAL and "block_table[2]" in str(e.value)
+
+
+def test_debug_planned_decode_rejects_a_non_permutation(monkeypatch):
+    L, kp, vp, bt, cl, q, _ = _setup()
+    out = torch.zeros(2, HQ, 128, dtype=torch.float32, device="cuda")
+    good = torch.tensor([1, 0], dtype=torch.int32, device="cuda")
+    bad = torch.tensor([1, 1], dtype=torch.int32, device="cuda")
+    monkeypatch.setenv("XQ_DEBUG", "1")
+    xq.xq_paged_decode_attention_planned(L, q, 2, HQ, kp, vp, bt, bt.shape[1], cl, 64, 0.088, 1, None, 0,
+                                         out, good)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), _decode(L, kp, vp, bt, cl, q))
+    with pytest.raises(xq.XqError) as e:
+        xq.xq_paged_decode_attention_planned(L, q, 2, HQ, kp, vp, bt, bt.shape[1], cl, 64, 0.088, 1, None, 0,
+                                             out, bad)
+    assert e.value.status == xq.EINVAL and "seq_order" in str(e.value)

@@ -399,3 +399,29 @@ def test_shared_prefix_pages():
     qb[1] = qb[0]
     got = _decode(W, cache, bt, cl, 0, to_dev(qb))
     assert np.array_equal(got[0], got[1])
+
+
+@pytest.mark.parametrize("dtype", [4, 8, 3, 0, 16])
+def test_planned_decode_is_bitwise_the_plain_decode(dtype):
+    """xq_decode_plan only changes which wave runs which sequence: the planned decode equals the
+    plain one bit for bit (and the oracle within the bar), on a batch large enough for the plan
+    to move sequences."""
+    _print_case("planned", dtype)
+    W = workloads.config(1, dtype=dtype, context_scale=0.25)
+    cache = make_cache(W)
+    bt, cl = upload_tables(W)
+    kv = {b: W.kv_bits(b) for b in range(W.batch)}
+    fill(cache, W, bt, kv=kv)
+    qb = W.q_bits()
+    q = to_dev(qb)
+    order = cache.plan([int(x) for x in W.context_lens], W.num_q_heads, W.max_context_len, 0)
+    assert sorted(order.cpu().tolist()) == list(range(W.batch))
+    assert order.cpu().tolist() != list(range(W.batch))
+    plain = cache.decode(q, bt[: W.batch], cl, W.max_context_len, W.softmax_scale, 0)
+    planned = cache.decode(q, bt[: W.batch], cl, W.max_context_len, W.softmax_scale, 0, seq_order=order)
+    torch.cuda.synchronize()
+    assert torch.equal(plain, planned)
+    got = planned.cpu().numpy().astype(np.float64)
+    for b in (0, 37, 128, 255):
+        want = _oracle_out(W, b, qb, kv[b])
+        assert np.max(np.abs(got[b] - want)) <= TOL
