@@ -124,8 +124,10 @@ template <> struct Stage<3> {
   static constexpr bool kOn = true;
   static constexpr int kHalf = 1024, kDma = 1, kOps = 4 * kDma + 2, kSlot = 4 * kHalf + 128;
 };
-// Layouts that pair (or quad) token blocks in the QK tile; the others use the one-block layout.
-template <int DT> constexpr bool kPairOk = DT == 4 || DT == 8;
+// Layouts that pair (turbo4, turbo8, turbo3) or quad (turbo4, turbo8) token blocks in the QK
+// tile; the other types use the one-block layout.
+template <int DT> constexpr bool kPairOk = DT == 4 || DT == 8 || DT == 3;
+template <int DT> constexpr bool kQuadOk = DT == 4 || DT == 8;
 constexpr int kLdsPerCu = 160 * 1024;
 // LDS for the wave's query preparation: kMaxGroup rows of 256 B, then their fp32 scales
 constexpr int kQueryLds = kMaxGroup * 256 + kMaxGroup * 4;
@@ -777,6 +779,11 @@ template <> struct PairTile<8> {
   v2i v[8];
   v2i ks, vs;
 };
+template <> struct PairTile<3> {
+  v2i k[4];            // the 48 bits (16 codes) of the lane's 16 dims per MFMA, from bit 0
+  v2i v[8];            // V as in Tile<3>
+  v2i ks, vs;
+};
 
 // Lane roles of the paired layout.
 struct PairLane {
@@ -800,7 +807,17 @@ __device__ __forceinline__ void read_slot_pair(PairTile<DT>& t, const uint8_t* s
   t.ks = *reinterpret_cast<const v2i*>(slot + 4 * S::kHalf + 32 * pl.jn + 8 * gg);
   t.vs = *reinterpret_cast<const v2i*>(slot + 4 * S::kHalf + 64 + 32 * pl.jn + 8 * gg);
   const uint8_t* kh = slot + pl.kb * S::kHalf;
-  if constexpr (DT == 4) {
+  if constexpr (DT == 3) {
+    // rows as stored (48 B): dims 32 m + 16 kp .. + 15 are bits 96 m + 48 kp .. + 47 of the row,
+    // i.e. bytes 12 m + 6 kp .. + 5: two aligned dwords from byte 12 m + 4 kp, shifted by 16 kp
+    const int* kr = reinterpret_cast<const int*>(kh + 48 * tk);
+    const uint32_t sh = 16u * (uint32_t)pl.kp;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t d0 = (uint32_t)kr[3 * m + pl.kp], d1 = (uint32_t)kr[3 * m + pl.kp + 1];
+      t.k[m] = v2i{(int)__builtin_amdgcn_alignbit(d1, d0, sh), (int)(d1 >> sh)};
+    }
+  } else if constexpr (DT == 4) {
     // half layout: row t, 16-byte chunk c (32 dims) at 16 (t + 16 c)
 #pragma unroll
     for (int m = 0; m < 4; ++m) t.k[m] = *reinterpret_cast<const v2i*>(kh + 16 * (tk + 16 * m) + 8 * pl.kp);
@@ -813,10 +830,15 @@ __device__ __forceinline__ void read_slot_pair(PairTile<DT>& t, const uint8_t* s
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      if constexpr (DT == 4)
+      if constexpr (DT == 3) {
+        const int* vr = reinterpret_cast<const int*>(slot + (2 + h) * S::kHalf + 48 * (4 * gg + r) +
+                                                     4 * ((3 * tk) >> 2));
+        t.v[4 * h + r] = v2i{vr[0], vr[1]};
+      } else if constexpr (DT == 4) {
         t.v[4 * h + r] = *reinterpret_cast<const int*>(slot + (2 + h) * S::kHalf + 256 * r + 4 * lane);
-      else
+      } else {
         t.v[4 * h + r] = *reinterpret_cast<const v2i*>(slot + (2 + h) * S::kHalf + 512 * r + 8 * lane);
+      }
     }
   }
 }
@@ -825,7 +847,13 @@ __device__ __forceinline__ void read_slot_pair(PairTile<DT>& t, const uint8_t* s
 // 8 (w >> 1) + 2 b + (w & 1) (turbo4) or 4 w + b (turbo8) of the lane's 16.
 template <int DT>
 __device__ __forceinline__ v4i pair_k_operand(const PairTile<DT>& t, int m) {
-  if constexpr (DT == 4) {
+  if constexpr (DT == 3) {
+    // dims 0..7 and 8..15 of the lane's 16: bits 0..23 and 24..47; 32 c in the top of each byte
+    const uint32_t y0 = spread3to6((uint32_t)t.k[m][0]);
+    const uint32_t y1 = spread3to6(__builtin_amdgcn_alignbit((uint32_t)t.k[m][1], (uint32_t)t.k[m][0], 24));
+    return v4i{(int)((y0 << 5) & 0xe0e0e0e0u), (int)((y0 << 2) & 0xe0e0e0e0u), (int)((y1 << 5) & 0xe0e0e0e0u),
+               (int)((y1 << 2) & 0xe0e0e0e0u)};
+  } else if constexpr (DT == 4) {
     const uint32_t x0 = (uint32_t)t.k[m][0], x1 = (uint32_t)t.k[m][1];
     return v4i{(int)((x0 << 4) & 0xf0f0f0f0u), (int)(x0 & 0xf0f0f0f0u), (int)((x1 << 4) & 0xf0f0f0f0u),
                (int)(x1 & 0xf0f0f0f0u)};
@@ -917,7 +945,16 @@ __device__ __forceinline__ void process_pair_tile(const PairTile<DT>& t, WaveSta
   st.accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, Bb, st.accb, 0, 0, 0);
   st.accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, Bb, st.accb, 0, 0, 0);
   uint32_t e[8], o[8];
-  if constexpr (DT == 4) {
+  if constexpr (DT == 3) {
+    const uint32_t sh = (24u * (uint32_t)(lane & 15)) & 31u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t x = __builtin_amdgcn_alignbit((uint32_t)t.v[j][1], (uint32_t)t.v[j][0], sh);
+      const uint32_t n = spread3to6(x ^ kBias3);    // c + 4 (0..7), two fields per byte
+      e[j] = (n << 5) & 0xe0e0e0e0u;                // (c + 4) << 5
+      o[j] = (n << 2) & 0xe0e0e0e0u;
+    }
+  } else if constexpr (DT == 4) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t x = (uint32_t)t.v[j];
@@ -1285,7 +1322,7 @@ void decode_split_kernel(DecodeParams p) {
   // rows arrive by LDS DMA ahead of the first tiles, so the work overlaps their latency
   // (paired and quad layouts: decode only, all columns sharing one row)
   const bool pair = kPairOk<DT> && G <= kPairMaxGroup && p.qt == 1;
-  const bool quad = pair && DEPTH >= 4 && G <= 4;   // the quad-block layout (pair too)
+  const bool quad = kQuadOk<DT> && pair && DEPTH >= 4 && G <= 4;   // the quad-block layout (pair too)
   const PairLane pl = pair_lane(lane, G);
   const QuadLane ql = quad_lane(lane, G);
   v4i qi[2][2] = {};
@@ -1456,7 +1493,7 @@ void decode_split_kernel(DecodeParams p) {
       if (DEPTH - 1 < ntiles) stage(DEPTH - 1, DEPTH - 1);
       // While tiles it .. it + DEPTH - 1 all exist, the number of tiles staged after the ones a
       // step reads is fixed and the wait takes a constant; only the last steps count down.
-      if constexpr (kPairOk<DT> && decltype(kPair)::value && DEPTH >= 4) {
+      if constexpr (kQuadOk<DT> && decltype(kPair)::value && DEPTH >= 4) {
         if (quad) {
           // two tiles per step, in slots cur and next_slot(cur)
           int cur = 0;
