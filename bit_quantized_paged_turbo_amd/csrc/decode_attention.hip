@@ -45,23 +45,26 @@
 // fp16 exponent field of the value scale, so every fp16 weight P' stays below 2^15 whatever
 // the scales are, while the normaliser sum(p) is kept in fp32.
 //
-// Work split: one wave per (split, kv head, sequence), walking the split's 32-token tiles in
-// order with one softmax state; a tile is two 16-token halves (two pages at page size 16).
-// Scores come out of the QK MFMA exactly where the PV MFMA wants its weights (lane l = 16 g + c:
-// head c, tokens 4 g + r), so no data moves between the two products. Code bytes are read with
-// buffer loads against a per-page resource descriptor (scalar base and bound from a scalar
-// block-table lookup, constant lane offsets, a read past the page block returns zero). For
-// turbo4 and turbo8 the loads go straight to LDS (a ring of DEPTH tile slots per wave, DEPTH
-// picked at launch from how many waves share a compute unit), with lane offsets that leave
-// every operand read linear in the lane index and V transposed; turbo3 and bf16 load into
-// registers, three tiles (two for bf16) in flight.
+// Work split: one wave per (split, kv head, row block), walking the split's 32-token tiles in
+// order with one softmax state; a tile is two 16-token halves (two pages at page size 16). A
+// decode row block is one sequence; a chunked prefill packs 16 / g query tokens of the chunk
+// into the 16 columns (one causal limit per column). Scores come out of the QK MFMA exactly
+// where the PV MFMA wants its weights (lane l = 16 g + c: head c, tokens 4 g + r), so no data
+// moves between the two products. Code bytes are read with buffer loads against a resource
+// descriptor (the pool's, or the page block's for pools past 4 GiB; a read past it returns zero)
+// and a block-table window held in registers. For turbo4, turbo8 and turbo3 the loads go
+// straight to LDS (a ring of DEPTH tile slots per wave, DEPTH picked at launch from how many
+// waves share a compute unit): turbo4/turbo8 with lane offsets that leave every operand read
+// linear in the lane index and V transposed, turbo3 as the rows are stored. turbo2, bf16 and
+// fp8 load into registers, three tiles (two for bf16) in flight.
 //
 // Each wave prepares the query digits of its kv head's query heads itself (rotation by an
 // in-register FWHT, scaling, digit split, packing in the operand layout), from rows fetched by
 // LDS DMA ahead of its first tiles.
-// A sequence that fits one split is normalised, rotated back and stored by its wave; otherwise
+// A row that fits one split is normalised, rotated back and stored by its wave; otherwise
 // (m, l, acc) partials go to the workspace and decode_combine_kernel merges them by
-// log-sum-exp, rotates back and stores.
+// log-sum-exp, rotates back and stores. An optional host plan (seq_order) only changes which
+// slot of the unit order runs which sequence.
 #include "xq_internal.h"
 
 #include <algorithm>
@@ -1010,7 +1013,7 @@ __device__ __forceinline__ QuadLane quad_lane(int lane, int G) {
 template <int DT> struct QuadK;
 template <> struct QuadK<4> { v4i k[4]; };   // the lane's token row: 16 B per 32 dims
 template <> struct QuadK<8> { v4i k[8]; };   // 16 B per 16 dims
-template <> struct QuadK<3> { v4i k[1]; };   // never used: turbo3 has no quad layout (kPairOk)
+template <> struct QuadK<3> { v4i k[1]; };   // never used: turbo3 has no quad layout (kQuadOk)
 
 template <int DT>
 __device__ __forceinline__ void read_quad_k(QuadK<DT>& t, const uint8_t* slot0, const uint8_t* slot1, int lane) {

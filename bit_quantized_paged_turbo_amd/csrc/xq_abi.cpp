@@ -404,8 +404,8 @@ xq_status xq_decode_plan(const xq_cache_layout* layout, int32_t batch, int32_t n
   for (int32_t b = 0; b < batch; ++b) host_seq_order[b] = b;
   if (batch == 0) return XQ_OK;
   const int32_t ctx = max_context_len > 0 ? max_context_len : 1;
-  const int32_t nsplits = (ctx + plan_tokens_per_split(layout, batch, ctx, num_splits_hint) - 1) /
-                          plan_tokens_per_split(layout, batch, ctx, num_splits_hint);
+  const int32_t tps = plan_tokens_per_split(layout, batch, ctx, num_splits_hint);
+  const int32_t nsplits = (ctx + tps - 1) / tps;
   // Waves fill the SIMDs round-robin: with every unit resident, workgroups i, i + S, i + 2S, ...
   // (S = SIMDs of the device) share a SIMD. With one partition per sequence and a batch that is a
   // multiple of 8, the decode's unit order puts sequence slots b, b + S / Hkv, b + 2 S / Hkv, ...
