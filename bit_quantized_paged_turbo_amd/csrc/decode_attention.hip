@@ -1770,7 +1770,11 @@ int pick_depth(const DecodeParams& p) {
     const int64_t slots = kLdsPerCu / (per_cu * Stage<DT>::kSlot);
     const int64_t cap = kMaxVmcnt / Stage<DT>::kOps + 1;
     const int64_t d = std::min<int64_t>(slots, cap);
-    if (per_cu <= 8 && d >= 4) return d >= 8 ? 8 : d >= 6 ? 6 : 4;   // two waves per SIMD at most
+    // Deep rings cost occupancy (two waves per SIMD at most). They pay where they enable the quad
+    // layout (turbo4, turbo8) with up to two waves per SIMD, and otherwise only for a single wave
+    // per SIMD: on c3's shape turbo3 at two units per SIMD runs 76.6 us with three slots against
+    // 78.1 with four.
+    if (per_cu <= (kQuadOk<DT> ? 8 : 4) && d >= 4) return d >= 8 ? 8 : d >= 6 ? 6 : 4;
     return d >= 3 ? 3 : 2;
   }
 }
