@@ -3,9 +3,12 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1] [--no-cpu]
 
 A step is one pass of the whole hot path for one layer of a decode batch:
-  1. one xq_quantize_append of the step's new K/V rows (rotate, quantize, pack, scatter into
-     their pages): every sequence's new row, plus the prefill chunk where the workload has one;
-  2. xq_paged_decode_attention over every sequence's paged, quantized context.
+  1. the new K/V rows are rotated, quantized, packed and stored in their pages: every
+     sequence's new row, plus the prefill chunk where the workload has one;
+  2. decode attention over every sequence's paged, quantized context.
+By default xq_quantize_append and the decode are two launches; with --fuse one
+xq_append_decode_attention launch does both for the decode batch (a chunk still goes through
+xq_quantize_append first). The decode uses the host plan (xq_decode_plan) unless --no-plan.
 The new row of sequence b goes to position L_b - 1, so every step has the same shape and
 the cache content stays what the oracle computes.
 
@@ -57,6 +60,8 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunk-prefill timing")
     ap.add_argument("--no-plan", action="store_true", help="decode without the host plan")
+    ap.add_argument("--fuse", action="store_true",
+                    help="append the batch's new rows inside the decode launch (xq_append_decode_attention)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run plain 512 MiB device copies (a known byte count for "
@@ -102,6 +107,8 @@ class Step:
         self.app, self.dec = app, dec
 
     def run(self, stream: int):
+        if self.app is None:            # the fused step appends inside the decode launch
+            return
         lib = self.lib
         c = self.cache
         kp, vp = c.k_pool.data_ptr(), c.v_pool.data_ptr()
@@ -112,8 +119,12 @@ class Step:
     def decode(self, stream: int):
         lib = self.lib
         c = self.cache
-        q, batch, hq, bt, maxp, cl, maxctx, scale, splits, ws, wsb, out, order = self.dec
-        if order is None:
+        q, batch, hq, bt, maxp, cl, maxctx, scale, splits, ws, wsb, out, order, fused = self.dec
+        if fused is not None:
+            st = lib.xq_append_decode_attention(self.L, fused[0], fused[1], q, batch, hq, c.k_pool.data_ptr(),
+                                                c.v_pool.data_ptr(), bt, maxp, cl, maxctx, scale, splits,
+                                                ws, wsb, out, order, stream)
+        elif order is None:
             st = lib.xq_paged_decode_attention(self.L, q, batch, hq, c.k_pool.data_ptr(),
                                                c.v_pool.data_ptr(), bt, maxp, cl, maxctx, scale,
                                                splits, ws, wsb, out, stream)
@@ -300,24 +311,30 @@ def main():
     app = (new_k.data_ptr(), new_v.data_ptr(), B, new_seq.data_ptr(), new_pos.data_ptr(),
            bt.data_ptr(), maxp)
     chunk = None
+    fuse = args.fuse
     if chunk_kv is not None:
-        # one append per step takes every new row: the chunk's and the decode batch's own
-        ck = to_dev(np.concatenate([chunk_kv[0], np.stack(last_k)]))
-        cv = to_dev(np.concatenate([chunk_kv[1], np.stack(last_v)]))
-        cs = to_dev(np.concatenate([np.full(W.chunk_tokens, W.batch, np.int32), np.arange(B, dtype=np.int32)]))
+        # one append per step takes every new row that the decode launch does not: the chunk's, and
+        # without the fused step the decode batch's own too
+        nb = 0 if fuse else B
+        ck = to_dev(np.concatenate([chunk_kv[0]] + ([] if fuse else [np.stack(last_k)])))
+        cv = to_dev(np.concatenate([chunk_kv[1]] + ([] if fuse else [np.stack(last_v)])))
+        cs = to_dev(np.concatenate([np.full(W.chunk_tokens, W.batch, np.int32), np.arange(nb, dtype=np.int32)]))
         cp = to_dev(np.concatenate([np.arange(W.chunk_tokens, dtype=np.int32),
-                                    (W.context_lens - 1).astype(np.int32)]))
+                                    (W.context_lens[:nb] - 1).astype(np.int32)]))
         keep = (ck, cv, cs, cp)
-        app = (ck.data_ptr(), cv.data_ptr(), W.chunk_tokens + B, cs.data_ptr(), cp.data_ptr(),
+        app = (ck.data_ptr(), cv.data_ptr(), W.chunk_tokens + nb, cs.data_ptr(), cp.data_ptr(),
                bt.data_ptr(), maxp)
         chunk = True
+    elif fuse:
+        app = None
     # the host plan: long and short sequences share SIMDs (identity where it cannot help)
     order = None
     if not args.no_plan:
         order = base.plan([int(x) for x in W.context_lens], hq, W.max_context_len, splits, device=dev)
     dec = (q.data_ptr(), B, hq, bt.data_ptr(), maxp, cl.data_ptr(), W.max_context_len,
            W.softmax_scale, splits, ws.data_ptr(), wsb, out.data_ptr(),
-           None if order is None else order.data_ptr())
+           None if order is None else order.data_ptr(),
+           (new_k.data_ptr(), new_v.data_ptr()) if fuse else None)
     runners = [Step(lib, c.layout, c, app, dec) for c in caches]
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
@@ -413,6 +430,7 @@ def main():
             "page_size": W.page_size, "context_tokens": tokens, "max_context": W.max_context_len,
             "splits": nsplits, "chunk_append_tokens": W.chunk_tokens, "pool_replicas": R,
             "plan": order is not None and order.cpu().tolist() != list(range(B)),
+            "fused_append": fuse,
         },
         "seq_tokens_per_s": round(tokens / (step_ms * 1e-3), 1),
         "decode_seqs_per_s": round(B / (step_ms * 1e-3), 1),
@@ -424,7 +442,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "xq_paged_decode_attention call (decode_split_kernel"
+                     "kernel": ("xq_append_decode_attention" if fuse else "xq_paged_decode_attention")
+                               + " call (decode_split_kernel"
                                + (" + decode_combine_kernel)" if nsplits > 1 else ")"),
                      "bytes_per_launch": kv_bytes},
     }

@@ -20,7 +20,7 @@ OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
 EXPORTS = ("xq_block_bytes", "xq_page_stride_bytes", "xq_pool_bytes", "xq_decode_num_splits",
            "xq_decode_workspace_bytes", "xq_status_string", "xq_last_error",
            "xq_quantize_append", "xq_paged_decode_attention", "xq_paged_prefill_attention",
-           "xq_decode_plan", "xq_paged_decode_attention_planned")
+           "xq_decode_plan", "xq_paged_decode_attention_planned", "xq_append_decode_attention")
 
 
 class XqError(RuntimeError):
@@ -68,6 +68,8 @@ def load() -> ctypes.CDLL:
         "xq_paged_prefill_attention": (I32, [LP, P, I32, I32, P, P, P, I32, I32, F32, I32,
                                              P, I64, P, P]),
         "xq_decode_plan": (I32, [LP, I32, I32, I32, I32, P, P]),
+        "xq_append_decode_attention": (I32, [LP, P, P, P, I32, I32, P, P, P, I32, P, I32, F32, I32,
+                                             P, I64, P, P, P]),
         "xq_paged_decode_attention_planned": (I32, [LP, P, I32, I32, P, P, P, I32, P, I32, F32, I32,
                                                     P, I64, P, P, P]),
     }
@@ -174,5 +176,17 @@ def xq_paged_decode_attention_planned(layout: CacheLayout, q, batch: int, num_q_
     _check(load().xq_paged_decode_attention_planned(
         ctypes.byref(layout), _ptr(q), batch, num_q_heads, _ptr(k_pool), _ptr(v_pool),
         _ptr(block_tables), max_pages_per_seq, _ptr(context_lens), max_context_len,
+        float(softmax_scale), num_splits_hint, _ptr(workspace), int(workspace_bytes), _ptr(out),
+        _ptr(seq_order), _stream(stream)))
+
+
+def xq_append_decode_attention(layout: CacheLayout, k_new, v_new, q, batch: int, num_q_heads: int,
+                               k_pool, v_pool, block_tables, max_pages_per_seq: int, context_lens,
+                               max_context_len: int, softmax_scale: float, num_splits_hint: int,
+                               workspace, workspace_bytes: int, out, seq_order=None, stream=None):
+    """See xq_append_decode_attention in include/xq.h. Tensors are passed by data_ptr()."""
+    _check(load().xq_append_decode_attention(
+        ctypes.byref(layout), _ptr(k_new), _ptr(v_new), _ptr(q), batch, num_q_heads, _ptr(k_pool),
+        _ptr(v_pool), _ptr(block_tables), max_pages_per_seq, _ptr(context_lens), max_context_len,
         float(softmax_scale), num_splits_hint, _ptr(workspace), int(workspace_bytes), _ptr(out),
         _ptr(seq_order), _stream(stream)))

@@ -7,7 +7,8 @@ from __future__ import annotations
 
 import torch
 
-from . import (CacheLayout, load, xq_decode_plan, xq_decode_workspace_bytes, xq_paged_decode_attention,
+from . import (CacheLayout, load, xq_append_decode_attention, xq_decode_plan, xq_decode_workspace_bytes,
+               xq_paged_decode_attention,
                xq_paged_decode_attention_planned, xq_paged_prefill_attention,
                xq_pool_bytes, xq_quantize_append)
 
@@ -62,6 +63,28 @@ class PagedKVCache:
                                               block_tables, int(block_tables.shape[1]), context_lens,
                                               int(max_context_len), softmax_scale, num_splits,
                                               workspace, wbytes, out, seq_order, stream)
+        return out
+
+    def append_decode(self, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                      block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                      softmax_scale: float, num_splits: int = 0, out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None, stream=None,
+                      seq_order: torch.Tensor | None = None) -> torch.Tensor:
+        """One step: row b of k_new/v_new (bf16 [B, Hkv, 128]) goes to position context_lens[b] - 1,
+        then the decode of q (bf16 [B, Hq, 128]) -> out fp32 [B, Hq, 128]."""
+        batch, hq = int(q.shape[0]), int(q.shape[1])
+        if out is None:
+            out = torch.empty((batch, hq, 128), dtype=torch.float32, device=q.device)
+        need = self.workspace_bytes(batch, hq, max_context_len, num_splits)
+        if workspace is None and need > 0:
+            if self._ws is None or self._ws.numel() < need:
+                self._ws = torch.empty((need,), dtype=torch.uint8, device=q.device)
+            workspace = self._ws
+        wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        xq_append_decode_attention(self.layout, k_new, v_new, q, batch, hq, self.k_pool, self.v_pool,
+                                   block_tables, int(block_tables.shape[1]), context_lens,
+                                   int(max_context_len), softmax_scale, num_splits, workspace, wbytes,
+                                   out, seq_order, stream)
         return out
 
     def plan(self, host_context_lens, num_q_heads: int, max_context_len: int, num_splits: int = 0,

@@ -65,6 +65,7 @@
 // (m, l, acc) partials go to the workspace and decode_combine_kernel merges them by
 // log-sum-exp, rotates back and stores. An optional host plan (seq_order) only changes which
 // slot of the unit order runs which sequence.
+#include "row_codec.h"
 #include "xq_internal.h"
 
 #include <algorithm>
@@ -1309,6 +1310,24 @@ void decode_split_kernel(DecodeParams p) {
   const int col0 = threadIdx.x & 15;
   const int tok_end_c = min(tok_end, row_context(p, b0 + min(col0, G - 1) / Gq));
   const int tok_end_min = min(tok_end, row_context(p, b0));
+
+  // Fused append (decode rows only): the wave of the sequence's last split first encodes the
+  // step's new K and V rows of its kv head into slot L - 1 (lanes 0..15 the K row, 16..31 the V
+  // row, as the append kernel would) and waits until the stores are done, so the loads it issues
+  // afterwards, which include that slot, read the new bytes.
+  if (p.k_new != nullptr && split == nsplit_b - 1) {
+    if (lane < 32) {
+      const bool is_v = lane >= 16;
+      const int pos = L - 1;
+      const int page = p.block_tables[(int64_t)b0 * p.bt_stride + (pos >> p.page_shift)];
+      const uint4 raw = *reinterpret_cast<const uint4*>((is_v ? p.v_new : p.k_new) +
+                                                        ((int64_t)b0 * p.hkv + kvh) * D + (lane & 15) * 8);
+      uint8_t* block = const_cast<uint8_t*>(is_v ? p.v_pool : p.k_pool) + (int64_t)page * p.page_stride +
+                       (int64_t)kvh * p.block_bytes;
+      codec::encode_row<DT>(raw, lane & 15, block, pos & (p.page_size - 1), p.page_size);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
 
   // the staging ring and the epilogue's output rows (plus 64 per-lane sums) share one LDS buffer
   constexpr int kOutBytes = kMaxGroup * (D + 4) * 4 + kThreads * 4;

@@ -196,7 +196,8 @@ xq_status attention(const xq_cache_layout* layout, const void* q, int32_t batch,
                     const void* k_pool, const void* v_pool, const int32_t* block_tables, int32_t bt_stride,
                     int32_t max_pages_per_seq, const int32_t* context_lens, int32_t ctx_base,
                     int32_t max_context_len, float softmax_scale, int32_t num_splits_hint, void* workspace,
-                    int64_t workspace_bytes, float* out, hipStream_t stream, const int32_t* seq_order = nullptr) {
+                    int64_t workspace_bytes, float* out, hipStream_t stream, const int32_t* seq_order = nullptr,
+                    const void* k_new = nullptr, const void* v_new = nullptr) {
   if (batch > 65535) return fail(XQ_EUNSUPPORTED, "batch %d > 65535", batch);
   if (num_q_heads < 1 || num_q_heads % layout->num_kv_heads != 0)
     return fail(XQ_EINVAL, "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads,
@@ -269,6 +270,8 @@ xq_status attention(const xq_cache_layout* layout, const void* q, int32_t batch,
   p.ctx_base = ctx_base;
   p.qt = qt;
   p.seq_order = seq_order;
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
   const hipError_t e = xq::launch_decode(layout->kv_dtype, p, stream);
   if (e != hipSuccess) return fail(XQ_EHIP, "attention launch: %s", hipGetErrorString(e));
   return XQ_OK;
@@ -391,6 +394,23 @@ xq_status xq_paged_decode_attention_planned(const xq_cache_layout* layout, const
   return attention(layout, q, batch, num_q_heads, k_pool, v_pool, block_tables, max_pages_per_seq,
                    max_pages_per_seq, context_lens, 0, max_context_len, softmax_scale, num_splits_hint,
                    workspace, workspace_bytes, out, static_cast<hipStream_t>(stream), seq_order);
+}
+
+xq_status xq_append_decode_attention(const xq_cache_layout* layout, const void* k_new, const void* v_new,
+                                     const void* q, int32_t batch, int32_t num_q_heads, void* k_pool,
+                                     void* v_pool, const int32_t* block_tables, int32_t max_pages_per_seq,
+                                     const int32_t* context_lens, int32_t max_context_len, float softmax_scale,
+                                     int32_t num_splits_hint, void* workspace, int64_t workspace_bytes,
+                                     float* out, const int32_t* seq_order, void* stream) {
+  if (xq_status st = check_layout(layout)) return st;
+  if (batch < 0) return fail(XQ_EINVAL, "batch %d < 0", batch);
+  if (batch == 0) return XQ_OK;
+  if (!context_lens || !k_new || !v_new) return fail(XQ_EINVAL, "a required pointer is NULL");
+  if (!aligned16(k_new) || !aligned16(v_new)) return fail(XQ_EINVAL, "k_new and v_new must be 16-byte aligned");
+  if (max_context_len < 0) return fail(XQ_EINVAL, "max_context_len %d < 0", max_context_len);
+  return attention(layout, q, batch, num_q_heads, k_pool, v_pool, block_tables, max_pages_per_seq,
+                   max_pages_per_seq, context_lens, 0, max_context_len, softmax_scale, num_splits_hint,
+                   workspace, workspace_bytes, out, static_cast<hipStream_t>(stream), seq_order, k_new, v_new);
 }
 
 xq_status xq_decode_plan(const xq_cache_layout* layout, int32_t batch, int32_t num_q_heads,

@@ -81,6 +81,8 @@ struct DecodeParams {
   int32_t qt;                   // rows per work unit: 1 (decode) or 16 / group (prefill)
   const int32_t* seq_order;     // null, or a permutation of the batch from xq_decode_plan: the
                                 // slot of sequence b in the unit order runs sequence seq_order[b]
+  const uint16_t* k_new;        // null, or bf16 [batch][hkv][128]: new rows appended at position
+  const uint16_t* v_new;        // context_lens[b] - 1 by the wave of b's last split, first
 };
 
 hipError_t launch_quantize_append(int dtype, const AppendParams& p, hipStream_t stream);

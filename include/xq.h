@@ -230,6 +230,33 @@ xq_status xq_paged_decode_attention_planned(const xq_cache_layout* layout,
                                             float* out, const int32_t* seq_order, void* stream);
 
 /*
+ * One decode step in one launch: append each sequence's new K/V row, then decode. Equivalent to
+ * xq_quantize_append of row b of k_new/v_new at position context_lens[b] - 1 of sequence b (for
+ * every b with context_lens[b] >= 1), followed by xq_paged_decode_attention (or, with a non-NULL
+ * seq_order, xq_paged_decode_attention_planned) with the same arguments: the stored bytes and
+ * the outputs are bitwise those of the two separate calls. The wave that decodes the last
+ * partition of a sequence encodes that sequence's new rows of its kv head first and waits for
+ * the stores before it loads the cache, so no separate launch is needed (the xInfer page's
+ * decode step, section "What actually sits between the request and the tokens": rotate and
+ * quantize the new rows, then attend).
+ *
+ *   k_new, v_new       bf16 [batch][num_kv_heads][128], 16-byte aligned: the step's new rows
+ *   k_pool, v_pool     written (the new rows) and read
+ *   seq_order          NULL, or a device plan as for xq_paged_decode_attention_planned
+ * Other arguments, errors and the workspace as for xq_paged_decode_attention. context_lens are
+ * the lengths after the append; the new row's slot must lie in a page of the block table.
+ */
+xq_status xq_append_decode_attention(const xq_cache_layout* layout,
+                                     const void* k_new, const void* v_new,
+                                     const void* q, int32_t batch, int32_t num_q_heads,
+                                     void* k_pool, void* v_pool,
+                                     const int32_t* block_tables, int32_t max_pages_per_seq,
+                                     const int32_t* context_lens, int32_t max_context_len,
+                                     float softmax_scale, int32_t num_splits_hint,
+                                     void* workspace, int64_t workspace_bytes,
+                                     float* out, const int32_t* seq_order, void* stream);
+
+/*
  * Chunked prefill attention over the paged (and, for turbo types, quantized) cache: the queries
  * of one chunk of one sequence, each attending causally to the sequence's cached rows. Defined
  * by the infero page, section "Beyond plain text decode", item "Continuous batching" (decodes
