@@ -70,3 +70,32 @@ def test_fused_step_equals_append_then_decode(dtype, hq, hkv, ps):
         k, v = kv[b]
         ref, _ = oracle.decode_sequence(dtype, qb[b], k, v, W.softmax_scale)
         assert np.max(np.abs(out[b] - ref)) <= TOL, b
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,ps", [(4, 8, 8, 256), (16, 8, 8, 256), (3, 8, 1, 128)])
+def test_fused_step_page_sizes_and_groups(dtype, hq, hkv, ps):
+    """Large pages (the new row deep inside a page) and one query head per kv head."""
+    print("CASE fused-ps", dtype, hq, hkv, ps, flush=True)
+    lens = [700, 1, 256, 257, 513, 90, 1000, 31]
+    W = workloads.make(f"fusedps-{dtype}", 990 + dtype, dtype, lens, hq, hkv, ps)
+    kv = {b: W.kv_bits(b) for b in range(W.batch)}
+    bt, cl = upload_tables(W)
+    qb = W.q_bits()
+    q = to_dev(qb)
+    new_k = to_dev(np.stack([kv[b][0][-1] for b in range(W.batch)]))
+    new_v = to_dev(np.stack([kv[b][1][-1] for b in range(W.batch)]))
+    seq = to_dev(np.arange(W.batch, dtype=np.int32))
+    pos = to_dev(np.array([L - 1 for L in lens], np.int32))
+    a, f = make_cache(W), make_cache(W)
+    _fill_all_but_last(a, W, bt, kv)
+    _fill_all_but_last(f, W, bt, kv)
+    a.append(new_k, new_v, seq, pos, bt)
+    want = a.decode(q, bt, cl, W.max_context_len, W.softmax_scale, 0)
+    got = f.append_decode(new_k, new_v, q, bt, cl, W.max_context_len, W.softmax_scale, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(a.k_pool, f.k_pool) and torch.equal(a.v_pool, f.v_pool)
+    assert torch.equal(want, got)
+    out = got.cpu().numpy().astype(np.float64)
+    for b in range(W.batch):
+        ref, _ = oracle.decode_sequence(dtype, qb[b], kv[b][0], kv[b][1], W.softmax_scale)
+        assert np.max(np.abs(out[b] - ref)) <= TOL, b

@@ -425,3 +425,22 @@ def test_planned_decode_is_bitwise_the_plain_decode(dtype):
     for b in (0, 37, 128, 255):
         want = _oracle_out(W, b, qb, kv[b])
         assert np.max(np.abs(got[b] - want)) <= TOL
+
+
+def test_planned_decode_where_the_plan_is_the_identity():
+    """A batch that is not a multiple of 8, and several partitions per sequence: the plan is the
+    identity and the planned call equals the plain one."""
+    _print_case("planned-identity")
+    lens = [300, 45, 700, 1, 1029, 64, 9]
+    W = workloads.make("plan-id", 960, 4, lens, 16, 8, 16)
+    cache = make_cache(W)
+    bt, cl = upload_tables(W)
+    fill(cache, W, bt)
+    q = to_dev(W.q_bits())
+    for splits in (0, 4):
+        order = cache.plan(lens, 16, W.max_context_len, splits)
+        assert order.cpu().tolist() == list(range(len(lens)))
+        a = cache.decode(q, bt, cl, W.max_context_len, W.softmax_scale, splits)
+        b = cache.decode(q, bt, cl, W.max_context_len, W.softmax_scale, splits, seq_order=order)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)

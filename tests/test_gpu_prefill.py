@@ -93,3 +93,16 @@ def test_prefill_full_chunk_of_the_mixed_step():
         want = oracle.prefill_sequence(W.dtype, q[i:i + 1], k[: i + 1], v[: i + 1], i, W.softmax_scale)
         err = np.max(np.abs(got[i] - want[0]))
         assert err <= TOL, f"query {i}: {err:.3e}"
+
+
+@pytest.mark.parametrize("dtype,start,chunk,hq,hkv,ps", [(16, 200, 90, 16, 8, 256), (0, 300, 33, 8, 1, 256),
+                                                         (2, 0, 130, 32, 8, 64)])
+def test_prefill_large_pages(dtype, start, chunk, hq, hkv, ps):
+    _case("prefill-ps", dtype, start, chunk, hq, hkv, ps)
+    W, cache, bt, kv, q = _setup(dtype, start, chunk, hq, hkv, ps, 860 + dtype)
+    k, v = kv[0]
+    want = oracle.prefill_sequence(dtype, q, k, v, start, W.softmax_scale)
+    out = cache.prefill(to_dev(q), bt[0], start, W.softmax_scale, 0)
+    torch.cuda.synchronize()
+    err = np.max(np.abs(out.cpu().numpy().astype(np.float64) - want), axis=(1, 2))
+    assert np.all(err <= TOL), f"worst query {int(np.argmax(err))} err {err.max():.3e}"
