@@ -1294,6 +1294,18 @@ void decode_split_kernel(DecodeParams p) {
   auto qrow = [&](int c) -> int64_t {   // row of column c in q, out and the partials
     return (int64_t)(b0 + c / Gq) * p.hq + qh0 + c % Gq;
   };
+  // The split's block-table window (at most kMaxSplitPages entries from its first page, within
+  // the row's max_pages) is loaded before the context length is known, so the two loads overlap;
+  // entries past the context are loaded but never used.
+  static_assert(kMaxSplitPages <= 128, "two registers of block-table entries");
+  int btw0 = 0, btw1 = 0;
+  {
+    const int lpw = (split * p.tokens_per_split) >> p.page_shift;
+    const int32_t* row = p.block_tables + (int64_t)b0 * p.bt_stride + lpw;
+    const int nwin = min(kMaxSplitPages, p.maxp - lpw);
+    if (lane < nwin) btw0 = row[lane];
+    if (lane + 64 < nwin) btw1 = row[lane + 64];
+  }
   const int L = row_context(p, b0 + nrow - 1);   // the unit's longest row (its last)
   if (L <= 0) {
     if (split == 0)
@@ -1444,20 +1456,12 @@ void decode_split_kernel(DecodeParams p) {
   // (fast form): one descriptor per pool, based at this kv head's block of page 0, serves the
   // whole unit and the page's byte offset rides in the instructions' offsets. Larger pools: a
   // descriptor per page block (reads past the block return zero).
-  static_assert(kMaxSplitPages <= 128, "two registers of block-table entries");
   const bool fast = p.pool_bytes <= (int64_t)0xFFFFFFFF;
   const uint32_t pool_rec = (uint32_t)(p.pool_bytes - head_off);
   const __amdgpu_buffer_rsrc_t k_pool_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.k_pool + head_off), (short)0, (int)pool_rec, kBufferConfig);
   const __amdgpu_buffer_rsrc_t v_pool_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.v_pool + head_off), (short)0, (int)pool_rec, kBufferConfig);
-  int btw0 = 0, btw1 = 0;
-  {
-    const int32_t* row = p.block_tables + (int64_t)b * p.bt_stride + lp0;
-    const int nwin = last_page - lp0 + 1;
-    if (lane < nwin) btw0 = row[lane];
-    if (lane + 64 < nwin) btw1 = row[lane + 64];
-  }
   const int nrec = (int)p.block_bytes;
   auto addr = [&](auto kFast, int t0, HalfAddr (&a)[2]) {
 #pragma unroll
