@@ -128,14 +128,20 @@ template <> struct Stage<3> {
   static constexpr bool kOn = true;
   static constexpr int kHalf = 1024, kDma = 1, kOps = 4 * kDma + 2, kSlot = 4 * kHalf + 128;
 };
-// Layouts that pair (turbo4, turbo8, turbo3) or quad (turbo4, turbo8) token blocks in the QK
-// tile; the other types use the one-block layout.
-template <int DT> constexpr bool kPairOk = DT == 4 || DT == 8 || DT == 3;
+// turbo2: the same, a half's 16 rows being 512 B (lanes 32..63 land in the padding).
+template <> struct Stage<2> {
+  static constexpr bool kOn = true;
+  static constexpr int kHalf = 1024, kDma = 1, kOps = 4 * kDma + 2, kSlot = 4 * kHalf + 128;
+};
+// Layouts that pair (turbo4, turbo8, turbo3, turbo2) or quad (turbo4, turbo8) token blocks in
+// the QK tile; the other types use the one-block layout.
+template <int DT> constexpr bool kPairOk = DT == 4 || DT == 8 || DT == 3 || DT == 2;
 template <int DT> constexpr bool kQuadOk = DT == 4 || DT == 8;
 constexpr int kLdsPerCu = 160 * 1024;
 // LDS for the wave's query preparation: kMaxGroup rows of 256 B, then their fp32 scales
 constexpr int kQueryLds = kMaxGroup * 256 + kMaxGroup * 4;
-static_assert(Stage<4>::kSlot >= kQueryLds && Stage<8>::kSlot >= kQueryLds && Stage<3>::kSlot >= kQueryLds,
+static_assert(Stage<4>::kSlot >= kQueryLds && Stage<8>::kSlot >= kQueryLds && Stage<3>::kSlot >= kQueryLds &&
+                  Stage<2>::kSlot >= kQueryLds,
               "query rows fit one ring slot");
 // Paired-block QK (turbo4, turbo8): with at most this many query heads per kv head, the 16
 // columns of the QK tile hold two 16-token blocks of the tile side by side.
@@ -407,8 +413,8 @@ __device__ __forceinline__ DmaOffsets dma_offsets(int lane) {
   if constexpr (DT == 4) {
     o.k[0] = (lane & 15) * 64 + 16 * (lane >> 4);
     o.v[0] = (4 * ((lane >> 2) & 3) + (lane >> 4)) * 64 + 16 * (lane & 3);
-  } else if constexpr (DT == 3) {
-    o.k[0] = 16 * lane;   // as stored: row c of the half at 48 c
+  } else if constexpr (DT == 3 || DT == 2) {
+    o.k[0] = 16 * lane;   // as stored: row c of the half at 48 c (turbo2: 32 c)
     o.v[0] = 16 * lane;
   } else if constexpr (DT == 8) {
 #pragma unroll
@@ -463,7 +469,16 @@ __device__ __forceinline__ void read_slot(Tile<DT>& t, const uint8_t* slot, int 
   for (int h = 0; h < 2; ++h) {
     t.ks[h] = *reinterpret_cast<const v2i*>(slot + 4 * S::kHalf + 32 * h + 8 * g);
     t.vs[h] = *reinterpret_cast<const v2i*>(slot + 4 * S::kHalf + 64 + 32 * h + 8 * g);
-    if constexpr (DT == 3) {
+    if constexpr (DT == 2) {
+      // the bytes the register path loads: K row c, bytes 8 g .. 8 g + 7; V rows 4 g + r, the
+      // dword of dims 16 (c >> 1) .. + 15
+      const int col = lane & 15;
+      const int* kr = reinterpret_cast<const int*>(slot + h * S::kHalf + 32 * col + 8 * g);
+      t.k[h] = v2i{kr[0], kr[1]};
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        t.v[4 * h + r] = *reinterpret_cast<const int*>(slot + (2 + h) * S::kHalf + 32 * (4 * g + r) + 4 * (col >> 1));
+    } else if constexpr (DT == 3) {
       // the bytes the register path loads: K row c, bytes 12 g .. 12 g + 11; V rows 4 g + r, the
       // two dwords from byte 4 ((3 c) >> 2) (read as dwords: the offsets are 4-byte aligned)
       const int col = lane & 15;
@@ -788,6 +803,11 @@ template <> struct PairTile<3> {
   v2i v[8];            // V as in Tile<3>
   v2i ks, vs;
 };
+template <> struct PairTile<2> {
+  int k[4];            // the 32 bits (16 codes) of the lane's 16 dims per MFMA
+  int v[8];            // V as in Tile<2>
+  v2i ks, vs;
+};
 
 // Lane roles of the paired layout.
 struct PairLane {
@@ -811,7 +831,11 @@ __device__ __forceinline__ void read_slot_pair(PairTile<DT>& t, const uint8_t* s
   t.ks = *reinterpret_cast<const v2i*>(slot + 4 * S::kHalf + 32 * pl.jn + 8 * gg);
   t.vs = *reinterpret_cast<const v2i*>(slot + 4 * S::kHalf + 64 + 32 * pl.jn + 8 * gg);
   const uint8_t* kh = slot + pl.kb * S::kHalf;
-  if constexpr (DT == 3) {
+  if constexpr (DT == 2) {
+    // rows as stored (32 B): dims 32 m + 16 kp .. + 15 are the dword at byte 8 m + 4 kp
+#pragma unroll
+    for (int m = 0; m < 4; ++m) t.k[m] = *reinterpret_cast<const int*>(kh + 32 * tk + 8 * m + 4 * pl.kp);
+  } else if constexpr (DT == 3) {
     // rows as stored (48 B): dims 32 m + 16 kp .. + 15 are bits 96 m + 48 kp .. + 47 of the row,
     // i.e. bytes 12 m + 6 kp .. + 5: two aligned dwords from byte 12 m + 4 kp, shifted by 16 kp
     const int* kr = reinterpret_cast<const int*>(kh + 48 * tk);
@@ -834,7 +858,9 @@ __device__ __forceinline__ void read_slot_pair(PairTile<DT>& t, const uint8_t* s
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      if constexpr (DT == 3) {
+      if constexpr (DT == 2) {
+        t.v[4 * h + r] = *reinterpret_cast<const int*>(slot + (2 + h) * S::kHalf + 32 * (4 * gg + r) + 4 * (tk >> 1));
+      } else if constexpr (DT == 3) {
         const int* vr = reinterpret_cast<const int*>(slot + (2 + h) * S::kHalf + 48 * (4 * gg + r) +
                                                      4 * ((3 * tk) >> 2));
         t.v[4 * h + r] = v2i{vr[0], vr[1]};
@@ -851,7 +877,12 @@ __device__ __forceinline__ void read_slot_pair(PairTile<DT>& t, const uint8_t* s
 // 8 (w >> 1) + 2 b + (w & 1) (turbo4) or 4 w + b (turbo8) of the lane's 16.
 template <int DT>
 __device__ __forceinline__ v4i pair_k_operand(const PairTile<DT>& t, int m) {
-  if constexpr (DT == 3) {
+  if constexpr (DT == 2) {
+    // code of dim 4 b + w (of the lane's 16) to the top two bits of byte b of dword w: 64 c
+    const uint32_t x = (uint32_t)t.k[m];
+    return v4i{(int)((x << 6) & 0xc0c0c0c0u), (int)((x << 4) & 0xc0c0c0c0u), (int)((x << 2) & 0xc0c0c0c0u),
+               (int)(x & 0xc0c0c0c0u)};
+  } else if constexpr (DT == 3) {
     // dims 0..7 and 8..15 of the lane's 16: bits 0..23 and 24..47; 32 c in the top of each byte
     const uint32_t y0 = spread3to6((uint32_t)t.k[m][0]);
     const uint32_t y1 = spread3to6(__builtin_amdgcn_alignbit((uint32_t)t.k[m][1], (uint32_t)t.k[m][0], 24));
@@ -949,7 +980,17 @@ __device__ __forceinline__ void process_pair_tile(const PairTile<DT>& t, WaveSta
   st.accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, Bb, st.accb, 0, 0, 0);
   st.accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, Bb, st.accb, 0, 0, 0);
   uint32_t e[8], o[8];
-  if constexpr (DT == 3) {
+  if constexpr (DT == 2) {
+    // as v_bytes<2>: the lane's 8 dims are the low or high 16 bits of the dword
+    const uint32_t sel = (lane & 1) ? 0x0c030c02u : 0x0c010c00u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t u = perm(0u, (uint32_t)t.v[j] ^ 0xaaaaaaaau, sel);   // c + 2 per field
+      const uint32_t n = (u & 0x000f000fu) | ((u << 4) & 0x0f000f00u);
+      e[j] = (n << 6) & 0xc0c0c0c0u;                // (c + 2) << 6
+      o[j] = (n << 4) & 0xc0c0c0c0u;
+    }
+  } else if constexpr (DT == 3) {
     const uint32_t sh = (24u * (uint32_t)(lane & 15)) & 31u;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -1014,7 +1055,8 @@ __device__ __forceinline__ QuadLane quad_lane(int lane, int G) {
 template <int DT> struct QuadK;
 template <> struct QuadK<4> { v4i k[4]; };   // the lane's token row: 16 B per 32 dims
 template <> struct QuadK<8> { v4i k[8]; };   // 16 B per 16 dims
-template <> struct QuadK<3> { v4i k[1]; };   // never used: turbo3 has no quad layout (kQuadOk)
+template <> struct QuadK<3> { v4i k[1]; };   // never used: turbo3 and turbo2 have no quad layout
+template <> struct QuadK<2> { v4i k[1]; };   // (kQuadOk)
 
 template <int DT>
 __device__ __forceinline__ void read_quad_k(QuadK<DT>& t, const uint8_t* slot0, const uint8_t* slot1, int lane) {
@@ -1236,7 +1278,7 @@ __device__ __forceinline__ void fwht_wave(float (*x)[D + 4], int rows, int lane)
 // Waves per SIMD the register budget is sized for: deep rings (4+ slots) are only picked when
 // at most two waves share a SIMD.
 template <int DT, int DEPTH>
-constexpr int kWavesPerEu = DT == 0 ? 1 : ((DT == 2 || DT == kFp8) ? 2 : (DEPTH >= 4 ? 2 : 3));
+constexpr int kWavesPerEu = DT == 0 ? 1 : (DT == kFp8 ? 2 : (DEPTH >= 4 ? 2 : 3));
 
 // DEPTH: tiles in flight per wave on the staged path (LDS slots); chosen at launch from how
 // many waves share a compute unit, so that the LDS of the resident waves holds as many tiles
