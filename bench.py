@@ -6,9 +6,9 @@ A step is one pass of the whole hot path for one layer of a decode batch:
   1. the new K/V rows are rotated, quantized, packed and stored in their pages: every
      sequence's new row, plus the prefill chunk where the workload has one;
   2. decode attention over every sequence's paged, quantized context.
-By default xq_quantize_append and the decode are two launches; with --fuse one
-xq_append_decode_attention launch does both for the decode batch (a chunk still goes through
-xq_quantize_append first). The decode uses the host plan (xq_decode_plan) unless --no-plan.
+By default one xq_append_decode_attention launch does both for the decode batch (a chunk still
+goes through xq_quantize_append first); --no-fuse runs xq_quantize_append and the decode as two
+launches. The decode uses the host plan (xq_decode_plan) unless --no-plan.
 The new row of sequence b goes to position L_b - 1, so every step has the same shape and
 the cache content stays what the oracle computes.
 
@@ -60,8 +60,8 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunk-prefill timing")
     ap.add_argument("--no-plan", action="store_true", help="decode without the host plan")
-    ap.add_argument("--fuse", action="store_true",
-                    help="append the batch's new rows inside the decode launch (xq_append_decode_attention)")
+    ap.add_argument("--no-fuse", action="store_true",
+                    help="append the batch's new rows in their own launch instead of the decode's")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run plain 512 MiB device copies (a known byte count for "
@@ -311,7 +311,7 @@ def main():
     app = (new_k.data_ptr(), new_v.data_ptr(), B, new_seq.data_ptr(), new_pos.data_ptr(),
            bt.data_ptr(), maxp)
     chunk = None
-    fuse = args.fuse
+    fuse = not args.no_fuse
     if chunk_kv is not None:
         # one append per step takes every new row that the decode launch does not: the chunk's, and
         # without the fused step the decode batch's own too

@@ -1365,21 +1365,32 @@ void decode_split_kernel(DecodeParams p) {
   const int tok_end_c = min(tok_end, row_context(p, b0 + min(col0, G - 1) / Gq));
   const int tok_end_min = min(tok_end, row_context(p, b0));
 
-  // Fused append (decode rows only): the wave of the sequence's last split first encodes the
-  // step's new K and V rows of its kv head into slot L - 1 (lanes 0..15 the K row, 16..31 the V
-  // row, as the append kernel would) and waits until the stores are done, so the loads it issues
-  // afterwards, which include that slot, read the new bytes.
-  if (p.k_new != nullptr && split == nsplit_b - 1) {
+  // Fused append (decode rows only): the wave of the sequence's last split encodes the step's new
+  // K and V rows of its kv head into slot L - 1 (lanes 0..15 the K row, 16..31 the V row, as the
+  // append kernel would) and waits until the stores are done before it loads the tile holding
+  // that slot. On the staged path with more tiles than the first DEPTH - 1 staged ones, this runs
+  // after those are issued (their loads and the new rows' overlap); otherwise first of all.
+  const bool fuse = p.k_new != nullptr && split == nsplit_b - 1;
+  uint4 new_raw = make_uint4(0u, 0u, 0u, 0u);   // this lane's 8 elements of the new K (or V) row
+  int new_page = 0;
+  auto load_new_row = [&]() __attribute__((always_inline)) {
+    new_page = p.block_tables[(int64_t)b0 * p.bt_stride + ((L - 1) >> p.page_shift)];
+    if (lane < 32)
+      new_raw = *reinterpret_cast<const uint4*>((lane >= 16 ? p.v_new : p.k_new) +
+                                                ((int64_t)b0 * p.hkv + kvh) * D + (lane & 15) * 8);
+  };
+  auto store_new_row = [&]() __attribute__((always_inline)) {
     if (lane < 32) {
-      const bool is_v = lane >= 16;
-      const int pos = L - 1;
-      const int page = p.block_tables[(int64_t)b0 * p.bt_stride + (pos >> p.page_shift)];
-      const uint4 raw = *reinterpret_cast<const uint4*>((is_v ? p.v_new : p.k_new) +
-                                                        ((int64_t)b0 * p.hkv + kvh) * D + (lane & 15) * 8);
-      uint8_t* block = const_cast<uint8_t*>(is_v ? p.v_pool : p.k_pool) + (int64_t)page * p.page_stride +
+      uint8_t* block = const_cast<uint8_t*>(lane >= 16 ? p.v_pool : p.k_pool) + (int64_t)new_page * p.page_stride +
                        (int64_t)kvh * p.block_bytes;
-      codec::encode_row<DT>(raw, lane & 15, block, pos & (p.page_size - 1), p.page_size);
+      codec::encode_row<DT>(new_raw, lane & 15, block, (L - 1) & (p.page_size - 1), p.page_size);
     }
+  };
+  const int ntiles = (tok_end - tok_begin + 31) >> 5;
+  const bool fuse_late = fuse && Stage<DT>::kOn && ntiles > DEPTH - 1;
+  if (fuse) load_new_row();   // ahead of every cache load, so that waiting for it waits for nothing else
+  if (fuse && !fuse_late) {
+    store_new_row();
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
@@ -1485,7 +1496,6 @@ void decode_split_kernel(DecodeParams p) {
 
   // ---- main loop: tiles 0 .. ntiles-1 of the unit, kDepth in flight --------------------------
   constexpr int R = Codec<DT>::kRow;
-  const int ntiles = (tok_end - tok_begin + 31) >> 5;
   const int ps = p.page_size;
   const int last_page = (L - 1) >> p.page_shift;
   const int64_t head_off = (int64_t)kvh * p.block_bytes;
@@ -1556,8 +1566,12 @@ void decode_split_kernel(DecodeParams p) {
       // LDS into registers, waits for those reads and refills the freed slots before the math,
       // so DEPTH tiles are in flight while it computes.
       for (int i = 0; i < DEPTH - 1 && i < ntiles; ++i) stage(i, i);
+      // the new rows' stores go out behind the first tiles (the extra operations only make the
+      // count-based waits below stricter); they are complete before any later tile is staged
+      if (fuse_late) store_new_row();
       wait_tiles<S::kOps, 0, DEPTH - 1>(min(DEPTH - 1, ntiles));
       load_query(qa);   // ends with its LDS reads complete
+      if (fuse_late) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       if (DEPTH - 1 < ntiles) stage(DEPTH - 1, DEPTH - 1);
       // While tiles it .. it + DEPTH - 1 all exist, the number of tiles staged after the ones a
       // step reads is fixed and the wait takes a constant; only the last steps count down.
