@@ -9,6 +9,12 @@ A step is one pass of the whole hot path for one layer of a decode batch:
 By default one xq_append_decode_attention launch does both for the decode batch (a chunk still
 goes through xq_quantize_append first); --no-fuse runs xq_quantize_append and the decode as two
 launches. The decode uses the host plan (xq_decode_plan) unless --no-plan.
+
+Steps are timed twice, K each after W warm-up steps: eagerly, with HIP events around every
+decode call (the roofline's launch duration), and replayed from HIP graphs captured per pool
+replica, the way a serving engine replays its decode step. `value` and `ms_per_step` come from
+the graph replay when every replica has its graph (--no-graph: from the eager launches); both
+are in `step_timing`.
 The new row of sequence b goes to position L_b - 1, so every step has the same shape and
 the cache content stays what the oracle computes.
 
@@ -404,7 +410,11 @@ def main():
     kv_bytes = int(W.context_lens.astype(np.int64).sum()) * hkv * 2 * rb
     tokens = int(W.context_lens.astype(np.int64).sum())
     nsplits = xq.xq_decode_num_splits(base.layout, B, hq, W.max_context_len, splits)
-    value = kv_bytes / (step_ms * 1e-3) / 1e9
+    # The reported step time: the captured step replayed from HIP graphs (as a serving engine
+    # replays its decode step) when every pool replica has its graph; else the eager launches.
+    by_graph = graph is not None and graph["replicas"] == R
+    timed_ms = graph["ms_per_step"] if by_graph else step_ms
+    value = kv_bytes / (timed_ms * 1e-3) / 1e9
     achieved = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
     tag = f"decode_call_{workloads.DTYPE_NAMES[W.dtype]}_{W.name}"
     traffic = committed_traffic(tag)
@@ -416,7 +426,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": Wm,
-        "ms_per_step": round(step_ms, 5),
+        "ms_per_step": round(timed_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -432,8 +442,13 @@ def main():
             "plan": order is not None and order.cpu().tolist() != list(range(B)),
             "fused_append": fuse,
         },
-        "seq_tokens_per_s": round(tokens / (step_ms * 1e-3), 1),
-        "decode_seqs_per_s": round(B / (step_ms * 1e-3), 1),
+        "step_timing": {"method": "hip graph replay of the captured step" if by_graph else "eager launches",
+                        "eager_ms_per_step": round(step_ms, 5),
+                        "eager_value": round(kv_bytes / (step_ms * 1e-3) / 1e9, 2),
+                        "graph_ms_per_step": graph["ms_per_step"] if graph is not None else None,
+                        "graph_replicas": graph["replicas"] if graph is not None else None},
+        "seq_tokens_per_s": round(tokens / (timed_ms * 1e-3), 1),
+        "decode_seqs_per_s": round(B / (timed_ms * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes,
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "decode_call_us": {"mean": round(dec_avg_ms * 1e3, 2),
@@ -449,11 +464,9 @@ def main():
     }
     if chunk is not None and not args.no_prefill:
         result["prefill"] = time_prefill(lib, base, W, bt, to_dev, stream, K, Wm)
-    if graph is not None:
-        graph["value"] = round(kv_bytes / (graph["ms_per_step"] * 1e-3) / 1e9, 2)
-        graph["seq_tokens_per_s"] = round(tokens / (graph["ms_per_step"] * 1e-3), 1)
-        result["graph_replay"] = graph
-    log(f"GPU: {step_ms * 1e3:.1f} us/step, decode call {dec_avg_ms * 1e3:.1f} us")
+    log(f"GPU: {step_ms * 1e3:.1f} us/step eager, "
+        f"{'%.1f' % (graph['ms_per_step'] * 1e3) if graph is not None else '-'} us/step graph, "
+        f"decode call {dec_avg_ms * 1e3:.1f} us")
     if not args.no_cpu:
         log("oracle baseline on the host")
         result["cpu_baseline"] = cpu_baseline(W, args.cpu_seconds)
