@@ -12,9 +12,11 @@ launches. The decode uses the host plan (xq_decode_plan) unless --no-plan.
 
 Steps are timed twice, K each after W warm-up steps: eagerly, with HIP events around every
 decode call (the roofline's launch duration), and replayed from HIP graphs captured per pool
-replica, the way a serving engine replays its decode step. `value` and `ms_per_step` come from
-the graph replay when every replica has its graph (--no-graph: from the eager launches); both
-are in `step_timing`.
+replica, the way a serving engine replays its decode step; when every replica has its graph,
+also from one graph holding a step on each replica in turn, as a model's decode graph holds one
+step per layer (K steps = K // R replays of it + K mod R single-step replays). `value` and
+`ms_per_step` come from that graph, else from the single-step graphs when every replica has
+one, else (--no-graph) from the eager launches; all figures are in `step_timing`.
 The new row of sequence b goes to position L_b - 1, so every step has the same shape and
 the cache content stays what the oracle computes.
 
@@ -404,16 +406,44 @@ def main():
         g_ms = gstart.elapsed_time(gstop) / K
         graph = {"ms_per_step": round(g_ms, 5), "replicas": NG}
         log(f"graph replay: {g_ms * 1e3:.1f} us/step")
+        # One graph holding a step on every replica in turn, as a model's decode graph holds one
+        # step per layer (the replicas' pools stand for the layers' caches): K steps are K // NG
+        # replays of it plus K % NG single-step replays.
+        if NG == R and R > 1:
+            layers = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(layers):
+                cs = torch.cuda.current_stream().cuda_stream
+                for r in runners:
+                    r.run(cs)
+                    r.decode(cs)
+            torch.cuda.synchronize()
+            for _ in range(max(1, Wm // R)):
+                layers.replay()
+            torch.cuda.synchronize()
+            gstart.record(stream)
+            for _ in range(K // R):
+                layers.replay()
+            for i in range(K % R):
+                graphs[i].replay()
+            gstop.record(stream)
+            torch.cuda.synchronize()
+            m_ms = gstart.elapsed_time(gstop) / K
+            graph["multi_step_ms_per_step"] = round(m_ms, 5)
+            graph["steps_per_graph"] = R
+            log(f"graph of {R} steps: {m_ms * 1e3:.1f} us/step")
+            del layers
         del graphs
 
     rb = row_bytes(W.dtype)
     kv_bytes = int(W.context_lens.astype(np.int64).sum()) * hkv * 2 * rb
     tokens = int(W.context_lens.astype(np.int64).sum())
     nsplits = xq.xq_decode_num_splits(base.layout, B, hq, W.max_context_len, splits)
-    # The reported step time: the captured step replayed from HIP graphs (as a serving engine
-    # replays its decode step) when every pool replica has its graph; else the eager launches.
+    # The reported step time: the steps replayed from HIP graphs (as a serving engine replays its
+    # decode step), R to a graph where possible, when every pool replica has its graph; else the
+    # eager launches.
     by_graph = graph is not None and graph["replicas"] == R
-    timed_ms = graph["ms_per_step"] if by_graph else step_ms
+    by_layers = by_graph and "multi_step_ms_per_step" in graph
+    timed_ms = graph["multi_step_ms_per_step"] if by_layers else graph["ms_per_step"] if by_graph else step_ms
     value = kv_bytes / (timed_ms * 1e-3) / 1e9
     achieved = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
     tag = f"decode_call_{workloads.DTYPE_NAMES[W.dtype]}_{W.name}"
@@ -442,10 +472,13 @@ def main():
             "plan": order is not None and order.cpu().tolist() != list(range(B)),
             "fused_append": fuse,
         },
-        "step_timing": {"method": "hip graph replay of the captured step" if by_graph else "eager launches",
+        "step_timing": {"method": (f"hip graph replay, {R} steps (one per pool replica, as one per layer) per graph"
+                                   if by_layers else "hip graph replay of the captured step" if by_graph
+                                   else "eager launches"),
                         "eager_ms_per_step": round(step_ms, 5),
                         "eager_value": round(kv_bytes / (step_ms * 1e-3) / 1e9, 2),
                         "graph_ms_per_step": graph["ms_per_step"] if graph is not None else None,
+                        "multi_step_graph_ms_per_step": graph.get("multi_step_ms_per_step") if graph is not None else None,
                         "graph_replicas": graph["replicas"] if graph is not None else None},
         "seq_tokens_per_s": round(tokens / (timed_ms * 1e-3), 1),
         "decode_seqs_per_s": round(B / (timed_ms * 1e-3), 1),
