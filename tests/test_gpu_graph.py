@@ -62,3 +62,61 @@ def test_step_replays_from_a_captured_graph(dtype, hq):
         assert torch.equal(out, want), f"replay {r} differs from the eager step"
         assert bool(torch.isfinite(scratch))
     del graph
+
+
+def test_layer_steps_replay_from_one_graph():
+    """Several fused append + decode steps, one per layer cache, captured into ONE graph (as a
+    model's decode graph holds a step per layer) and replayed: every layer's output must equal
+    its eager step bit for bit on every replay."""
+    print("CASE graph layers", flush=True)
+    lens = [300, 45, 700, 1, 1029, 64, 513, 128, 2000, 17, 900, 31, 256, 640, 77, 1500]
+    hq, layers = 16, []
+    for layer in range(3):
+        W = workloads.make(f"graph-layer-{layer}", 950 + layer, 4, lens, hq, 8, 16)
+        cache = make_cache(W)
+        bt, cl = upload_tables(W)
+        kv = {b: W.kv_bits(b) for b in range(W.batch)}
+        fill(cache, W, bt, kv=kv)
+        k_new = to_dev(np.stack([kv[b][0][-1] for b in range(W.batch)]))
+        v_new = to_dev(np.stack([kv[b][1][-1] for b in range(W.batch)]))
+        max_ctx = W.max_context_len
+        ws = torch.empty((max(16, cache.workspace_bytes(W.batch, hq, max_ctx, 0)),), dtype=torch.uint8,
+                         device="cuda")
+        order = cache.plan([int(x) for x in W.context_lens], hq, max_ctx, 0)
+        out = torch.empty((W.batch, hq, 128), dtype=torch.float32, device="cuda")
+        layers.append((W, cache, bt, cl, to_dev(W.q_bits()), k_new, v_new, ws, order, out))
+
+    def step(layer):
+        W, cache, bt, cl, q, k_new, v_new, ws, order, out = layer
+        cache.append_decode(k_new, v_new, q, bt, cl, W.max_context_len, W.softmax_scale, 0, out=out,
+                            workspace=ws, seq_order=order)
+
+    want = []
+    for layer in layers:
+        step(layer)
+        torch.cuda.synchronize()
+        want.append(layer[-1].clone())
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for layer in layers:
+            step(layer)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for layer in layers:
+            step(layer)
+    torch.cuda.synchronize()
+    for r in range(3):
+        for layer in layers:
+            layer[-1].fill_(float("nan"))
+        scratch = torch.randn(1 << 20, device="cuda").sum()     # unrelated eager work
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, layer in enumerate(layers):
+            assert torch.equal(layer[-1], want[i]), f"replay {r}, layer {i} differs from its eager step"
+        assert bool(torch.isfinite(scratch))
+    del graph
