@@ -30,9 +30,10 @@ def upload_tables(W: workloads.Workload):
 
 
 def fill(cache: PagedKVCache, W: workloads.Workload, bt: torch.Tensor, seqs=None,
-         max_rows: int = 1 << 20, kv=None):
+         max_rows: int = 1 << 20, kv=None, last=None):
     """Append every position of the given sequences (default: all, incl. a chunk sequence).
-    `kv` optionally maps seq -> (k_bits, v_bits) already drawn."""
+    `kv` optionally maps seq -> (k_bits, v_bits) already drawn; `last`, a dict, receives each
+    sequence's last K and V rows (seq -> (k_row, v_row))."""
     seqs = range(W.num_seqs) if seqs is None else seqs
     pend_k, pend_v, pend_s, pend_p, n = [], [], [], [], 0
 
@@ -52,6 +53,8 @@ def fill(cache: PagedKVCache, W: workloads.Workload, bt: torch.Tensor, seqs=None
         if L == 0:
             continue
         k, v = kv[b] if kv is not None and b in kv else W.kv_bits(b)
+        if last is not None:
+            last[b] = (k[-1].copy(), v[-1].copy())
         pend_k.append(k)
         pend_v.append(v)
         pend_s.append(np.full(L, b, np.int32))

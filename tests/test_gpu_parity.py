@@ -222,16 +222,27 @@ FULL = [("c1", 1, None, list(range(0, 256, 17))), ("c2-turbo8", 2, 8, [0, 31]),
 
 @pytest.mark.parametrize("name,cfg,dtype,sample", FULL, ids=[f[0] for f in FULL])
 def test_full_size_sampled(name, cfg, dtype, sample):
+    """The benchmark's step: one fused launch appends every sequence's newest row (its last
+    position again, so the cache stays what the oracle sees) and decodes, in the order of the
+    host plan, with the preset's split hint."""
     _print_case("full", name)
     W = workloads.config(cfg, dtype=dtype)
     cache = make_cache(W, fill_byte=None)
     bt, cl = upload_tables(W)
-    fill(cache, W, bt)
+    last = {}
+    fill(cache, W, bt, last=last)
     torch.cuda.synchronize()
+    B, qb = W.batch, W.q_bits()
+    k_new = to_dev(np.stack([last[b][0] for b in range(B)]))
+    v_new = to_dev(np.stack([last[b][1] for b in range(B)]))
+    order = cache.plan([int(x) for x in W.context_lens], W.num_q_heads, W.max_context_len, W.num_splits)
+    out = cache.append_decode(k_new, v_new, to_dev(qb), bt[:B], cl, W.max_context_len, W.softmax_scale,
+                              W.num_splits, seq_order=order)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    # the codes after the step (the fused append rewrote position L - 1 of every sequence)
     check_codes = sample[:1] + ([W.batch] if W.chunk_tokens else [])
     _codec_check(W, cache, check_codes)
-    qb = W.q_bits()
-    got = _decode(W, cache, bt, cl, W.num_splits, to_dev(qb))
     assert np.all(np.isfinite(got))
     for b in sample:
         want = _oracle_out(W, b, qb)
