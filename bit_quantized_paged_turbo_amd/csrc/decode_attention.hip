@@ -17,11 +17,15 @@
 // The grouped-query tile is a dense contraction, so both products run on the matrix cores:
 //
 //   QK  v_mfma_i32_16x16x64_i8. Rows = 16 tokens, columns = the g query heads of the kv head
-//       (g <= 16). The rotated query is rounded to an integer q (|q| <= 32000, one fp32 scale
-//       per head) and split into two signed 8-bit digits, q = 256 d1 + d0. A K code c enters
-//       as the signed byte c * 2^(8 - bits) (the code's bits moved to the top of the byte:
-//       two instructions per four codes, no bias), so the integer dot products are exact up
-//       to that power of two, folded into the query scale. Two MFMAs per digit cover 128 dims.
+//       (g <= 16). The rotated query is rounded to an integer q (|q| <= 127 * 2^16, one fp32
+//       scale per head, so every element is within 2^-23 of the head's largest) and split into
+//       three signed 8-bit digits, q = 65536 d2 + 256 d1 + d0. A K code c enters as the signed
+//       byte c * 2^(8 - bits) (the code's bits moved to the top of the byte: two instructions
+//       per four codes, no bias), so each digit's integer dot product is exact up to that power
+//       of two, folded into the query scale; the three are summed in fp32. Two MFMAs per digit
+//       cover 128 dims. (Two digits, q <= 32000, left a query with one dominant rotated element
+//       -- a constant offset maps to sqrt(128) e0 -- only 2^-15 of that element on the others,
+//       which moved outputs by up to 3e-2 on keys with outlier channels.)
 //   PV  v_mfma_f32_16x16x32_f16. Rows = heads, k = 32 tokens, columns = 16 dimensions (eight
 //       MFMAs cover 128). The weight of token t for head h is P'[h,t] = p[h,t] * s_v[t], split
 //       into an fp16 high part (round toward zero) and the fp16 remainder; each enters its own
@@ -79,7 +83,8 @@ constexpr int kThreads = 64;              // one wave per work unit
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRotC = 0x1.6a09e6p-4f;   // fp32 nearest to 1/sqrt(128)
 constexpr float kLazy = 8.0f;             // rescale only when a score beats m by > 2^8
-constexpr float kQiMax = 32000.f;         // |q| bound for two signed 8-bit digits
+constexpr int kDigits = 3;                // signed 8-bit digits of the integer query
+constexpr float kQiMax = 127.f * 65536.f; // |q| bound: 65536 d2 + 256 d1 + d0, digits in [-128, 127]
 constexpr float kWeightExp = 21.f;
 // Initial softmax reference: finite, so that a column with no token in its split (a prefill
 // query whose position lies before the split) gets weights 2^(-inf - ref) = 0 rather than NaN;
@@ -138,8 +143,14 @@ template <> struct Stage<2> {
 template <int DT> constexpr bool kPairOk = DT == 4 || DT == 8 || DT == 3 || DT == 2;
 template <int DT> constexpr bool kQuadOk = DT == 4 || DT == 8;
 constexpr int kLdsPerCu = 160 * 1024;
-// LDS for the wave's query preparation: kMaxGroup rows of 256 B, then their fp32 scales
-constexpr int kQueryLds = kMaxGroup * 256 + kMaxGroup * 4;
+// LDS for the wave's query preparation: kMaxGroup raw rows of 256 B land there; the digits of
+// up to kQPhaseRows rows (kQRowBytes each, the operand layout) and every row's fp32 score scale
+// then take its start. Units with more query columns write and read their digits in two phases.
+constexpr int kQRowBytes = 128 * kDigits;
+constexpr int kQPhaseRows = 8;
+constexpr int kQueryScaleOff = kQPhaseRows * kQRowBytes;
+constexpr int kQueryLds = kMaxGroup * 256 > kQueryScaleOff + kMaxGroup * 4 ? kMaxGroup * 256
+                                                                            : kQueryScaleOff + kMaxGroup * 4;
 static_assert(Stage<4>::kSlot >= kQueryLds && Stage<8>::kSlot >= kQueryLds && Stage<3>::kSlot >= kQueryLds &&
                   Stage<2>::kSlot >= kQueryLds,
               "query rows fit one ring slot");
@@ -203,15 +214,16 @@ __device__ __forceinline__ uint32_t spread3to6(uint32_t x) {
 constexpr uint32_t kBias3 = 0x924924u;   // bit 2 of every 3-bit field: c -> c + 4
 
 // ---------------------------------------------------------------------------------------
-// Query preparation, done by the decode wave itself: q' = H q, q = rint(q' * 32000 / max|q'|),
-// two signed digits, packed in the QK operand layout. The G query rows of the kv head arrive in
-// LDS (row h at 256 h, bf16). The whole wave takes part: head h < G owns the aligned group of
+// Query preparation, done by the decode wave itself: q' = H q, q = rint(q' * kQiMax / max|q'|),
+// three signed digits, packed in the QK operand layout. The G query rows of the kv head arrive
+// in LDS (row h at 256 h, bf16). The whole wave takes part: head h < G owns the aligned group of
 // 128 / NPL lanes starting at lane (128 / NPL) h, and lane r of the group holds the NPL
 // consecutive dimensions [NPL r, NPL r + NPL) (NPL = 8 for G <= 4, 16 for G <= 8, else 32).
-// The FWHT stages below NPL run in-lane, the others exchange with lane r ^ (stage / NPL). The
-// digits of dimension d go to operand byte 64 (d >> 5) + lin(d & 31) of the row (low digit; the
-// high digit 16 bytes on), which other lanes read from: the wave's LDS reads all precede its
-// writes. The score scale of head h goes to sc[h].
+// The FWHT stages below NPL run in-lane, the others exchange with lane r ^ (stage / NPL). Every
+// lane has read its raw row before any digit is written (one wave, its LDS operations in
+// order). Digit k of dimension d of a row goes to byte 96 (d >> 5) + operand_byte(d & 31) +
+// 16 k of the row's kQRowBytes, which other lanes read as operands; the score scale of head h
+// goes to sc[h].
 // ---------------------------------------------------------------------------------------
 // Value held by lane (lane ^ M), M = 1, 2, 4 or 8: DPP quad_perm (M = 1, 2) and row_ror:8
 // (M = 8) are VALU operand modifiers; M = 4 is a ds_swizzle in bit-mask mode (no memory access).
@@ -240,8 +252,9 @@ __device__ __forceinline__ void fwht_cross(float (&x)[N], int r) {
   }
 }
 
-// Operand byte (low digit) of dimension e (0..31) of a 32-dimension group: 32 m + 4 w + b for
-// operand half/chunk m, dword w, byte b. The map is linear in the bits of e.
+// Operand byte (digit 0) of dimension e (0..31) of a 32-dimension group: 48 m + 4 w + b for
+// operand half/chunk m, dword w, byte b (digits 1 and 2 follow at + 16 and + 32). The map is
+// linear in the bits of e.
 //   turbo8 (both layouts):              e = 16 m + 4 w + b
 //   paired-block turbo4:                e = 16 m + 8 (w >> 1) + 2 b + (w & 1)
 //   one-block turbo4/turbo3 (m = chunk): e = 8 w + 2 b + m
@@ -258,14 +271,24 @@ __device__ __forceinline__ int operand_byte(int e) {
   } else {
     m = e & 1; w = e >> 3; b = (e >> 1) & 3;
   }
-  return 32 * m + 4 * w + b;
+  return 16 * kDigits * m + 4 * w + b;
 }
 
-template <int DT, bool PAIRED, int NPL>
-__device__ __forceinline__ void prep_query_lanes(uint8_t* qa, float* sc_out, int h, int r, float softmax_scale) {
+// One lane's share of a rotated query row: dimensions [NPL r, NPL r + NPL), the factor that
+// maps them to integers (kQiMax / max|q'|, signed like the softmax scale) and the head's score
+// scale.
+template <int NPL> struct QueryLane {
+  float x[NPL];
+  float inv;
+  float sc;
+};
+
+template <int DT, int NPL>
+__device__ __forceinline__ void rotate_query_lane(const uint8_t* qa, int h, int r, float softmax_scale,
+                                                  QueryLane<NPL>& o) {
   static_assert(NPL == 8 || NPL == 16 || NPL == 32, "8..32 dimensions per lane");
   constexpr int kLanes = 128 / NPL;
-  float x[NPL];
+  float (&x)[NPL] = o.x;
   const uint4* src = reinterpret_cast<const uint4*>(qa + 256 * h + 2 * NPL * r);
 #pragma unroll
   for (int i = 0; i < NPL / 8; ++i) {
@@ -305,20 +328,38 @@ __device__ __forceinline__ void prep_query_lanes(uint8_t* qa, float* sc_out, int
   // scores. A K byte is c * kKMul, so the integer dot product is kKMul times q.c.
   float sc = am > 0.f ? (am / kQiMax) * softmax_scale * kLog2e / (float)Codec<DT>::kKMul : 0.f;
   const bool zero = !(sc != 0.f);
-  const float inv = zero ? 0.f : (sc < 0.f ? -kQiMax : kQiMax) / am;
-  sc = zero ? 1.f : fabsf(sc);
+  o.inv = zero ? 0.f : (sc < 0.f ? -kQiMax : kQiMax) / am;
+  o.sc = zero ? 1.f : fabsf(sc);
+}
+
+// Digits of the lane's dimensions into row `row` of the digit area at qa (and the head's score
+// scale into sc_out[h] from lane r = 0).
+template <int DT, bool PAIRED, int NPL>
+__device__ __forceinline__ void write_query_digits(const QueryLane<NPL>& o, uint8_t* qa, float* sc_out, int h,
+                                                   int row, int r) {
   const int d0 = NPL * r;   // the lane's dimensions are d0 + e, e < NPL, with d0 a multiple of NPL
-  uint8_t* row = qa + 256 * h + 64 * (d0 >> 5) + operand_byte<DT, PAIRED>(d0 & 31);
+  uint8_t* dst = qa + kQRowBytes * row + 32 * kDigits * (d0 >> 5) + operand_byte<DT, PAIRED>(d0 & 31);
 #pragma unroll
   for (int e = 0; e < NPL; ++e) {
-    const int q = (int)rintf(x[e] * inv);
-    const int lo = ((q + 128) & 255) - 128;
-    const int hi = (q - lo) >> 8;
+    // |q| <= kQiMax + 1 (the product rounds once): digits q = 65536 d2 + 256 d1 + d0, each in
+    // [-128, 127]
+    const int q = (int)rintf(o.x[e] * o.inv);
+    const int g0 = ((q + 128) & 255) - 128;
+    const int q1 = (q - g0) >> 8;
+    const int g1 = ((q1 + 128) & 255) - 128;
+    const int g2 = (q1 - g1) >> 8;
     const int off = operand_byte<DT, PAIRED>(e);
-    row[off] = (uint8_t)lo;
-    row[off + 16] = (uint8_t)hi;
+    dst[off] = (uint8_t)g0;
+    dst[off + 16] = (uint8_t)g1;
+    dst[off + 32] = (uint8_t)g2;
   }
-  if (r == 0) sc_out[h] = sc;
+  if (r == 0) sc_out[h] = o.sc;
+}
+
+// q.c from the three digits' integer dot products: 65536 s2 + 256 s1 + s0. Each |s_k| < 2^21,
+// so the low part is exact in int32; the sum is rounded to fp32.
+__device__ __forceinline__ float digit_sum(int s0, int s1, int s2) {
+  return __builtin_fmaf((float)s2, 65536.f, (float)((s1 << 8) + s0));
 }
 
 // ---------------------------------------------------------------------------------------
@@ -622,7 +663,7 @@ struct WaveState {
 // token slots 16 h + r >= lim are masked.
 template <int DT>
 __device__ __forceinline__ void process_tile(const Tile<DT>& t, WaveState& st,
-                                             const v4i (&qi)[2][2], const v8bf (&qb)[4],
+                                             const v4i (&qi)[2][kDigits], const v8bf (&qb)[4],
                                              float qs, int lim, int lim_rows, bool full, int col, int g) {
   // ---- scores: y = log2-domain score; w = y + exponent field of s_v (turbo) --------------------
   float y[8], w[8];
@@ -633,19 +674,21 @@ __device__ __forceinline__ void process_tile(const Tile<DT>& t, WaveState& st,
       v4i a0, a1;
       k_operands<DT>(t, h, a0, a1);
       const v4i z = {0, 0, 0, 0};
-      v4i s0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, qi[0][0], z, 0, 0, 0);
-      s0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, qi[1][0], s0, 0, 0, 0);
-      v4i s1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, qi[0][1], z, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, qi[1][1], s1, 0, 0, 0);
+      v4i s[kDigits];
+#pragma unroll
+      for (int k = 0; k < kDigits; ++k) {
+        s[k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, qi[0][k], z, 0, 0, 0);
+        s[k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, qi[1][k], s[k], 0, 0, 0);
+      }
       const uint32_t ks[4] = {(uint32_t)t.ks[h][0], (uint32_t)t.ks[h][0] >> 16, (uint32_t)t.ks[h][1],
                               (uint32_t)t.ks[h][1] >> 16};
       const uint32_t vs[4] = {(uint32_t)t.vs[h][0], (uint32_t)t.vs[h][0] >> 16, (uint32_t)t.vs[h][1],
                               (uint32_t)t.vs[h][1] >> 16};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int zi = (s1[r] << 8) + s0[r];
+        const float zf = digit_sum(s[0][r], s[1][r], s[2][r]);
         // fma with a zero addend keeps the fp16 operand in a mixed-precision fma
-        y[4 * h + r] = __builtin_fmaf(half_lo(ks[r]), (float)zi * qs, 0.f);
+        y[4 * h + r] = __builtin_fmaf(half_lo(ks[r]), zf * qs, 0.f);
         sv[4 * h + r] = vs[r];
         w[4 * h + r] = y[4 * h + r] + (float)((vs[r] >> 10) & 31u);
       }
@@ -898,16 +941,18 @@ __device__ __forceinline__ v4i pair_k_operand(const PairTile<DT>& t, int m) {
 }
 
 template <int DT>
-__device__ __forceinline__ void process_pair_tile(const PairTile<DT>& t, WaveState& st, const v4i (&qj)[4][2],
+__device__ __forceinline__ void process_pair_tile(const PairTile<DT>& t, WaveState& st, const v4i (&qj)[4][kDigits],
                                                   float qs, int lim, bool full, const PairLane& pl, int G,
                                                   int lane) {
   // ---- scores: y' = s_k * (q.c) in integer-digit units; the log2-domain score is y' * qs ------
-  v4i s0 = {0, 0, 0, 0}, s1 = {0, 0, 0, 0};
+  v4i s[kDigits];
+#pragma unroll
+  for (int k = 0; k < kDigits; ++k) s[k] = v4i{0, 0, 0, 0};
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const v4i a = pair_k_operand<DT>(t, m);
-    s0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qj[m][0], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qj[m][1], s1, 0, 0, 0);
+#pragma unroll
+    for (int k = 0; k < kDigits; ++k) s[k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qj[m][k], s[k], 0, 0, 0);
   }
   const uint32_t ks[4] = {(uint32_t)t.ks[0], (uint32_t)t.ks[0] >> 16, (uint32_t)t.ks[1], (uint32_t)t.ks[1] >> 16};
   uint32_t sv[4] = {(uint32_t)t.vs[0] & 0xffffu, (uint32_t)t.vs[0] >> 16, (uint32_t)t.vs[1] & 0xffffu,
@@ -915,8 +960,7 @@ __device__ __forceinline__ void process_pair_tile(const PairTile<DT>& t, WaveSta
   float y[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int zi = (s1[r] << 8) + s0[r];
-    y[r] = __builtin_fmaf(half_lo(ks[r]), (float)zi, 0.f);
+    y[r] = __builtin_fmaf(half_lo(ks[r]), digit_sum(s[0][r], s[1][r], s[2][r]), 0.f);
   }
   if (!full) {
 #pragma unroll
@@ -1073,9 +1117,9 @@ __device__ __forceinline__ void read_quad_k(QuadK<DT>& t, const uint8_t* slot0, 
 }
 
 template <int DT>
-__device__ __forceinline__ void quad_qk(const QuadK<DT>& t, const v4i (&qq)[8][2], v4i& s0, v4i& s1) {
-  s0 = v4i{0, 0, 0, 0};
-  s1 = v4i{0, 0, 0, 0};
+__device__ __forceinline__ void quad_qk(const QuadK<DT>& t, const v4i (&qq)[8][kDigits], v4i (&s)[kDigits]) {
+#pragma unroll
+  for (int k = 0; k < kDigits; ++k) s[k] = v4i{0, 0, 0, 0};
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
     v4i a;
@@ -1086,8 +1130,8 @@ __device__ __forceinline__ void quad_qk(const QuadK<DT>& t, const v4i (&qq)[8][2
     } else {
       a = t.k[m];
     }
-    s0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qq[m][0], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qq[m][1], s1, 0, 0, 0);
+#pragma unroll
+    for (int k = 0; k < kDigits; ++k) s[k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qq[m][k], s[k], 0, 0, 0);
   }
 }
 
@@ -1177,12 +1221,12 @@ __device__ __forceinline__ void read_quad(QuadData<DT>& d, const uint8_t* slot0,
 
 // One 64-token group, from registers.
 template <int DT>
-__device__ __forceinline__ void process_quad(const QuadData<DT>& d, WaveState& st, const v4i (&qq)[8][2],
+__device__ __forceinline__ void process_quad(const QuadData<DT>& d, WaveState& st, const v4i (&qq)[8][kDigits],
                                              float qs, int lim, bool full, const QuadLane& ql, int G,
                                              int lane) {
   const int gg = lane >> 4;
-  v4i s0, s1;
-  quad_qk<DT>(d.k, qq, s0, s1);
+  v4i s[kDigits];
+  quad_qk<DT>(d.k, qq, s);
   const v2i ksw = d.ksw, vsw = d.vsw;
   const uint32_t ks[4] = {(uint32_t)ksw[0], (uint32_t)ksw[0] >> 16, (uint32_t)ksw[1], (uint32_t)ksw[1] >> 16};
   uint32_t sv[4] = {(uint32_t)vsw[0] & 0xffffu, (uint32_t)vsw[0] >> 16, (uint32_t)vsw[1] & 0xffffu,
@@ -1190,8 +1234,7 @@ __device__ __forceinline__ void process_quad(const QuadData<DT>& d, WaveState& s
   float y[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int zi = (s1[r] << 8) + s0[r];
-    y[r] = __builtin_fmaf(half_lo(ks[r]), (float)zi, 0.f);
+    y[r] = __builtin_fmaf(half_lo(ks[r]), digit_sum(s[0][r], s[1][r], s[2][r]), 0.f);
   }
   if (!full) {
 #pragma unroll
@@ -1276,9 +1319,10 @@ __device__ __forceinline__ void fwht_wave(float (*x)[D + 4], int rows, int lane)
 // in order, keeping kDepth of them in flight, and finishes the unit alone (no cross-wave merge,
 // no barrier in the loop).
 // Waves per SIMD the register budget is sized for: deep rings (4+ slots) are only picked when
-// at most two waves share a SIMD.
+// at most two waves share a SIMD; turbo8's 8 KB slots keep even its two-slot rings at about two
+// waves per SIMD through the LDS, so it takes the two-wave budget at every depth.
 template <int DT, int DEPTH>
-constexpr int kWavesPerEu = DT == 0 ? 1 : (DT == kFp8 ? 2 : (DEPTH >= 4 ? 2 : 3));
+constexpr int kWavesPerEu = DT == 0 ? 1 : (DT == kFp8 || DT == 8 ? 2 : (DEPTH >= 4 ? 2 : 3));
 
 // DEPTH: tiles in flight per wave on the staged path (LDS slots); chosen at launch from how
 // many waves share a compute unit, so that the LDS of the resident waves holds as many tiles
@@ -1405,16 +1449,16 @@ void decode_split_kernel(DecodeParams p) {
   const int col = lane & 15, g = lane >> 4;
 
   // ---- query operands ---------------------------------------------------------------------
-  // turbo types: the wave rotates and quantizes its G query rows itself (prep_query_lanes); the
+  // turbo types: the wave rotates and quantizes its G query rows itself (rotate_query_lane); the
   // rows arrive by LDS DMA ahead of the first tiles, so the work overlaps their latency
   // (paired and quad layouts: decode only, all columns sharing one row)
   const bool pair = kPairOk<DT> && G <= kPairMaxGroup && p.qt == 1;
   const bool quad = kQuadOk<DT> && pair && DEPTH >= 4 && G <= 4;   // the quad-block layout (pair too)
   const PairLane pl = pair_lane(lane, G);
   const QuadLane ql = quad_lane(lane, G);
-  v4i qi[2][2] = {};
-  v4i qj[4][2] = {};
-  v4i qq[8][2] = {};
+  v4i qi[2][kDigits] = {};
+  v4i qj[4][kDigits] = {};
+  v4i qq[8][kDigits] = {};
   v8bf qb[4] = {};
   float qs = 0.f;
   auto issue_query = [&](uint8_t* qa) __attribute__((always_inline)) {   // G rows of 256 B to qa
@@ -1429,19 +1473,47 @@ void decode_split_kernel(DecodeParams p) {
     }
   };
   auto load_query = [&](uint8_t* qa) __attribute__((always_inline)) {    // after the rows have landed in qa
-    float* qsc = reinterpret_cast<float*>(qa + kMaxGroup * 256);
+    float* qsc = reinterpret_cast<float*>(qa + kQueryScaleOff);
     if (G <= 4) {
+      QueryLane<8> qr;
       if (lane < 16 * G) {
-        if (pair) prep_query_lanes<DT, true, 8>(qa, qsc, lane >> 4, lane & 15, p.softmax_scale);
-        else prep_query_lanes<DT, false, 8>(qa, qsc, lane >> 4, lane & 15, p.softmax_scale);
+        rotate_query_lane<DT, 8>(qa, lane >> 4, lane & 15, p.softmax_scale, qr);
+        if (pair) write_query_digits<DT, true, 8>(qr, qa, qsc, lane >> 4, lane >> 4, lane & 15);
+        else write_query_digits<DT, false, 8>(qr, qa, qsc, lane >> 4, lane >> 4, lane & 15);
       }
     } else if (G <= 8) {
+      QueryLane<16> qr;
       if (lane < 8 * G) {
-        if (pair) prep_query_lanes<DT, true, 16>(qa, qsc, lane >> 3, lane & 7, p.softmax_scale);
-        else prep_query_lanes<DT, false, 16>(qa, qsc, lane >> 3, lane & 7, p.softmax_scale);
+        rotate_query_lane<DT, 16>(qa, lane >> 3, lane & 7, p.softmax_scale, qr);
+        if (pair) write_query_digits<DT, true, 16>(qr, qa, qsc, lane >> 3, lane >> 3, lane & 7);
+        else write_query_digits<DT, false, 16>(qr, qa, qsc, lane >> 3, lane >> 3, lane & 7);
       }
-    } else if (lane < 4 * G) {
-      prep_query_lanes<DT, false, 32>(qa, qsc, lane >> 2, lane & 3, p.softmax_scale);
+    } else {
+      // more than kQPhaseRows columns (one-block layout): every lane rotates its rows first; the
+      // digits of heads 0..7 are written, read as operands by their columns, then overwritten by
+      // those of heads 8 and up
+      QueryLane<32> qr;
+      const int h = lane >> 2;
+      if (lane < 4 * G) rotate_query_lane<DT, 32>(qa, h, lane & 3, p.softmax_scale, qr);
+      for (int ph = 0; ph * kQPhaseRows < G; ++ph) {
+        if (lane < 4 * G && h / kQPhaseRows == ph)
+          write_query_digits<DT, false, 32>(qr, qa, qsc, h, h - ph * kQPhaseRows, lane & 3);
+        __syncthreads();
+        if (col < G && col / kQPhaseRows == ph) {
+          const v4i* s = reinterpret_cast<const v4i*>(qa + (col - ph * kQPhaseRows) * kQRowBytes + 32 * kDigits * g);
+#pragma unroll
+          for (int k = 0; k < kDigits; ++k) {
+            qi[0][k] = s[k];
+            qi[1][k] = s[kDigits + k];
+          }
+          qs = qsc[col];
+        }
+        // the operand reads complete before the next phase overwrites the digits, or a later DMA
+        // refills this LDS
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __syncthreads();
+      }
+      return;
     }
     __syncthreads();
     if (quad) {
@@ -1449,9 +1521,10 @@ void decode_split_kernel(DecodeParams p) {
       if (ql.jn == g) {
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-          const v4i* s = reinterpret_cast<const v4i*>(qa + (ql.hn * 4 + (m >> 1)) * 64 + 32 * (m & 1));
-          qq[m][0] = s[0];
-          qq[m][1] = s[1];
+          const v4i* s = reinterpret_cast<const v4i*>(qa + ql.hn * kQRowBytes + (m >> 1) * 32 * kDigits +
+                                                      16 * kDigits * (m & 1));
+#pragma unroll
+          for (int k = 0; k < kDigits; ++k) qq[m][k] = s[k];
         }
       }
       qs = qsc[ql.hn];
@@ -1460,15 +1533,19 @@ void decode_split_kernel(DecodeParams p) {
       if (pl.jn == pl.kb) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const v4i* s = reinterpret_cast<const v4i*>(qa + (pl.hn * 4 + m) * 64 + 32 * pl.kp);
-          qj[m][0] = s[0];
-          qj[m][1] = s[1];
+          const v4i* s = reinterpret_cast<const v4i*>(qa + pl.hn * kQRowBytes + m * 32 * kDigits + 16 * kDigits * pl.kp);
+#pragma unroll
+          for (int k = 0; k < kDigits; ++k) qj[m][k] = s[k];
         }
       }
       qs = qsc[pl.hn];
     } else if (col < G) {
-      const v4i* s = reinterpret_cast<const v4i*>(qa + (col * 4 + g) * 64);
-      qi[0][0] = s[0]; qi[0][1] = s[1]; qi[1][0] = s[2]; qi[1][1] = s[3];
+      const v4i* s = reinterpret_cast<const v4i*>(qa + col * kQRowBytes + 32 * kDigits * g);
+#pragma unroll
+      for (int k = 0; k < kDigits; ++k) {
+        qi[0][k] = s[k];
+        qi[1][k] = s[kDigits + k];
+      }
       qs = qsc[col];
     }
     // the operand reads complete before a later DMA may refill this LDS

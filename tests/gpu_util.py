@@ -8,6 +8,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
+import oracle
 import workloads
 from bit_quantized_paged_turbo_amd.cache import PagedKVCache
 
@@ -83,3 +84,30 @@ def gather(pool: np.ndarray, W: workloads.Workload, block_bytes: int, b: int, po
                    for h in range(hkv)], axis=1)
     scales = sc[..., 0].astype(np.uint16) | (sc[..., 1].astype(np.uint16) << 8)
     return codes, scales
+
+
+def hadamard_sign_rows(ks) -> np.ndarray:
+    """Rows k of the unnormalised Sylvester sign pattern, (-1)^popcount(i & k) over i < 128: a
+    query shaped like this rotates to a multiple of one basis vector (test input only)."""
+    i = np.arange(128)
+    par = np.zeros((len(ks), 128), np.int64)
+    x = np.asarray(ks)[:, None] & i[None, :]
+    while np.any(x):
+        par ^= x & 1
+        x >>= 1
+    return np.where(par == 1, -1.0, 1.0)
+
+
+def dominant_queries(qb: np.ndarray, kind, seed: int) -> np.ndarray:
+    """Queries whose rotation has one dominant element: the draw plus a constant (which rotates
+    to offset * sqrt(128) on element 0), or a signed Hadamard row plus N(0, 0.3^2) noise (which
+    rotates to +-sqrt(128) on another element). bf16 bits of qb's shape."""
+    q = oracle.bf16_bits_to_f32(qb)
+    if kind == "had":
+        r = np.random.default_rng(seed)
+        rows = hadamard_sign_rows(r.integers(0, 128, size=q.shape[:-1]).reshape(-1))
+        sign = r.choice([-1.0, 1.0], size=(rows.shape[0], 1))
+        q = (sign * rows).reshape(q.shape) + 0.3 * r.standard_normal(q.shape)
+    else:
+        q = q + np.float32(kind)
+    return workloads.round_to_bf16_bits(q.astype(np.float32))

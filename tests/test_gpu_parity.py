@@ -12,7 +12,7 @@ import oracle
 import workloads
 import bit_quantized_paged_turbo_amd as xq
 from bit_quantized_paged_turbo_amd import xq_block_bytes
-from tests.gpu_util import fill, gather, make_cache, to_dev, upload_tables
+from tests.gpu_util import dominant_queries, fill, gather, make_cache, to_dev, upload_tables
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
@@ -301,6 +301,54 @@ def test_query_and_scale_edge_cases(dtype, hq):
             assert err <= TOL, f"scale {scale} seq {b}: {err:.3e}"
 
 
+# The presets (reduced) plus shapes with more than 8 query heads per kv head, whose queries are
+# prepared in two passes of eight rows.
+DOMINANT = [
+    ("c0-turbo4", dict(cfg=0)),
+    ("c1-turbo4-b16", dict(cfg=1, batch=16)),
+    ("c2-turbo8-b2", dict(cfg=2, dtype=8, batch=2, scale=1 / 8)),
+    ("c2-turbo4-b2", dict(cfg=2, dtype=4, batch=2, scale=1 / 8)),
+    ("c3-turbo3", dict(cfg=3, scale=1 / 64)),
+    ("c3-turbo2", dict(cfg=3, dtype=2, scale=1 / 64)),
+    ("c2-fp8-b2", dict(cfg=2, dtype=16, batch=2, scale=1 / 8)),
+    ("c2-bf16-b2", dict(cfg=2, dtype=0, batch=2, scale=1 / 8)),
+    ("g16-turbo4", dict(dtype=4, hq=16, hkv=1)),
+    ("g12-turbo8", dict(dtype=8, hq=12, hkv=1)),
+    ("g16-turbo3", dict(dtype=3, hq=32, hkv=2)),
+    ("g10-turbo2", dict(dtype=2, hq=10, hkv=1)),
+]
+
+
+@pytest.mark.parametrize("name,spec", DOMINANT, ids=[d[0] for d in DOMINANT])
+def test_queries_with_a_dominant_rotated_element(name, spec):
+    """The score precision must hold relative to each rotated query element, not only to the
+    head's largest: constant offsets 1, 2, 3, 10, 30 on the preset draw and Hadamard-row queries,
+    over keys with outlier channels (x20 on the c0/c1 shapes, x30 on c2's), at split counts 0
+    and 5, every sequence against the oracle."""
+    _print_case("dominant", name)
+    if "cfg" in spec:
+        W = workloads.config(spec["cfg"], dtype=spec.get("dtype"), batch=spec.get("batch"),
+                             context_scale=spec.get("scale", 1.0))
+    else:
+        W = workloads.make(name, 450 + spec["dtype"], spec["dtype"], [1, 130, 700], spec["hq"],
+                           spec["hkv"], 16, outlier_channels=8, outlier_scale=30.0)
+    cache = make_cache(W)
+    bt, cl = upload_tables(W)
+    kv = {b: W.kv_bits(b) for b in range(W.num_seqs)}
+    fill(cache, W, bt, kv=kv)
+    worst = 0.0
+    for kind in (1, 2, 3, 10, 30, "had"):
+        qb = dominant_queries(W.q_bits(), kind, seed=W.cfg)
+        for splits in (0, 5):
+            got = _decode(W, cache, bt, cl, splits, to_dev(qb))
+            for b in range(W.batch):
+                want = _oracle_out(W, b, qb, kv[b])
+                err = np.max(np.abs(got[b] - want))
+                worst = max(worst, err)
+                assert err <= TOL, f"{name} query {kind} splits {splits} seq {b}: max abs err {err:.3e}"
+    print(f"{name}: worst max abs err {worst:.3e}", flush=True)
+
+
 @pytest.mark.parametrize("dtype,hq", [(4, 16), (4, 96), (3, 40), (0, 16), (2, 16), (16, 32)])
 def test_pool_beyond_4gib(dtype, hq):
     """Pools larger than 4 GiB take per-page buffer descriptors and 64-bit page offsets; the
@@ -378,9 +426,11 @@ def test_splits_agree_and_repeat_is_deterministic():
     # fp16 weight split (~22 bits) and the matrix-core accumulation (measured loss below 2^-18
     # of a code step per accumulation) round differently; the inverse rotation sums the 128
     # rotated dimensions into output dimension 0, where such same-signed rounding adds up.
+    # Measured on MI355X: 1.4e-5 at most over 2, 8 and 64 splits.
     for s in (2, 8, 64):
         c = _decode(W, cache, bt, cl, s, q)
-        assert np.max(np.abs(c - a)) < 1e-4
+        print(f"splits {s} against 1: max abs difference {np.max(np.abs(c - a)):.3e}", flush=True)
+        assert np.max(np.abs(c - a)) < 2e-5
 
 
 def test_page_placement_does_not_change_output():

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import workloads
-from tests.gpu_util import fill, make_cache, to_dev, upload_tables
+from tests.gpu_util import dominant_queries, fill, make_cache, to_dev, upload_tables
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
@@ -46,6 +46,32 @@ def test_prefill_matches_oracle(dtype, start, chunk, hq, hkv, ps):
         got = out.cpu().numpy().astype(np.float64)
         err = np.max(np.abs(got - want), axis=(1, 2))
         assert np.all(err <= TOL), f"splits {splits}: worst query {int(np.argmax(err))} err {err.max():.3e}"
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,ps", [(8, 32, 8, 16), (4, 32, 8, 16), (3, 40, 8, 64), (2, 8, 8, 16),
+                                            (4, 16, 1, 32), (16, 32, 8, 16)])
+def test_prefill_queries_with_a_dominant_rotated_element(dtype, hq, hkv, ps):
+    """Chunk queries whose rotation has one dominant element (constant offsets 3 and 30, Hadamard
+    rows): a prefill unit packs up to 16 (query, head) columns, so its queries are prepared in two
+    passes of eight rows; every query against the oracle."""
+    _case("prefill-dominant", dtype, hq, hkv, ps)
+    start, chunk = 100, 40
+    W = workloads.make(f"prefill-dom-{dtype}", 880 + dtype, dtype, [start + chunk], hq, hkv, ps,
+                       outlier_channels=8, outlier_scale=30.0)
+    cache = make_cache(W)
+    bt, _ = upload_tables(W)
+    k, v = W.kv_bits(0)
+    fill(cache, W, bt, kv={0: (k, v)})
+    r = np.random.default_rng(dtype)
+    q0 = workloads.round_to_bf16_bits(r.standard_normal((chunk, hq, 128)).astype(np.float32))
+    for kind in (3, 30, "had"):
+        q = dominant_queries(q0, kind, seed=dtype)
+        want = oracle.prefill_sequence(dtype, q, k, v, start, W.softmax_scale)
+        for splits in (0, 3):
+            out = cache.prefill(to_dev(q), bt[0], start, W.softmax_scale, splits)
+            torch.cuda.synchronize()
+            err = np.max(np.abs(out.cpu().numpy().astype(np.float64) - want), axis=(1, 2))
+            assert np.all(err <= TOL), f"query {kind} splits {splits}: worst {int(np.argmax(err))} err {err.max():.3e}"
 
 
 @pytest.mark.parametrize("hq,hkv,exact", [(16, 1, True), (16, 8, False), (32, 8, False)])
