@@ -1,42 +1,47 @@
 """Benchmark of one decode step over a TurboQuant paged KV cache on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4] [--no-cpu]
 
-A step is one pass of the whole hot path for one layer of a decode batch:
-  1. the new K/V rows are rotated, quantized, packed and stored in their pages: every
-     sequence's new row, plus the prefill chunk where the workload has one;
+A step is one pass of the whole hot path for one layer:
+  1. new K/V rows are rotated, quantized, packed and stored in their pages: every decoded
+     sequence's new row, plus the prefill chunk where the workload has one (the default, the
+     mixed step: a 2,048-token chunk appended for a new sequence, then a batch of 64 decodes);
   2. decode attention over every sequence's paged, quantized context.
-By default one xq_append_decode_attention launch does both for the decode batch (a chunk still
-goes through xq_quantize_append first); --no-fuse runs xq_quantize_append and the decode as two
-launches. The decode uses the host plan (xq_decode_plan) unless --no-plan.
+By default one xq_append_decode_attention launch appends the batch's new rows and decodes (the
+chunk goes through xq_quantize_append first); --no-fuse runs xq_quantize_append and the decode
+as two launches. The decode uses the host plan (xq_decode_plan) unless --no-plan.
 
 Steps are timed twice, K each after W warm-up steps: eagerly, with HIP events around every
-decode call (the roofline's launch duration), and replayed from HIP graphs captured per pool
-replica, the way a serving engine replays its decode step; when every replica has its graph,
-also from one graph holding a step on each replica in turn, as a model's decode graph holds one
-step per layer (K steps = K // R replays of it + K mod R single-step replays). `value` and
-`ms_per_step` come from that graph, else from the single-step graphs when every replica has
-one, else (--no-graph) from the eager launches; all figures are in `step_timing`.
-The new row of sequence b goes to position L_b - 1, so every step has the same shape and
-the cache content stays what the oracle computes.
+decode call and every append call (on the stream they are launched on), and replayed from HIP
+graphs captured per pool replica, the way a serving engine replays its decode step; when every
+replica has its graph, also from one graph holding a step on each replica in turn, as a model's
+decode graph holds one step per layer. `value` and `ms_per_step` come from the graph replay,
+else (--no-graph) from the eager launches; all figures are in `step_timing`. The new row of
+sequence b goes to position L_b - 1, so every step has the same shape and the cache content
+stays what the oracle computes.
 
-Inputs are seeded synthetic draws (workloads/), resident in HBM before timing starts.
-Steps rotate over R copies of the K/V pools, R x footprint >= 1 GiB, so the 256 MB
-Infinity Cache cannot serve the KV reads of one step from the previous ones.
+Inputs are seeded synthetic draws (workloads/), resident in HBM before timing starts. Steps
+rotate over R copies of the K/V pools, R x footprint >= 1 GiB, so the 256 MB Infinity Cache
+cannot serve one step's KV reads from the previous ones.
 
-Prints ONE JSON line. `value` is KV GB/s: the algorithmic KV bytes the decode reads per
-step (sum_b L_b * Hkv * 2 * row_bytes) over the whole step time. `roofline` is for the
-decode call, which is the dominant work of the step: decode_split_kernel and, when a
-sequence spans several partitions, decode_combine_kernel, timed together with HIP events
-around each decode call on its stream inside the timed region (the rocprofv3 summary under
-profiles/ lists the kernels separately); `traffic` is the measured HBM bytes of
-those kernels per call. `cpu_baseline` is the oracle on the host cores.
+Prints ONE JSON line. `value` is KV GB/s: the algorithmic KV bytes the decode reads per step
+(sum_b L_b * Hkv * 2 * row_bytes) over the whole step time. `roofline` is for the decode call,
+the dominant work of the step (decode_split_kernel, plus decode_combine_kernel when a sequence
+spans several partitions): achieved = those bytes / the mean of the HIP-event durations of the
+decode calls in the timed region; `frac_kernel_trace` is the same bytes over the kernels' mean
+duration in the committed rocprofv3 summary of this command (while the kernel sources are the
+ones it was taken on); `traffic` is the HBM bytes the counters measured per call.
+`hbm_reference` is a plain streaming-read kernel over 4 GiB (sequentially, and in 1 KiB blocks
+gathered in a random order, the decode's pattern). `append` reports the quantize-append kernel's
+own rate. `cpu_baseline` is the oracle (oracle/, float64 attention over the quantized cache) on
+the host's cores, in worker processes started before anything touches the GPU.
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
+import multiprocessing as mp
 import os
 import re
 import sys
@@ -52,25 +57,35 @@ import workloads  # noqa: E402  (seeded inputs; no arithmetic of the method)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 PROFILES = os.path.join(ROOT, "profiles")
-DECODE_SRC = os.path.join(ROOT, "bit_quantized_paged_turbo_amd", "csrc", "decode_attention.hip")
+CSRC = os.path.join(ROOT, "bit_quantized_paged_turbo_amd", "csrc")
+DECODE_SOURCES = [os.path.join(CSRC, f) for f in ("decode_attention.hip", "row_codec.h")]
+MAX_WORKERS = 16               # the machine's CPU share for one GPU
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", type=int, default=1, help="workload preset 0..4 (default 1)")
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=4, help="workload preset 0..4 (default 4, the mixed step)")
     ap.add_argument("--dtype", type=int, default=None, help="override the preset's cache type")
     ap.add_argument("--splits", type=int, default=None, help="override the split hint")
     ap.add_argument("--replica-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--cpu-workers", type=int, default=None,
+                    help="oracle worker processes (default: the host's cores, at most 16)")
+    ap.add_argument("--cpu-reps", type=int, default=3, help="timed oracle repetitions (median)")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunk-prefill timing")
+    ap.add_argument("--no-probe", action="store_true", help="skip the streaming-read reference")
     ap.add_argument("--no-plan", action="store_true", help="decode without the host plan")
     ap.add_argument("--no-fuse", action="store_true",
                     help="append the batch's new rows in their own launch instead of the decode's")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--serial-draws", action="store_true",
+                    help="draw the inputs in this process (no worker pool; for profiler runs, whose "
+                         "library has the GPU initialised before the program starts)")
+    ap.add_argument("--inputs-cache", default=None,
+                    help="an .npz of the drawn K/V rows: loaded if it exists, else written after drawing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run plain 512 MiB device copies (a known byte count for "
                          "scaling HBM counters)")
@@ -85,27 +100,181 @@ def row_bytes(dtype: int) -> int:
     return 256 if dtype == 0 else 128 if dtype == workloads.FP8 else 16 * dtype + 2
 
 
-def source_digest(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def sources_digest() -> str:
+    h = hashlib.sha256()
+    for path in DECODE_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def committed_traffic(kernel_tag: str):
-    """HBM bytes per launch from a committed counter summary, or None when there is none
-    or the decode kernel's source has changed since the counters were taken."""
-    path = os.path.join(PROFILES, f"{kernel_tag}_pmc.txt")
-    if not os.path.exists(path):
-        return None
-    text = open(path).read()
-    m = re.search(r"source_sha256_16:\s*([0-9a-f]{16})", text)
-    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m or not t or m.group(1) != source_digest(DECODE_SRC):
-        return None
-    return float(t.group(1))
+def committed_profile(tag: str):
+    """Figures from the committed rocprofv3 summaries of this workload, or None where there is no
+    summary or the decode sources have changed since it was taken: (kernel-trace mean
+    microseconds of the decode call's kernels, HBM bytes per call from the counters)."""
+    out = {}
+    for kind, key in (("kernel_trace", "decode_call_kernel_us"), ("pmc", "hbm_bytes_per_launch")):
+        path = os.path.join(PROFILES, f"{tag}_{kind}.txt")
+        if not os.path.exists(path):
+            continue
+        text = open(path).read()
+        m = re.search(r"sources_sha256_16:\s*([0-9a-f]{16})", text)
+        t = re.search(key + r":\s*([0-9.eE+]+)", text)
+        if m and t and m.group(1) == sources_digest():
+            out[key] = float(t.group(1))
+    return out
 
 
+def host_info() -> dict:
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "cpu_model": model}
+
+
+# ---------------------------------------------------------------------------------------------
+# Host work in worker processes, forked before the GPU is touched: the seeded draws (which the
+# GPU's cache is filled from) and the oracle baseline.
+# ---------------------------------------------------------------------------------------------
+_W = None
+
+
+def _pool_init(cfg, dtype):
+    global _W
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)
+    _W = workloads.config(cfg, dtype=dtype)
+
+
+def _draw(b):
+    return b, _W.kv_bits(b)
+
+
+def _balanced(lens, n):
+    """Sequences dealt to n workers, longest first, each to the least loaded."""
+    loads, parts = [0] * n, [[] for _ in range(n)]
+    for b in sorted(range(len(lens)), key=lambda i: -int(lens[i])):
+        w = int(np.argmin(loads))
+        parts[w].append(b)
+        loads[w] += int(lens[b])
+    return parts
+
+
+def _oracle_worker(wid, cfg, dtype, seqs, chunk_rows, reps, barrier, results):
+    """One oracle worker: its sequences' context rows quantized once (untimed), then per
+    repetition (the first a warm-up), between barriers: (a) quantize the step's new rows (each of
+    its sequences' row L - 1 and its slice of the chunk), (b) decode its sequences in float64 over
+    the quantized context."""
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)
+    import oracle
+    W = workloads.config(cfg, dtype=dtype)
+    fp8 = W.dtype == workloads.FP8
+    ctx, new = {}, {}
+    for b in seqs:
+        k, v = W.kv_bits(b)
+        new[b] = (k[-1:], v[-1:])
+        if W.dtype == 0:
+            ctx[b] = (k[:-1], v[:-1])
+        elif fp8:
+            ctx[b] = (oracle.fp8_encode_rows_bf16(k[:-1]), oracle.fp8_encode_rows_bf16(v[:-1]))
+        else:
+            ctx[b] = (oracle.quantize_rows_bf16(k[:-1], W.dtype), oracle.quantize_rows_bf16(v[:-1], W.dtype))
+    chunk = None
+    if chunk_rows is not None:
+        k, v = W.kv_bits(W.batch)
+        chunk = (k[chunk_rows[0]:chunk_rows[1]], v[chunk_rows[0]:chunk_rows[1]])
+    qb = W.q_bits()
+
+    def encode(rows):
+        if W.dtype == 0:
+            return rows
+        if fp8:
+            return oracle.fp8_encode_rows_bf16(rows)
+        return oracle.quantize_rows_bf16(rows, W.dtype)
+
+    times = []
+    for _ in range(reps + 1):
+        barrier.wait()
+        t0 = time.perf_counter()
+        enc = {b: (encode(new[b][0]), encode(new[b][1])) for b in seqs}
+        if chunk is not None:
+            encode(chunk[0])
+            encode(chunk[1])
+        t1 = time.perf_counter()
+        barrier.wait()
+        t2 = time.perf_counter()
+        for b in seqs:
+            (kc, vc), (kn, vn) = ctx[b], enc[b]
+            if W.dtype == 0:
+                oracle.decode_attention_bf16(qb[b], np.concatenate([kc, kn]), np.concatenate([vc, vn]),
+                                             W.softmax_scale)
+            elif fp8:
+                oracle.decode_attention_fp8(qb[b], np.concatenate([kc, kn]), np.concatenate([vc, vn]),
+                                            W.softmax_scale)
+            else:
+                oracle.decode_attention_turbo(qb[b], np.concatenate([kc[0], kn[0]]), np.concatenate([kc[1], kn[1]]),
+                                              np.concatenate([vc[0], vn[0]]), np.concatenate([vc[1], vn[1]]),
+                                              W.softmax_scale)
+        t3 = time.perf_counter()
+        times.append((t0, t1, t2, t3))
+    results.put((wid, times))
+
+
+def cpu_baseline(W, workers: int, reps: int) -> dict:
+    """The oracle on `workers` host processes (one thread each) over the whole step of the
+    workload: quantize the step's new rows, then decode every sequence; each phase timed across
+    all workers (earliest start to latest end), median of `reps` after one warm-up."""
+    ctx = mp.get_context("fork")
+    parts = _balanced(W.context_lens, workers)
+    chunk_parts = [None] * workers
+    if W.chunk_tokens:
+        edges = np.linspace(0, W.chunk_tokens, workers + 1).astype(int)
+        chunk_parts = [(int(edges[i]), int(edges[i + 1])) for i in range(workers)]
+    barrier = ctx.Barrier(workers)
+    results = ctx.Queue()
+    procs = [ctx.Process(target=_oracle_worker, args=(w, W.cfg, W.dtype, parts[w], chunk_parts[w], reps, barrier,
+                                                      results)) for w in range(workers)]
+    t_start = time.perf_counter()
+    for p in procs:
+        p.start()
+    got = [results.get() for _ in procs]
+    for p in procs:
+        p.join()
+        if p.exitcode != 0:
+            raise RuntimeError(f"oracle worker exited with {p.exitcode}")
+    wall = time.perf_counter() - t_start
+    quant, dec = [], []
+    for r in range(1, reps + 1):
+        quant.append(max(t[r][1] for _, t in got) - min(t[r][0] for _, t in got))
+        dec.append(max(t[r][3] for _, t in got) - min(t[r][2] for _, t in got))
+    tq, td = float(np.median(quant)), float(np.median(dec))
+    kv_bytes = int(W.context_lens.astype(np.int64).sum()) * W.num_kv_heads * 2 * row_bytes(W.dtype)
+    tokens = int(W.context_lens.sum())
+    new_rows = (W.batch + W.chunk_tokens) * W.num_kv_heads * 2
+    return {"value": round(kv_bytes / (tq + td) / 1e9, 4), "unit": "GB/s",
+            "seq_tokens_per_s": round(tokens / (tq + td), 1), "cores": workers, "kind": "oracle",
+            "quantize_s": round(tq, 5), "decode_s": round(td, 5),
+            "quantize_rows_per_s": round(new_rows / tq, 1), "decode_kv_GBps": round(kv_bytes / td / 1e9, 4),
+            "reps": reps, "wall_s_incl_setup": round(wall, 2), **host_info(),
+            "sample": f"the whole step of {W.name}: quantize its {new_rows} new K/V rows "
+                      f"({W.chunk_tokens}-token chunk + one row per sequence), then float64 decode of "
+                      f"all {W.batch} sequences ({tokens} context tokens) over the quantized cache; "
+                      f"{workers} worker processes x 1 thread, each phase timed from the earliest "
+                      f"worker start to the latest end, median of {reps} after a warm-up; the "
+                      f"context rows are quantized once beforehand, untimed"}
+
+
+# ---------------------------------------------------------------------------------------------
+# GPU side
+# ---------------------------------------------------------------------------------------------
 class Step:
-    """Precomputed ctypes arguments for the two calls of one step on one replica."""
+    """Precomputed ctypes arguments for the calls of one step on one replica."""
 
     def __init__(self, lib, layout, cache, app, dec):
         import ctypes
@@ -117,12 +286,10 @@ class Step:
     def run(self, stream: int):
         if self.app is None:            # the fused step appends inside the decode launch
             return
-        lib = self.lib
         c = self.cache
-        kp, vp = c.k_pool.data_ptr(), c.v_pool.data_ptr()
-        st = lib.xq_quantize_append(self.L, *self.app, kp, vp, stream)
+        st = self.lib.xq_quantize_append(self.L, *self.app, c.k_pool.data_ptr(), c.v_pool.data_ptr(), stream)
         if st:
-            raise RuntimeError(lib.xq_last_error().decode())
+            raise RuntimeError(self.lib.xq_last_error().decode())
 
     def decode(self, stream: int):
         lib = self.lib
@@ -144,7 +311,50 @@ class Step:
             raise RuntimeError(lib.xq_last_error().decode())
 
 
-def time_prefill(lib, cache, W, bt, to_dev, stream, K, Wm):
+def event_pairs(n):
+    import torch
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+
+def hbm_reference(xq, stream, reps: int = 5) -> dict:
+    """A plain streaming-read kernel over 4 GiB: one sequential stream, and 1 KiB blocks in a
+    random order (the decode's gather of page blocks). Best and median of `reps` launches.
+    `stream` is the torch stream: events are recorded on it, the library gets its handle."""
+    import torch
+    assert isinstance(stream, torch.cuda.Stream)
+    sh = stream.cuda_stream
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(0x5A)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    nblk = nbytes // 1024
+    order_h = np.random.default_rng(11).permutation(nblk).astype(np.int32)
+    assert order_h.min() >= 0 and order_h.max() < nblk          # every block inside buf
+    order = torch.from_numpy(order_h).cuda()
+    out = {}
+    # sequential: 64 KiB blocks back to back; gather: 1 KiB blocks in a random order
+    for name, blocks, bb, od in (("sequential", nbytes // 65536, 65536, None), ("gather_1KiB", nblk, 1024, order)):
+        for _ in range(2):
+            xq.xq_hbm_read_probe(buf, nbytes, blocks, bb, bb, od, sink, sh)
+        ev = event_pairs(reps)
+        for a, b in ev:
+            a.record(stream)
+            xq.xq_hbm_read_probe(buf, nbytes, blocks, bb, bb, od, sink, sh)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = np.array([a.elapsed_time(b) for a, b in ev])
+        out[name + "_GBps"] = {"best": round(nbytes / (ms.min() * 1e-3) / 1e9, 1),
+                               "median": round(nbytes / (np.median(ms) * 1e-3) / 1e9, 1)}
+    del buf, order
+    torch.cuda.empty_cache()
+    out["bytes"] = nbytes
+    out["note"] = ("xq_hbm_read_probe: non-temporal 16 B loads, 1 KiB per wave instruction, four in "
+                   "flight per lane; HIP events around each launch")
+    log(f"HBM reference: {out}")
+    return out
+
+
+def time_prefill(cache, W, bt, to_dev, stream, K, Wm):
     """The chunk's queries attending causally to the chunk (xq_paged_prefill_attention from
     position 0 over the chunk's appended rows): HIP events around each call on its stream."""
     import torch
@@ -155,82 +365,19 @@ def time_prefill(lib, cache, W, bt, to_dev, stream, K, Wm):
     for _ in range(Wm):
         cache.prefill(q, row, 0, W.softmax_scale)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    for i in range(K):
-        ev[i][0].record(stream)
+    ev = event_pairs(K)
+    for a, b in ev:
+        a.record(stream)
         cache.prefill(q, row, 0, W.softmax_scale)
-        ev[i][1].record(stream)
+        b.record(stream)
     torch.cuda.synchronize()
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     pairs = n * (n + 1) // 2                      # (query, key) pairs of the causal chunk
     flops = 4 * 128 * hq * pairs                  # QK and PV multiply-adds
-    rows_bytes = n * W.num_kv_heads * 2 * row_bytes(W.dtype)
     log(f"prefill of the {n}-token chunk: {ms * 1e3:.1f} us")
     return {"queries": n, "start": 0, "call_us": round(ms * 1e3, 2),
             "query_tokens_per_s": round(n / (ms * 1e-3), 1),
-            "tflops": round(flops / (ms * 1e-3) / 1e12, 3), "flops_per_call": flops,
-            "kv_bytes_once": rows_bytes,
-            "note": "the decode kernel with 16/g query tokens x g heads in the 16 matrix-core "
-                    "columns of a unit; each unit reads its causal prefix (from L2/MALL for this "
-                    "chunk)"}
-
-
-def cpu_baseline(W, seconds: float):
-    """The oracle on the host: per sequence, quantize its new row and attend over its
-    (already quantized) context, sequence after sequence, for about `seconds`."""
-    import oracle
-    from threadpoolctl import threadpool_limits
-    with threadpool_limits(1):              # one host thread (numpy's own loops are serial)
-        return _cpu_baseline(oracle, W, seconds)
-
-
-def _cpu_baseline(oracle, W, seconds: float):
-    qb = W.q_bits()
-    rb = row_bytes(W.dtype)
-    done_seqs = done_bytes = done_tokens = 0
-    elapsed = 0.0
-    prepared = {}                    # sequence -> its context rows, quantized once, untimed
-    b = 0
-    while elapsed < seconds:
-        if b not in prepared:
-            k, v = W.kv_bits(b)
-            if W.dtype == workloads.FP8:
-                prepared[b] = (k[-1:], v[-1:], oracle.fp8_encode_rows_bf16(k[:-1]),
-                               oracle.fp8_encode_rows_bf16(v[:-1]))
-            elif W.dtype:
-                prepared[b] = (k[-1:], v[-1:], oracle.quantize_rows_bf16(k[:-1], W.dtype),
-                               oracle.quantize_rows_bf16(v[:-1], W.dtype))
-            else:
-                prepared[b] = (k, v)
-        t0 = time.perf_counter()
-        if W.dtype == workloads.FP8:
-            k1, v1, kf, vf = prepared[b]
-            kf2 = np.concatenate([kf, oracle.fp8_encode_rows_bf16(k1)])
-            vf2 = np.concatenate([vf, oracle.fp8_encode_rows_bf16(v1)])
-            oracle.decode_attention_fp8(qb[b], kf2, vf2, W.softmax_scale)
-        elif W.dtype:
-            k1, v1, (kc, ks), (vc, vs) = prepared[b]
-            nk = oracle.quantize_rows_bf16(k1, W.dtype)
-            nv = oracle.quantize_rows_bf16(v1, W.dtype)
-            kc2, ks2 = np.concatenate([kc, nk[0]]), np.concatenate([ks, nk[1]])
-            vc2, vs2 = np.concatenate([vc, nv[0]]), np.concatenate([vs, nv[1]])
-            oracle.decode_attention_turbo(qb[b], kc2, ks2, vc2, vs2, W.softmax_scale)
-        else:
-            k, v = prepared[b]
-            oracle.decode_attention_bf16(qb[b], k, v, W.softmax_scale)
-        elapsed += time.perf_counter() - t0
-        L = int(W.context_lens[b])
-        done_seqs += 1
-        done_tokens += L
-        done_bytes += L * W.num_kv_heads * 2 * rb
-        if done_seqs % 256 == 0:
-            log(f"oracle: {done_seqs} sequences, {elapsed:.1f} s timed")
-        b = (b + 1) % W.batch
-    return {"value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s",
-            "seq_tokens_per_s": round(done_tokens / elapsed, 1), "cores": 1, "kind": "oracle",
-            "sample": f"{done_seqs} sequence-decodes cycling over sequences of the same "
-                      f"workload: quantize the step's new K/V row, then float64 decode "
-                      f"attention over the quantized context; {elapsed:.1f} s on 1 host thread"}
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 3), "flops_per_call": flops}
 
 
 def main():
@@ -240,9 +387,34 @@ def main():
               f"(the decode path runs on one GPU with no collectives)", file=sys.stderr)
         sys.exit(2)
 
+    W = workloads.config(args.config, dtype=args.dtype)
+    log(f"workload {W.name}: batch {W.batch}, {W.total_tokens()} context tokens")
+    splits = W.num_splits if args.splits is None else args.splits
+    workers = max(1, min(MAX_WORKERS, args.cpu_workers or len(os.sched_getaffinity(0))))
+
+    # ---- host work first, in processes forked before any GPU call --------------------------------
+    cpu = None
+    if not args.no_cpu:
+        log(f"oracle baseline on {workers} host processes")
+        cpu = cpu_baseline(W, workers, args.cpu_reps)
+        log(f"oracle: quantize {cpu['quantize_s'] * 1e3:.1f} ms, decode {cpu['decode_s'] * 1e3:.1f} ms per step")
+    t0 = time.perf_counter()
+    if args.inputs_cache and os.path.exists(args.inputs_cache):
+        with np.load(args.inputs_cache) as z:
+            drawn = {b: (z[f"k{b}"], z[f"v{b}"]) for b in range(W.num_seqs)}
+        log(f"inputs loaded from {args.inputs_cache} in {time.perf_counter() - t0:.1f} s")
+    else:
+        if args.serial_draws:
+            drawn = {b: W.kv_bits(b) for b in range(W.num_seqs)}
+        else:
+            with mp.get_context("fork").Pool(workers, initializer=_pool_init, initargs=(W.cfg, W.dtype)) as pool:
+                drawn = dict(pool.imap_unordered(_draw, range(W.num_seqs), chunksize=1))
+        log(f"inputs drawn in {time.perf_counter() - t0:.1f} s")
+        if args.inputs_cache:
+            np.savez(args.inputs_cache, **{f"{n}{b}": a for b, kv in drawn.items() for n, a in zip("kv", kv)})
+
     import torch
     import bit_quantized_paged_turbo_amd as xq
-    import workloads
     from bit_quantized_paged_turbo_amd.cache import PagedKVCache
 
     lib = xq.load()
@@ -251,6 +423,8 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
     dev = "cuda"
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
 
     if args.copy_calibration:
         n = 512 << 20
@@ -262,25 +436,21 @@ def main():
         del src, dst
         log(f"copy calibration: 3 copies of {n} bytes")
 
-    W = workloads.config(args.config, dtype=args.dtype)
-    log(f"workload {W.name}: batch {W.batch}, {W.total_tokens()} context tokens")
-    splits = W.num_splits if args.splits is None else args.splits
-
     def to_dev(a):
         a = np.ascontiguousarray(a)
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
-    # ---- fill one replica with every sequence's context through the append path --------
+    # ---- fill one replica with every sequence's context through the append path, timed ---------
     base = PagedKVCache(W.dtype, W.num_kv_heads, W.page_size, W.num_pages)
     bt = to_dev(W.block_tables.astype(np.int32))
     last_k, last_v = [], []
     chunk_kv = None
-    pend = []
+    pend, batches = [], []
     for b in range(W.num_seqs):
         L = W.seq_len(b)
-        k, v = W.kv_bits(b)
+        k, v = drawn.pop(b)
         if b < W.batch:
             last_k.append(k[-1])
             last_v.append(v[-1])
@@ -288,12 +458,21 @@ def main():
             chunk_kv = (k, v)
         pend.append((k, v, np.full(L, b, np.int32), np.arange(L, dtype=np.int32)))
         if sum(len(p[2]) for p in pend) >= (1 << 19) or b == W.num_seqs - 1:
-            cat = [np.concatenate([p[i] for p in pend]) for i in range(4)]
-            base.append(to_dev(cat[0]), to_dev(cat[1]), to_dev(cat[2]), to_dev(cat[3]), bt)
+            batches.append(tuple(to_dev(np.concatenate([p[i] for p in pend])) for i in range(4)))
             pend = []
     torch.cuda.synchronize()
+    fill_ev = event_pairs(len(batches))
+    for (a, b), (k, v, s, p) in zip(fill_ev, batches):
+        a.record(stream)
+        base.append(k, v, s, p, bt)
+        b.record(stream)
+    torch.cuda.synchronize()
+    fill_ms = sum(a.elapsed_time(b) for a, b in fill_ev)
+    fill_rows = sum(int(x[0].shape[0]) for x in batches) * W.num_kv_heads * 2
+    rb = row_bytes(W.dtype)
+    del batches
+    log(f"cache filled through xq_quantize_append: {fill_rows} rows in {fill_ms:.2f} ms")
 
-    log("cache filled through xq_quantize_append")
     footprint = 2 * base.pool_bytes
     R = max(1, int(np.ceil(args.replica_bytes / footprint)))
     caches = [base]
@@ -316,10 +495,9 @@ def main():
     wsb = base.workspace_bytes(B, hq, W.max_context_len, splits)
     ws = torch.empty((max(wsb, 16),), dtype=torch.uint8, device=dev)
     maxp = W.max_pages_per_seq
-    app = (new_k.data_ptr(), new_v.data_ptr(), B, new_seq.data_ptr(), new_pos.data_ptr(),
-           bt.data_ptr(), maxp)
-    chunk = None
     fuse = not args.no_fuse
+    app = (new_k.data_ptr(), new_v.data_ptr(), B, new_seq.data_ptr(), new_pos.data_ptr(), bt.data_ptr(), maxp)
+    app_rows = B
     if chunk_kv is not None:
         # one append per step takes every new row that the decode launch does not: the chunk's, and
         # without the fused step the decode batch's own too
@@ -329,10 +507,9 @@ def main():
         cs = to_dev(np.concatenate([np.full(W.chunk_tokens, W.batch, np.int32), np.arange(nb, dtype=np.int32)]))
         cp = to_dev(np.concatenate([np.arange(W.chunk_tokens, dtype=np.int32),
                                     (W.context_lens[:nb] - 1).astype(np.int32)]))
-        keep = (ck, cv, cs, cp)
-        app = (ck.data_ptr(), cv.data_ptr(), W.chunk_tokens + nb, cs.data_ptr(), cp.data_ptr(),
-               bt.data_ptr(), maxp)
-        chunk = True
+        keep = (ck, cv, cs, cp)  # noqa: F841  (alive for the step's pointers)
+        app = (ck.data_ptr(), cv.data_ptr(), W.chunk_tokens + nb, cs.data_ptr(), cp.data_ptr(), bt.data_ptr(), maxp)
+        app_rows = W.chunk_tokens + nb
     elif fuse:
         app = None
     # the host plan: long and short sequences share SIMDs (identity where it cannot help)
@@ -344,8 +521,6 @@ def main():
            None if order is None else order.data_ptr(),
            (new_k.data_ptr(), new_v.data_ptr()) if fuse else None)
     runners = [Step(lib, c.layout, c, app, dec) for c in caches]
-    stream = torch.cuda.current_stream()
-    sp = stream.cuda_stream
 
     log(f"{R} pool replicas of {footprint} bytes; timing")
     K, Wm = args.steps, args.warmup
@@ -355,14 +530,18 @@ def main():
         r.decode(sp)
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
+    ev = event_pairs(K)
+    app_ev = event_pairs(K) if app is not None else None
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(K):
         r = runners[(Wm + i) % R]
+        if app_ev is not None:
+            app_ev[i][0].record(stream)
         r.run(sp)
+        if app_ev is not None:
+            app_ev[i][1].record(stream)
         ev[i][0].record(stream)
         r.decode(sp)
         ev[i][1].record(stream)
@@ -371,6 +550,7 @@ def main():
     step_ms = start.elapsed_time(stop) / K
     dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
     dec_avg_ms = float(dec_ms.mean())
+    app_avg_ms = float(np.mean([a.elapsed_time(b) for a, b in app_ev])) if app_ev is not None else None
 
     # ---- the same steps replayed from captured HIP graphs (one per pool replica): the library
     # allocates, clears and waits on nothing, so a step captures whole ---------------------------
@@ -434,20 +614,26 @@ def main():
             del layers
         del graphs
 
-    rb = row_bytes(W.dtype)
     kv_bytes = int(W.context_lens.astype(np.int64).sum()) * hkv * 2 * rb
     tokens = int(W.context_lens.astype(np.int64).sum())
     nsplits = xq.xq_decode_num_splits(base.layout, B, hq, W.max_context_len, splits)
-    # The reported step time: the steps replayed from HIP graphs (as a serving engine replays its
-    # decode step), R to a graph where possible, when every pool replica has its graph; else the
-    # eager launches.
     by_graph = graph is not None and graph["replicas"] == R
     by_layers = by_graph and "multi_step_ms_per_step" in graph
     timed_ms = graph["multi_step_ms_per_step"] if by_layers else graph["ms_per_step"] if by_graph else step_ms
     value = kv_bytes / (timed_ms * 1e-3) / 1e9
     achieved = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
     tag = f"decode_call_{workloads.DTYPE_NAMES[W.dtype]}_{W.name}"
-    traffic = committed_traffic(tag)
+    prof = committed_profile(tag)
+    kernel_us = prof.get("decode_call_kernel_us")
+
+    # the append kernel's own rate: bf16 rows in, code rows and scales out
+    append = {"bytes_per_row": 256 + rb,
+              "fill_rows": fill_rows, "fill_ms": round(fill_ms, 4),
+              "fill_GBps": round(fill_rows * (256 + rb) / (fill_ms * 1e-3) / 1e9, 1)}
+    if app_avg_ms is not None:
+        rows = app_rows * hkv * 2
+        append.update({"step_rows": rows, "step_call_us": round(app_avg_ms * 1e3, 2),
+                       "step_GBps": round(rows * (256 + rb) / (app_avg_ms * 1e-3) / 1e9, 1)})
 
     result = {
         "metric": "quantized paged decode attn: KV GB/s (% of HBM peak) and seq-tokens/s",
@@ -460,8 +646,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {4: "i4xi16->i32 QK, f32 softmax/PV", 3: "i3xi16->i32 QK, f32 softmax/PV",
-                  2: "i2xi16->i32 QK, f32 softmax/PV", 8: "i8xi16->i32 QK, f32 softmax/PV",
+        "dtype": {4: "i4xi8->i32 QK (3 query digits), f32 softmax, f16 PV->f32",
+                  3: "i3xi8->i32 QK (3 query digits), f32 softmax, f16 PV->f32",
+                  2: "i2xi8->i32 QK (3 query digits), f32 softmax, f16 PV->f32",
+                  8: "i8xi8->i32 QK (3 query digits), f32 softmax, f16 PV->f32",
                   0: "bf16xbf16->f32", workloads.FP8: "e4m3->bf16, bf16xbf16->f32"}[W.dtype],
         "data": "synthetic",
         "config": {
@@ -489,20 +677,28 @@ def main():
                            "p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
+                     "traffic": prof.get("hbm_bytes_per_launch"),
+                     "frac_kernel_trace": (round(kv_bytes / (kernel_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                                           if kernel_us else None),
+                     "kernel_trace_us": kernel_us,
                      "kernel": ("xq_append_decode_attention" if fuse else "xq_paged_decode_attention")
                                + " call (decode_split_kernel"
                                + (" + decode_combine_kernel)" if nsplits > 1 else ")"),
-                     "bytes_per_launch": kv_bytes},
+                     "bytes_per_launch": kv_bytes,
+                     "bytes_note": "algorithmic: sum_b L_b x Hkv x (K row + V row), a row being "
+                                   f"{rb} B (codes + fp16 scale)"},
+        "append": append,
     }
-    if chunk is not None and not args.no_prefill:
-        result["prefill"] = time_prefill(lib, base, W, bt, to_dev, stream, K, Wm)
+    if chunk_kv is not None and not args.no_prefill:
+        result["prefill"] = time_prefill(base, W, bt, to_dev, stream, K, Wm)
+    if not args.no_probe:
+        del caches, runners
+        result["hbm_reference"] = hbm_reference(xq, stream)
     log(f"GPU: {step_ms * 1e3:.1f} us/step eager, "
         f"{'%.1f' % (graph['ms_per_step'] * 1e3) if graph is not None else '-'} us/step graph, "
         f"decode call {dec_avg_ms * 1e3:.1f} us")
-    if not args.no_cpu:
-        log("oracle baseline on the host")
-        result["cpu_baseline"] = cpu_baseline(W, args.cpu_seconds)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 

@@ -20,7 +20,8 @@ OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
 EXPORTS = ("xq_block_bytes", "xq_page_stride_bytes", "xq_pool_bytes", "xq_decode_num_splits",
            "xq_decode_workspace_bytes", "xq_status_string", "xq_last_error",
            "xq_quantize_append", "xq_paged_decode_attention", "xq_paged_prefill_attention",
-           "xq_decode_plan", "xq_paged_decode_attention_planned", "xq_append_decode_attention")
+           "xq_decode_plan", "xq_paged_decode_attention_planned", "xq_append_decode_attention",
+           "xq_hbm_read_probe")
 
 
 class XqError(RuntimeError):
@@ -72,6 +73,7 @@ def load() -> ctypes.CDLL:
                                              P, I64, P, P, P]),
         "xq_paged_decode_attention_planned": (I32, [LP, P, I32, I32, P, P, P, I32, P, I32, F32, I32,
                                                     P, I64, P, P, P]),
+        "xq_hbm_read_probe": (I32, [P, I64, I64, I32, I64, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -190,3 +192,10 @@ def xq_append_decode_attention(layout: CacheLayout, k_new, v_new, q, batch: int,
         _ptr(v_pool), _ptr(block_tables), max_pages_per_seq, _ptr(context_lens), max_context_len,
         float(softmax_scale), num_splits_hint, _ptr(workspace), int(workspace_bytes), _ptr(out),
         _ptr(seq_order), _stream(stream)))
+
+
+def xq_hbm_read_probe(buf, buf_bytes: int, n_blocks: int, block_bytes: int, block_stride: int,
+                      block_order, sink, stream=None):
+    """See xq_hbm_read_probe in include/xq.h (a streaming-read reference for the roofline)."""
+    _check(load().xq_hbm_read_probe(_ptr(buf), int(buf_bytes), int(n_blocks), int(block_bytes),
+                                    int(block_stride), _ptr(block_order), _ptr(sink), _stream(stream)))

@@ -338,8 +338,11 @@ xq_status xq_quantize_append(const xq_cache_layout* layout, const void* k_new, c
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
     return fail(XQ_EINVAL, "k_new, v_new and the pools must be 16-byte aligned");
   if (max_pages_per_seq < 1) return fail(XQ_EINVAL, "max_pages_per_seq %d < 1", max_pages_per_seq);
-  if ((int64_t)n_tokens * layout->num_kv_heads > ((int64_t)1 << 31) * 16)
-    return fail(XQ_EINVAL, "n_tokens * num_kv_heads too large for one launch");
+  // one 16-lane group per (token, kv head) row: the launch's work-items (16 per row) must stay
+  // below 2^32
+  if ((int64_t)n_tokens * layout->num_kv_heads >= ((int64_t)1 << 28))
+    return fail(XQ_EUNSUPPORTED, "n_tokens * num_kv_heads = %lld rows: at most 2^28 - 1 per call",
+                (long long)n_tokens * layout->num_kv_heads);
   if (debug_on())
     if (xq_status st = debug_check_append(layout, n_tokens, token_seq, token_pos, block_tables, max_pages_per_seq,
                                           static_cast<hipStream_t>(stream)))
@@ -472,6 +475,27 @@ xq_status xq_paged_prefill_attention(const xq_cache_layout* layout, const void* 
   return attention(layout, q, n_query, num_q_heads, k_pool, v_pool, block_table, 0, max_pages, nullptr,
                    start_pos + 1, start_pos + n_query, softmax_scale, num_splits_hint, workspace,
                    workspace_bytes, out, static_cast<hipStream_t>(stream));
+}
+
+xq_status xq_hbm_read_probe(const void* buf, int64_t buf_bytes, int64_t n_blocks, int32_t block_bytes,
+                             int64_t block_stride, const int32_t* block_order, uint32_t* sink, void* stream) {
+  if (n_blocks < 0) return fail(XQ_EINVAL, "n_blocks %lld < 0", (long long)n_blocks);
+  if (n_blocks == 0) return XQ_OK;
+  if (!buf || !sink) return fail(XQ_EINVAL, "a required pointer is NULL");
+  if (!aligned16(buf)) return fail(XQ_EINVAL, "buf must be 16-byte aligned");
+  if (block_bytes < 1024 || block_bytes > (1 << 20) || !pow2(block_bytes))
+    return fail(XQ_EINVAL, "block_bytes %d is not a power of two in [1024, 2^20]", block_bytes);
+  if (block_stride < block_bytes || block_stride % 16 != 0)
+    return fail(XQ_EINVAL, "block_stride %lld must be a multiple of 16 and at least block_bytes",
+                (long long)block_stride);
+  if (n_blocks * (block_bytes / 1024) > INT32_MAX)
+    return fail(XQ_EUNSUPPORTED, "n_blocks * block_bytes is 2 TiB or more", (long long)n_blocks);
+  if (!block_order && (n_blocks - 1) * block_stride + block_bytes > buf_bytes)
+    return fail(XQ_EINVAL, "n_blocks blocks at block_stride do not fit buf_bytes");
+  const hipError_t e = xq::launch_hbm_probe(static_cast<const uint8_t*>(buf), n_blocks, block_bytes, block_stride,
+                                            block_order, sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(XQ_EHIP, "hbm probe launch: %s", hipGetErrorString(e));
+  return XQ_OK;
 }
 
 }  // extern "C"

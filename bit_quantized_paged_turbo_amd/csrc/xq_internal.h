@@ -87,5 +87,9 @@ struct DecodeParams {
 
 hipError_t launch_quantize_append(int dtype, const AppendParams& p, hipStream_t stream);
 hipError_t launch_decode(int dtype, const DecodeParams& p, hipStream_t stream);
+// Streaming-read reference: n_blocks blocks of block_bytes (1 KiB times a power of two), block i at
+// order[i] * stride (i * stride when order is null).
+hipError_t launch_hbm_probe(const uint8_t* buf, int64_t n_blocks, int32_t block_bytes, int64_t stride,
+                            const int32_t* order, uint32_t* sink, hipStream_t stream);
 
 }  // namespace xq

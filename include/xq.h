@@ -292,6 +292,28 @@ xq_status xq_paged_prefill_attention(const xq_cache_layout* layout,
                                      void* workspace, int64_t workspace_bytes,
                                      float* out, void* stream);
 
+/*
+ * Streaming-read reference for the decode's roofline: a measurement aid, not part of the attention
+ * method. The decode reads each cache byte once per step, so its ceiling is the rate at which this
+ * GPU's HBM delivers bytes to a kernel that only reads; this call launches such a kernel.
+ *
+ *   buf            device memory of buf_bytes bytes, 16-byte aligned; only read
+ *   n_blocks       blocks to read (0 is a no-op; n_blocks * block_bytes below 2 TiB)
+ *   block_bytes    bytes of a block: a power of two from 1024 to 2^20 (a wave reads 1 KiB at a
+ *                  time)
+ *   block_stride   bytes between block starts (a multiple of 16, >= block_bytes)
+ *   block_order    NULL: block i starts at i * block_stride, all within buf_bytes (checked);
+ *                  else device int32 [n_blocks]: block i starts at block_order[i] * block_stride,
+ *                  which must lie, with its block_bytes, inside buf (the caller's contract,
+ *                  not checked on the device)
+ *   sink           device uint32 [1]: written only if the XOR of everything read equals a fixed
+ *                  value (so the reads cannot be optimised away); its contents do not matter
+ * Time it with events on `stream`: bytes read = n_blocks * block_bytes. XQ_EINVAL on invalid
+ * arguments, XQ_EHIP if the launch fails.
+ */
+xq_status xq_hbm_read_probe(const void* buf, int64_t buf_bytes, int64_t n_blocks, int32_t block_bytes,
+                            int64_t block_stride, const int32_t* block_order, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -122,6 +122,11 @@ def test_append_argument_errors(lib):
     assert call(s=None) == xq.EINVAL
     assert call(kp=24) == xq.EINVAL
     assert call(maxp=0) == xq.EINVAL
+    # 2^28 rows (tokens x kv heads) would need 2^32 work-items in one launch
+    big = xq.CacheLayout(4, 16, 16, 10)
+    call16 = lambda n: lib.xq_quantize_append(ctypes.byref(big), 16, 16, n, 16, 16, 16, 4, 16, 16, None)
+    assert call16(1 << 24) == xq.EUNSUPPORTED
+    assert b"2^28" in lib.xq_last_error()
     assert lib.xq_status_string(xq.EHIP) == b"HIP runtime error"
 
 
