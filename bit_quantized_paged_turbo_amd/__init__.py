@@ -21,7 +21,7 @@ EXPORTS = ("xq_block_bytes", "xq_page_stride_bytes", "xq_pool_bytes", "xq_decode
            "xq_decode_workspace_bytes", "xq_status_string", "xq_last_error",
            "xq_quantize_append", "xq_paged_decode_attention", "xq_paged_prefill_attention",
            "xq_decode_plan", "xq_paged_decode_attention_planned", "xq_append_decode_attention",
-           "xq_hbm_read_probe")
+           "xq_hbm_read_probe", "xq_paged_decode_attention_noalloc")
 
 
 class XqError(RuntimeError):
@@ -74,6 +74,7 @@ def load() -> ctypes.CDLL:
         "xq_paged_decode_attention_planned": (I32, [LP, P, I32, I32, P, P, P, I32, P, I32, F32, I32,
                                                     P, I64, P, P, P]),
         "xq_hbm_read_probe": (I32, [P, I64, I64, I32, I64, P, P, P]),
+        "xq_paged_decode_attention_noalloc": (I32, [LP, P, I32, I32, P, P, P, I32, P, I32, F32, I32, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -199,3 +200,17 @@ def xq_hbm_read_probe(buf, buf_bytes: int, n_blocks: int, block_bytes: int, bloc
     """See xq_hbm_read_probe in include/xq.h (a streaming-read reference for the roofline)."""
     _check(load().xq_hbm_read_probe(_ptr(buf), int(buf_bytes), int(n_blocks), int(block_bytes),
                                     int(block_stride), _ptr(block_order), _ptr(sink), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def xq_paged_decode_attention_noalloc(layout: CacheLayout, q, batch: int, num_q_heads: int, k_pool,
+                                      v_pool, block_tables, max_pages_per_seq: int, context_lens,
+                                      max_context_len: int, softmax_scale: float, num_splits_hint: int,
+                                      out, stream=None):
+    """See xq_paged_decode_attention_noalloc in include/xq.h (no workspace: the library's scratch)."""
+    _check(load().xq_paged_decode_attention_noalloc(
+        ctypes.byref(layout), _ptr(q), batch, num_q_heads, _ptr(k_pool), _ptr(v_pool),
+        _ptr(block_tables), max_pages_per_seq, _ptr(context_lens), max_context_len,
+        float(softmax_scale), num_splits_hint, _ptr(out), _stream(stream)))

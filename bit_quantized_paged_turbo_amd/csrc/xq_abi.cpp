@@ -12,6 +12,7 @@
 #include <string>
 #include <unordered_set>
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "xq_internal.h"
@@ -197,7 +198,7 @@ xq_status attention(const xq_cache_layout* layout, const void* q, int32_t batch,
                     int32_t max_pages_per_seq, const int32_t* context_lens, int32_t ctx_base,
                     int32_t max_context_len, float softmax_scale, int32_t num_splits_hint, void* workspace,
                     int64_t workspace_bytes, float* out, hipStream_t stream, const int32_t* seq_order = nullptr,
-                    const void* k_new = nullptr, const void* v_new = nullptr) {
+                    const void* k_new = nullptr, const void* v_new = nullptr, bool checked_ok = true) {
   if (batch > 65535) return fail(XQ_EUNSUPPORTED, "batch %d > 65535", batch);
   if (num_q_heads < 1 || num_q_heads % layout->num_kv_heads != 0)
     return fail(XQ_EINVAL, "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads,
@@ -235,7 +236,7 @@ xq_status attention(const xq_cache_layout* layout, const void* q, int32_t batch,
     if (!aligned16(workspace)) return fail(XQ_EINVAL, "workspace must be 16-byte aligned");
   }
   uint8_t* wsp = static_cast<uint8_t*>(workspace);
-  if (debug_on()) {
+  if (checked_ok && debug_on()) {
     xq_status st = ctx_base > 0 ? debug_check_prefill(layout, block_tables, max_context_len, stream)
                                 : debug_check_decode(layout, batch, block_tables, max_pages_per_seq, context_lens,
                                                      max_context_len, stream);
@@ -274,6 +275,35 @@ xq_status attention(const xq_cache_layout* layout, const void* q, int32_t batch,
   p.v_new = static_cast<const uint16_t*>(v_new);
   const hipError_t e = xq::launch_decode(layout->kv_dtype, p, stream);
   if (e != hipSuccess) return fail(XQ_EHIP, "attention launch: %s", hipGetErrorString(e));
+  return XQ_OK;
+}
+
+// ---- scratch of the allocation-free decode ----------------------------------------------
+// xq_paged_decode_attention_noalloc keeps its split partials in this file-scope device array: one
+// copy per GPU the library runs on, held until the process ends. In host code `scratch` is only
+// a stand-in for the symbol; its device address on each device comes from hipGetSymbolAddress,
+// taken once per device (with that device current) on the entry point's first call there.
+constexpr int64_t kScratchBytes = int64_t(16) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+xq_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(XQ_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(XQ_EUNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(XQ_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
   return XQ_OK;
 }
 
@@ -380,6 +410,29 @@ xq_status xq_paged_decode_attention(const xq_cache_layout* layout, const void* q
   return attention(layout, q, batch, num_q_heads, k_pool, v_pool, block_tables, max_pages_per_seq,
                    max_pages_per_seq, context_lens, 0, max_context_len, softmax_scale, num_splits_hint,
                    workspace, workspace_bytes, out, static_cast<hipStream_t>(stream));
+}
+
+xq_status xq_paged_decode_attention_noalloc(const xq_cache_layout* layout, const void* q, int32_t batch,
+                                            int32_t num_q_heads, const void* k_pool, const void* v_pool,
+                                            const int32_t* block_tables, int32_t max_pages_per_seq,
+                                            const int32_t* context_lens, int32_t max_context_len,
+                                            float softmax_scale, int32_t num_splits_hint, float* out,
+                                            void* stream) {
+  if (xq_status st = check_layout(layout)) return st;
+  if (batch < 0) return fail(XQ_EINVAL, "batch %d < 0", batch);
+  if (batch == 0) return XQ_OK;
+  if (!context_lens) return fail(XQ_EINVAL, "a required pointer is NULL");
+  if (max_context_len < 0) return fail(XQ_EINVAL, "max_context_len %d < 0", max_context_len);
+  const int64_t need = xq_decode_workspace_bytes(layout, batch, num_q_heads, max_context_len, num_splits_hint);
+  if (need < 0) return fail(XQ_EINVAL, "invalid batch, head count, context length or split hint");
+  if (need > kScratchBytes)
+    return fail(XQ_EWORKSPACE, "split partials of %lld bytes needed; the built-in scratch holds %lld",
+                (long long)need, (long long)kScratchBytes);
+  void* ws = nullptr;
+  if (xq_status st = scratch_address(&ws)) return st;
+  return attention(layout, q, batch, num_q_heads, k_pool, v_pool, block_tables, max_pages_per_seq,
+                   max_pages_per_seq, context_lens, 0, max_context_len, softmax_scale, num_splits_hint, ws,
+                   kScratchBytes, out, static_cast<hipStream_t>(stream), nullptr, nullptr, nullptr, false);
 }
 
 xq_status xq_paged_decode_attention_planned(const xq_cache_layout* layout, const void* q, int32_t batch,

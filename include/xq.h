@@ -194,6 +194,29 @@ xq_status xq_paged_decode_attention(const xq_cache_layout* layout,
                                     float* out, void* stream);
 
 /*
+ * xq_paged_decode_attention for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same decode, with the
+ * split partials in a scratch array built into the library instead of a caller workspace.
+ * Arguments, results and errors are those of xq_paged_decode_attention without the workspace;
+ * the output is bitwise that of xq_paged_decode_attention with the same arguments.
+ *
+ * The scratch holds 16 MiB (XQ_NOALLOC_SCRATCH_BYTES) on each GPU the library runs on, until the
+ * process ends: a call whose xq_decode_workspace_bytes(...) exceeds it returns XQ_EWORKSPACE and
+ * launches nothing. The call allocates and frees nothing (its first call on a device only looks
+ * up the array's address there) and ignores XQ_DEBUG (the checked mode copies to host memory).
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap on one GPU (other
+ * streams, other host threads) race and must be ordered by the caller.
+ */
+#define XQ_NOALLOC_SCRATCH_BYTES (16ll << 20)
+xq_status xq_paged_decode_attention_noalloc(const xq_cache_layout* layout,
+                                            const void* q, int32_t batch, int32_t num_q_heads,
+                                            const void* k_pool, const void* v_pool,
+                                            const int32_t* block_tables, int32_t max_pages_per_seq,
+                                            const int32_t* context_lens, int32_t max_context_len,
+                                            float softmax_scale, int32_t num_splits_hint,
+                                            float* out, void* stream);
+
+/*
  * Optional host-side plan for a decode (the split into a host "plan" and a device "run" of
  * batched-attention libraries): from the host's copy of the context lengths, a permutation of the
  * batch that puts long and short sequences on the same SIMDs, so that the SIMDs finish together.

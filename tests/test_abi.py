@@ -112,6 +112,20 @@ def test_decode_argument_errors(lib):
     assert _decode_status(lib, bad) == xq.EINVAL
 
 
+def test_noalloc_decode_rejects_what_its_scratch_cannot_hold(lib):
+    """The allocation-free decode checks its partials against the built-in 16 MiB before anything
+    touches a device: too many (sequence, head, split) partials give XQ_EWORKSPACE."""
+    L = xq.CacheLayout(4, 8, 16, 1 << 20)
+    need = xq.xq_decode_workspace_bytes(L, 4096, 64, 16384, 16)
+    assert need > xq.NOALLOC_SCRATCH_BYTES
+    st = lib.xq_paged_decode_attention_noalloc(ctypes.byref(L), 16, 4096, 64, 16, 16, 16, 1024, 16, 16384,
+                                               0.1, 16, 16, None)
+    assert st == xq.EWORKSPACE
+    assert b"16777216" in lib.xq_last_error()
+    assert lib.xq_paged_decode_attention_noalloc(ctypes.byref(L), 16, 0, 64, 16, 16, 16, 1024, 16, 16384,
+                                                 0.1, 16, 16, None) == xq.OK     # empty batch
+
+
 def test_append_argument_errors(lib):
     L = xq.CacheLayout(4, 2, 16, 10)
     call = lambda **kw: lib.xq_quantize_append(
