@@ -294,11 +294,11 @@ class Step:
     def decode(self, stream: int):
         lib = self.lib
         c = self.cache
-        q, batch, hq, bt, maxp, cl, maxctx, scale, splits, ws, wsb, out, order, fused = self.dec
+        q, batch, hq, bt, maxp, cl, maxctx, scale, splits, ws, wsb, out, order, n_order, fused = self.dec
         if fused is not None:
             st = lib.xq_append_decode_attention(self.L, fused[0], fused[1], q, batch, hq, c.k_pool.data_ptr(),
                                                 c.v_pool.data_ptr(), bt, maxp, cl, maxctx, scale, splits,
-                                                ws, wsb, out, order, stream)
+                                                ws, wsb, out, order, n_order, stream)
         elif order is None:
             st = lib.xq_paged_decode_attention(self.L, q, batch, hq, c.k_pool.data_ptr(),
                                                c.v_pool.data_ptr(), bt, maxp, cl, maxctx, scale,
@@ -306,7 +306,7 @@ class Step:
         else:
             st = lib.xq_paged_decode_attention_planned(self.L, q, batch, hq, c.k_pool.data_ptr(),
                                                        c.v_pool.data_ptr(), bt, maxp, cl, maxctx,
-                                                       scale, splits, ws, wsb, out, order, stream)
+                                                       scale, splits, ws, wsb, out, order, n_order, stream)
         if st:
             raise RuntimeError(lib.xq_last_error().decode())
 
@@ -518,7 +518,7 @@ def main():
         order = base.plan([int(x) for x in W.context_lens], hq, W.max_context_len, splits, device=dev)
     dec = (q.data_ptr(), B, hq, bt.data_ptr(), maxp, cl.data_ptr(), W.max_context_len,
            W.softmax_scale, splits, ws.data_ptr(), wsb, out.data_ptr(),
-           None if order is None else order.data_ptr(),
+           None if order is None else order.data_ptr(), 0 if order is None else int(order.numel()),
            (new_k.data_ptr(), new_v.data_ptr()) if fuse else None)
     runners = [Step(lib, c.layout, c, app, dec) for c in caches]
 
@@ -657,7 +657,8 @@ def main():
             "batch": B, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": 128,
             "page_size": W.page_size, "context_tokens": tokens, "max_context": W.max_context_len,
             "splits": nsplits, "chunk_append_tokens": W.chunk_tokens, "pool_replicas": R,
-            "plan": order is not None and order.cpu().tolist() != list(range(B)),
+            "plan": (None if order is None else "permutation of the batch" if int(order.numel()) == B
+                     else "unit placement (longest first, balanced SIMDs)"),
             "fused_append": fuse,
         },
         "step_timing": {"method": (f"hip graph replay, {R} steps (one per pool replica, as one per layer) per graph"

@@ -21,7 +21,7 @@ EXPORTS = ("xq_block_bytes", "xq_page_stride_bytes", "xq_pool_bytes", "xq_decode
            "xq_decode_workspace_bytes", "xq_status_string", "xq_last_error",
            "xq_quantize_append", "xq_paged_decode_attention", "xq_paged_prefill_attention",
            "xq_decode_plan", "xq_paged_decode_attention_planned", "xq_append_decode_attention",
-           "xq_hbm_read_probe", "xq_paged_decode_attention_noalloc")
+           "xq_hbm_read_probe", "xq_paged_decode_attention_noalloc", "xq_decode_plan_entries")
 
 
 class XqError(RuntimeError):
@@ -69,10 +69,11 @@ def load() -> ctypes.CDLL:
         "xq_paged_prefill_attention": (I32, [LP, P, I32, I32, P, P, P, I32, I32, F32, I32,
                                              P, I64, P, P]),
         "xq_decode_plan": (I32, [LP, I32, I32, I32, I32, P, P]),
+        "xq_decode_plan_entries": (I32, [LP, I32, I32, I32, I32]),
         "xq_append_decode_attention": (I32, [LP, P, P, P, I32, I32, P, P, P, I32, P, I32, F32, I32,
-                                             P, I64, P, P, P]),
+                                             P, I64, P, P, I32, P]),
         "xq_paged_decode_attention_planned": (I32, [LP, P, I32, I32, P, P, P, I32, P, I32, F32, I32,
-                                                    P, I64, P, P, P]),
+                                                    P, I64, P, P, I32, P]),
         "xq_hbm_read_probe": (I32, [P, I64, I64, I32, I64, P, P, P]),
         "xq_paged_decode_attention_noalloc": (I32, [LP, P, I32, I32, P, P, P, I32, P, I32, F32, I32, P, P]),
     }
@@ -89,6 +90,11 @@ def _ptr(x):
     if isinstance(x, int):
         return x
     return x.data_ptr()
+
+
+def _entries(plan) -> int:
+    """Entries of a device plan (a tensor) for the planned calls; 0 without one."""
+    return 0 if plan is None else int(plan.numel())
 
 
 def _stream(stream):
@@ -160,15 +166,25 @@ def xq_paged_prefill_attention(layout: CacheLayout, q, n_query: int, num_q_heads
         _ptr(workspace), int(workspace_bytes), _ptr(out), _stream(stream)))
 
 
+def xq_decode_plan_entries(layout: CacheLayout, batch: int, num_q_heads: int, max_context_len: int,
+                           num_splits_hint: int = 0) -> int:
+    return load().xq_decode_plan_entries(ctypes.byref(layout), batch, num_q_heads, max_context_len,
+                                         num_splits_hint)
+
+
 def xq_decode_plan(layout: CacheLayout, batch: int, num_q_heads: int, max_context_len: int,
                    num_splits_hint: int, context_lens) -> "list[int]":
-    """See xq_decode_plan in include/xq.h. context_lens: host sequence of ints; returns the order."""
+    """See xq_decode_plan in include/xq.h. context_lens: host sequence of ints; returns the plan
+    (xq_decode_plan_entries entries)."""
+    n = xq_decode_plan_entries(layout, batch, num_q_heads, max_context_len, num_splits_hint)
+    if n < 0:
+        raise XqError(EINVAL, "invalid layout, batch, head count, context length or split hint")
     lens = (ctypes.c_int32 * max(1, batch))(*[int(x) for x in context_lens])
-    order = (ctypes.c_int32 * max(1, batch))()
+    order = (ctypes.c_int32 * max(1, n))()
     _check(load().xq_decode_plan(ctypes.byref(layout), batch, num_q_heads, max_context_len,
                                  num_splits_hint, ctypes.cast(lens, ctypes.c_void_p),
                                  ctypes.cast(order, ctypes.c_void_p)))
-    return list(order)[:batch]
+    return list(order)[:n]
 
 
 def xq_paged_decode_attention_planned(layout: CacheLayout, q, batch: int, num_q_heads: int, k_pool,
@@ -180,7 +196,7 @@ def xq_paged_decode_attention_planned(layout: CacheLayout, q, batch: int, num_q_
         ctypes.byref(layout), _ptr(q), batch, num_q_heads, _ptr(k_pool), _ptr(v_pool),
         _ptr(block_tables), max_pages_per_seq, _ptr(context_lens), max_context_len,
         float(softmax_scale), num_splits_hint, _ptr(workspace), int(workspace_bytes), _ptr(out),
-        _ptr(seq_order), _stream(stream)))
+        _ptr(seq_order), _entries(seq_order), _stream(stream)))
 
 
 def xq_append_decode_attention(layout: CacheLayout, k_new, v_new, q, batch: int, num_q_heads: int,
@@ -192,7 +208,7 @@ def xq_append_decode_attention(layout: CacheLayout, k_new, v_new, q, batch: int,
         ctypes.byref(layout), _ptr(k_new), _ptr(v_new), _ptr(q), batch, num_q_heads, _ptr(k_pool),
         _ptr(v_pool), _ptr(block_tables), max_pages_per_seq, _ptr(context_lens), max_context_len,
         float(softmax_scale), num_splits_hint, _ptr(workspace), int(workspace_bytes), _ptr(out),
-        _ptr(seq_order), _stream(stream)))
+        _ptr(seq_order), _entries(seq_order), _stream(stream)))
 
 
 def xq_hbm_read_probe(buf, buf_bytes: int, n_blocks: int, block_bytes: int, block_stride: int,

@@ -1364,9 +1364,23 @@ void decode_split_kernel(DecodeParams p) {
       split = (int)(group % (uint32_t)p.nsplits);
       b = (int)(group / (uint32_t)p.nsplits);
     }
-    // a host plan may hand this slot another sequence (long and short ones sharing a SIMD)
-    // (clamped: an entry outside the batch, outside the contract, still indexes the batch's arrays)
-    if (p.seq_order) b = min(max(p.seq_order[b], 0), p.batch - 1);
+    if (p.seq_order) {
+      if (p.nsplits > 1) {
+        // a unit plan (xq_decode_plan with several partitions): this slot runs unit
+        // (b nsplits + split) hkv + kvh, or nothing (-1, or an entry outside the units)
+        const int u = p.seq_order[id];
+        if (u < 0 || (uint32_t)u >= units) return;
+        kvh = (int)((uint32_t)u % hkv);
+        const uint32_t r = (uint32_t)u / hkv;
+        split = (int)(r % (uint32_t)p.nsplits);
+        b = (int)(r / (uint32_t)p.nsplits);
+      } else {
+        // a host plan may hand this slot another sequence (long and short ones sharing a SIMD)
+        // (clamped: an entry outside the batch, outside the contract, still indexes the batch's
+        // arrays)
+        b = min(max(p.seq_order[b], 0), p.batch - 1);
+      }
+    }
   }
   const int lane = threadIdx.x;
   // Columns of the unit's MFMA tiles: c = t Gq + h is head h (of the kv head's Gq) of row
@@ -1935,6 +1949,18 @@ int pick_depth(const DecodeParams& p) {
   }
 }
 
+// Waves per SIMD the launch runs at once when all its workgroups are resident: the register
+// budget's target, or fewer where the LDS of one compute unit holds fewer rings.
+template <int DT>
+int waves_per_simd(const DecodeParams& p) {
+  const int depth = Stage<DT>::kOn ? (p.fixed_splits ? 3 : pick_depth<DT>(p)) : 3;
+  const int regs = depth >= 4 ? kWavesPerEu<DT, 4> : kWavesPerEu<DT, 3>;
+  constexpr int kOut = kMaxGroup * (D + 4) * 4 + kThreads * 4;
+  const int ring = depth * Stage<DT>::kSlot;
+  const int by_lds = (kLdsPerCu / std::max(kOut, ring)) / 4;
+  return std::max(1, std::min(regs, by_lds));
+}
+
 template <int DT, int DEPTH>
 void launch_split(const DecodeParams& p, hipStream_t stream) {
   const int64_t units = unit_count(p);
@@ -1969,6 +1995,18 @@ hipError_t launch_dt(const DecodeParams& p, hipStream_t stream) {
 }
 
 }  // namespace
+
+int decode_waves_per_simd(int dtype, const DecodeParams& p) {
+  switch (dtype) {
+    case 0: return waves_per_simd<0>(p);
+    case 8: return waves_per_simd<8>(p);
+    case 4: return waves_per_simd<4>(p);
+    case 3: return waves_per_simd<3>(p);
+    case 2: return waves_per_simd<2>(p);
+    case kFp8: return waves_per_simd<kFp8>(p);
+    default: return 1;
+  }
+}
 
 hipError_t launch_decode(int dtype, const DecodeParams& p, hipStream_t stream) {
   switch (dtype) {

@@ -101,6 +101,32 @@ xq_status debug_check_order(int32_t batch, const int32_t* seq_order, hipStream_t
   return XQ_OK;
 }
 
+// planned decode with several partitions: every entry is -1 or a unit index below `units`, no unit
+// appears twice, and every unit with tokens (split < ceil(context_lens[b] / tps)) appears, and
+// partition 0 of every sequence (which writes an empty sequence's zero output).
+xq_status debug_check_unit_plan(int32_t batch, int32_t hkv, int32_t nsplits, int32_t tps, int32_t max_ctx,
+                                const int32_t* context_lens, const int32_t* plan, hipStream_t s) {
+  const int64_t units = (int64_t)nsplits * hkv * batch;
+  std::vector<int32_t> o, cl;
+  if (xq_status st = fetch(o, plan, units, s)) return st;
+  if (xq_status st = fetch(cl, context_lens, batch, s)) return st;
+  std::vector<char> seen((size_t)units, 0);
+  for (int64_t i = 0; i < units; ++i) {
+    if (o[i] < -1 || o[i] >= units || (o[i] >= 0 && seen[(size_t)o[i]]))
+      return fail(XQ_EINVAL, "XQ_DEBUG: plan[%lld] = %d: not -1 or a unit that appears once", (long long)i, o[i]);
+    if (o[i] >= 0) seen[(size_t)o[i]] = 1;
+  }
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t L = std::min(std::max(cl[b], 0), max_ctx);
+    const int32_t n = std::max(1, (L + tps - 1) / tps);   // partition 0 of an empty sequence writes zeros
+    for (int32_t sp = 0; sp < n; ++sp)
+      for (int32_t k = 0; k < hkv; ++k)
+        if (!seen[((size_t)b * nsplits + sp) * hkv + k])
+          return fail(XQ_EINVAL, "XQ_DEBUG: the plan misses partition %d, kv head %d of sequence %d", sp, k, b);
+  }
+  return XQ_OK;
+}
+
 // prefill: the pages of positions 0 .. max_ctx - 1 in the chunk's block-table row are page ids
 // in [0, num_pages).
 xq_status debug_check_prefill(const xq_cache_layout* L, const int32_t* block_table, int32_t max_ctx,
@@ -240,7 +266,10 @@ xq_status attention(const xq_cache_layout* layout, const void* q, int32_t batch,
     xq_status st = ctx_base > 0 ? debug_check_prefill(layout, block_tables, max_context_len, stream)
                                 : debug_check_decode(layout, batch, block_tables, max_pages_per_seq, context_lens,
                                                      max_context_len, stream);
-    if (!st && seq_order) st = debug_check_order(batch, seq_order, stream);
+    if (!st && seq_order)
+      st = nsplits > 1 ? debug_check_unit_plan(batch, layout->num_kv_heads, nsplits, tps, max_context_len, context_lens,
+                                               seq_order, stream)
+                       : debug_check_order(batch, seq_order, stream);
     if (st) return st;
   }
 
@@ -289,6 +318,11 @@ static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
+
+// A plan's entry count must be the one xq_decode_plan writes for these arguments: the kernel reads
+// one entry per sequence or per work slot and cannot check the array's length.
+xq_status check_plan_entries(const xq_cache_layout* layout, int32_t batch, int32_t num_q_heads,
+                             int32_t max_context_len, int32_t num_splits_hint, int32_t plan_entries);
 
 xq_status scratch_address(void** out) {
   int dev = 0;
@@ -441,12 +475,14 @@ xq_status xq_paged_decode_attention_planned(const xq_cache_layout* layout, const
                                             const int32_t* context_lens, int32_t max_context_len,
                                             float softmax_scale, int32_t num_splits_hint, void* workspace,
                                             int64_t workspace_bytes, float* out, const int32_t* seq_order,
-                                            void* stream) {
+                                            int32_t plan_entries, void* stream) {
   if (xq_status st = check_layout(layout)) return st;
   if (batch < 0) return fail(XQ_EINVAL, "batch %d < 0", batch);
   if (batch == 0) return XQ_OK;
   if (!context_lens || !seq_order) return fail(XQ_EINVAL, "a required pointer is NULL");
   if (max_context_len < 0) return fail(XQ_EINVAL, "max_context_len %d < 0", max_context_len);
+  if (xq_status st = check_plan_entries(layout, batch, num_q_heads, max_context_len, num_splits_hint, plan_entries))
+    return st;
   return attention(layout, q, batch, num_q_heads, k_pool, v_pool, block_tables, max_pages_per_seq,
                    max_pages_per_seq, context_lens, 0, max_context_len, softmax_scale, num_splits_hint,
                    workspace, workspace_bytes, out, static_cast<hipStream_t>(stream), seq_order);
@@ -457,16 +493,33 @@ xq_status xq_append_decode_attention(const xq_cache_layout* layout, const void* 
                                      void* v_pool, const int32_t* block_tables, int32_t max_pages_per_seq,
                                      const int32_t* context_lens, int32_t max_context_len, float softmax_scale,
                                      int32_t num_splits_hint, void* workspace, int64_t workspace_bytes,
-                                     float* out, const int32_t* seq_order, void* stream) {
+                                     float* out, const int32_t* seq_order, int32_t plan_entries, void* stream) {
   if (xq_status st = check_layout(layout)) return st;
   if (batch < 0) return fail(XQ_EINVAL, "batch %d < 0", batch);
   if (batch == 0) return XQ_OK;
   if (!context_lens || !k_new || !v_new) return fail(XQ_EINVAL, "a required pointer is NULL");
   if (!aligned16(k_new) || !aligned16(v_new)) return fail(XQ_EINVAL, "k_new and v_new must be 16-byte aligned");
   if (max_context_len < 0) return fail(XQ_EINVAL, "max_context_len %d < 0", max_context_len);
+  if (seq_order)
+    if (xq_status st = check_plan_entries(layout, batch, num_q_heads, max_context_len, num_splits_hint, plan_entries))
+      return st;
   return attention(layout, q, batch, num_q_heads, k_pool, v_pool, block_tables, max_pages_per_seq,
                    max_pages_per_seq, context_lens, 0, max_context_len, softmax_scale, num_splits_hint,
                    workspace, workspace_bytes, out, static_cast<hipStream_t>(stream), seq_order, k_new, v_new);
+}
+
+int32_t xq_decode_plan_entries(const xq_cache_layout* layout, int32_t batch, int32_t num_q_heads,
+                               int32_t max_context_len, int32_t num_splits_hint) {
+  if (check_layout(layout) != XQ_OK) return -1;
+  if (batch < 0 || num_q_heads < 1 || max_context_len < 0) return -1;
+  if (num_splits_hint < 0 && !fixed_split_ok(layout, num_splits_hint)) return -1;
+  if (batch == 0) return 0;
+  const int32_t ctx = max_context_len > 0 ? max_context_len : 1;
+  const int32_t tps = plan_tokens_per_split(layout, batch, ctx, num_splits_hint);
+  const int64_t nsplits = (ctx + tps - 1) / tps;
+  if (nsplits == 1) return batch;
+  const int64_t units = nsplits * layout->num_kv_heads * batch;
+  return units >= ((int64_t)1 << 26) ? -1 : (int32_t)units;
 }
 
 xq_status xq_decode_plan(const xq_cache_layout* layout, int32_t batch, int32_t num_q_heads,
@@ -477,16 +530,10 @@ xq_status xq_decode_plan(const xq_cache_layout* layout, int32_t batch, int32_t n
   if (batch > 0 && (!host_context_lens || !host_seq_order)) return fail(XQ_EINVAL, "a required pointer is NULL");
   if (num_splits_hint < 0 && !fixed_split_ok(layout, num_splits_hint))
     return fail(XQ_EINVAL, "num_splits_hint %d is not a valid fixed partition", num_splits_hint);
-  for (int32_t b = 0; b < batch; ++b) host_seq_order[b] = b;
   if (batch == 0) return XQ_OK;
   const int32_t ctx = max_context_len > 0 ? max_context_len : 1;
   const int32_t tps = plan_tokens_per_split(layout, batch, ctx, num_splits_hint);
   const int32_t nsplits = (ctx + tps - 1) / tps;
-  // Waves fill the SIMDs round-robin: with every unit resident, workgroups i, i + S, i + 2S, ...
-  // (S = SIMDs of the device) share a SIMD. With one partition per sequence and a batch that is a
-  // multiple of 8, the decode's unit order puts sequence slots b, b + S / Hkv, b + 2 S / Hkv, ...
-  // on the same SIMDs (all their kv heads). Sorted by length, sequences are dealt to those slot
-  // groups in snake order, so a SIMD's units add up to about the same number of tiles.
   const int64_t hkv = layout->num_kv_heads;
   int simds = 1024;   // MI355X: 256 compute units x 4 SIMDs, if the device cannot be asked
   int dev = 0, cus = 0;
@@ -495,20 +542,77 @@ xq_status xq_decode_plan(const xq_cache_layout* layout, int32_t batch, int32_t n
     simds = 4 * cus;
   else
     (void)hipGetLastError();
-  if (nsplits != 1 || batch % 8 != 0 || simds % (8 * hkv) != 0) return XQ_OK;
-  const int64_t period = simds / hkv;   // slots b and b + period share SIMDs
-  if (period >= batch) return XQ_OK;
-  std::vector<int32_t> idx((size_t)batch);
-  for (int32_t b = 0; b < batch; ++b) idx[(size_t)b] = b;
-  std::stable_sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) {
-    return host_context_lens[a] > host_context_lens[b];
-  });
-  size_t next = 0;
-  for (int64_t k = 0; next < idx.size(); ++k) {       // pass k fills member k of every group
-    for (int64_t j = 0; j < period && next < idx.size(); ++j) {
-      const int64_t group = (k & 1) ? period - 1 - j : j;
-      const int64_t slot = group + k * period;
-      if (slot < batch) host_seq_order[slot] = idx[next++];
+
+  if (nsplits == 1) {
+    // Waves fill the SIMDs round-robin: with every unit resident, workgroups i, i + S, i + 2S, ...
+    // (S = SIMDs of the device) share a SIMD. With one partition per sequence and a batch that is
+    // a multiple of 8, the decode's unit order puts sequence slots b, b + S / Hkv, b + 2 S / Hkv,
+    // ... on the same SIMDs (all their kv heads). Sorted by length, sequences are dealt to those
+    // slot groups in snake order, so a SIMD's units add up to about the same number of tiles.
+    for (int32_t b = 0; b < batch; ++b) host_seq_order[b] = b;
+    if (batch % 8 != 0 || simds % (8 * hkv) != 0) return XQ_OK;
+    const int64_t period = simds / hkv;   // slots b and b + period share SIMDs
+    if (period >= batch) return XQ_OK;
+    std::vector<int32_t> idx((size_t)batch);
+    for (int32_t b = 0; b < batch; ++b) idx[(size_t)b] = b;
+    std::stable_sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) {
+      return host_context_lens[a] > host_context_lens[b];
+    });
+    size_t next = 0;
+    for (int64_t k = 0; next < idx.size(); ++k) {       // pass k fills member k of every group
+      for (int64_t j = 0; j < period && next < idx.size(); ++j) {
+        const int64_t group = (k & 1) ? period - 1 - j : j;
+        const int64_t slot = group + k * period;
+        if (slot < batch) host_seq_order[slot] = idx[next++];
+      }
+    }
+    return XQ_OK;
+  }
+
+  // Several partitions: a unit plan, one entry per work slot (workgroup id) of the launch, giving
+  // the unit (b nsplits + split) hkv + kvh it runs or -1. With all units of R rounds resident
+  // (R waves per SIMD), workgroup i runs on SIMD i mod S. The (sequence, partition) groups, each
+  // hkv units of equal length, are placed longest first (LPT) on the least loaded column of
+  // SIMDs that has a round free, a group's kv heads on one XCD (XCD = id mod 8) so that its L2
+  // fetches each line of a page once: column (x, y) of a round r holds ids
+  // x + 8 (hkv y + k) + S r, k < hkv. Groups beyond the resident rounds follow in the same order.
+  const int64_t units = (int64_t)nsplits * hkv * batch;
+  if (units >= ((int64_t)1 << 26)) return fail(XQ_EUNSUPPORTED, "%lld work units >= 2^26", (long long)units);
+  for (int64_t i = 0; i < units; ++i) host_seq_order[i] = -1;
+  struct Group { int32_t b, split, tiles; };
+  std::vector<Group> groups;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t L = std::min(std::max(host_context_lens[b], 0), max_context_len);
+    // partition 0 of an empty sequence too: its unit writes the sequence's zero output
+    for (int32_t sp = 0; sp == 0 || (int64_t)sp * tps < L; ++sp) {
+      const int32_t n = std::max(0, std::min(L, (sp + 1) * tps) - sp * tps);
+      groups.push_back({b, sp, (n + 31) / 32});
+    }
+  }
+  std::stable_sort(groups.begin(), groups.end(), [](const Group& a, const Group& c) { return a.tiles > c.tiles; });
+  auto unit = [&](const Group& g, int64_t k) { return (int32_t)(((int64_t)g.b * nsplits + g.split) * hkv + k); };
+  xq::DecodeParams q{};
+  q.batch = batch;
+  q.hkv = (int32_t)hkv;
+  q.nsplits = nsplits;
+  q.qt = 1;
+  q.fixed_splits = num_splits_hint < 0 ? 1 : 0;
+  // columns of hkv SIMDs in one XCD; without them (a SIMD count that is not a multiple of 8 hkv) no
+  // placement, only the longest-first order
+  const int64_t cols = (simds % (8 * hkv) == 0) ? simds / hkv : 0;
+  const int64_t rounds = cols > 0 ? std::min<int64_t>(xq::decode_waves_per_simd(layout->kv_dtype, q), units / simds) : 0;
+  std::vector<int64_t> load((size_t)cols, 0), used((size_t)cols, 0);
+  int64_t next = rounds * simds;   // slots after the resident rounds
+  for (const Group& g : groups) {
+    int64_t best = -1;
+    for (int64_t c = 0; c < cols && rounds > 0; ++c)
+      if (used[(size_t)c] < rounds && (best < 0 || load[(size_t)c] < load[(size_t)best])) best = c;
+    if (best >= 0) {
+      const int64_t x = best % 8, y = best / 8, r = used[(size_t)best]++;
+      load[(size_t)best] += g.tiles;
+      for (int64_t k = 0; k < hkv; ++k) host_seq_order[x + 8 * (hkv * y + k) + simds * r] = unit(g, k);
+    } else {
+      for (int64_t k = 0; k < hkv; ++k) host_seq_order[next++] = unit(g, k);
     }
   }
   return XQ_OK;
@@ -552,3 +656,15 @@ xq_status xq_hbm_read_probe(const void* buf, int64_t buf_bytes, int64_t n_blocks
 }
 
 }  // extern "C"
+
+namespace {
+xq_status check_plan_entries(const xq_cache_layout* layout, int32_t batch, int32_t num_q_heads,
+                             int32_t max_context_len, int32_t num_splits_hint, int32_t plan_entries) {
+  const int32_t want = xq_decode_plan_entries(layout, batch, num_q_heads, max_context_len, num_splits_hint);
+  if (want < 0) return fail(XQ_EINVAL, "invalid batch, head count, context length or split hint");
+  if (plan_entries != want)
+    return fail(XQ_EINVAL, "plan of %d entries given; these arguments take a plan of %d (xq_decode_plan_entries)",
+                plan_entries, want);
+  return XQ_OK;
+}
+}  // namespace

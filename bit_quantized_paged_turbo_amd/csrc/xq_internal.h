@@ -79,14 +79,20 @@ struct DecodeParams {
   int32_t ctx_base;             // 0: row b attends to context_lens[b] tokens; > 0: to
                                 // ctx_base + b tokens (query b of a prefill chunk)
   int32_t qt;                   // rows per work unit: 1 (decode) or 16 / group (prefill)
-  const int32_t* seq_order;     // null, or a permutation of the batch from xq_decode_plan: the
-                                // slot of sequence b in the unit order runs sequence seq_order[b]
+  const int32_t* seq_order;     // null, or a plan from xq_decode_plan: with one partition per
+                                // sequence a permutation of the batch (the slot of sequence b in
+                                // the unit order runs sequence seq_order[b]); with several, one
+                                // entry per work slot: the unit (b nsplits + split) hkv + kvh that
+                                // workgroup id runs, or -1
   const uint16_t* k_new;        // null, or bf16 [batch][hkv][128]: new rows appended at position
   const uint16_t* v_new;        // context_lens[b] - 1 by the wave of b's last split, first
 };
 
 hipError_t launch_quantize_append(int dtype, const AppendParams& p, hipStream_t stream);
 hipError_t launch_decode(int dtype, const DecodeParams& p, hipStream_t stream);
+// Waves of the decode's split kernel resident on one SIMD for the launch launch_decode would make
+// with these parameters (the register budget and the LDS of a compute unit).
+int decode_waves_per_simd(int dtype, const DecodeParams& p);
 // Streaming-read reference: n_blocks blocks of block_bytes (1 KiB times a power of two), block i at
 // order[i] * stride (i * stride when order is null).
 hipError_t launch_hbm_probe(const uint8_t* buf, int64_t n_blocks, int32_t block_bytes, int64_t stride,

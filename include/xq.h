@@ -218,17 +218,21 @@ xq_status xq_paged_decode_attention_noalloc(const xq_cache_layout* layout,
 
 /*
  * Optional host-side plan for a decode (the split into a host "plan" and a device "run" of
- * batched-attention libraries): from the host's copy of the context lengths, a permutation of the
- * batch that puts long and short sequences on the same SIMDs, so that the SIMDs finish together.
- * With every work unit resident, the GPU fills its SIMDs round-robin by workgroup id, and with one
- * partition per sequence the decode's unit order puts sequence slots b, b + S / num_kv_heads, ...
- * (S SIMDs) on the same SIMDs; sequences sorted by length are dealt to those slot groups in snake
- * order. Where the plan cannot help (several partitions, a batch that is not a multiple of 8) it
- * returns the identity. The order changes where a sequence runs, never what it computes: outputs
- * are bitwise those of xq_paged_decode_attention.
+ * batched-attention libraries): from the host's copy of the context lengths, where each piece of
+ * work runs, so that the SIMDs finish together. With every work unit resident, the GPU fills its
+ * SIMDs round-robin by workgroup id (workgroup i runs on SIMD i mod S, S SIMDs). The order changes
+ * where work runs, never what it computes: outputs are bitwise those of xq_paged_decode_attention.
+ *   - One partition per sequence: a permutation of the batch that puts long and short sequences
+ *     on the same SIMDs (the decode's unit order puts sequence slots b, b + S / num_kv_heads, ...
+ *     on the same SIMDs; sequences sorted by length are dealt to those slot groups in snake
+ *     order); the identity where that cannot help (a batch that is not a multiple of 8).
+ *   - Several partitions: a unit plan with one entry per work slot (workgroup id) of the launch:
+ *     the work unit (b * nsplits + split) * num_kv_heads + kv_head it runs, or -1. The (sequence,
+ *     partition) groups are placed longest first on the least loaded SIMDs, the kv heads of a
+ *     group on one XCD.
  *
  *   host_context_lens  int32 [batch], host memory: the lengths the decode will see
- *   host_seq_order     int32 [batch], host memory, written: slot b runs sequence host_seq_order[b]
+ *   host_seq_order     int32 [xq_decode_plan_entries(...)], host memory, written
  * Other arguments as for xq_decode_num_splits. The device is queried for its SIMD count (1024,
  * MI355X's, if that fails). Nothing is launched; XQ_EINVAL on invalid arguments.
  */
@@ -236,12 +240,20 @@ xq_status xq_decode_plan(const xq_cache_layout* layout, int32_t batch, int32_t n
                          int32_t max_context_len, int32_t num_splits_hint,
                          const int32_t* host_context_lens, int32_t* host_seq_order);
 
+/* Entries of the plan xq_decode_plan writes for these arguments: batch with one partition per
+ * sequence, else the launch's work slots (splits x kv heads x batch). -1 on invalid arguments. */
+int32_t xq_decode_plan_entries(const xq_cache_layout* layout, int32_t batch, int32_t num_q_heads,
+                               int32_t max_context_len, int32_t num_splits_hint);
+
 /*
- * xq_paged_decode_attention with a plan: seq_order is device int32 [batch], a permutation of
- * 0 .. batch-1 (the plan's host_seq_order, copied to the device by the caller); the result is
- * bitwise that of xq_paged_decode_attention with the same arguments. A seq_order that is not a
- * permutation is outside the contract (rejected under XQ_DEBUG; otherwise some sequences are
- * computed twice and others not at all).
+ * xq_paged_decode_attention with a plan: seq_order is device int32 [plan_entries], the plan's
+ * host_seq_order for the same arguments and host lengths, copied to the device by the caller;
+ * plan_entries must equal xq_decode_plan_entries for these arguments (XQ_EINVAL otherwise, nothing
+ * launched). The result is bitwise that of xq_paged_decode_attention with the same arguments. A
+ * seq_order that is not such a plan (not a permutation; a unit plan that repeats a unit, or misses
+ * one with tokens or partition 0 of a sequence, which writes an empty sequence's zeros) is outside
+ * the contract: rejected under XQ_DEBUG, otherwise some work is done twice and other work not at
+ * all (unit entries outside the units are skipped).
  */
 xq_status xq_paged_decode_attention_planned(const xq_cache_layout* layout,
                                             const void* q, int32_t batch, int32_t num_q_heads,
@@ -250,7 +262,8 @@ xq_status xq_paged_decode_attention_planned(const xq_cache_layout* layout,
                                             const int32_t* context_lens, int32_t max_context_len,
                                             float softmax_scale, int32_t num_splits_hint,
                                             void* workspace, int64_t workspace_bytes,
-                                            float* out, const int32_t* seq_order, void* stream);
+                                            float* out, const int32_t* seq_order, int32_t plan_entries,
+                                            void* stream);
 
 /*
  * One decode step in one launch: append each sequence's new K/V row, then decode. Equivalent to
@@ -266,6 +279,7 @@ xq_status xq_paged_decode_attention_planned(const xq_cache_layout* layout,
  *   k_new, v_new       bf16 [batch][num_kv_heads][128], 16-byte aligned: the step's new rows
  *   k_pool, v_pool     written (the new rows) and read
  *   seq_order          NULL, or a device plan as for xq_paged_decode_attention_planned
+ *   plan_entries       its entries (ignored when seq_order is NULL)
  * Other arguments, errors and the workspace as for xq_paged_decode_attention. context_lens are
  * the lengths after the append; the new row's slot must lie in a page of the block table.
  */
@@ -277,7 +291,8 @@ xq_status xq_append_decode_attention(const xq_cache_layout* layout,
                                      const int32_t* context_lens, int32_t max_context_len,
                                      float softmax_scale, int32_t num_splits_hint,
                                      void* workspace, int64_t workspace_bytes,
-                                     float* out, const int32_t* seq_order, void* stream);
+                                     float* out, const int32_t* seq_order, int32_t plan_entries,
+                                     void* stream);
 
 /*
  * Chunked prefill attention over the paged (and, for turbo types, quantized) cache: the queries

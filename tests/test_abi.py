@@ -184,7 +184,57 @@ def test_decode_plan_pairs_long_with_short(lib):
     # the k-th longest shares its SIMDs with the k-th shortest
     srt = sorted(lens, reverse=True)
     assert lens[order[0]] == srt[0] and lens[order[period]] == srt[-1]
-    # several partitions, or a batch that is not a multiple of 8: the identity
-    assert xq.xq_decode_plan(L, 256, 16, max(lens), 4, lens) == list(range(256))
+    # a batch that is not a multiple of 8: the identity
     assert xq.xq_decode_plan(L, 255, 16, max(lens), 0, lens[:255]) == list(range(255))
     assert xq.xq_decode_plan(L, 0, 16, 0, 0, []) == []
+    assert xq.xq_decode_plan_entries(L, 256, 16, max(lens), 0) == 256
+
+
+def test_unit_plan_balances_the_mixed_step(lib):
+    """Several partitions per sequence (the mixed step's 64 sequences, 15 partitions of 2,048
+    tokens): the plan holds one entry per work slot, every unit with tokens exactly once and -1
+    elsewhere; the kv heads of a (sequence, partition) sit on one XCD (slot mod 8); the resident
+    rounds (three waves a SIMD, slot i on SIMD i mod 1024 of the 1,024 this container assumes) give
+    every SIMD within one partition's tiles of every other (the unplanned order, measured on MI355X,
+    gave SIMDs from 17 to 192 tiles)."""
+    import numpy as np
+    import workloads
+    W = workloads.config(4)
+    L = xq.CacheLayout(4, 8, 16, W.num_pages)
+    lens = [int(x) for x in W.context_lens]
+    n = xq.xq_decode_plan_entries(L, 64, 32, W.max_context_len, 0)
+    nsplits = xq.xq_decode_num_splits(L, 64, 32, W.max_context_len, 0)
+    assert nsplits == 15 and n == 15 * 8 * 64
+    plan = np.array(xq.xq_decode_plan(L, 64, 32, W.max_context_len, 0, lens))
+    assert len(plan) == n
+    tps = -(-W.max_context_len // nsplits)
+    tps = -(-tps // 32) * 32
+    real = {((b * nsplits + s) * 8 + k) for b in range(64) for s in range(-(-lens[b] // tps)) for k in range(8)}
+    used = plan[plan >= 0]
+    assert len(used) == len(set(used.tolist())) == len(real) and set(used.tolist()) == real
+    tiles = {}
+    for i, u in enumerate(plan):
+        if u < 0:
+            continue
+        k, r = u % 8, u // 8
+        s, b = r % nsplits, r // nsplits
+        tiles[i] = -(-(min(lens[b], (s + 1) * tps) - s * tps) // 32)
+        # the 8 kv heads of this unit's group share its slot's XCD
+        assert all(plan[j] // 8 == r for j in range(i % 8, n, 8) if plan[j] >= 0 and plan[j] // 8 == r)
+    load = np.zeros(1024, int)
+    for i, t in tiles.items():
+        assert i < 3 * 1024                      # 2,560 units fit the three resident rounds
+        load[i % 1024] += t
+    # longest-first placement: every SIMD within one partition (64 tiles) of every other
+    assert load.max() - load.min() <= 64 and load.min() >= load.mean() - 32, (load.max(), load.min(), load.mean())
+    # a planned decode must be given the plan's length
+    st = lib.xq_paged_decode_attention_planned(ctypes.byref(L), 16, 64, 32, 16, 16, 16, 2048, 16,
+                                               W.max_context_len, 0.1, 0, 16, 1 << 30, 16, 16, 64, None)
+    assert st == xq.EINVAL and b"xq_decode_plan_entries" in lib.xq_last_error()
+    # an empty sequence keeps its partition 0 (whose unit writes its zero output); a sequence of 500
+    # tokens with 1,024-token partitions has only partition 0
+    L = xq.CacheLayout(4, 2, 16, 4096)
+    plan = xq.xq_decode_plan(L, 3, 4, 3000, 3, [0, 500, 3000])
+    assert len(plan) == 3 * 3 * 2
+    want = {((b * 3 + s) * 2 + k) for b, ns in ((0, 1), (1, 1), (2, 3)) for s in range(ns) for k in range(2)}
+    assert set(u for u in plan if u >= 0) == want and sum(u >= 0 for u in plan) == len(want)

@@ -48,15 +48,14 @@ def test_fused_step_equals_append_then_decode(dtype, hq, hkv, ps):
     live = [b for b in range(W.batch) if lens[b] > 0]
     seq = to_dev(np.array(live, np.int32))
     pos = to_dev(np.array([lens[b] - 1 for b in live], np.int32))
-    order = None
     for splits in (0, 3, -256):
         for planned in (False, True):
             a, f = make_cache(W), make_cache(W)
             _fill_all_but_last(a, W, bt, kv)
             _fill_all_but_last(f, W, bt, kv)
-            if planned and order is None:
-                order = a.plan([int(x) for x in lens], hq, W.max_context_len, 0)
-            so = order if planned else None
+            # the plan of these arguments: a permutation of the batch with one partition per
+            # sequence, a unit placement with several
+            so = a.plan([int(x) for x in lens], hq, W.max_context_len, splits) if planned else None
             a.append(new_k[live].contiguous(), new_v[live].contiguous(), seq, pos, bt)
             want = a.decode(q, bt, cl, W.max_context_len, W.softmax_scale, splits, seq_order=so)
             got = f.append_decode(new_k, new_v, q, bt, cl, W.max_context_len, W.softmax_scale, splits,

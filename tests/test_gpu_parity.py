@@ -488,20 +488,26 @@ def test_planned_decode_is_bitwise_the_plain_decode(dtype):
         assert np.max(np.abs(got[b] - want)) <= TOL
 
 
-def test_planned_decode_where_the_plan_is_the_identity():
-    """A batch that is not a multiple of 8, and several partitions per sequence: the plan is the
-    identity and the planned call equals the plain one."""
+def test_planned_decode_with_identity_and_unit_plans():
+    """A batch that is not a multiple of 8 with one partition per sequence: the plan is the identity;
+    with several partitions it is a unit placement. Either way the planned call equals the plain one
+    bit for bit, an empty sequence (whose output is zeros) included."""
     _print_case("planned-identity")
-    lens = [300, 45, 700, 1, 1029, 64, 9]
+    lens = [300, 45, 700, 1, 1029, 0, 9]
     W = workloads.make("plan-id", 960, 4, lens, 16, 8, 16)
     cache = make_cache(W)
     bt, cl = upload_tables(W)
     fill(cache, W, bt)
     q = to_dev(W.q_bits())
-    for splits in (0, 4):
+    for splits in (1, 4, 0):
         order = cache.plan(lens, 16, W.max_context_len, splits)
-        assert order.cpu().tolist() == list(range(len(lens)))
+        if splits == 1:
+            assert order.cpu().tolist() == list(range(len(lens)))
+        else:
+            # (the library's own choice for 7 sequences of up to 1,029 tokens: 17 partitions of 64)
+            assert order.numel() == (4 if splits == 4 else 17) * 8 * len(lens)
         a = cache.decode(q, bt, cl, W.max_context_len, W.softmax_scale, splits)
         b = cache.decode(q, bt, cl, W.max_context_len, W.softmax_scale, splits, seq_order=order)
         torch.cuda.synchronize()
         assert torch.equal(a, b)
+        assert not torch.any(b[5])
