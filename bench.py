@@ -460,7 +460,10 @@ def main():
         if sum(len(p[2]) for p in pend) >= (1 << 19) or b == W.num_seqs - 1:
             batches.append(tuple(to_dev(np.concatenate([p[i] for p in pend])) for i in range(4)))
             pend = []
+    for k, v, s, p in batches:          # fills the cache (the first launches also load the kernel)
+        base.append(k, v, s, p, bt)
     torch.cuda.synchronize()
+    # timed: the same rows again (same slots, same bytes), as a steady-state bulk append
     fill_ev = event_pairs(len(batches))
     for (a, b), (k, v, s, p) in zip(fill_ev, batches):
         a.record(stream)

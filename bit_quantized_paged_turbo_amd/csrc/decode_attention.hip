@@ -986,7 +986,11 @@ __device__ __forceinline__ void process_pair_tile(const PairTile<DT>& t, WaveSta
     st.m = up ? mx : st.m;
     st.l *= f;
     // PV row 4 gg + r is column n = 4 gg + r: head (n mod 2G) mod G, whose factor lane n has
-    const int g4 = (lane >> 4) * 4;
+    // (computed here from an opaque copy of the lane id, not hoisted into registers the tile
+    // loop lacks)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int g4 = (ln >> 4) * 4;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int nr = g4 + r;
@@ -1249,16 +1253,22 @@ __device__ __forceinline__ void process_quad(const QuadData<DT>& d, WaveState& s
   float mx = __builtin_fmaf(ymax, qs, (float)(smax >> 10));
   if (__builtin_expect(__any(mx > st.m + kLazy), 0)) {
     // head maximum over the lanes of head hn: columns hn + G j (j = 0..3), all lane groups
-    const int base = lane & 48, J4 = 4 * G;
-    mx = fmaxf(mx, __shfl(mx, base | ((ql.ne + G) % J4)));
-    mx = fmaxf(mx, __shfl(mx, base | ((ql.ne + 2 * G) % J4)));
+    // The source lanes are recomputed here from an opaque copy of the lane id: hoisted out of the
+    // tile loop, their divisions by G would hold registers the loop lacks (and be spilled, their
+    // reloads draining the ring's loads).
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int base = ln & 48, J4 = 4 * G, n = ln & 15;
+    const int ne = n < J4 ? n : n % J4;
+    mx = fmaxf(mx, __shfl(mx, base | ((ne + G) % J4)));
+    mx = fmaxf(mx, __shfl(mx, base | ((ne + 2 * G) % J4)));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const bool up = mx > st.m + kLazy;
     const float f = up ? __builtin_amdgcn_exp2f(st.m - mx) : 1.f;
     st.m = up ? mx : st.m;
     st.l *= f;
-    const int g4 = gg * 4;
+    const int g4 = (ln >> 4) * 4;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int nr = g4 + r;

@@ -10,8 +10,10 @@
 // section "Getting a server up: the commands in the README"): the nearest finite OCP E4M3 value of
 // each element, ties to even, saturating at 448; bf16: the row as it is.
 //
-// Sixteen lanes own a row (an aligned group of 16 lanes of a wave), eight consecutive elements
-// each. The arithmetic is compiled without FP contraction so codes and scales are bit-identical
+// LPR lanes (an aligned group of a wave) own a row: lane l of the group holds the 16 / LPR groups
+// of eight consecutive elements 8 (l + LPR k) .. 8 (l + LPR k) + 7, k < 16 / LPR, so that for
+// each k the group's lanes hold one contiguous piece of the row (one coalesced 16-byte load per
+// lane). The arithmetic is compiled without FP contraction so codes and scales are bit-identical
 // to the CPU definition.
 #pragma once
 
@@ -60,121 +62,238 @@ __device__ __forceinline__ float shfl_xor16(float v) {
   }
 }
 
-template <int M>
-__device__ __forceinline__ void fwht_cross(float (&r)[8], int lane16) {
-  const bool upper = (lane16 & M) != 0;
+// Cross-lane butterfly stage h = 8 M (partner lane l ^ M): the lane holding the lower element of
+// each pair keeps a + b, its partner a - b. The partner negates its own value first, so both lanes
+// add: other + (-b) is exactly a - b in IEEE arithmetic, and b + a exactly a + b.
+template <int M, int K>
+__device__ __forceinline__ void fwht_cross(float (&r)[K][8], int l) {
+  const uint32_t neg = (l & M) ? 0x80000000u : 0u;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float other = shfl_xor16<M>(r[e]);
-    r[e] = upper ? (other - r[e]) : (r[e] + other);
+  for (int k = 0; k < K; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float mine = __uint_as_float(__float_as_uint(r[k][e]) ^ neg);
+      r[k][e] = shfl_xor16<M>(r[k][e]) + mine;
+    }
+}
+
+template <int M>
+__device__ __forceinline__ float max_xor(float v) {
+  return fmaxf(v, shfl_xor16<M>(v));
+}
+
+// Unnormalised FWHT of the row in stage order h = 1, 2, ..., 64: element 8 (l + LPR k) + e sits
+// in r[k][e] of lane l, so stages 1..4 pair elements of one lane's group, stages 8 .. 4 LPR pair
+// lanes, and stages 8 LPR .. 64 pair groups k of one lane.
+template <int LPR>
+__device__ __forceinline__ void fwht_row(float (&r)[16 / LPR][8], int l) {
+#pragma clang fp contract(off)
+  constexpr int K = 16 / LPR;
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if ((e & h) == 0) {
+          const float a = r[k][e], b = r[k][e + h];
+          r[k][e] = a + b;
+          r[k][e + h] = a - b;
+        }
+  if constexpr (LPR >= 2) fwht_cross<1>(r, l);
+  if constexpr (LPR >= 4) fwht_cross<2>(r, l);
+  if constexpr (LPR >= 8) fwht_cross<4>(r, l);
+  if constexpr (LPR >= 16) fwht_cross<8>(r, l);
+#pragma unroll
+  for (int m = 1; m < K; m <<= 1)
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      if ((k & m) == 0)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float a = r[k][e], b = r[k + m][e];
+          r[k][e] = a + b;
+          r[k + m][e] = a - b;
+        }
+}
+
+// Eight codes (their low bits) packed little-endian into one 8 BITS-bit field.
+template <int BITS>
+__device__ __forceinline__ uint32_t pack8(const uint32_t (&c)[8]) {
+  constexpr uint32_t mask = (1u << BITS) - 1u;
+  if constexpr (BITS == 4) {
+    uint32_t p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = ((c[2 * i + 1] << 4) | (c[2 * i] & mask)) & 0xffu;
+    return p[0] | (p[1] << 8) | (p[2] << 16) | (p[3] << 24);
+  } else {
+    static_assert(BITS == 2 || BITS == 3, "turbo8 packs bytes");
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w |= (c[e] & mask) << (BITS * e);
+    return w;
   }
 }
 
-// Encode one row: raw = this lane's eight bf16 elements (8 lane16 .. 8 lane16 + 7); block = the
-// (page, kv head) block, slot = the token's slot in the page.
-template <int BITS>
-__device__ __forceinline__ void encode_row(const uint4 raw, int lane16, uint8_t* block, int slot, int page_size) {
+// The row's codes from the transform output x (unscaled), packed: w[k][0] holds group k's field
+// (8 BITS bits; turbo8 uses w[k][0] and w[k][1], four bytes each). The definition is
+// c = clamp(rint(fl(fl(x C) / s16)), +-qmax), 0 when s16 = 0. For turbo4/3/2 (qmax <= 7) the
+// quotient is first taken as y = x * fl(C * rcp(s16)): the hardware reciprocal is within one ulp,
+// so |y - fl(fl(x C) / s16)| <= (qmax + 1/4) * 2^-21.4 < 2^-18 whenever the row's largest |y| is
+// below qmax + 1/4, and rint(y) (taken by adding 1.5 * 2^23, whose sum holds the integer in its
+// low mantissa bits) is the exact code unless y lies within 2^-16 of a half-integer. A lane where
+// that can fail (a near tie, a large or non-finite |y|) recomputes its codes with IEEE division.
+template <int BITS, int K>
+__device__ __forceinline__ void quantize_pack(const float (&x)[K][8], float xmax, float sf, uint32_t (&w)[K][2]) {
 #pragma clang fp contract(off)
+  constexpr int qmax = (1 << (BITS - 1)) - 1;
+  bool exact = true;
+  if constexpr (qmax <= 7) {
+    constexpr float kMagic = 0x1.8p23f;
+    constexpr float kEps = 0x1p-16f;
+    const float kq = sf != 0.f ? kRotC * __builtin_amdgcn_rcpf(sf) : 0.f;
+    bool redo = !(xmax * kq < (float)qmax + 0.25f);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      uint32_t c[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float y = x[k][e] * kq;
+        const float m = y + kMagic;
+        const float d = (m - kMagic) - y;
+        redo |= !(fabsf(d) < 0.5f - kEps);
+        c[e] = __float_as_uint(m);
+      }
+      w[k][0] = pack8<BITS>(c);
+      w[k][1] = 0u;
+    }
+    exact = redo;
+  }
+  if (exact) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      uint32_t c[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float q = fminf(fmaxf(rintf((x[k][e] * kRotC) / sf), (float)-qmax), (float)qmax);
+        c[e] = (uint32_t)(int)(sf != 0.f ? q : 0.f);   // (a select: no branch per element)
+      }
+      if constexpr (BITS == 8) {
+        w[k][0] = (c[0] & 0xffu) | ((c[1] & 0xffu) << 8) | ((c[2] & 0xffu) << 16) | (c[3] << 24);
+        w[k][1] = (c[4] & 0xffu) | ((c[5] & 0xffu) << 8) | ((c[6] & 0xffu) << 16) | (c[7] << 24);
+      } else {
+        w[k][0] = pack8<BITS>(c);
+        w[k][1] = 0u;
+      }
+    }
+  }
+}
+
+// Encode one row: raw[k] = this lane's eight bf16 elements 8 (l + LPR k) .. + 7; block = the
+// (page, kv head) block, slot = the token's slot in the page.
+template <int BITS, int LPR>
+__device__ __forceinline__ void encode_row_lanes(const uint4 (&raw)[16 / LPR], int l, uint8_t* block, int slot,
+                                                 int page_size) {
+#pragma clang fp contract(off)
+  constexpr int K = 16 / LPR;
   if constexpr (BITS == 0) {
     // unquantized cache: copy the bf16 row into its slot
-    *reinterpret_cast<uint4*>(block + (int64_t)slot * 256 + lane16 * 16) = raw;
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      *reinterpret_cast<uint4*>(block + (int64_t)slot * 256 + (l + LPR * k) * 16) = raw[k];
     return;
   } else if constexpr (BITS == kFp8) {
-    // fp8 cache: eight E4M3 bytes per lane, elements 8 lane16 .. 8 lane16 + 7
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-    uint32_t lo = 0, hi = 0;
+    // fp8 cache: eight E4M3 bytes per group
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t b0 = fp8_e4m3(bf16_lo(w[e])), b1 = fp8_e4m3(bf16_hi(w[e]));
-      const uint32_t pair = b0 | (b1 << 8);
-      if (e < 2) lo |= pair << (16 * e);
-      else hi |= pair << (16 * (e - 2));
+    for (int k = 0; k < K; ++k) {
+      const uint32_t w[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t b0 = fp8_e4m3(bf16_lo(w[e])), b1 = fp8_e4m3(bf16_hi(w[e]));
+        const uint32_t pair = b0 | (b1 << 8);
+        if (e < 2) lo |= pair << (16 * e);
+        else hi |= pair << (16 * (e - 2));
+      }
+      *reinterpret_cast<uint2*>(block + (int64_t)slot * 128 + (l + LPR * k) * 8) = make_uint2(lo, hi);
     }
-    *reinterpret_cast<uint2*>(block + (int64_t)slot * 128 + lane16 * 8) = make_uint2(lo, hi);
     return;
   } else {
     constexpr int qmax = (1 << (BITS - 1)) - 1;
-    float r[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
-                  bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
-    // in-lane stages h = 1, 2, 4 (element index 8*lane16 + e)
+    float r[K][8];
 #pragma unroll
-    for (int h = 1; h < 8; h <<= 1) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if ((e & h) == 0) {
-          const float a = r[e], b = r[e + h];
-          r[e] = a + b;
-          r[e + h] = a - b;
-        }
-      }
+    for (int k = 0; k < K; ++k) {
+      r[k][0] = bf16_lo(raw[k].x);
+      r[k][1] = bf16_hi(raw[k].x);
+      r[k][2] = bf16_lo(raw[k].y);
+      r[k][3] = bf16_hi(raw[k].y);
+      r[k][4] = bf16_lo(raw[k].z);
+      r[k][5] = bf16_hi(raw[k].z);
+      r[k][6] = bf16_lo(raw[k].w);
+      r[k][7] = bf16_hi(raw[k].w);
     }
-    // cross-lane stages h = 8, 16, 32, 64: the lane with bit (h/8) clear holds the lower
-    // element of every pair and keeps a + b; its partner keeps a - b.
-    fwht_cross<1>(r, lane16);
-    fwht_cross<2>(r, lane16);
-    fwht_cross<4>(r, lane16);
-    fwht_cross<8>(r, lane16);
-    float amax = 0.f;
+    fwht_row<LPR>(r, l);
+    // absmax of the rotated row: max |fl(x C)| = fl(max |x| * C), rounding being monotonic
+    // (NaN elements are passed over, as by fmaxf)
+    float xm = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      r[e] = r[e] * kRotC;
-      amax = fmaxf(amax, fabsf(r[e]));
-    }
-    amax = fmaxf(amax, shfl_xor16<1>(amax));
-    amax = fmaxf(amax, shfl_xor16<2>(amax));
-    amax = fmaxf(amax, shfl_xor16<4>(amax));
-    amax = fmaxf(amax, shfl_xor16<8>(amax));
-
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xm = fmaxf(xm, fabsf(r[k][e]));
+    if constexpr (LPR >= 2) xm = max_xor<1>(xm);
+    if constexpr (LPR >= 4) xm = max_xor<2>(xm);
+    if constexpr (LPR >= 8) xm = max_xor<4>(xm);
+    if constexpr (LPR >= 16) xm = max_xor<8>(xm);
+    const float amax = xm * kRotC;
     const float s32 = amax / (float)qmax;
     const _Float16 s16 = (_Float16)fminf(s32, 65504.f);
     const float sf = (float)s16;
-    int code[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float c = 0.f;
-      if (sf != 0.f) c = fminf(fmaxf(rintf(r[e] / sf), (float)-qmax), (float)qmax);
-      code[e] = (int)c;
-    }
+    uint32_t pw[K][2];
+    quantize_pack<BITS, K>(r, xm, sf, pw);
 
     constexpr int rowb = 16 * BITS;
     uint8_t* dst = block + (int64_t)slot * rowb;
-    if constexpr (BITS == 4) {
-      uint32_t w = 0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w |= (uint32_t)(code[e] & 0xf) << (4 * e);
-      *reinterpret_cast<uint32_t*>(dst + 4 * lane16) = w;
-    } else if constexpr (BITS == 8) {
-      uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        w0 |= (uint32_t)(code[e] & 0xff) << (8 * e);
-        w1 |= (uint32_t)(code[e + 4] & 0xff) << (8 * e);
+    for (int k = 0; k < K; ++k) {
+      const int grp = l + LPR * k;   // group of eight elements within the row
+      if constexpr (BITS == 8) {
+        *reinterpret_cast<uint2*>(dst + 8 * grp) = make_uint2(pw[k][0], pw[k][1]);
+      } else if constexpr (BITS == 4) {
+        *reinterpret_cast<uint32_t*>(dst + 4 * grp) = pw[k][0];
+      } else if constexpr (BITS == 2) {
+        *reinterpret_cast<uint16_t*>(dst + 2 * grp) = (uint16_t)pw[k][0];
+      } else {
+        // BITS == 3: 24 bits per group at bit offset 24 grp. The LPR groups of one k are
+        // contiguous (3 LPR / 4 dwords); dword j of them starts in group (32 j) / 24 at bit
+        // (32 j) mod 24, so lane j < 3 LPR / 4 joins its group's field with the next lane's.
+        const uint32_t v = pw[k][0];
+        const int src = (32 * l) / 24, off = (32 * l) % 24;
+        uint32_t lo, hi;
+        if constexpr (LPR == 4) {
+          // lane l takes lanes l (l < 3: src = l) and l + 1 of its quad (DPP quad_perm [1,2,3,3])
+          lo = v;
+          hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xF9, 0xF, 0xF, true);
+        } else {
+          const int base = (threadIdx.x & 63) & ~(LPR - 1);
+          lo = (uint32_t)__shfl((int)v, base + min(src, LPR - 1), 64);
+          hi = (uint32_t)__shfl((int)v, base + min(src + 1, LPR - 1), 64);
+        }
+        const uint32_t wd = (lo >> off) | (hi << (24 - off));
+        if (l < 3 * LPR / 4) *reinterpret_cast<uint32_t*>(dst + 3 * LPR * k + 4 * l) = wd;
       }
-      *reinterpret_cast<uint2*>(dst + 8 * lane16) = make_uint2(w0, w1);
-    } else if constexpr (BITS == 2) {   // 16 bits per lane, two bytes
-      uint32_t w = 0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) w |= (uint32_t)(code[e] & 0x3) << (2 * e);
-      *reinterpret_cast<uint16_t*>(dst + 2 * lane16) = (uint16_t)w;
-    } else {  // BITS == 3: 24 bits per lane at bit offset 24*lane16; 12 dwords per row
-      uint32_t v = 0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v |= (uint32_t)(code[e] & 0x7) << (3 * e);
-      // dword k of the row starts in lane (32k)/24 at bit offset 32k mod 24
-      const int k = lane16;
-      const int src_lane = (32 * k) / 24;
-      const int off = (32 * k) % 24;
-      const int base = threadIdx.x & ~15;
-      const uint32_t lo = (uint32_t)__shfl((int)v, base + min(src_lane, 15), 64);
-      const uint32_t hi = (uint32_t)__shfl((int)v, base + min(src_lane + 1, 15), 64);
-      const uint32_t w = (lo >> off) | (hi << (24 - off));
-      if (k < 12) *reinterpret_cast<uint32_t*>(dst + 4 * k) = w;
     }
-    if (lane16 == 0) {
+    if (l == 0) {
       uint16_t* sdst = reinterpret_cast<uint16_t*>(block + (int64_t)page_size * rowb) + slot;
       *sdst = __builtin_bit_cast(uint16_t, s16);
     }
   }
+}
+
+// Sixteen lanes per row, one group each (the fused append + decode path).
+template <int BITS>
+__device__ __forceinline__ void encode_row(const uint4 raw, int lane16, uint8_t* block, int slot, int page_size) {
+  const uint4 g[1] = {raw};
+  encode_row_lanes<BITS, 16>(g, lane16, block, slot, page_size);
 }
 
 }  // namespace codec

@@ -3,15 +3,31 @@ partitions) captured once into a HIP graph and replayed: the library allocates n
 nothing with memset and never waits on the host, so the captured launches are the whole step.
 The xInfer page replays its decode step as a captured graph (section "What actually sits
 between the request and the tokens"). Every replay, with eager work and synchronisations in
-between, must reproduce the eager step bit for bit."""
+between, must reproduce the eager step bit for bit, and every replay's output is also checked
+against the oracle at the parity bar (2e-3 max-abs)."""
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads
 from tests.gpu_util import fill, make_cache, to_dev, upload_tables
 
 pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def _oracle_outs(W, q_bits, kv):
+    """The oracle's decode of every sequence (its rows after the step's append)."""
+    return [oracle.decode_sequence(W.dtype, q_bits[b], kv[b][0], kv[b][1], W.softmax_scale)[0]
+            for b in range(W.batch)]
+
+
+def _check_oracle(W, out, wants, what):
+    got = out.cpu().numpy().astype(np.float64)
+    for b, want in enumerate(wants):
+        err = np.max(np.abs(got[b] - want))
+        assert err <= TOL, f"{what}: seq {b} (L={W.seq_len(b)}): {err:.3e} from the oracle"
 
 
 @pytest.mark.parametrize("dtype,hq", [(4, 16), (8, 32), (3, 40)])
@@ -23,7 +39,8 @@ def test_step_replays_from_a_captured_graph(dtype, hq):
     bt, cl = upload_tables(W)
     kv = {b: W.kv_bits(b) for b in range(W.batch)}
     fill(cache, W, bt, kv=kv)
-    q = to_dev(W.q_bits())
+    qb = W.q_bits()
+    q = to_dev(qb)
     # the step's new rows: each sequence's last position again (same data, so every replay
     # leaves the cache as it was)
     k_new = to_dev(np.stack([kv[b][0][-1] for b in range(W.batch)]))
@@ -53,6 +70,7 @@ def test_step_replays_from_a_captured_graph(dtype, hq):
     with torch.cuda.graph(graph):
         step()
     torch.cuda.synchronize()
+    wants = _oracle_outs(W, qb, kv)
     for r in range(4):
         out.fill_(float("nan"))
         scratch = torch.randn(1 << 20, device="cuda").sum()     # unrelated eager work
@@ -61,16 +79,17 @@ def test_step_replays_from_a_captured_graph(dtype, hq):
         torch.cuda.synchronize()
         assert torch.equal(out, want), f"replay {r} differs from the eager step"
         assert bool(torch.isfinite(scratch))
+        _check_oracle(W, out, wants, f"replay {r}")
     del graph
 
 
 def test_layer_steps_replay_from_one_graph():
     """Several fused append + decode steps, one per layer cache, captured into ONE graph (as a
     model's decode graph holds a step per layer) and replayed: every layer's output must equal
-    its eager step bit for bit on every replay."""
+    its eager step bit for bit on every replay, and the oracle's decode within the parity bar."""
     print("CASE graph layers", flush=True)
     lens = [300, 45, 700, 1, 1029, 64, 513, 128, 2000, 17, 900, 31, 256, 640, 77, 1500]
-    hq, layers = 16, []
+    hq, layers, refs = 16, [], []
     for layer in range(3):
         W = workloads.make(f"graph-layer-{layer}", 950 + layer, 4, lens, hq, 8, 16)
         cache = make_cache(W)
@@ -85,6 +104,7 @@ def test_layer_steps_replay_from_one_graph():
         order = cache.plan([int(x) for x in W.context_lens], hq, max_ctx, 0)
         out = torch.empty((W.batch, hq, 128), dtype=torch.float32, device="cuda")
         layers.append((W, cache, bt, cl, to_dev(W.q_bits()), k_new, v_new, ws, order, out))
+        refs.append(_oracle_outs(W, W.q_bits(), kv))
 
     def step(layer):
         W, cache, bt, cl, q, k_new, v_new, ws, order, out = layer
@@ -118,5 +138,6 @@ def test_layer_steps_replay_from_one_graph():
         torch.cuda.synchronize()
         for i, layer in enumerate(layers):
             assert torch.equal(layer[-1], want[i]), f"replay {r}, layer {i} differs from its eager step"
+            _check_oracle(layer[0], layer[-1], refs[i], f"replay {r}, layer {i}")
         assert bool(torch.isfinite(scratch))
     del graph
