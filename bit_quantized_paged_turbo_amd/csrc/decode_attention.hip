@@ -940,10 +940,12 @@ __device__ __forceinline__ v4i pair_k_operand(const PairTile<DT>& t, int m) {
   }
 }
 
-template <int DT>
+// refill(): called once the tile's products are issued (the ring's next load goes out while
+// the matrix cores work).
+template <int DT, typename Refill>
 __device__ __forceinline__ void process_pair_tile(const PairTile<DT>& t, WaveState& st, const v4i (&qj)[4][kDigits],
                                                   float qs, int lim, bool full, const PairLane& pl, int G,
-                                                  int lane) {
+                                                  int lane, Refill&& refill) {
   // ---- scores: y' = s_k * (q.c) in integer-digit units; the log2-domain score is y' * qs ------
   v4i s[kDigits];
 #pragma unroll
@@ -954,6 +956,7 @@ __device__ __forceinline__ void process_pair_tile(const PairTile<DT>& t, WaveSta
 #pragma unroll
     for (int k = 0; k < kDigits; ++k) s[k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qj[m][k], s[k], 0, 0, 0);
   }
+  refill();
   const uint32_t ks[4] = {(uint32_t)t.ks[0], (uint32_t)t.ks[0] >> 16, (uint32_t)t.ks[1], (uint32_t)t.ks[1] >> 16};
   uint32_t sv[4] = {(uint32_t)t.vs[0] & 0xffffu, (uint32_t)t.vs[0] >> 16, (uint32_t)t.vs[1] & 0xffffu,
                     (uint32_t)t.vs[1] >> 16};
@@ -1224,13 +1227,14 @@ __device__ __forceinline__ void read_quad(QuadData<DT>& d, const uint8_t* slot0,
 }
 
 // One 64-token group, from registers.
-template <int DT>
+template <int DT, typename Refill>
 __device__ __forceinline__ void process_quad(const QuadData<DT>& d, WaveState& st, const v4i (&qq)[8][kDigits],
                                              float qs, int lim, bool full, const QuadLane& ql, int G,
-                                             int lane) {
+                                             int lane, Refill&& refill) {
   const int gg = lane >> 4;
   v4i s[kDigits];
   quad_qk<DT>(d.k, qq, s);
+  refill();   // as for a pair tile
   const v2i ksw = d.ksw, vsw = d.vsw;
   const uint32_t ks[4] = {(uint32_t)ksw[0], (uint32_t)ksw[0] >> 16, (uint32_t)ksw[1], (uint32_t)ksw[1] >> 16};
   uint32_t sv[4] = {(uint32_t)vsw[0] & 0xffffu, (uint32_t)vsw[0] >> 16, (uint32_t)vsw[1] & 0xffffu,
@@ -1664,7 +1668,8 @@ void decode_split_kernel(DecodeParams p) {
       // Tiles 0 .. DEPTH - 2 go to their slots beside the query rows (last slot); loads complete
       // in issue order, so the rows are in once at most the staged tiles' loads are pending.
       // After the query is prepared its slot takes tile DEPTH - 1. A step reads its tiles from
-      // LDS into registers, waits for those reads and refills the freed slots before the math,
+      // LDS into registers, issues their QK products, then waits for the reads and refills the
+      // freed slots (the paired and quad layouts; the one-block layout refills before its math),
       // so DEPTH tiles are in flight while it computes.
       for (int i = 0; i < DEPTH - 1 && i < ntiles; ++i) stage(i, i);
       // the new rows' stores go out behind the first tiles (the extra operations only make the
@@ -1688,11 +1693,15 @@ void decode_split_kernel(DecodeParams p) {
             const int nxt = next_slot(cur);
             QuadData<DT> qd;
             read_quad<DT>(qd, smem + cur * S::kSlot, smem + nxt * S::kSlot, ql, lane);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            if (it + DEPTH < ntiles) stage(it + DEPTH, cur);
-            if (it + DEPTH + 1 < ntiles) stage(it + DEPTH + 1, nxt);
+            // the freed slots are refilled once the reads are complete, after the step's QK
+            // products are issued
+            auto refill = [&]() __attribute__((always_inline)) {
+              asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+              if (it + DEPTH < ntiles) stage(it + DEPTH, cur);
+              if (it + DEPTH + 1 < ntiles) stage(it + DEPTH + 1, nxt);
+            };
             const int t0 = tok_begin + 32 * it;
-            process_quad<DT>(qd, st, qq, qs, tok_end - t0 - 4 * g, t0 + 64 <= tok_end, ql, G, lane);
+            process_quad<DT>(qd, st, qq, qs, tok_end - t0 - 4 * g, t0 + 64 <= tok_end, ql, G, lane, refill);
             cur = next_slot(nxt);
           }
           return;
@@ -1704,18 +1713,21 @@ void decode_split_kernel(DecodeParams p) {
         // outstanding
         if (it + DEPTH - 1 < ntiles) wait_vm<(DEPTH - 1) * S::kOps>();
         else wait_tiles<S::kOps, 0, DEPTH - 1>(ntiles - 1 - it);
-        if constexpr (decltype(kPair)::value) {
-          read_slot_pair<DT>(tile, smem + cur * S::kSlot, lane, pl);
-        } else {
-          read_slot<DT>(tile, smem + cur * S::kSlot, lane);
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if (it + DEPTH < ntiles) stage(it + DEPTH, cur);
+        const int rs = cur;   // the slot read
+        auto refill = [&]() __attribute__((always_inline)) {
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          if (it + DEPTH < ntiles) stage(it + DEPTH, rs);
+        };
         cur = next_slot(cur);
         if constexpr (decltype(kPair)::value) {
+          read_slot_pair<DT>(tile, smem + rs * S::kSlot, lane, pl);
+          // the freed slot is refilled once the reads are complete, after the QK products are
+          // issued
           const int t0 = tok_begin + 32 * it;
-          process_pair_tile<DT>(tile, st, qj, qs, tok_end - t0 - 4 * g, t0 + 32 <= tok_end, pl, G, lane);
+          process_pair_tile<DT>(tile, st, qj, qs, tok_end - t0 - 4 * g, t0 + 32 <= tok_end, pl, G, lane, refill);
         } else {
+          read_slot<DT>(tile, smem + rs * S::kSlot, lane);
+          refill();
           run(tile, it);
         }
       }
@@ -1950,12 +1962,16 @@ int pick_depth(const DecodeParams& p) {
     const int64_t slots = kLdsPerCu / (per_cu * Stage<DT>::kSlot);
     const int64_t cap = kMaxVmcnt / Stage<DT>::kOps + 1;
     const int64_t d = std::min<int64_t>(slots, cap);
-    // Deep rings cost occupancy (two waves per SIMD at most). They pay where they enable the quad
-    // layout (turbo4, turbo8) with up to two waves per SIMD, and otherwise only for a single wave
-    // per SIMD: on c3's shape turbo3 at two units per SIMD runs 76.6 us with three slots against
-    // 78.1 with four.
-    if (per_cu <= (kQuadOk<DT> ? 8 : 4) && d >= 4) return d >= 8 ? 8 : d >= 6 ? 6 : 4;
-    return d >= 3 ? 3 : 2;
+    // Deep rings cost occupancy (two waves per SIMD at most) and pay only for a single wave per
+    // SIMD, or for turbo8's quad layout at up to two. Measured on MI355X with two or three waves
+    // per SIMD, the loads in flight are not what limits a unit: two slots run as fast as three or
+    // four (turbo4, 256 sequences of up to 1,024 tokens: 40.7 us with two slots, 41.4 with three,
+    // 42.7 with four in the quad layout; turbo3, one 262,144-token sequence in 256 partitions:
+    // 80.0, 81.0, 81.2), six run far slower (57 and 116 us), and turbo8 gains from its quad
+    // layout (32 sequences of 8,192 tokens: 109 us with four slots, 116 with two or three).
+    if (per_cu <= 4 && d >= 4) return d >= 8 ? 8 : d >= 6 ? 6 : 4;
+    if (DT == 8 && per_cu <= 8 && d >= 4) return 4;
+    return 2;
   }
 }
 
