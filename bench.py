@@ -7,9 +7,11 @@ A step is one pass of the whole hot path for one layer:
      sequence's new row, plus the prefill chunk where the workload has one (the default, the
      mixed step: a 2,048-token chunk appended for a new sequence, then a batch of 64 decodes);
   2. decode attention over every sequence's paged, quantized context.
-By default one xq_append_decode_attention launch appends the batch's new rows and decodes (the
-chunk goes through xq_quantize_append first); --no-fuse runs xq_quantize_append and the decode
-as two launches. The decode uses the host plan (xq_decode_plan) unless --no-plan.
+By default one decode launch appends the batch's new rows and decodes (the chunk goes through
+xq_quantize_append first); --no-fuse runs xq_quantize_append and the decode as two launches. The
+decode runs over a length-aware plan by default (xq_decode_plan_balanced: each sequence gets its
+own partition size, all work units about equal); --plan uniform takes the split hint's partitions
+placed by xq_decode_plan, --plan none (or --no-plan) neither.
 
 Steps are timed twice, K each after W warm-up steps: eagerly, with HIP events around every
 decode call and every append call (on the stream they are launched on), and replayed from HIP
@@ -78,7 +80,10 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunk-prefill timing")
     ap.add_argument("--no-probe", action="store_true", help="skip the streaming-read reference")
-    ap.add_argument("--no-plan", action="store_true", help="decode without the host plan")
+    ap.add_argument("--plan", choices=("balanced", "uniform", "none"), default="balanced",
+                    help="host plan of the decode: length-aware partitions (xq_decode_plan_balanced), "
+                         "the split hint's partitions placed by xq_decode_plan, or none")
+    ap.add_argument("--no-plan", action="store_true", help="the same as --plan none")
     ap.add_argument("--no-fuse", action="store_true",
                     help="append the batch's new rows in their own launch instead of the decode's")
     ap.add_argument("--serial-draws", action="store_true",
@@ -294,8 +299,13 @@ class Step:
     def decode(self, stream: int):
         lib = self.lib
         c = self.cache
-        q, batch, hq, bt, maxp, cl, maxctx, scale, splits, ws, wsb, out, order, n_order, fused = self.dec
-        if fused is not None:
+        q, batch, hq, bt, maxp, cl, maxctx, scale, splits, ws, wsb, out, order, n_order, fused, bal = self.dec
+        if bal is not None:
+            kn, vn = fused if fused is not None else (None, None)
+            st = lib.xq_decode_attention_balanced(self.L, q, batch, hq, c.k_pool.data_ptr(), c.v_pool.data_ptr(),
+                                                  bt, maxp, cl, maxctx, scale, bal[0], bal[1], bal[2], kn, vn,
+                                                  ws, wsb, out, stream)
+        elif fused is not None:
             st = lib.xq_append_decode_attention(self.L, fused[0], fused[1], q, batch, hq, c.k_pool.data_ptr(),
                                                 c.v_pool.data_ptr(), bt, maxp, cl, maxctx, scale, splits,
                                                 ws, wsb, out, order, n_order, stream)
@@ -495,7 +505,14 @@ def main():
     q = to_dev(W.q_bits())
     cl = to_dev(W.context_lens.astype(np.int32))
     out = torch.empty((B, hq, 128), dtype=torch.float32, device=dev)
-    wsb = base.workspace_bytes(B, hq, W.max_context_len, splits)
+    if args.no_plan:
+        args.plan = "none"
+    bal = None
+    if args.plan == "balanced":
+        bal = base.plan_balanced([int(x) for x in W.context_lens], hq, W.max_context_len, device=dev)
+        wsb = xq.xq_decode_workspace_bytes_balanced(base.layout, B, hq, bal[0])
+    else:
+        wsb = base.workspace_bytes(B, hq, W.max_context_len, splits)
     ws = torch.empty((max(wsb, 16),), dtype=torch.uint8, device=dev)
     maxp = W.max_pages_per_seq
     fuse = not args.no_fuse
@@ -517,12 +534,13 @@ def main():
         app = None
     # the host plan: long and short sequences share SIMDs (identity where it cannot help)
     order = None
-    if not args.no_plan:
+    if args.plan == "uniform":
         order = base.plan([int(x) for x in W.context_lens], hq, W.max_context_len, splits, device=dev)
     dec = (q.data_ptr(), B, hq, bt.data_ptr(), maxp, cl.data_ptr(), W.max_context_len,
            W.softmax_scale, splits, ws.data_ptr(), wsb, out.data_ptr(),
            None if order is None else order.data_ptr(), 0 if order is None else int(order.numel()),
-           (new_k.data_ptr(), new_v.data_ptr()) if fuse else None)
+           (new_k.data_ptr(), new_v.data_ptr()) if fuse else None,
+           None if bal is None else (bal[0], bal[1].data_ptr(), bal[2].data_ptr()))
     runners = [Step(lib, c.layout, c, app, dec) for c in caches]
 
     log(f"{R} pool replicas of {footprint} bytes; timing")
@@ -619,7 +637,7 @@ def main():
 
     kv_bytes = int(W.context_lens.astype(np.int64).sum()) * hkv * 2 * rb
     tokens = int(W.context_lens.astype(np.int64).sum())
-    nsplits = xq.xq_decode_num_splits(base.layout, B, hq, W.max_context_len, splits)
+    nsplits = bal[0] if bal is not None else xq.xq_decode_num_splits(base.layout, B, hq, W.max_context_len, splits)
     by_graph = graph is not None and graph["replicas"] == R
     by_layers = by_graph and "multi_step_ms_per_step" in graph
     timed_ms = graph["multi_step_ms_per_step"] if by_layers else graph["ms_per_step"] if by_graph else step_ms
@@ -660,7 +678,8 @@ def main():
             "batch": B, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": 128,
             "page_size": W.page_size, "context_tokens": tokens, "max_context": W.max_context_len,
             "splits": nsplits, "chunk_append_tokens": W.chunk_tokens, "pool_replicas": R,
-            "plan": (None if order is None else "permutation of the batch" if int(order.numel()) == B
+            "plan": ("length-aware partitions (xq_decode_plan_balanced)" if bal is not None else
+                     None if order is None else "permutation of the batch" if int(order.numel()) == B
                      else "unit placement (longest first, balanced SIMDs)"),
             "fused_append": fuse,
         },
@@ -685,7 +704,8 @@ def main():
                      "frac_kernel_trace": (round(kv_bytes / (kernel_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
                                            if kernel_us else None),
                      "kernel_trace_us": kernel_us,
-                     "kernel": ("xq_append_decode_attention" if fuse else "xq_paged_decode_attention")
+                     "kernel": ("xq_decode_attention_balanced" if bal is not None else
+                                "xq_append_decode_attention" if fuse else "xq_paged_decode_attention")
                                + " call (decode_split_kernel"
                                + (" + decode_combine_kernel)" if nsplits > 1 else ")"),
                      "bytes_per_launch": kv_bytes,

@@ -21,7 +21,8 @@ EXPORTS = ("xq_block_bytes", "xq_page_stride_bytes", "xq_pool_bytes", "xq_decode
            "xq_decode_workspace_bytes", "xq_status_string", "xq_last_error",
            "xq_quantize_append", "xq_paged_decode_attention", "xq_paged_prefill_attention",
            "xq_decode_plan", "xq_paged_decode_attention_planned", "xq_append_decode_attention",
-           "xq_hbm_read_probe", "xq_paged_decode_attention_noalloc", "xq_decode_plan_entries")
+           "xq_hbm_read_probe", "xq_paged_decode_attention_noalloc", "xq_decode_plan_entries",
+           "xq_decode_plan_balanced", "xq_decode_workspace_bytes_balanced", "xq_decode_attention_balanced")
 
 
 class XqError(RuntimeError):
@@ -76,6 +77,10 @@ def load() -> ctypes.CDLL:
                                                     P, I64, P, P, I32, P]),
         "xq_hbm_read_probe": (I32, [P, I64, I64, I32, I64, P, P, P]),
         "xq_paged_decode_attention_noalloc": (I32, [LP, P, I32, I32, P, P, P, I32, P, I32, F32, I32, P, P]),
+        "xq_decode_plan_balanced": (I32, [LP, I32, I32, I32, P, P, P]),
+        "xq_decode_workspace_bytes_balanced": (I64, [LP, I32, I32, I32]),
+        "xq_decode_attention_balanced": (I32, [LP, P, I32, I32, P, P, P, I32, P, I32, F32, I32, P, P,
+                                               P, P, P, I64, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -209,6 +214,42 @@ def xq_append_decode_attention(layout: CacheLayout, k_new, v_new, q, batch: int,
         _ptr(v_pool), _ptr(block_tables), max_pages_per_seq, _ptr(context_lens), max_context_len,
         float(softmax_scale), num_splits_hint, _ptr(workspace), int(workspace_bytes), _ptr(out),
         _ptr(seq_order), _entries(seq_order), _stream(stream)))
+
+
+def xq_decode_plan_balanced(layout: CacheLayout, batch: int, num_q_heads: int, max_context_len: int,
+                            context_lens):
+    """See xq_decode_plan_balanced in include/xq.h. context_lens: host sequence of ints. Returns
+    (nsplits, seq_tps list [batch], units list of 2 * batch * nsplits * num_kv_heads ints)."""
+    lib = load()
+    lens = (ctypes.c_int32 * max(1, batch))(*[int(x) for x in context_lens])
+    tps = (ctypes.c_int32 * max(1, batch))()
+    ns = lib.xq_decode_plan_balanced(ctypes.byref(layout), batch, num_q_heads, max_context_len,
+                                     ctypes.cast(lens, ctypes.c_void_p), ctypes.cast(tps, ctypes.c_void_p), None)
+    if ns < 1:
+        raise XqError(EINVAL, lib.xq_last_error().decode())
+    n = 2 * batch * ns * layout.num_kv_heads
+    units = (ctypes.c_int32 * max(1, n))()
+    ns2 = lib.xq_decode_plan_balanced(ctypes.byref(layout), batch, num_q_heads, max_context_len,
+                                      ctypes.cast(lens, ctypes.c_void_p), ctypes.cast(tps, ctypes.c_void_p),
+                                      ctypes.cast(units, ctypes.c_void_p))
+    assert ns2 == ns
+    return ns, list(tps)[:batch], list(units)[:n]
+
+
+def xq_decode_workspace_bytes_balanced(layout: CacheLayout, batch: int, num_q_heads: int, nsplits: int) -> int:
+    return load().xq_decode_workspace_bytes_balanced(ctypes.byref(layout), batch, num_q_heads, nsplits)
+
+
+def xq_decode_attention_balanced(layout: CacheLayout, q, batch: int, num_q_heads: int, k_pool, v_pool,
+                                 block_tables, max_pages_per_seq: int, context_lens, max_context_len: int,
+                                 softmax_scale: float, nsplits: int, units, seq_tps, k_new, v_new,
+                                 workspace, workspace_bytes: int, out, stream=None):
+    """See xq_decode_attention_balanced in include/xq.h. Tensors are passed by data_ptr()."""
+    _check(load().xq_decode_attention_balanced(
+        ctypes.byref(layout), _ptr(q), batch, num_q_heads, _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+        max_pages_per_seq, _ptr(context_lens), max_context_len, float(softmax_scale), nsplits, _ptr(units),
+        _ptr(seq_tps), _ptr(k_new), _ptr(v_new), _ptr(workspace), int(workspace_bytes), _ptr(out),
+        _stream(stream)))
 
 
 def xq_hbm_read_probe(buf, buf_bytes: int, n_blocks: int, block_bytes: int, block_stride: int,

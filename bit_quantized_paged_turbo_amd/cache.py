@@ -7,7 +7,8 @@ from __future__ import annotations
 
 import torch
 
-from . import (CacheLayout, load, xq_append_decode_attention, xq_decode_plan, xq_decode_workspace_bytes,
+from . import (CacheLayout, load, xq_append_decode_attention, xq_decode_attention_balanced, xq_decode_plan,
+               xq_decode_plan_balanced, xq_decode_workspace_bytes, xq_decode_workspace_bytes_balanced,
                xq_paged_decode_attention,
                xq_paged_decode_attention_planned, xq_paged_prefill_attention,
                xq_pool_bytes, xq_quantize_append)
@@ -93,6 +94,36 @@ class PagedKVCache:
         order = xq_decode_plan(self.layout, len(host_context_lens), num_q_heads, int(max_context_len),
                                num_splits, host_context_lens)
         return torch.tensor(order, dtype=torch.int32, device=device)
+
+    def plan_balanced(self, host_context_lens, num_q_heads: int, max_context_len: int, device="cuda"):
+        """xq_decode_plan_balanced from host lengths -> (nsplits, units int32 [2 * slots], seq_tps int32
+        [batch]) on the device, for decode_balanced()."""
+        ns, tps, units = xq_decode_plan_balanced(self.layout, len(host_context_lens), num_q_heads,
+                                                 int(max_context_len), host_context_lens)
+        return (ns, torch.tensor(units, dtype=torch.int32, device=device),
+                torch.tensor(tps, dtype=torch.int32, device=device))
+
+    def decode_balanced(self, q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                        max_context_len: int, softmax_scale: float, plan, k_new=None, v_new=None,
+                        out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                        stream=None) -> torch.Tensor:
+        """The decode with a length-aware plan (plan_balanced()); with k_new/v_new (bf16 [B, Hkv, 128])
+        each sequence's new row is appended at context_lens[b] - 1 first. -> out fp32 [B, Hq, 128]."""
+        ns, units, tps = plan
+        batch, hq = int(q.shape[0]), int(q.shape[1])
+        if out is None:
+            out = torch.empty((batch, hq, 128), dtype=torch.float32, device=q.device)
+        need = xq_decode_workspace_bytes_balanced(self.layout, batch, hq, ns)
+        if workspace is None and need > 0:
+            if self._ws is None or self._ws.numel() < need:
+                self._ws = torch.empty((need,), dtype=torch.uint8, device=q.device)
+            workspace = self._ws
+        wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        xq_decode_attention_balanced(self.layout, q, batch, hq, self.k_pool, self.v_pool, block_tables,
+                                     int(block_tables.shape[1]), context_lens, int(max_context_len),
+                                     softmax_scale, ns, units, tps, k_new, v_new, workspace, wbytes, out,
+                                     stream)
+        return out
 
     def prefill(self, q: torch.Tensor, block_table: torch.Tensor, start_pos: int,
                 softmax_scale: float, num_splits: int = 0, out: torch.Tensor | None = None,

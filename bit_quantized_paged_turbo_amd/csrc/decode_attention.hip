@@ -1354,6 +1354,7 @@ void decode_split_kernel(DecodeParams p) {
   // A unit's rows: row block b (p.qt consecutive rows: sequences of a decode, where qt = 1, or
   // queries of a prefill chunk).
   int split, kvh, b;
+  int unit_tps = p.tokens_per_split;   // tokens per partition of this unit's sequence
   const uint32_t nblocks = ((uint32_t)p.batch + (uint32_t)p.qt - 1u) / (uint32_t)p.qt;
   {
     const uint32_t id = blockIdx.x, hkv = (uint32_t)p.hkv;
@@ -1378,7 +1379,16 @@ void decode_split_kernel(DecodeParams p) {
       split = (int)(group % (uint32_t)p.nsplits);
       b = (int)(group / (uint32_t)p.nsplits);
     }
-    if (p.seq_order) {
+    if (p.seq_tps) {
+      // a length-aware plan: this slot runs the unit of its pair, or nothing
+      const int2 e = reinterpret_cast<const int2*>(p.seq_order)[id];
+      if (e.x < 0 || (uint32_t)e.x >= units) return;
+      kvh = (int)((uint32_t)e.x % hkv);
+      const uint32_t r = (uint32_t)e.x / hkv;
+      split = (int)(r % (uint32_t)p.nsplits);
+      b = (int)(r / (uint32_t)p.nsplits);
+      unit_tps = e.y;
+    } else if (p.seq_order) {
       if (p.nsplits > 1) {
         // a unit plan (xq_decode_plan with several partitions): this slot runs unit
         // (b nsplits + split) hkv + kvh, or nothing (-1, or an entry outside the units)
@@ -1414,7 +1424,7 @@ void decode_split_kernel(DecodeParams p) {
   static_assert(kMaxSplitPages <= 128, "two registers of block-table entries");
   int btw0 = 0, btw1 = 0;
   {
-    const int lpw = (split * p.tokens_per_split) >> p.page_shift;
+    const int lpw = (split * unit_tps) >> p.page_shift;
     const int32_t* row = p.block_tables + (int64_t)b0 * p.bt_stride + lpw;
     const int nwin = min(kMaxSplitPages, p.maxp - lpw);
     if (lane < nwin) btw0 = row[lane];
@@ -1426,7 +1436,7 @@ void decode_split_kernel(DecodeParams p) {
       for (int i = lane; i < G * D; i += kThreads) p.out[qrow(i >> 7) * D + (i & 127)] = 0.f;
     return;
   }
-  const int tps = p.tokens_per_split;
+  const int tps = unit_tps;
   const int tok_begin = split * tps;
   if (tok_begin >= L) return;
   const int tok_end = min(L, tok_begin + tps);
@@ -1870,7 +1880,8 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodePara
   const int t = threadIdx.x;
   // the split count of b's unit (its last row's), which the split kernel used for every row
   const int L = row_context(p, min(p.batch - 1, (b / p.qt) * p.qt + p.qt - 1));
-  const int ns = (L + p.tokens_per_split - 1) / p.tokens_per_split;
+  const int tps = p.seq_tps ? p.seq_tps[b] : p.tokens_per_split;
+  const int ns = (L + tps - 1) / tps;
   if (ns <= 1) return;  // written by the split kernel
   const float* part = p.partials + ((int64_t)b * p.hq + qh) * p.nsplits * kPartialStride;
   __shared__ float4 accs[kCombGroups][32];

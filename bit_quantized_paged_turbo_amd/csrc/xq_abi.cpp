@@ -127,6 +127,47 @@ xq_status debug_check_unit_plan(int32_t batch, int32_t hkv, int32_t nsplits, int
   return XQ_OK;
 }
 
+// length-aware plan: seq_tps[b] is a positive multiple of max(32, page_size) of at most
+// kMaxSplitPages pages with ceil(context_lens[b] / seq_tps[b]) <= nsplits; every pair is {-1, *}
+// or {unit, seq_tps[b]} of a unit of the launch, no unit appears twice, and every unit with
+// tokens (and partition 0 of every sequence) appears.
+xq_status debug_check_balanced(const xq_cache_layout* L, int32_t batch, int32_t nsplits, int32_t max_ctx,
+                               const int32_t* context_lens, const int32_t* pairs, const int32_t* seq_tps,
+                               hipStream_t s) {
+  const int64_t hkv = L->num_kv_heads, units = (int64_t)nsplits * hkv * batch;
+  const int32_t unit_tok = std::max<int32_t>(32, L->page_size);
+  std::vector<int32_t> o, cl, tp;
+  if (xq_status st = fetch(o, pairs, 2 * units, s)) return st;
+  if (xq_status st = fetch(cl, context_lens, batch, s)) return st;
+  if (xq_status st = fetch(tp, seq_tps, batch, s)) return st;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t Lb = std::min(std::max(cl[b], 0), max_ctx);
+    if (tp[b] <= 0 || tp[b] % unit_tok != 0 || (int64_t)tp[b] > (int64_t)xq::kMaxSplitPages * L->page_size ||
+        (Lb + tp[b] - 1) / tp[b] > nsplits)
+      return fail(XQ_EINVAL, "XQ_DEBUG: seq_tps[%d] = %d is not a valid partition of %d tokens in %d", b, tp[b], Lb,
+                  nsplits);
+  }
+  std::vector<char> seen((size_t)units, 0);
+  for (int64_t i = 0; i < units; ++i) {
+    const int32_t u = o[(size_t)(2 * i)];
+    if (u == -1) continue;
+    if (u < 0 || u >= units || seen[(size_t)u] || o[(size_t)(2 * i + 1)] != tp[(size_t)(u / hkv / nsplits)])
+      return fail(XQ_EINVAL, "XQ_DEBUG: plan pair %lld = {%d, %d}: not -1 or a unit of the launch, once, with its "
+                  "sequence's partition", (long long)i, u, o[(size_t)(2 * i + 1)]);
+    seen[(size_t)u] = 1;
+  }
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t Lb = std::min(std::max(cl[b], 0), max_ctx);
+    const int32_t n = std::max(1, (Lb + tp[b] - 1) / tp[b]);
+    for (int32_t sp = 0; sp < n; ++sp)
+      for (int64_t k = 0; k < hkv; ++k)
+        if (!seen[(size_t)(((int64_t)b * nsplits + sp) * hkv + k)])
+          return fail(XQ_EINVAL, "XQ_DEBUG: the plan misses partition %d, kv head %lld of sequence %d", sp,
+                      (long long)k, b);
+  }
+  return XQ_OK;
+}
+
 // prefill: the pages of positions 0 .. max_ctx - 1 in the chunk's block-table row are page ids
 // in [0, num_pages).
 xq_status debug_check_prefill(const xq_cache_layout* L, const int32_t* block_table, int32_t max_ctx,
@@ -224,7 +265,8 @@ xq_status attention(const xq_cache_layout* layout, const void* q, int32_t batch,
                     int32_t max_pages_per_seq, const int32_t* context_lens, int32_t ctx_base,
                     int32_t max_context_len, float softmax_scale, int32_t num_splits_hint, void* workspace,
                     int64_t workspace_bytes, float* out, hipStream_t stream, const int32_t* seq_order = nullptr,
-                    const void* k_new = nullptr, const void* v_new = nullptr, bool checked_ok = true) {
+                    const void* k_new = nullptr, const void* v_new = nullptr, bool checked_ok = true,
+                    const int32_t* seq_tps = nullptr, int32_t balanced_nsplits = 0) {
   if (batch > 65535) return fail(XQ_EUNSUPPORTED, "batch %d > 65535", batch);
   if (num_q_heads < 1 || num_q_heads % layout->num_kv_heads != 0)
     return fail(XQ_EINVAL, "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads,
@@ -245,8 +287,9 @@ xq_status attention(const xq_cache_layout* layout, const void* q, int32_t batch,
   if (!(softmax_scale == softmax_scale)) return fail(XQ_EINVAL, "softmax_scale is NaN");
 
   const int32_t ctx = max_context_len > 0 ? max_context_len : 1;
-  const int32_t tps = plan_tokens_per_split(layout, batch, ctx, num_splits_hint);
-  const int32_t nsplits = (ctx + tps - 1) / tps;
+  // a length-aware plan brings its own partitions (seq_tps) and their stride
+  const int32_t tps = seq_tps ? 0 : plan_tokens_per_split(layout, batch, ctx, num_splits_hint);
+  const int32_t nsplits = seq_tps ? balanced_nsplits : (ctx + tps - 1) / tps;
   if (nsplits > 65535) return fail(XQ_EUNSUPPORTED, "%d splits > 65535", nsplits);
   // One 64-lane workgroup per (split, kv head, row block) on a one-dimensional grid. A prefill
   // packs 16 / g query tokens (all g heads of each) into the 16 columns of a unit's MFMA tiles.
@@ -266,7 +309,9 @@ xq_status attention(const xq_cache_layout* layout, const void* q, int32_t batch,
     xq_status st = ctx_base > 0 ? debug_check_prefill(layout, block_tables, max_context_len, stream)
                                 : debug_check_decode(layout, batch, block_tables, max_pages_per_seq, context_lens,
                                                      max_context_len, stream);
-    if (!st && seq_order)
+    if (!st && seq_tps)
+      st = debug_check_balanced(layout, batch, nsplits, max_context_len, context_lens, seq_order, seq_tps, stream);
+    else if (!st && seq_order)
       st = nsplits > 1 ? debug_check_unit_plan(batch, layout->num_kv_heads, nsplits, tps, max_context_len, context_lens,
                                                seq_order, stream)
                        : debug_check_order(batch, seq_order, stream);
@@ -302,6 +347,7 @@ xq_status attention(const xq_cache_layout* layout, const void* q, int32_t batch,
   p.seq_order = seq_order;
   p.k_new = static_cast<const uint16_t*>(k_new);
   p.v_new = static_cast<const uint16_t*>(v_new);
+  p.seq_tps = seq_tps;
   const hipError_t e = xq::launch_decode(layout->kv_dtype, p, stream);
   if (e != hipSuccess) return fail(XQ_EHIP, "attention launch: %s", hipGetErrorString(e));
   return XQ_OK;
@@ -570,12 +616,16 @@ xq_status xq_decode_plan(const xq_cache_layout* layout, int32_t batch, int32_t n
   }
 
   // Several partitions: a unit plan, one entry per work slot (workgroup id) of the launch, giving
-  // the unit (b nsplits + split) hkv + kvh it runs or -1. With all units of R rounds resident
-  // (R waves per SIMD), workgroup i runs on SIMD i mod S. The (sequence, partition) groups, each
-  // hkv units of equal length, are placed longest first (LPT) on the least loaded column of
-  // SIMDs that has a round free, a group's kv heads on one XCD (XCD = id mod 8) so that its L2
-  // fetches each line of a page once: column (x, y) of a round r holds ids
-  // x + 8 (hkv y + k) + S r, k < hkv. Groups beyond the resident rounds follow in the same order.
+  // the unit (b nsplits + split) hkv + kvh it runs or -1. The n units with work come first, in ids
+  // 0 .. n-1, and every later id is -1: a workgroup that exits at once frees its slot for the next
+  // id, so a -1 among the first ids would move every later workgroup off its SIMD. With the first
+  // ids resident (R waves per SIMD), workgroup i runs on SIMD i mod S. The (sequence, partition)
+  // groups, each hkv units of equal length, are placed longest first (LPT) on the least loaded
+  // column of SIMDs that has a free cell, a group's kv heads on one XCD (XCD = id mod 8) so that
+  // its L2 fetches each line of a page once: the cell of column (x, y) in round r holds ids
+  // x + 8 (hkv y + k) + S r, k < hkv, and is free when all of them are below min(n, R S).
+  // Groups left over fill the ids below n that no cell took, then the ones after, in the same
+  // longest-first order.
   const int64_t units = (int64_t)nsplits * hkv * batch;
   if (units >= ((int64_t)1 << 26)) return fail(XQ_EUNSUPPORTED, "%lld work units >= 2^26", (long long)units);
   for (int64_t i = 0; i < units; ++i) host_seq_order[i] = -1;
@@ -591,6 +641,7 @@ xq_status xq_decode_plan(const xq_cache_layout* layout, int32_t batch, int32_t n
   }
   std::stable_sort(groups.begin(), groups.end(), [](const Group& a, const Group& c) { return a.tiles > c.tiles; });
   auto unit = [&](const Group& g, int64_t k) { return (int32_t)(((int64_t)g.b * nsplits + g.split) * hkv + k); };
+  const int64_t n = (int64_t)groups.size() * hkv;   // units with work, ids 0 .. n-1
   xq::DecodeParams q{};
   q.batch = batch;
   q.hkv = (int32_t)hkv;
@@ -600,22 +651,189 @@ xq_status xq_decode_plan(const xq_cache_layout* layout, int32_t batch, int32_t n
   // columns of hkv SIMDs in one XCD; without them (a SIMD count that is not a multiple of 8 hkv) no
   // placement, only the longest-first order
   const int64_t cols = (simds % (8 * hkv) == 0) ? simds / hkv : 0;
-  const int64_t rounds = cols > 0 ? std::min<int64_t>(xq::decode_waves_per_simd(layout->kv_dtype, q), units / simds) : 0;
-  std::vector<int64_t> load((size_t)cols, 0), used((size_t)cols, 0);
-  int64_t next = rounds * simds;   // slots after the resident rounds
+  const int64_t rounds = cols > 0 ? xq::decode_waves_per_simd(layout->kv_dtype, q) : 0;
+  const int64_t limit = std::min<int64_t>(n, rounds * simds);   // cells lie below this id
+  std::vector<int64_t> load((size_t)cols, 0), used((size_t)cols, 0), cap((size_t)cols, 0);
+  for (int64_t c = 0; c < cols; ++c)
+    for (int64_t r = 0; r < rounds; ++r)
+      if (c % 8 + 8 * (hkv * (c / 8) + hkv - 1) + simds * r < limit) cap[(size_t)c] = r + 1;
+  std::vector<const Group*> rest;
   for (const Group& g : groups) {
     int64_t best = -1;
-    for (int64_t c = 0; c < cols && rounds > 0; ++c)
-      if (used[(size_t)c] < rounds && (best < 0 || load[(size_t)c] < load[(size_t)best])) best = c;
+    for (int64_t c = 0; c < cols; ++c)
+      if (used[(size_t)c] < cap[(size_t)c] && (best < 0 || load[(size_t)c] < load[(size_t)best])) best = c;
     if (best >= 0) {
       const int64_t x = best % 8, y = best / 8, r = used[(size_t)best]++;
       load[(size_t)best] += g.tiles;
       for (int64_t k = 0; k < hkv; ++k) host_seq_order[x + 8 * (hkv * y + k) + simds * r] = unit(g, k);
     } else {
-      for (int64_t k = 0; k < hkv; ++k) host_seq_order[next++] = unit(g, k);
+      rest.push_back(&g);
     }
   }
+  int64_t next = 0;
+  for (const Group* g : rest)
+    for (int64_t k = 0; k < hkv; ++k) {
+      while (host_seq_order[next] >= 0) ++next;   // the next id no cell took (below n first)
+      host_seq_order[next++] = unit(*g, k);
+    }
   return XQ_OK;
+}
+
+int32_t xq_decode_plan_balanced(const xq_cache_layout* layout, int32_t batch, int32_t num_q_heads,
+                                int32_t max_context_len, const int32_t* host_context_lens, int32_t* host_seq_tps,
+                                int32_t* host_units) {
+  if (check_layout(layout) != XQ_OK) return -1;
+  if (batch < 0 || num_q_heads < 1 || num_q_heads % layout->num_kv_heads != 0 || max_context_len < 0) {
+    fail(XQ_EINVAL, "invalid batch, head count or context length");
+    return -1;
+  }
+  if (batch == 0) return 1;
+  if (!host_context_lens || !host_seq_tps) {
+    fail(XQ_EINVAL, "a required pointer is NULL");
+    return -1;
+  }
+  const int64_t hkv = layout->num_kv_heads;
+  const int32_t ps = layout->page_size;
+  const int32_t unit_tok = std::max<int32_t>(32, ps), unit_tiles = unit_tok / 32;   // whole tiles and pages
+  const int32_t cap_tiles = xq::kMaxSplitPages * ps / 32;                           // the block-table window
+  int simds = 1024;   // MI355X: 256 compute units x 4 SIMDs, if the device cannot be asked
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+    simds = 4 * cus;
+  else
+    (void)hipGetLastError();
+
+  // Partitions of about T tiles each, T the smallest (in whole pages) for which all units fit the
+  // waves resident at once: every SIMD then runs the same number of units of about the same length,
+  // whatever SIMD of its compute unit the hardware gives each of them. T is at least 32 tiles
+  // (1,024 tokens): below that a unit's set-up, partials and merge cost more than the balance
+  // gains (measured on MI355X, 256 sequences of 64 to 1,024 tokens: 42.3 us unsplit, 45.8 us in
+  // partitions of 12 tiles; 64 sequences of 1,024 to 32,768 tokens: 130 us in partitions of
+  // about 48 tiles, 139 us in uniform ones of 64 tiles).
+  std::vector<int32_t> Lb((size_t)batch), tiles((size_t)batch);
+  int64_t total = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    Lb[(size_t)b] = std::min(std::max(host_context_lens[b], 0), max_context_len);
+    tiles[(size_t)b] = (Lb[(size_t)b] + 31) / 32;
+    total += tiles[(size_t)b] * hkv;
+  }
+  auto units_for = [&](int64_t T) {
+    int64_t n = 0;
+    for (int32_t b = 0; b < batch; ++b) n += std::max<int64_t>(1, (tiles[(size_t)b] + T - 1) / T) * hkv;
+    return n;
+  };
+  auto tiles_per_unit = [&](int64_t slots) {
+    int64_t T = std::max<int64_t>(32, (total + slots - 1) / slots);
+    T = (T + unit_tiles - 1) / unit_tiles * unit_tiles;
+    while (T < cap_tiles && units_for(T) > slots) T += unit_tiles;
+    return std::min<int64_t>(T, cap_tiles);
+  };
+  auto stride_for = [&](int64_t T) {
+    int32_t ns = 1;
+    for (int32_t b = 0; b < batch; ++b) {
+      const int64_t parts = std::max<int64_t>(1, (tiles[(size_t)b] + T - 1) / T);
+      int64_t tps = (Lb[(size_t)b] + parts - 1) / parts;
+      tps = std::min<int64_t>(std::max<int64_t>(unit_tok, (tps + unit_tok - 1) / unit_tok * unit_tok),
+                              (int64_t)cap_tiles * 32);
+      host_seq_tps[b] = (int32_t)tps;
+      ns = std::max<int32_t>(ns, (int32_t)std::max<int64_t>(1, (Lb[(size_t)b] + tps - 1) / tps));
+    }
+    return ns;
+  };
+  // resident waves per SIMD of the launch (its ring depth follows its unit count): estimated for a
+  // launch of many units, then taken again for the stride found
+  xq::DecodeParams q{};
+  q.batch = batch;
+  q.hkv = (int32_t)hkv;
+  q.qt = 1;
+  q.nsplits = (int32_t)std::max<int64_t>(1, (3 * (int64_t)simds + batch * hkv - 1) / (batch * hkv));
+  int64_t R = xq::decode_waves_per_simd(layout->kv_dtype, q);
+  int32_t nsplits = stride_for(tiles_per_unit(R * simds));
+  q.nsplits = nsplits;
+  const int64_t R2 = xq::decode_waves_per_simd(layout->kv_dtype, q);
+  if (R2 != R) {
+    R = R2;
+    nsplits = stride_for(tiles_per_unit(R * simds));
+  }
+  if ((int64_t)nsplits * hkv * batch >= ((int64_t)1 << 26)) {
+    fail(XQ_EUNSUPPORTED, "%lld work units >= 2^26", (long long)nsplits * hkv * batch);
+    return -1;
+  }
+  if (!host_units) return nsplits;
+
+  // The units, longest first, in ids 0 .. n-1 (later ids: {-1, 0}); workgroup i runs on XCD
+  // i mod 8 and compute unit i mod C (C = SIMDs / 4), and, while the first ids are all resident
+  // (measured: with two waves per SIMD), on SIMD i mod S. Whole rounds of S ids deal the
+  // (sequence, partition) groups to columns of hkv SIMDs in one XCD, snaking, so that the units
+  // sharing a SIMD (and a compute unit) sum to about the same; the column (x, y) of round r holds
+  // ids x + 8 (hkv y + k) + S r, k < hkv, so a group's kv heads share an XCD's L2. The groups
+  // after the whole rounds follow in order.
+  const int64_t entries = (int64_t)nsplits * hkv * batch;
+  for (int64_t i = 0; i < entries; ++i) {
+    host_units[2 * i] = -1;
+    host_units[2 * i + 1] = 0;
+  }
+  struct Group { int32_t b, split, tiles; };
+  std::vector<Group> groups;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t tps = host_seq_tps[b];
+    for (int32_t sp = 0; sp == 0 || (int64_t)sp * tps < Lb[(size_t)b]; ++sp) {
+      const int32_t n = std::max(0, std::min(Lb[(size_t)b], (sp + 1) * tps) - sp * tps);
+      groups.push_back({b, sp, (n + 31) / 32});
+    }
+  }
+  std::stable_sort(groups.begin(), groups.end(), [](const Group& a, const Group& c) { return a.tiles > c.tiles; });
+  const int64_t C = simds;   // ids per round
+  const int64_t cols = (C % (8 * hkv) == 0) ? C / hkv : 0;
+  const int64_t full = cols > 0 ? (int64_t)groups.size() / cols : 0;   // whole rounds
+  for (int64_t gi = 0; gi < (int64_t)groups.size(); ++gi) {
+    const Group& g = groups[(size_t)gi];
+    const int32_t u0 = (int32_t)(((int64_t)g.b * nsplits + g.split) * hkv);
+    for (int64_t k = 0; k < hkv; ++k) {
+      int64_t id;
+      const int64_t r = cols > 0 ? gi / cols : 0;
+      if (r < full) {
+        int64_t j = gi % cols;
+        if (r & 1) j = cols - 1 - j;
+        id = j % 8 + 8 * (hkv * (j / 8) + k) + C * r;
+      } else {
+        id = full * cols * hkv + (gi - full * cols) * hkv + k;
+      }
+      host_units[2 * id] = u0 + (int32_t)k;
+      host_units[2 * id + 1] = host_seq_tps[g.b];
+    }
+  }
+  return nsplits;
+}
+
+int64_t xq_decode_workspace_bytes_balanced(const xq_cache_layout* layout, int32_t batch, int32_t num_q_heads,
+                                           int32_t nsplits) {
+  if (check_layout(layout) != XQ_OK) return -1;
+  if (batch < 0 || num_q_heads < 1 || nsplits < 1) return -1;
+  return xq::workspace_layout(layout->kv_dtype, batch, num_q_heads, nsplits).total;
+}
+
+xq_status xq_decode_attention_balanced(const xq_cache_layout* layout, const void* q, int32_t batch,
+                                       int32_t num_q_heads, void* k_pool, void* v_pool,
+                                       const int32_t* block_tables, int32_t max_pages_per_seq,
+                                       const int32_t* context_lens, int32_t max_context_len, float softmax_scale,
+                                       int32_t nsplits, const int32_t* units, const int32_t* seq_tps,
+                                       const void* k_new, const void* v_new, void* workspace,
+                                       int64_t workspace_bytes, float* out, void* stream) {
+  if (xq_status st = check_layout(layout)) return st;
+  if (batch < 0) return fail(XQ_EINVAL, "batch %d < 0", batch);
+  if (batch == 0) return XQ_OK;
+  if (!context_lens || !units || !seq_tps) return fail(XQ_EINVAL, "a required pointer is NULL");
+  if ((k_new == nullptr) != (v_new == nullptr)) return fail(XQ_EINVAL, "k_new and v_new: both or neither");
+  if (k_new && (!aligned16(k_new) || !aligned16(v_new)))
+    return fail(XQ_EINVAL, "k_new and v_new must be 16-byte aligned");
+  if (nsplits < 1) return fail(XQ_EINVAL, "nsplits %d < 1", nsplits);
+  if (max_context_len < 0) return fail(XQ_EINVAL, "max_context_len %d < 0", max_context_len);
+  return attention(layout, q, batch, num_q_heads, k_pool, v_pool, block_tables, max_pages_per_seq,
+                   max_pages_per_seq, context_lens, 0, max_context_len, softmax_scale, 0, workspace,
+                   workspace_bytes, out, static_cast<hipStream_t>(stream), units, k_new, v_new, true, seq_tps,
+                   nsplits);
 }
 
 xq_status xq_paged_prefill_attention(const xq_cache_layout* layout, const void* q, int32_t n_query,

@@ -86,6 +86,11 @@ struct DecodeParams {
                                 // workgroup id runs, or -1
   const uint16_t* k_new;        // null, or bf16 [batch][hkv][128]: new rows appended at position
   const uint16_t* v_new;        // context_lens[b] - 1 by the wave of b's last split, first
+  // Length-aware partitions (xq_decode_plan_balanced): when set, sequence b is cut into
+  // partitions of seq_tps[b] tokens, and seq_order holds one pair {unit, tokens per partition}
+  // per work slot (unit = (b nsplits + split) hkv + kvh, or -1 for none); tokens_per_split is
+  // unused and nsplits is the partitions' stride (at least every sequence's count).
+  const int32_t* seq_tps;
 };
 
 hipError_t launch_quantize_append(int dtype, const AppendParams& p, hipStream_t stream);

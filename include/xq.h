@@ -295,6 +295,54 @@ xq_status xq_append_decode_attention(const xq_cache_layout* layout,
                                      void* stream);
 
 /*
+ * Length-aware partitions for a decode over sequences of mixed lengths (the infero page, section
+ * "Beyond plain text decode", item "Continuous batching": decodes of long and short sequences
+ * share one step). Host only; nothing is launched. From the host's copy of the context lengths,
+ * every sequence gets its own partition size so that all work units (partition x kv head) hold
+ * about the same number of tokens and all fit the waves the GPU keeps resident at once: no
+ * unit is left to run alone at the end. Units are ordered longest first and dealt over the
+ * compute units, the kv heads of a partition on one XCD.
+ *   host_context_lens  int32 [batch], host memory: the lengths the decode will see
+ *   host_seq_tps       int32 [batch], host memory, written: tokens per partition of sequence b, a
+ *                      multiple of 32 and of page_size, at most 128 pages
+ *   host_units         NULL, or int32 pairs [batch * nsplits * num_kv_heads][2], host memory,
+ *                      written: pair i = {unit, host_seq_tps[b]} for work slot i, unit =
+ *                      (b * nsplits + partition) * num_kv_heads + kv_head, or {-1, 0}
+ * Returns nsplits, the partitions' stride (the largest partition count of a sequence, >= 1), or
+ * -1 on invalid arguments (xq_last_error says why). Call once with host_units = NULL to size it.
+ */
+int32_t xq_decode_plan_balanced(const xq_cache_layout* layout, int32_t batch, int32_t num_q_heads,
+                                int32_t max_context_len, const int32_t* host_context_lens,
+                                int32_t* host_seq_tps, int32_t* host_units);
+
+/* Workspace bytes of xq_decode_attention_balanced for a plan of stride nsplits; -1 on invalid
+ * arguments. */
+int64_t xq_decode_workspace_bytes_balanced(const xq_cache_layout* layout, int32_t batch,
+                                           int32_t num_q_heads, int32_t nsplits);
+
+/*
+ * The decode (optionally with the step's append, as xq_append_decode_attention) over a
+ * length-aware plan: units and seq_tps are device copies of the plan's host_units (pairs) and
+ * host_seq_tps for the same lengths, nsplits its return value. Each unit covers its partition
+ * of seq_tps[b] tokens; sequences with several partitions are merged by log-sum-exp as for the
+ * other decodes. Results equal xq_paged_decode_attention's up to the rounding of a different
+ * partitioning (within the split-agreement bound).
+ *   k_new, v_new  NULL (no append), or both bf16 [batch][num_kv_heads][128], 16-byte aligned
+ * Other arguments and errors as for xq_paged_decode_attention; the workspace is
+ * xq_decode_workspace_bytes_balanced(layout, batch, num_q_heads, nsplits) bytes. A plan that
+ * does not match the lengths (a unit twice or missing, a pair whose size is not its sequence's)
+ * is outside the contract: rejected under XQ_DEBUG.
+ */
+xq_status xq_decode_attention_balanced(const xq_cache_layout* layout, const void* q, int32_t batch,
+                                       int32_t num_q_heads, void* k_pool, void* v_pool,
+                                       const int32_t* block_tables, int32_t max_pages_per_seq,
+                                       const int32_t* context_lens, int32_t max_context_len,
+                                       float softmax_scale, int32_t nsplits, const int32_t* units,
+                                       const int32_t* seq_tps, const void* k_new, const void* v_new,
+                                       void* workspace, int64_t workspace_bytes, float* out,
+                                       void* stream);
+
+/*
  * Chunked prefill attention over the paged (and, for turbo types, quantized) cache: the queries
  * of one chunk of one sequence, each attending causally to the sequence's cached rows. Defined
  * by the infero page, section "Beyond plain text decode", item "Continuous batching" (decodes

@@ -238,3 +238,46 @@ def test_unit_plan_balances_the_mixed_step(lib):
     assert len(plan) == 3 * 3 * 2
     want = {((b * 3 + s) * 2 + k) for b, ns in ((0, 1), (1, 1), (2, 3)) for s in range(ns) for k in range(2)}
     assert set(u for u in plan if u >= 0) == want and sum(u >= 0 for u in plan) == len(want)
+
+
+def test_balanced_plan_partitions_every_sequence(lib):
+    """The length-aware plan (no launch) on the mixed step and the batched decode: every sequence's
+    partition size is a whole number of pages and 32-token tiles within the block-table window;
+    the units with work fill ids 0 .. n-1 (pairs {unit, its sequence's size}), each exactly once,
+    and fit the three waves per SIMD the decode keeps resident (1,024 SIMDs when no device is
+    there to ask); the kv heads of a partition share an XCD in the whole rounds."""
+    import numpy as np
+    import workloads
+    for cfg in (4, 1):
+        W = workloads.config(cfg)
+        L = xq.CacheLayout(4, 8, W.page_size, W.num_pages)
+        lens = [int(x) for x in W.context_lens]
+        ns, tps, units = xq.xq_decode_plan_balanced(L, W.batch, W.num_q_heads, W.max_context_len, lens)
+        u = np.array(units).reshape(-1, 2)
+        assert len(u) == W.batch * ns * 8
+        unit_tok = max(32, W.page_size)
+        assert all(t % unit_tok == 0 and 0 < t <= 128 * W.page_size for t in tps)
+        want = {((b * ns + s) * 8 + k) for b in range(W.batch)
+                for s in range(max(1, -(-lens[b] // tps[b]))) for k in range(8)}
+        real = int((u[:, 0] >= 0).sum())
+        assert (u[:real, 0] >= 0).all() and (u[real:, 0] == -1).all()
+        assert real == len(want) and set(u[:real, 0].tolist()) == want
+        assert real <= 3 * 1024
+        assert all(t == tps[x // 8 // ns] for x, t in u[:real])
+        # partitions of about equal length: none above the first (longest) one's, and the units of the
+        # whole rounds within a few tiles of each other
+        sizes = np.array([-(-(min(lens[x // 8 // ns], (x // 8 % ns + 1) * t) - (x // 8 % ns) * t) // 32)
+                          for x, t in u[:real]])
+        assert sizes.max() <= 128 * W.page_size // 32
+        # kv heads of one partition on one XCD (id mod 8) in the whole rounds of 1,024 ids
+        full = real // 1024 * 1024
+        xcd = {}
+        for i in range(full):
+            xcd.setdefault(int(u[i, 0]) // 8, set()).add(i % 8)
+        assert all(len(v) == 1 for v in xcd.values())
+    # an empty sequence keeps partition 0 (its zero output); a larger batch of one-token sequences
+    L = xq.CacheLayout(4, 2, 16, 4096)
+    ns, tps, units = xq.xq_decode_plan_balanced(L, 3, 4, 3000, [0, 500, 3000])
+    u = np.array(units).reshape(-1, 2)
+    assert {int(x) // 2 // ns for x in u[u[:, 0] >= 0, 0]} == {0, 1, 2}
+    assert lib.xq_decode_plan_balanced(ctypes.byref(L), 3, 5, 3000, None, None, None) == -1   # 5 % 2 != 0
