@@ -707,10 +707,12 @@ int32_t xq_decode_plan_balanced(const xq_cache_layout* layout, int32_t batch, in
   // Partitions of about T tiles each, T the smallest (in whole pages) for which all units fit the
   // waves resident at once: every SIMD then runs the same number of units of about the same length,
   // whatever SIMD of its compute unit the hardware gives each of them. T is at least 32 tiles
-  // (1,024 tokens): below that a unit's set-up, partials and merge cost more than the balance
-  // gains (measured on MI355X, 256 sequences of 64 to 1,024 tokens: 42.3 us unsplit, 45.8 us in
-  // partitions of 12 tiles; 64 sequences of 1,024 to 32,768 tokens: 130 us in partitions of
-  // about 48 tiles, 139 us in uniform ones of 64 tiles).
+  // (1,024 tokens) where partitions that long still give half the resident waves work: below
+  // that a unit's set-up, partials and merge cost more than the balance gains (measured on
+  // MI355X, 256 sequences of 64 to 1,024 tokens: 42.3 us unsplit, 45.8 us in partitions of 12
+  // tiles; 64 sequences of 1,024 to 32,768 tokens: 130 us in partitions of about 48 tiles, 139 us
+  // in uniform ones of 64 tiles). A small batch keeps short partitions: its units run alone, and
+  // more of them shorten the longest.
   std::vector<int32_t> Lb((size_t)batch), tiles((size_t)batch);
   int64_t total = 0;
   for (int32_t b = 0; b < batch; ++b) {
@@ -724,7 +726,8 @@ int32_t xq_decode_plan_balanced(const xq_cache_layout* layout, int32_t batch, in
     return n;
   };
   auto tiles_per_unit = [&](int64_t slots) {
-    int64_t T = std::max<int64_t>(32, (total + slots - 1) / slots);
+    int64_t T = std::max<int64_t>(unit_tiles, (total + slots - 1) / slots);
+    if (T < 32 && units_for(32) >= slots / 2) T = 32;
     T = (T + unit_tiles - 1) / unit_tiles * unit_tiles;
     while (T < cap_tiles && units_for(T) > slots) T += unit_tiles;
     return std::min<int64_t>(T, cap_tiles);
