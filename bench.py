@@ -79,6 +79,9 @@ def parse():
     ap.add_argument("--cpu-reps", type=int, default=3, help="timed oracle repetitions (median)")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunk-prefill timing")
+    ap.add_argument("--chunk-append", choices=("decode", "kernel"), default="decode",
+                    help="where the prefill chunk's rows are appended with the length-aware plan and the "
+                         "fused step: by the decode launch (default) or by a separate append kernel")
     ap.add_argument("--no-probe", action="store_true", help="skip the streaming-read reference")
     ap.add_argument("--plan", choices=("balanced", "uniform", "none"), default="balanced",
                     help="host plan of the decode: length-aware partitions (xq_decode_plan_balanced), "
@@ -299,12 +302,13 @@ class Step:
     def decode(self, stream: int):
         lib = self.lib
         c = self.cache
-        q, batch, hq, bt, maxp, cl, maxctx, scale, splits, ws, wsb, out, order, n_order, fused, bal = self.dec
+        q, batch, hq, bt, maxp, cl, maxctx, scale, splits, ws, wsb, out, order, n_order, fused, bal, chunk = self.dec
         if bal is not None:
             kn, vn = fused if fused is not None else (None, None)
+            ck, cv, cn, cs, cp = chunk if chunk is not None else (None, None, 0, None, None)
             st = lib.xq_decode_attention_balanced(self.L, q, batch, hq, c.k_pool.data_ptr(), c.v_pool.data_ptr(),
                                                   bt, maxp, cl, maxctx, scale, bal[0], bal[1], bal[2], kn, vn,
-                                                  ws, wsb, out, stream)
+                                                  ck, cv, cn, cs, cp, ws, wsb, out, stream)
         elif fused is not None:
             st = lib.xq_append_decode_attention(self.L, fused[0], fused[1], q, batch, hq, c.k_pool.data_ptr(),
                                                 c.v_pool.data_ptr(), bt, maxp, cl, maxctx, scale, splits,
@@ -516,6 +520,7 @@ def main():
     ws = torch.empty((max(wsb, 16),), dtype=torch.uint8, device=dev)
     maxp = W.max_pages_per_seq
     fuse = not args.no_fuse
+    chunk = None
     app = (new_k.data_ptr(), new_v.data_ptr(), B, new_seq.data_ptr(), new_pos.data_ptr(), bt.data_ptr(), maxp)
     app_rows = B
     if chunk_kv is not None:
@@ -530,6 +535,10 @@ def main():
         keep = (ck, cv, cs, cp)  # noqa: F841  (alive for the step's pointers)
         app = (ck.data_ptr(), cv.data_ptr(), W.chunk_tokens + nb, cs.data_ptr(), cp.data_ptr(), bt.data_ptr(), maxp)
         app_rows = W.chunk_tokens + nb
+        if fuse and bal is not None and args.chunk_append == "decode":
+            # the chunk's rows ride in the decode launch, appended by workgroups after its units
+            chunk = (ck.data_ptr(), cv.data_ptr(), W.chunk_tokens, cs.data_ptr(), cp.data_ptr())
+            app = None
     elif fuse:
         app = None
     # the host plan: long and short sequences share SIMDs (identity where it cannot help)
@@ -540,7 +549,7 @@ def main():
            W.softmax_scale, splits, ws.data_ptr(), wsb, out.data_ptr(),
            None if order is None else order.data_ptr(), 0 if order is None else int(order.numel()),
            (new_k.data_ptr(), new_v.data_ptr()) if fuse else None,
-           None if bal is None else (bal[0], bal[1].data_ptr(), bal[2].data_ptr()))
+           None if bal is None else (bal[0], bal[1].data_ptr(), bal[2].data_ptr()), chunk)
     runners = [Step(lib, c.layout, c, app, dec) for c in caches]
 
     log(f"{R} pool replicas of {footprint} bytes; timing")
@@ -642,7 +651,11 @@ def main():
     by_layers = by_graph and "multi_step_ms_per_step" in graph
     timed_ms = graph["multi_step_ms_per_step"] if by_layers else graph["ms_per_step"] if by_graph else step_ms
     value = kv_bytes / (timed_ms * 1e-3) / 1e9
-    achieved = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
+    # the decode launch's algorithmic bytes: the KV rows it reads, plus the chunk's rows (bf16 in,
+    # codes and scale out) where it appends them too
+    chunk_bytes = W.chunk_tokens * hkv * 2 * (256 + rb) if chunk is not None else 0
+    launch_bytes = kv_bytes + chunk_bytes
+    achieved = launch_bytes / (dec_avg_ms * 1e-3) / 1e9
     tag = f"decode_call_{workloads.DTYPE_NAMES[W.dtype]}_{W.name}"
     prof = committed_profile(tag)
     kernel_us = prof.get("decode_call_kernel_us")
@@ -682,6 +695,8 @@ def main():
                      None if order is None else "permutation of the batch" if int(order.numel()) == B
                      else "unit placement (longest first, balanced SIMDs)"),
             "fused_append": fuse,
+            "chunk_append": (None if not W.chunk_tokens else "in the decode launch" if chunk is not None
+                             else "separate append kernel"),
         },
         "step_timing": {"method": (f"hip graph replay, {R} steps (one per pool replica, as one per layer) per graph"
                                    if by_layers else "hip graph replay of the captured step" if by_graph
@@ -701,16 +716,19 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": prof.get("hbm_bytes_per_launch"),
-                     "frac_kernel_trace": (round(kv_bytes / (kernel_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                     "frac_kernel_trace": (round(launch_bytes / (kernel_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
                                            if kernel_us else None),
                      "kernel_trace_us": kernel_us,
                      "kernel": ("xq_decode_attention_balanced" if bal is not None else
                                 "xq_append_decode_attention" if fuse else "xq_paged_decode_attention")
                                + " call (decode_split_kernel"
                                + (" + decode_combine_kernel)" if nsplits > 1 else ")"),
-                     "bytes_per_launch": kv_bytes,
+                     "bytes_per_launch": launch_bytes,
                      "bytes_note": "algorithmic: sum_b L_b x Hkv x (K row + V row), a row being "
-                                   f"{rb} B (codes + fp16 scale)"},
+                                   f"{rb} B (codes + fp16 scale)"
+                                   + (f"; plus the chunk's {W.chunk_tokens} x Hkv x (K, V) rows appended in "
+                                      f"the launch, {256 + rb} B each (bf16 in, codes + scale out)"
+                                      if chunk is not None else "")},
         "append": append,
     }
     if chunk_kv is not None and not args.no_prefill:

@@ -80,7 +80,7 @@ def load() -> ctypes.CDLL:
         "xq_decode_plan_balanced": (I32, [LP, I32, I32, I32, P, P, P]),
         "xq_decode_workspace_bytes_balanced": (I64, [LP, I32, I32, I32]),
         "xq_decode_attention_balanced": (I32, [LP, P, I32, I32, P, P, P, I32, P, I32, F32, I32, P, P,
-                                               P, P, P, I64, P, P]),
+                                               P, P, P, P, I32, P, P, P, I64, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -243,13 +243,14 @@ def xq_decode_workspace_bytes_balanced(layout: CacheLayout, batch: int, num_q_he
 def xq_decode_attention_balanced(layout: CacheLayout, q, batch: int, num_q_heads: int, k_pool, v_pool,
                                  block_tables, max_pages_per_seq: int, context_lens, max_context_len: int,
                                  softmax_scale: float, nsplits: int, units, seq_tps, k_new, v_new,
-                                 workspace, workspace_bytes: int, out, stream=None):
+                                 workspace, workspace_bytes: int, out, stream=None, chunk_k=None, chunk_v=None,
+                                 chunk_tokens: int = 0, chunk_seq=None, chunk_pos=None):
     """See xq_decode_attention_balanced in include/xq.h. Tensors are passed by data_ptr()."""
     _check(load().xq_decode_attention_balanced(
         ctypes.byref(layout), _ptr(q), batch, num_q_heads, _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
         max_pages_per_seq, _ptr(context_lens), max_context_len, float(softmax_scale), nsplits, _ptr(units),
-        _ptr(seq_tps), _ptr(k_new), _ptr(v_new), _ptr(workspace), int(workspace_bytes), _ptr(out),
-        _stream(stream)))
+        _ptr(seq_tps), _ptr(k_new), _ptr(v_new), _ptr(chunk_k), _ptr(chunk_v), int(chunk_tokens),
+        _ptr(chunk_seq), _ptr(chunk_pos), _ptr(workspace), int(workspace_bytes), _ptr(out), _stream(stream)))
 
 
 def xq_hbm_read_probe(buf, buf_bytes: int, n_blocks: int, block_bytes: int, block_stride: int,

@@ -106,9 +106,11 @@ class PagedKVCache:
     def decode_balanced(self, q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
                         max_context_len: int, softmax_scale: float, plan, k_new=None, v_new=None,
                         out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                        stream=None) -> torch.Tensor:
+                        stream=None, chunk=None) -> torch.Tensor:
         """The decode with a length-aware plan (plan_balanced()); with k_new/v_new (bf16 [B, Hkv, 128])
-        each sequence's new row is appended at context_lens[b] - 1 first. -> out fp32 [B, Hq, 128]."""
+        each sequence's new row is appended at context_lens[b] - 1 first. chunk = (k, v, token_seq,
+        token_pos) appends rows of other sequences in the same launch (as append() would; none in a
+        page the decode reads). -> out fp32 [B, Hq, 128]."""
         ns, units, tps = plan
         batch, hq = int(q.shape[0]), int(q.shape[1])
         if out is None:
@@ -122,7 +124,8 @@ class PagedKVCache:
         xq_decode_attention_balanced(self.layout, q, batch, hq, self.k_pool, self.v_pool, block_tables,
                                      int(block_tables.shape[1]), context_lens, int(max_context_len),
                                      softmax_scale, ns, units, tps, k_new, v_new, workspace, wbytes, out,
-                                     stream)
+                                     stream, *(() if chunk is None else
+                                               (chunk[0], chunk[1], int(chunk[0].shape[0]), chunk[2], chunk[3])))
         return out
 
     def prefill(self, q: torch.Tensor, block_table: torch.Tensor, start_pos: int,

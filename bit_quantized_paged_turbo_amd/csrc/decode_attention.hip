@@ -1344,6 +1344,15 @@ constexpr int kWavesPerEu = DT == 0 ? 1 : (DT == kFp8 || DT == 8 ? 2 : (DEPTH >=
 template <int DT, int DEPTH>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEu<DT, DEPTH>)))
 void decode_split_kernel(DecodeParams p) {
+  // Workgroups after the units append the rows of other sequences (xa): the hardware dispatches
+  // them last, so they run as the units finish, on SIMDs the units' tail leaves idle.
+  if (p.x_groups > 0) {
+    const uint32_t nunits = (uint32_t)p.nsplits * (uint32_t)p.hkv * (((uint32_t)p.batch + p.qt - 1u) / p.qt);
+    if (blockIdx.x >= nunits) {
+      codec::append_passes<DT>(p.xa, blockIdx.x - nunits, (uint32_t)p.x_groups, threadIdx.x);
+      return;
+    }
+  }
   // Work unit of this wave. Workgroups go to the eight XCDs round-robin by id (XCD = id mod 8).
   // The kv heads of one (split, sequence) share an XCD, whose L2 then fetches each line of a
   // page once for all of them (a page's kv-head blocks are adjacent but not line aligned).
@@ -2000,8 +2009,8 @@ int waves_per_simd(const DecodeParams& p) {
 
 template <int DT, int DEPTH>
 void launch_split(const DecodeParams& p, hipStream_t stream) {
-  const int64_t units = unit_count(p);
-  hipLaunchKernelGGL((decode_split_kernel<DT, DEPTH>), dim3((unsigned)units), dim3(kThreads), 0, stream, p);
+  const int64_t grid = unit_count(p) + p.x_groups;
+  hipLaunchKernelGGL((decode_split_kernel<DT, DEPTH>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
 }
 
 // With fixed partitions (batch-invariant mode) the kernel variants do not depend on the batch:

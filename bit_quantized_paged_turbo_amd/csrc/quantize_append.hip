@@ -16,9 +16,8 @@
 // and 32, 64 run inside a lane, h = 8, 16 across the row's lanes (DPP within a quad). A wave
 // encodes 16 rows per pass, one kv head of 16 consecutive tokens: a chunk's consecutive
 // positions fill consecutive slots of a page, so the pass writes one contiguous run of codes
-// and one of scales per page. Waves walk their passes with the next pass's rows already
-// loading (the rows are streamed once: the loads are non-temporal). blockIdx.y = 0 encodes K
-// rows, 1 V rows.
+// and one of scales per page. Waves walk their passes (K rows, then V rows) with the next
+// pass's rows already loading (the rows are streamed once: the loads are non-temporal).
 //
 // The fp8 cache type (same page, section "Getting a server up: the commands in the README",
 // and its compression table: 2x against BF16) stores each bf16 element as the nearest finite
@@ -30,80 +29,24 @@
 namespace xq {
 namespace {
 
-constexpr int kLanesPerRow = 4;
-constexpr int kRowsPerPass = 64 / kLanesPerRow;   // rows a wave encodes at once
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-// Workgroups per launch at most (per K/V half): the two halves' waves, four per SIMD, are about
-// what the registers (about 100 a lane) keep resident at once; larger appends loop.
-constexpr int kMaxBlocks = 512;
-
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
-
-struct RowIn {
-  uint4 raw[kLanesPerRow];   // this lane's four pieces
-  int seq, pos;              // the row's token: its sequence and position
-};
+// Workgroups per launch at most: about four waves per SIMD, what the registers (about 100 a lane)
+// keep resident at once; larger appends loop.
+constexpr int kMaxBlocks = 1024;
 
 template <int BITS>
 __global__ __launch_bounds__(kThreads) void quantize_append_kernel(AppendParams p) {
-  const int lane = threadIdx.x & 63;
-  const int l = lane & (kLanesPerRow - 1);      // lane of the row
-  const int rw = lane / kLanesPerRow;           // token of the pass's 16
-  const uint32_t ntok = (uint32_t)p.n_tokens;   // n_tokens * hkv < 2^28, checked by the caller
-  const uint32_t hkv = (uint32_t)p.hkv;
-  // pass = 16-token block * hkv + kv head
-  const uint32_t npass = (ntok + kRowsPerPass - 1) / kRowsPerPass * hkv;
-  const bool is_v = blockIdx.y != 0;
-  const uint16_t* src = is_v ? p.v_new : p.k_new;
-  uint8_t* pool = is_v ? p.v_pool : p.k_pool;
-  const uint32_t stride = gridDim.x * kWaves;
-  const int shift = __builtin_ctz((unsigned)p.page_size);
-
-  auto token_of = [&](uint32_t pass) { return pass / hkv * kRowsPerPass + rw; };
-  auto load = [&](uint32_t pass, RowIn& in) __attribute__((always_inline)) {
-    const uint32_t tok = token_of(pass);
-    if (tok < ntok) {
-      const uint32_t row = tok * hkv + pass % hkv;
-      const uint16_t* s = src + (int64_t)row * kHeadDim + 8 * l;
-#pragma unroll
-      for (int k = 0; k < kLanesPerRow; ++k) {
-        const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(s + 8 * kLanesPerRow * k));
-        in.raw[k] = make_uint4(v[0], v[1], v[2], v[3]);
-      }
-      in.seq = p.token_seq[tok];
-      in.pos = p.token_pos[tok];
-    }
-  };
-
-  uint32_t pass = blockIdx.x * kWaves + (threadIdx.x >> 6);
-  RowIn cur;
-  if (pass < npass) load(pass, cur);
-  while (pass < npass) {
-    const uint32_t tok = token_of(pass);
-    const uint32_t head = pass % hkv;
-    int page = 0;
-    if (tok < ntok) page = p.block_tables[(int64_t)cur.seq * p.maxp + (cur.pos >> shift)];
-    // the next pass's rows load while this one is encoded
-    const uint32_t next = pass + stride;
-    RowIn nxt;
-    if (next < npass) load(next, nxt);
-    if (tok < ntok) {
-      uint8_t* block = pool + (int64_t)page * p.page_stride + (int64_t)head * p.block_bytes;
-      codec::encode_row_lanes<BITS, kLanesPerRow>(cur.raw, l, block, cur.pos & (p.page_size - 1), p.page_size);
-    }
-    cur = nxt;
-    pass = next;
-  }
+  codec::append_passes<BITS>(p, blockIdx.x * kWaves + (threadIdx.x >> 6), gridDim.x * kWaves, threadIdx.x & 63);
 }
 
 }  // namespace
 
 hipError_t launch_quantize_append(int dtype, const AppendParams& p, hipStream_t stream) {
   if (p.n_tokens <= 0) return hipSuccess;
-  const int64_t passes = ((int64_t)p.n_tokens + kRowsPerPass - 1) / kRowsPerPass * p.hkv;
+  const int64_t passes = 2 * (((int64_t)p.n_tokens + codec::kAppendRows - 1) / codec::kAppendRows * p.hkv);
   const int64_t blocks = std::min<int64_t>((passes + kWaves - 1) / kWaves, kMaxBlocks);
-  dim3 grid((unsigned)blocks, 2, 1);
+  dim3 grid((unsigned)blocks, 1, 1);
   switch (dtype) {
     case 0: hipLaunchKernelGGL(quantize_append_kernel<0>, grid, dim3(kThreads), 0, stream, p); break;
     case 8: hipLaunchKernelGGL(quantize_append_kernel<8>, grid, dim3(kThreads), 0, stream, p); break;

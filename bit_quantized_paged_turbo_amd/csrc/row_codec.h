@@ -289,6 +289,65 @@ __device__ __forceinline__ void encode_row_lanes(const uint4 (&raw)[16 / LPR], i
   }
 }
 
+// The passes of an append: four lanes a row, 16 rows a pass, one kv head of 16 consecutive
+// tokens (a chunk's consecutive positions fill consecutive slots of a page, so a pass writes one
+// run of codes and one of scales per page). Passes 0 .. npass - 1 encode K rows, npass ..
+// 2 npass - 1 V rows; the calling wave runs passes first, first + stride, ..., each with the next
+// one's rows already loading (the rows are streamed once: non-temporal loads).
+constexpr int kAppendLanes = 4;
+constexpr int kAppendRows = 64 / kAppendLanes;
+
+template <int BITS>
+__device__ __forceinline__ void append_passes(const AppendParams& p, uint32_t first, uint32_t stride, int lane) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  struct RowIn {
+    uint4 raw[kAppendLanes];   // this lane's four pieces
+    int seq, pos;              // the row's token: its sequence and position
+  };
+  const int l = lane & (kAppendLanes - 1);      // lane of the row
+  const int rw = lane / kAppendLanes;           // token of the pass's 16
+  const uint32_t ntok = (uint32_t)p.n_tokens;   // n_tokens * hkv < 2^28, checked by the caller
+  const uint32_t hkv = (uint32_t)p.hkv;
+  const uint32_t npass = (ntok + kAppendRows - 1) / kAppendRows * hkv;   // 16-token block x kv head
+  const int shift = __builtin_ctz((unsigned)p.page_size);
+
+  auto token_of = [&](uint32_t pass) { return (pass % npass) / hkv * kAppendRows + rw; };
+  auto load = [&](uint32_t pass, RowIn& in) __attribute__((always_inline)) {
+    const uint32_t tok = token_of(pass);
+    if (tok < ntok) {
+      const uint32_t row = tok * hkv + (pass % npass) % hkv;
+      const uint16_t* s = (pass < npass ? p.k_new : p.v_new) + (int64_t)row * kHeadDim + 8 * l;
+#pragma unroll
+      for (int k = 0; k < kAppendLanes; ++k) {
+        const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(s + 8 * kAppendLanes * k));
+        in.raw[k] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+      in.seq = p.token_seq[tok];
+      in.pos = p.token_pos[tok];
+    }
+  };
+
+  uint32_t pass = first;
+  RowIn cur;
+  if (pass < 2 * npass) load(pass, cur);
+  while (pass < 2 * npass) {
+    const uint32_t tok = token_of(pass);
+    const uint32_t head = (pass % npass) % hkv;
+    int page = 0;
+    if (tok < ntok) page = p.block_tables[(int64_t)cur.seq * p.maxp + (cur.pos >> shift)];
+    const uint32_t next = pass + stride;
+    RowIn nxt;
+    if (next < 2 * npass) load(next, nxt);
+    if (tok < ntok) {
+      uint8_t* block = (pass < npass ? p.k_pool : p.v_pool) + (int64_t)page * p.page_stride +
+                       (int64_t)head * p.block_bytes;
+      encode_row_lanes<BITS, kAppendLanes>(cur.raw, l, block, cur.pos & (p.page_size - 1), p.page_size);
+    }
+    cur = nxt;
+    pass = next;
+  }
+}
+
 // Sixteen lanes per row, one group each (the fused append + decode path).
 template <int BITS>
 __device__ __forceinline__ void encode_row(const uint4 raw, int lane16, uint8_t* block, int slot, int page_size) {

@@ -215,6 +215,31 @@ xq_status debug_check_append(const xq_cache_layout* L, int32_t n, const int32_t*
   return XQ_OK;
 }
 
+// rows appended by a decode launch beside its units: no row may land in a page that the decode
+// reads (a page of sequences 0 .. batch - 1 holding one of their context_lens rows), since the
+// launch's units and appenders run in no fixed order.
+xq_status debug_check_disjoint(const xq_cache_layout* L, int32_t batch, const int32_t* context_lens,
+                               const int32_t* block_tables, int32_t maxp, int32_t n, const int32_t* token_seq,
+                               const int32_t* token_pos, hipStream_t s) {
+  std::vector<int32_t> lens, seq, pos, bt;
+  if (xq_status st = fetch(lens, context_lens, batch, s)) return st;
+  if (xq_status st = fetch(seq, token_seq, n, s)) return st;
+  if (xq_status st = fetch(pos, token_pos, n, s)) return st;
+  int32_t rows = batch;
+  for (int32_t i = 0; i < n; ++i) rows = std::max(rows, seq[i] + 1);
+  if (xq_status st = fetch(bt, block_tables, (int64_t)rows * maxp, s)) return st;
+  std::unordered_set<int32_t> read;
+  for (int32_t b = 0; b < batch; ++b)
+    for (int64_t t = 0; t < (int64_t)lens[b]; t += L->page_size) read.insert(bt[(size_t)b * maxp + t / L->page_size]);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t pg = bt[(size_t)seq[i] * maxp + pos[i] / L->page_size];
+    if (read.count(pg))
+      return fail(XQ_EINVAL, "XQ_DEBUG: chunk row %d (sequence %d, position %d) writes page %d, which the decode reads",
+                  i, seq[i], pos[i], pg);
+  }
+  return XQ_OK;
+}
+
 int64_t block_bytes_of(const xq_cache_layout* L) {
   const int64_t row = xq::row_code_bytes(L->kv_dtype);
   const int64_t bytes = L->page_size * row + (xq::has_scales(L->kv_dtype) ? 2 * L->page_size : 0);
@@ -266,7 +291,8 @@ xq_status attention(const xq_cache_layout* layout, const void* q, int32_t batch,
                     int32_t max_context_len, float softmax_scale, int32_t num_splits_hint, void* workspace,
                     int64_t workspace_bytes, float* out, hipStream_t stream, const int32_t* seq_order = nullptr,
                     const void* k_new = nullptr, const void* v_new = nullptr, bool checked_ok = true,
-                    const int32_t* seq_tps = nullptr, int32_t balanced_nsplits = 0) {
+                    const int32_t* seq_tps = nullptr, int32_t balanced_nsplits = 0,
+                    const xq::AppendParams* extra = nullptr) {
   if (batch > 65535) return fail(XQ_EUNSUPPORTED, "batch %d > 65535", batch);
   if (num_q_heads < 1 || num_q_heads % layout->num_kv_heads != 0)
     return fail(XQ_EINVAL, "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads,
@@ -297,6 +323,12 @@ xq_status attention(const xq_cache_layout* layout, const void* q, int32_t batch,
   const int64_t units = (int64_t)nsplits * layout->num_kv_heads * ((batch + qt - 1) / qt);
   if (units >= ((int64_t)1 << 26))
     return fail(XQ_EUNSUPPORTED, "%lld work units (splits x kv heads x rows) >= 2^26", (long long)units);
+  if (extra && extra->n_tokens > 0 && checked_ok && debug_on())
+    if (xq_status st = debug_check_append(layout, extra->n_tokens, extra->token_seq, extra->token_pos,
+                                          extra->block_tables, extra->maxp, stream);
+        st || (st = debug_check_disjoint(layout, batch, context_lens, block_tables, max_pages_per_seq,
+                                         extra->n_tokens, extra->token_seq, extra->token_pos, stream)))
+      return st;
   const xq::WorkspaceLayout ws = xq::workspace_layout(layout->kv_dtype, batch, num_q_heads, nsplits);
   if (ws.total > 0) {
     if (!workspace || workspace_bytes < ws.total)
@@ -348,6 +380,12 @@ xq_status attention(const xq_cache_layout* layout, const void* q, int32_t batch,
   p.k_new = static_cast<const uint16_t*>(k_new);
   p.v_new = static_cast<const uint16_t*>(v_new);
   p.seq_tps = seq_tps;
+  if (extra && extra->n_tokens > 0) {
+    // one pass = 16 rows; a workgroup per pass up to one per SIMD, looping beyond
+    const int64_t passes = 2 * (((int64_t)extra->n_tokens + 15) / 16 * layout->num_kv_heads);
+    p.xa = *extra;
+    p.x_groups = (int32_t)std::min<int64_t>(passes, 1024);
+  }
   const hipError_t e = xq::launch_decode(layout->kv_dtype, p, stream);
   if (e != hipSuccess) return fail(XQ_EHIP, "attention launch: %s", hipGetErrorString(e));
   return XQ_OK;
@@ -822,8 +860,10 @@ xq_status xq_decode_attention_balanced(const xq_cache_layout* layout, const void
                                        const int32_t* block_tables, int32_t max_pages_per_seq,
                                        const int32_t* context_lens, int32_t max_context_len, float softmax_scale,
                                        int32_t nsplits, const int32_t* units, const int32_t* seq_tps,
-                                       const void* k_new, const void* v_new, void* workspace,
-                                       int64_t workspace_bytes, float* out, void* stream) {
+                                       const void* k_new, const void* v_new, const void* chunk_k,
+                                       const void* chunk_v, int32_t chunk_tokens, const int32_t* chunk_seq,
+                                       const int32_t* chunk_pos, void* workspace, int64_t workspace_bytes,
+                                       float* out, void* stream) {
   if (xq_status st = check_layout(layout)) return st;
   if (batch < 0) return fail(XQ_EINVAL, "batch %d < 0", batch);
   if (batch == 0) return XQ_OK;
@@ -833,10 +873,32 @@ xq_status xq_decode_attention_balanced(const xq_cache_layout* layout, const void
     return fail(XQ_EINVAL, "k_new and v_new must be 16-byte aligned");
   if (nsplits < 1) return fail(XQ_EINVAL, "nsplits %d < 1", nsplits);
   if (max_context_len < 0) return fail(XQ_EINVAL, "max_context_len %d < 0", max_context_len);
+  if (chunk_tokens < 0) return fail(XQ_EINVAL, "chunk_tokens %d < 0", chunk_tokens);
+  xq::AppendParams x{};
+  if (chunk_tokens > 0) {
+    if (!chunk_k || !chunk_v || !chunk_seq || !chunk_pos) return fail(XQ_EINVAL, "a required chunk pointer is NULL");
+    if (!aligned16(chunk_k) || !aligned16(chunk_v)) return fail(XQ_EINVAL, "chunk_k and chunk_v must be 16-byte aligned");
+    if ((int64_t)chunk_tokens * layout->num_kv_heads >= ((int64_t)1 << 28))
+      return fail(XQ_EUNSUPPORTED, "chunk_tokens * num_kv_heads = %lld rows: at most 2^28 - 1 per call",
+                  (long long)chunk_tokens * layout->num_kv_heads);
+    x.k_new = static_cast<const uint16_t*>(chunk_k);
+    x.v_new = static_cast<const uint16_t*>(chunk_v);
+    x.token_seq = chunk_seq;
+    x.token_pos = chunk_pos;
+    x.block_tables = block_tables;
+    x.k_pool = static_cast<uint8_t*>(k_pool);
+    x.v_pool = static_cast<uint8_t*>(v_pool);
+    x.block_bytes = block_bytes_of(layout);
+    x.page_stride = x.block_bytes * layout->num_kv_heads;
+    x.n_tokens = chunk_tokens;
+    x.hkv = layout->num_kv_heads;
+    x.page_size = layout->page_size;
+    x.maxp = max_pages_per_seq;
+  }
   return attention(layout, q, batch, num_q_heads, k_pool, v_pool, block_tables, max_pages_per_seq,
                    max_pages_per_seq, context_lens, 0, max_context_len, softmax_scale, 0, workspace,
                    workspace_bytes, out, static_cast<hipStream_t>(stream), units, k_new, v_new, true, seq_tps,
-                   nsplits);
+                   nsplits, &x);
 }
 
 xq_status xq_paged_prefill_attention(const xq_cache_layout* layout, const void* q, int32_t n_query,

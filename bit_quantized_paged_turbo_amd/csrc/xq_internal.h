@@ -91,6 +91,10 @@ struct DecodeParams {
   // per work slot (unit = (b nsplits + split) hkv + kvh, or -1 for none); tokens_per_split is
   // unused and nsplits is the partitions' stride (at least every sequence's count).
   const int32_t* seq_tps;
+  // Rows of other sequences appended by the same launch (a prefill chunk beside the decodes):
+  // x_groups workgroups after the decode's units run xa's append passes; none when 0.
+  AppendParams xa;
+  int32_t x_groups;
 };
 
 hipError_t launch_quantize_append(int dtype, const AppendParams& p, hipStream_t stream);

@@ -328,6 +328,17 @@ int64_t xq_decode_workspace_bytes_balanced(const xq_cache_layout* layout, int32_
  * other decodes. Results equal xq_paged_decode_attention's up to the rounding of a different
  * partitioning (within the split-agreement bound).
  *   k_new, v_new  NULL (no append), or both bf16 [batch][num_kv_heads][128], 16-byte aligned
+ * The same launch can also append rows of sequences it does not decode, as xq_quantize_append
+ * does (the step's prefill chunk, continuous batching as the infero page describes it in
+ * section "Beyond plain text decode"): the appenders run after the decode's units, in the
+ * idle end of the launch, and their codes and scales equal xq_quantize_append's bit for bit.
+ *   chunk_tokens  rows to append (0: none; then the chunk pointers may be NULL)
+ *   chunk_k, chunk_v, chunk_seq, chunk_pos  as xq_quantize_append's k_new, v_new, token_seq,
+ *                 token_pos, with chunk_seq indexing rows of the same block_tables (any row,
+ *                 not only the first batch) and at most 2^28 - 1 (token, kv head) rows
+ * No chunk row may land in a page that the decode reads (a page holding rows 0 .. L_b - 1 of
+ * a decoded sequence b): the decode's units and the appenders run in no fixed order, so such
+ * a row would race the decode (rejected under XQ_DEBUG, with xq_quantize_append's checks).
  * Other arguments and errors as for xq_paged_decode_attention; the workspace is
  * xq_decode_workspace_bytes_balanced(layout, batch, num_q_heads, nsplits) bytes. A plan that
  * does not match the lengths (a unit twice or missing, a pair whose size is not its sequence's)
@@ -339,6 +350,8 @@ xq_status xq_decode_attention_balanced(const xq_cache_layout* layout, const void
                                        const int32_t* context_lens, int32_t max_context_len,
                                        float softmax_scale, int32_t nsplits, const int32_t* units,
                                        const int32_t* seq_tps, const void* k_new, const void* v_new,
+                                       const void* chunk_k, const void* chunk_v, int32_t chunk_tokens,
+                                       const int32_t* chunk_seq, const int32_t* chunk_pos,
                                        void* workspace, int64_t workspace_bytes, float* out,
                                        void* stream);
 

@@ -8,9 +8,11 @@ import numpy as np
 import pytest
 import torch
 
+import bit_quantized_paged_turbo_amd as xq
 import oracle
 import workloads
 from tests.gpu_util import fill, make_cache, to_dev, upload_tables
+from tests.test_gpu_parity import _codec_check
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
@@ -145,3 +147,67 @@ def test_balanced_full_size(name, cfg, dtype, sample):
     for b in sample:
         err = np.max(np.abs(got[b] - oracle.decode_sequence(W.dtype, qb[b], *W.kv_bits(b), W.softmax_scale)[0]))
         assert err <= TOL, f"{name} seq {b}: {err:.3e}"
+
+
+@pytest.mark.parametrize("dtype", [4, 3, 8, 2, 0, workloads.FP8])
+def test_balanced_step_appends_a_chunk_in_the_same_launch(dtype, monkeypatch):
+    """A prefill chunk of a sequence outside the decoded batch (continuous batching, infero page,
+    section "Beyond plain text decode") appended by the decode's own launch: the pools hold the
+    bytes of the separate append kernel, the chunk's rows equal the oracle's encoding, and the
+    decode's outputs are bit-identical to the same plan's without the chunk."""
+    print("CASE balanced chunk", dtype, flush=True)
+    monkeypatch.setenv("XQ_DEBUG", "1")             # also checks that no chunk page is read
+    lens = [5, 700, 3000, 64, 1, 1500, 2049, 96, 333]
+    hq, hkv = 32, 8
+    W = workloads.make(f"balc-{dtype}", 1400 + dtype, dtype, lens, hq, hkv, 16, chunk_tokens=1037)
+    B = W.batch
+    kv = {b: W.kv_bits(b) for b in range(W.num_seqs)}
+    qb = W.q_bits()
+    q = to_dev(qb)
+    chunk = (to_dev(kv[B][0]), to_dev(kv[B][1]), to_dev(np.full(W.chunk_tokens, B, np.int32)),
+             to_dev(np.arange(W.chunk_tokens, dtype=np.int32)))
+    k_new = to_dev(np.stack([kv[b][0][-1] for b in range(B)]))
+    v_new = to_dev(np.stack([kv[b][1][-1] for b in range(B)]))
+    outs, pools = [], []
+    for inline in (False, True):
+        cache = make_cache(W)
+        bt, cl = upload_tables(W)
+        fill(cache, W, bt, seqs=range(B), kv=kv)      # the decoded sequences; the chunk's pages unwritten
+        plan = cache.plan_balanced(lens, hq, W.max_context_len)
+        if not inline:
+            cache.append(*chunk[:2], chunk[2], chunk[3], bt)
+        out = cache.decode_balanced(q, bt, cl, W.max_context_len, W.softmax_scale, plan, k_new, v_new,
+                                    chunk=chunk if inline else None)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+        pools.append((cache.k_pool.cpu().numpy(), cache.v_pool.cpu().numpy()))
+    assert np.array_equal(pools[0][0], pools[1][0]) and np.array_equal(pools[0][1], pools[1][1])
+    assert np.array_equal(outs[0], outs[1])
+    _codec_check(W, cache, [B])
+    got = outs[1].astype(np.float64)
+    for b in range(B):
+        err = np.max(np.abs(got[b] - _oracle(W, b, qb, kv)))
+        assert err <= TOL, f"seq {b} (L={lens[b]}): {err:.3e}"
+
+
+def test_balanced_chunk_into_a_read_page_is_rejected(monkeypatch):
+    """Under XQ_DEBUG a chunk row that lands in a page the decode reads is refused before any
+    launch (the decode's units and the appenders run in no fixed order)."""
+    print("CASE balanced chunk rejected", flush=True)
+    monkeypatch.setenv("XQ_DEBUG", "1")
+    lens = [40, 90]
+    W = workloads.make("balc-bad", 1500, 4, lens, 16, 8, 16, chunk_tokens=20)
+    cache = make_cache(W)
+    bt, cl = upload_tables(W)
+    fill(cache, W, bt)
+    q = to_dev(W.q_bits())
+    k, v = W.kv_bits(2)
+    # positions 70..89 of sequence 1: rows the decode reads
+    chunk = (to_dev(k), to_dev(v), to_dev(np.full(20, 1, np.int32)), to_dev(np.arange(70, 90, dtype=np.int32)))
+    plan = cache.plan_balanced(lens, 16, W.max_context_len)
+    before = cache.k_pool.clone()
+    with pytest.raises(xq.XqError) as e:
+        cache.decode_balanced(q, bt, cl, W.max_context_len, W.softmax_scale, plan, chunk=chunk)
+    assert e.value.status == xq.EINVAL and "which the decode reads" in str(e.value)
+    torch.cuda.synchronize()
+    assert torch.equal(cache.k_pool, before)
