@@ -204,14 +204,22 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// Eight 3-bit fields in the low 24 bits of x (bits 24..31 are ignored) -> two fields per byte:
-// field 2i in bits 0..2 and field 2i+1 in bits 3..5 of byte i. A shift by 5 (by 2) then moves
-// the even (odd) fields to the top three bits of their bytes.
-__device__ __forceinline__ uint32_t spread3to6(uint32_t x) {
-  x = (x & 0xfffu) | ((x & 0xfff000u) << 4);
-  return (x & 0x003f003fu) | ((x & 0x0fc00fc0u) << 2);
+// Eight 3-bit fields, bytes o .. o + 2 of the eight bytes hi:lo (lo = bytes 0..3), -> two fields
+// per byte: field 2i in bits 0..2 and field 2i+1 in bits 3..5 of byte i (bits 6 and 7 are left
+// undefined). A shift by 5 (by 2) and the mask 0xe0 then give the even (odd) fields in the top
+// three bits of their bytes. sel = spread_sel(o). Four operations: a byte gather (bytes o, o + 1
+// to the low half, o + 1, o + 2 to the high half: fields 0..3 at bits 0..11, fields 4..7 at bits
+// 20..31), the high half shifted down by 4 on its own (a packed 16-bit shift), and fields 2, 3
+// and 6, 7 moved up by 2 into the next byte.
+constexpr uint32_t spread_sel(int o) {
+  return (uint32_t)o | (uint32_t)(o + 1) << 8 | (uint32_t)(o + 1) << 16 | (uint32_t)(o + 2) << 24;
 }
-constexpr uint32_t kBias3 = 0x924924u;   // bit 2 of every 3-bit field: c -> c + 4
+__device__ __forceinline__ uint32_t spread3to6(uint32_t hi, uint32_t lo, uint32_t sel) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  const uint32_t y = __builtin_amdgcn_perm(hi, lo, sel);
+  const uint32_t z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, y) >> u16x2{0, 4});
+  return (z & 0x003f003fu) | ((z << 2) & ~0x003f003fu);
+}
 
 // ---------------------------------------------------------------------------------------
 // Query preparation, done by the decode wave itself: q' = H q, q = rint(q' * kQiMax / max|q'|),
@@ -558,11 +566,12 @@ __device__ __forceinline__ void k_operands(const Tile<DT>& t, int h, v4i& a0, v4
     }
   } else if constexpr (DT == 3) {
     const uint32_t d0 = (uint32_t)t.k[h][0], d1 = (uint32_t)t.k[h][1], d2 = (uint32_t)t.k[h][2];
-    const uint32_t grp[4] = {d0, __builtin_amdgcn_alignbit(d1, d0, 24), __builtin_amdgcn_alignbit(d2, d1, 16),
-                             d2 >> 8};
+    // fields 8 w .. 8 w + 7: bytes 3 w .. 3 w + 2 of d0 d1 d2
+    const uint32_t grp[4] = {spread3to6(d1, d0, spread_sel(0)), spread3to6(d1, d0, spread_sel(3)),
+                             spread3to6(d2, d1, spread_sel(2)), spread3to6(d2, d1, spread_sel(5))};
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const uint32_t n = spread3to6(grp[w]);              // raw 3-bit fields, two per byte
+      const uint32_t n = grp[w];                           // raw 3-bit fields, two per byte
       a0[w] = (int)((n << 5) & 0xe0e0e0e0u);               // 32 c
       a1[w] = (int)((n << 2) & 0xe0e0e0e0u);
     }
@@ -594,13 +603,13 @@ __device__ __forceinline__ void v_bytes(const Tile<DT>& t, uint32_t (&e)[8], uin
       o[j] = u & 0xf0f0f0f0u;                              // odd dims, already in the high nibble
     }
   } else if constexpr (DT == 3) {
-    const uint32_t sh = (24u * col) & 31u;
+    // the lane's 8 dims start at byte (3 col) mod 4 of its two dwords
+    const uint32_t sel = spread_sel((3 * col) & 3);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t x = __builtin_amdgcn_alignbit((uint32_t)t.v[j][1], (uint32_t)t.v[j][0], sh);
-      const uint32_t n = spread3to6(x ^ kBias3);    // c + 4 (0..7), two fields per byte
-      e[j] = (n << 5) & 0xe0e0e0e0u;                // (c + 4) << 5
-      o[j] = (n << 2) & 0xe0e0e0e0u;
+      const uint32_t n = spread3to6((uint32_t)t.v[j][1], (uint32_t)t.v[j][0], sel);   // two fields per byte
+      e[j] = ((n << 5) & 0xe0e0e0e0u) ^ 0x80808080u;       // (c + 4) << 5: the top bit flipped
+      o[j] = ((n << 2) & 0xe0e0e0e0u) ^ 0x80808080u;
     }
   } else if constexpr (DT == 8) {
 #pragma unroll
@@ -842,7 +851,7 @@ template <> struct PairTile<8> {
   v2i ks, vs;
 };
 template <> struct PairTile<3> {
-  v2i k[4];            // the 48 bits (16 codes) of the lane's 16 dims per MFMA, from bit 0
+  v2i k[4];            // two dwords holding the 48 bits (16 codes) of the lane's 16 dims per MFMA
   v2i v[8];            // V as in Tile<3>
   v2i ks, vs;
 };
@@ -858,12 +867,15 @@ struct PairLane {
   int hn;      // query head of this lane's column (0 .. G-1)
   int kb;      // token block of this lane's K operand (lane group >> 1)
   int kp;      // which 16 of each 32 dimensions this lane's K operand holds (lane group & 1)
+  uint32_t ksel0, ksel1;   // turbo3: byte gathers of its K fields 0..7 and 8..15 (spread3to6)
+  uint32_t vsel;           // turbo3: byte gather of its 8 V dims (spread3to6)
 };
 
 __device__ __forceinline__ PairLane pair_lane(int lane, int G) {
   const int n = lane & 15, gg = lane >> 4;
   const int ne = n < 2 * G ? n : n % (2 * G);
-  return PairLane{ne / G, ne % G, gg >> 1, gg & 1};
+  const int kp = gg & 1;
+  return PairLane{ne / G, ne % G, gg >> 1, kp, spread_sel(2 * kp), spread_sel(2 * kp + 3), spread_sel((3 * n) & 3)};
 }
 
 template <int DT>
@@ -880,14 +892,11 @@ __device__ __forceinline__ void read_slot_pair(PairTile<DT>& t, const uint8_t* s
     for (int m = 0; m < 4; ++m) t.k[m] = *reinterpret_cast<const int*>(kh + 32 * tk + 8 * m + 4 * pl.kp);
   } else if constexpr (DT == 3) {
     // rows as stored (48 B): dims 32 m + 16 kp .. + 15 are bits 96 m + 48 kp .. + 47 of the row,
-    // i.e. bytes 12 m + 6 kp .. + 5: two aligned dwords from byte 12 m + 4 kp, shifted by 16 kp
+    // i.e. bytes 12 m + 6 kp .. + 5: bytes 2 kp .. 2 kp + 5 of the two aligned dwords from byte
+    // 12 m + 4 kp (pair_k_operand gathers them)
     const int* kr = reinterpret_cast<const int*>(kh + 48 * tk);
-    const uint32_t sh = 16u * (uint32_t)pl.kp;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const uint32_t d0 = (uint32_t)kr[3 * m + pl.kp], d1 = (uint32_t)kr[3 * m + pl.kp + 1];
-      t.k[m] = v2i{(int)__builtin_amdgcn_alignbit(d1, d0, sh), (int)(d1 >> sh)};
-    }
+    for (int m = 0; m < 4; ++m) t.k[m] = v2i{kr[3 * m + pl.kp], kr[3 * m + pl.kp + 1]};
   } else if constexpr (DT == 4) {
     // half layout: row t, 16-byte chunk c (32 dims) at 16 (t + 16 c)
 #pragma unroll
@@ -919,16 +928,18 @@ __device__ __forceinline__ void read_slot_pair(PairTile<DT>& t, const uint8_t* s
 // K operand of MFMA m: 16 codes as bytes c * kKMul; byte 4 w + b is dimension
 // 8 (w >> 1) + 2 b + (w & 1) (turbo4) or 4 w + b (turbo8) of the lane's 16.
 template <int DT>
-__device__ __forceinline__ v4i pair_k_operand(const PairTile<DT>& t, int m) {
+__device__ __forceinline__ v4i pair_k_operand(const PairTile<DT>& t, int m, const PairLane& pl) {
   if constexpr (DT == 2) {
     // code of dim 4 b + w (of the lane's 16) to the top two bits of byte b of dword w: 64 c
     const uint32_t x = (uint32_t)t.k[m];
     return v4i{(int)((x << 6) & 0xc0c0c0c0u), (int)((x << 4) & 0xc0c0c0c0u), (int)((x << 2) & 0xc0c0c0c0u),
                (int)(x & 0xc0c0c0c0u)};
   } else if constexpr (DT == 3) {
-    // dims 0..7 and 8..15 of the lane's 16: bits 0..23 and 24..47; 32 c in the top of each byte
-    const uint32_t y0 = spread3to6((uint32_t)t.k[m][0]);
-    const uint32_t y1 = spread3to6(__builtin_amdgcn_alignbit((uint32_t)t.k[m][1], (uint32_t)t.k[m][0], 24));
+    // dims 0..7 and 8..15 of the lane's 16: bytes o .. o + 2 and o + 3 .. o + 5 of the two
+    // dwords, o = 2 kp; 32 c in the top of each byte
+    const uint32_t k0 = (uint32_t)t.k[m][0], k1 = (uint32_t)t.k[m][1];
+    const uint32_t y0 = spread3to6(k1, k0, pl.ksel0);
+    const uint32_t y1 = spread3to6(k1, k0, pl.ksel1);
     return v4i{(int)((y0 << 5) & 0xe0e0e0e0u), (int)((y0 << 2) & 0xe0e0e0e0u), (int)((y1 << 5) & 0xe0e0e0e0u),
                (int)((y1 << 2) & 0xe0e0e0e0u)};
   } else if constexpr (DT == 4) {
@@ -952,7 +963,7 @@ __device__ __forceinline__ void process_pair_tile(const PairTile<DT>& t, WaveSta
   for (int k = 0; k < kDigits; ++k) s[k] = v4i{0, 0, 0, 0};
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const v4i a = pair_k_operand<DT>(t, m);
+    const v4i a = pair_k_operand<DT>(t, m, pl);
 #pragma unroll
     for (int k = 0; k < kDigits; ++k) s[k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qj[m][k], s[k], 0, 0, 0);
   }
@@ -1042,13 +1053,11 @@ __device__ __forceinline__ void process_pair_tile(const PairTile<DT>& t, WaveSta
       o[j] = (n << 4) & 0xc0c0c0c0u;
     }
   } else if constexpr (DT == 3) {
-    const uint32_t sh = (24u * (uint32_t)(lane & 15)) & 31u;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t x = __builtin_amdgcn_alignbit((uint32_t)t.v[j][1], (uint32_t)t.v[j][0], sh);
-      const uint32_t n = spread3to6(x ^ kBias3);    // c + 4 (0..7), two fields per byte
-      e[j] = (n << 5) & 0xe0e0e0e0u;                // (c + 4) << 5
-      o[j] = (n << 2) & 0xe0e0e0e0u;
+      const uint32_t n = spread3to6((uint32_t)t.v[j][1], (uint32_t)t.v[j][0], pl.vsel);   // two fields per byte
+      e[j] = ((n << 5) & 0xe0e0e0e0u) ^ 0x80808080u;       // (c + 4) << 5: the top bit flipped
+      o[j] = ((n << 2) & 0xe0e0e0e0u) ^ 0x80808080u;
     }
   } else if constexpr (DT == 4) {
 #pragma unroll
