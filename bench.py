@@ -7,13 +7,15 @@ A step is one pass of the whole hot path for one layer:
      sequence's new row, plus the prefill chunk where the workload has one (the default, the
      mixed step: a 2,048-token chunk appended for a new sequence, then a batch of 64 decodes);
   2. decode attention over every sequence's paged, quantized context.
-By default one decode launch appends the batch's new rows and decodes (the chunk goes through
-xq_quantize_append first); --no-fuse runs xq_quantize_append and the decode as two launches. The
-decode runs over a length-aware plan by default (xq_decode_plan_balanced: each sequence gets its
-own partition size, all work units about equal); --plan uniform takes the split hint's partitions
-placed by xq_decode_plan, --plan none (or --no-plan) neither.
+By default one decode launch does all of it: it appends the batch's new rows, decodes, and
+appends the chunk's rows with workgroups after its units (--chunk-append kernel: the chunk goes
+through xq_quantize_append first); --no-fuse runs xq_quantize_append and the decode as two
+launches. The decode runs over a length-aware plan by default (xq_decode_plan_balanced: each
+sequence gets its own partition size, all work units about equal); --plan uniform takes the split
+hint's partitions placed by xq_decode_plan, --plan none (or --no-plan) neither.
 
-Steps are timed twice, K each after W warm-up steps: eagerly, with HIP events around every
+Steps are timed twice, K each after W warm-up steps (and as many more untimed ones as bring the
+warm-up to 30 ms of GPU work, so that the clocks have left idle): eagerly, with HIP events around every
 decode call and every append call (on the stream they are launched on), and replayed from HIP
 graphs captured per pool replica, the way a serving engine replays its decode step; when every
 replica has its graph, also from one graph holding a step on each replica in turn, as a model's
@@ -41,6 +43,7 @@ the host's cores, in worker processes started before anything touches the GPU.
 from __future__ import annotations
 
 import argparse
+import math
 import hashlib
 import json
 import multiprocessing as mp
@@ -325,6 +328,28 @@ class Step:
             raise RuntimeError(lib.xq_last_error().decode())
 
 
+def warm(step, n: int, stream, min_ms: float = 30.0) -> int:
+    """The W untimed warmup steps (step(i) runs step i), then more untimed steps until the warmup
+    has kept the GPU busy for min_ms, so that its clocks have left idle (the host's oracle run and
+    the graph captures leave it idle for seconds) before the timed steps. -> steps run."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    i = 0
+    while i < max(n, 1):
+        step(i)
+        i += 1
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    if ms < min_ms:
+        for _ in range(int(math.ceil((min_ms - ms) / max(ms / i, 1e-3)))):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
+    return i
+
+
 def event_pairs(n):
     import torch
     return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
@@ -554,11 +579,13 @@ def main():
 
     log(f"{R} pool replicas of {footprint} bytes; timing")
     K, Wm = args.steps, args.warmup
-    for i in range(Wm):
+
+    def eager_step(i):
         r = runners[i % R]
         r.run(sp)
         r.decode(sp)
-    torch.cuda.synchronize()
+
+    Wm = warm(eager_step, Wm, stream)
 
     ev = event_pairs(K)
     app_ev = event_pairs(K) if app is not None else None
@@ -604,13 +631,11 @@ def main():
             graphs.append(g)
         torch.cuda.synchronize()
         NG = len(graphs)
-        for i in range(Wm):
-            graphs[i % NG].replay()
-        torch.cuda.synchronize()
+        Wg = warm(lambda i: graphs[i % NG].replay(), args.warmup, stream)
         gstart, gstop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         gstart.record(stream)
         for i in range(K):
-            graphs[(Wm + i) % NG].replay()
+            graphs[(Wg + i) % NG].replay()
         gstop.record(stream)
         torch.cuda.synchronize()
         g_ms = gstart.elapsed_time(gstop) / K
@@ -627,9 +652,7 @@ def main():
                     r.run(cs)
                     r.decode(cs)
             torch.cuda.synchronize()
-            for _ in range(max(1, Wm // R)):
-                layers.replay()
-            torch.cuda.synchronize()
+            warm(lambda i: layers.replay(), max(1, args.warmup // R), stream)
             gstart.record(stream)
             for _ in range(K // R):
                 layers.replay()
@@ -675,7 +698,7 @@ def main():
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": Wm,
+        "warmup": args.warmup,
         "ms_per_step": round(timed_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -732,7 +755,7 @@ def main():
         "append": append,
     }
     if chunk_kv is not None and not args.no_prefill:
-        result["prefill"] = time_prefill(base, W, bt, to_dev, stream, K, Wm)
+        result["prefill"] = time_prefill(base, W, bt, to_dev, stream, K, args.warmup)
     if not args.no_probe:
         del caches, runners
         result["hbm_reference"] = hbm_reference(xq, stream)
