@@ -31,8 +31,9 @@ cannot serve one step's KV reads from the previous ones.
 Prints ONE JSON line. `value` is KV GB/s: the algorithmic KV bytes the decode reads per step
 (sum_b L_b * Hkv * 2 * row_bytes) over the whole step time. `roofline` is for the decode call,
 the dominant work of the step (decode_split_kernel, plus decode_combine_kernel when a sequence
-spans several partitions): achieved = those bytes / the mean of the HIP-event durations of the
-decode calls in the timed region; `frac_kernel_trace` is the same bytes over the kernels' mean
+spans several partitions): achieved = those bytes / the mean duration of the decode call, from
+one HIP event pair around K back-to-back replays of graphs holding only that call (eager
+per-call events, also reported, include the host's launch gaps; without graphs they are used); `frac_kernel_trace` is the same bytes over the kernels' mean
 duration in the committed rocprofv3 summary of this command (while the kernel sources are the
 ones it was taken on); `traffic` is the HBM bytes the counters measured per call.
 `hbm_reference` is a plain streaming-read kernel over 4 GiB (sequentially, and in 1 KiB blocks
@@ -666,6 +667,27 @@ def main():
             log(f"graph of {R} steps: {m_ms * 1e3:.1f} us/step")
             del layers
         del graphs
+        # The decode call alone, replayed from graphs holding only it: one HIP event pair on the
+        # stream around K back-to-back replays, so the mean carries neither host launch gaps nor
+        # the cost of per-call event markers.
+        dgraphs = []
+        for r in runners[:64]:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                r.decode(torch.cuda.current_stream().cuda_stream)
+            dgraphs.append(g)
+        torch.cuda.synchronize()
+        ND = len(dgraphs)
+        Wd = warm(lambda i: dgraphs[i % ND].replay(), args.warmup, stream)
+        gstart.record(stream)
+        for i in range(K):
+            dgraphs[(Wd + i) % ND].replay()
+        gstop.record(stream)
+        torch.cuda.synchronize()
+        dg_us = gstart.elapsed_time(gstop) / K * 1e3
+        graph["decode_call_us"] = round(dg_us, 2)
+        log(f"decode call replayed alone: {dg_us:.1f} us")
+        del dgraphs
 
     kv_bytes = int(W.context_lens.astype(np.int64).sum()) * hkv * 2 * rb
     tokens = int(W.context_lens.astype(np.int64).sum())
@@ -678,7 +700,9 @@ def main():
     # codes and scale out) where it appends them too
     chunk_bytes = W.chunk_tokens * hkv * 2 * (256 + rb) if chunk is not None else 0
     launch_bytes = kv_bytes + chunk_bytes
-    achieved = launch_bytes / (dec_avg_ms * 1e-3) / 1e9
+    # the decode call's duration: replayed alone from a graph where there is one, else eager
+    call_ms = graph["decode_call_us"] * 1e-3 if graph is not None else dec_avg_ms
+    achieved = launch_bytes / (call_ms * 1e-3) / 1e9
     tag = f"decode_call_{workloads.DTYPE_NAMES[W.dtype]}_{W.name}"
     prof = committed_profile(tag)
     kernel_us = prof.get("decode_call_kernel_us")
@@ -735,9 +759,14 @@ def main():
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "decode_call_us": {"mean": round(dec_avg_ms * 1e3, 2),
                            "p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
-                           "p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2)},
+                           "p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
+                           "method": "HIP events around each eager call in the timed steps"},
+        "decode_call_graph_us": graph["decode_call_us"] if graph is not None else None,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "duration": ("decode_call_graph_us: one HIP event pair around K back-to-back replays of "
+                                  "graphs holding only the decode call" if graph is not None
+                                  else "decode_call_us (eager)"),
                      "traffic": prof.get("hbm_bytes_per_launch"),
                      "frac_kernel_trace": (round(launch_bytes / (kernel_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
                                            if kernel_us else None),
