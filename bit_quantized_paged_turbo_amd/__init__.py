@@ -18,7 +18,7 @@ OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
 
 # Every symbol include/xq.h declares.
 EXPORTS = ("xq_block_bytes", "xq_page_stride_bytes", "xq_pool_bytes", "xq_decode_num_splits",
-           "xq_decode_workspace_bytes", "xq_status_string", "xq_last_error",
+           "xq_decode_workspace_bytes", "xq_prefill_workspace_bytes", "xq_status_string", "xq_last_error",
            "xq_quantize_append", "xq_paged_decode_attention", "xq_paged_prefill_attention",
            "xq_decode_plan", "xq_paged_decode_attention_planned", "xq_append_decode_attention",
            "xq_hbm_read_probe", "xq_paged_decode_attention_noalloc", "xq_decode_plan_entries",
@@ -62,6 +62,7 @@ def load() -> ctypes.CDLL:
         "xq_pool_bytes": (I64, [LP]),
         "xq_decode_num_splits": (I32, [LP, I32, I32, I32, I32]),
         "xq_decode_workspace_bytes": (I64, [LP, I32, I32, I32, I32]),
+        "xq_prefill_workspace_bytes": (I64, [LP, I32, I32, I32, I32]),
         "xq_status_string": (ctypes.c_char_p, [I32]),
         "xq_last_error": (ctypes.c_char_p, []),
         "xq_quantize_append": (I32, [LP, P, P, I32, P, P, P, I32, P, P, P]),
@@ -137,6 +138,11 @@ def xq_decode_num_splits(layout, batch, num_q_heads, max_context_len, num_splits
 def xq_decode_workspace_bytes(layout, batch, num_q_heads, max_context_len, num_splits_hint=0) -> int:
     return load().xq_decode_workspace_bytes(ctypes.byref(layout), batch, num_q_heads,
                                             max_context_len, num_splits_hint)
+
+
+def xq_prefill_workspace_bytes(layout, n_query, num_q_heads, start_pos, num_splits_hint=0) -> int:
+    return load().xq_prefill_workspace_bytes(ctypes.byref(layout), n_query, num_q_heads,
+                                             start_pos, num_splits_hint)
 
 
 def xq_quantize_append(layout: CacheLayout, k_new, v_new, n_tokens: int, token_seq, token_pos,

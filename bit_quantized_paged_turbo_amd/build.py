@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libxq.so")
 ARCH = "gfx950"
 
-SOURCES = ["xq_abi.cpp", "quantize_append.hip", "decode_attention.hip", "hbm_probe.hip"]
+SOURCES = ["xq_abi.cpp", "quantize_append.hip", "decode_attention.hip", "prefill_attention.hip", "hbm_probe.hip"]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 

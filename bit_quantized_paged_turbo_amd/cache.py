@@ -9,6 +9,7 @@ import torch
 
 from . import (CacheLayout, load, xq_append_decode_attention, xq_decode_attention_balanced, xq_decode_plan,
                xq_decode_plan_balanced, xq_decode_workspace_bytes, xq_decode_workspace_bytes_balanced,
+               xq_prefill_workspace_bytes,
                xq_paged_decode_attention,
                xq_paged_decode_attention_planned, xq_paged_prefill_attention,
                xq_pool_bytes, xq_quantize_append)
@@ -137,7 +138,7 @@ class PagedKVCache:
         n, hq = int(q.shape[0]), int(q.shape[1])
         if out is None:
             out = torch.empty((n, hq, 128), dtype=torch.float32, device=q.device)
-        need = self.workspace_bytes(n, hq, start_pos + n, num_splits)
+        need = xq_prefill_workspace_bytes(self.layout, n, hq, int(start_pos), num_splits)
         if workspace is None and need > 0:
             if self._ws is None or self._ws.numel() < need:
                 self._ws = torch.empty((need,), dtype=torch.uint8, device=q.device)

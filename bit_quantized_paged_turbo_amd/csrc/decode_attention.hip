@@ -2022,6 +2022,14 @@ void launch_split(const DecodeParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((decode_split_kernel<DT, DEPTH>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
 }
 
+template <int DT>
+void combine_dt(const DecodeParams& p, hipStream_t stream) {
+  if (p.nsplits > 32 && !p.fixed_splits)
+    hipLaunchKernelGGL((decode_combine_kernel<DT, 512>), dim3(p.hq, p.batch), dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_combine_kernel<DT, 128>), dim3(p.hq, p.batch), dim3(128), 0, stream, p);
+}
+
 // With fixed partitions (batch-invariant mode) the kernel variants do not depend on the batch:
 // a three-slot ring (the paired/one-block layouts, never the quad one, whose blocking of the
 // softmax differs) and the 128-thread combine, so a sequence's output depends only on its own
@@ -2039,13 +2047,7 @@ hipError_t launch_dt(const DecodeParams& p, hipStream_t stream) {
   } else {
     launch_split<DT, 3>(p, stream);
   }
-  if (p.nsplits > 1)
-  {
-    if (p.nsplits > 32 && !p.fixed_splits)
-      hipLaunchKernelGGL((decode_combine_kernel<DT, 512>), dim3(p.hq, p.batch), dim3(512), 0, stream, p);
-    else
-      hipLaunchKernelGGL((decode_combine_kernel<DT, 128>), dim3(p.hq, p.batch), dim3(128), 0, stream, p);
-  }
+  if (p.nsplits > 1) combine_dt<DT>(p, stream);
   return hipGetLastError();
 }
 
@@ -2061,6 +2063,19 @@ int decode_waves_per_simd(int dtype, const DecodeParams& p) {
     case kFp8: return waves_per_simd<kFp8>(p);
     default: return 1;
   }
+}
+
+hipError_t launch_combine(int dtype, const DecodeParams& p, hipStream_t stream) {
+  switch (dtype) {
+    case 0: combine_dt<0>(p, stream); break;
+    case 8: combine_dt<8>(p, stream); break;
+    case 4: combine_dt<4>(p, stream); break;
+    case 3: combine_dt<3>(p, stream); break;
+    case 2: combine_dt<2>(p, stream); break;
+    case kFp8: combine_dt<kFp8>(p, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(int dtype, const DecodeParams& p, hipStream_t stream) {

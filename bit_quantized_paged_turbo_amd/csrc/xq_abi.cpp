@@ -391,6 +391,94 @@ xq_status attention(const xq_cache_layout* layout, const void* q, int32_t batch,
   return XQ_OK;
 }
 
+// ---- chunked prefill on the tile kernel ---------------------------------------------------
+// Partitions of a tiled prefill: whole 64-token tiles and whole pages. hint > 0 asks for that many
+// partitions of the longest query's context; 0 cuts the context only when the chunk's workgroups
+// are fewer than two per compute unit, into partitions of at least 256 tokens (the query set-up and the partial store of a workgroup cost about as much as a few tiles).
+struct TilePlan {
+  int32_t tps, nsplits, block_queries;
+};
+
+TilePlan tile_prefill_plan(const xq_cache_layout* L, int32_t n_query, int32_t num_q_heads, int32_t ctx,
+                           int32_t hint) {
+  TilePlan t{};
+  const int32_t g = num_q_heads / L->num_kv_heads;
+  t.block_queries = xq::prefill_block_queries(g);
+  const int64_t blocks = xq::prefill_workgroups(n_query, g, L->num_kv_heads, 1);
+  const int64_t unit = L->page_size > 64 ? L->page_size : 64;
+  int64_t tps;
+  if (hint > 0) {
+    tps = ((int64_t)ctx + hint - 1) / hint;
+  } else {
+    const int64_t want = blocks >= 512 ? 1 : (512 + blocks - 1) / blocks;
+    tps = std::max<int64_t>(((int64_t)ctx + want - 1) / want, 256);
+  }
+  tps = (tps + unit - 1) / unit * unit;
+  t.tps = (int32_t)std::min<int64_t>(tps, ((int64_t)ctx + unit - 1) / unit * unit);
+  t.nsplits = (int32_t)(((int64_t)ctx + t.tps - 1) / t.tps);
+  return t;
+}
+
+xq_status tile_prefill(const xq_cache_layout* layout, const void* q, int32_t n_query, int32_t num_q_heads,
+                       const void* k_pool, const void* v_pool, const int32_t* block_table, int32_t max_pages,
+                       int32_t start_pos, float softmax_scale, int32_t hint, void* workspace,
+                       int64_t workspace_bytes, float* out, hipStream_t stream) {
+  if (n_query > 65535) return fail(XQ_EUNSUPPORTED, "n_query %d > 65535", n_query);
+  if (num_q_heads < 1 || num_q_heads % layout->num_kv_heads != 0)
+    return fail(XQ_EINVAL, "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads,
+                layout->num_kv_heads);
+  const int32_t g = num_q_heads / layout->num_kv_heads;
+  if (g > xq::kMaxGroup) return fail(XQ_EUNSUPPORTED, "group size %d > %d", g, xq::kMaxGroup);
+  if (!q || !k_pool || !v_pool || !block_table || !out) return fail(XQ_EINVAL, "a required pointer is NULL");
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(XQ_EINVAL, "q and the pools must be 16-byte aligned");
+  if (max_pages < 1) return fail(XQ_EINVAL, "max_pages %d < 1", max_pages);
+  const int32_t ctx = start_pos + n_query;
+  if ((int64_t)ctx > (int64_t)max_pages * layout->page_size)
+    return fail(XQ_EINVAL, "context of %d tokens exceeds max_pages * page_size", ctx);
+  if (!(softmax_scale == softmax_scale)) return fail(XQ_EINVAL, "softmax_scale is NaN");
+  const TilePlan plan = tile_prefill_plan(layout, n_query, num_q_heads, ctx, hint);
+  if (plan.nsplits > 65535) return fail(XQ_EUNSUPPORTED, "%d splits > 65535", plan.nsplits);
+  const int64_t units = xq::prefill_workgroups(n_query, g, layout->num_kv_heads, plan.nsplits);
+  if (units >= ((int64_t)1 << 31)) return fail(XQ_EUNSUPPORTED, "%lld workgroups", (long long)units);
+  const xq::WorkspaceLayout ws = xq::workspace_layout(layout->kv_dtype, n_query, num_q_heads, plan.nsplits);
+  if (ws.total > 0) {
+    if (!workspace || workspace_bytes < ws.total)
+      return fail(XQ_EWORKSPACE, "workspace of %lld bytes needed (xq_prefill_workspace_bytes), %lld given",
+                  (long long)ws.total, (long long)workspace_bytes);
+    if (!aligned16(workspace)) return fail(XQ_EINVAL, "workspace must be 16-byte aligned");
+  }
+  if (debug_on())
+    if (xq_status st = debug_check_prefill(layout, block_table, ctx, stream)) return st;
+
+  xq::DecodeParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_pool = static_cast<const uint8_t*>(k_pool);
+  p.v_pool = static_cast<const uint8_t*>(v_pool);
+  p.block_tables = block_table;
+  p.out = out;
+  p.partials = ws.part_bytes ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + ws.part_off) : nullptr;
+  p.block_bytes = block_bytes_of(layout);
+  p.page_stride = p.block_bytes * layout->num_kv_heads;
+  p.pool_bytes = p.page_stride * layout->num_pages;
+  p.batch = n_query;
+  p.hq = num_q_heads;
+  p.hkv = layout->num_kv_heads;
+  p.group = g;
+  p.page_size = layout->page_size;
+  p.page_shift = __builtin_ctz((unsigned)layout->page_size);
+  p.maxp = max_pages;
+  p.tokens_per_split = plan.tps;
+  p.nsplits = plan.nsplits;
+  p.max_context_len = ctx;
+  p.softmax_scale = softmax_scale;
+  p.ctx_base = start_pos + 1;
+  p.qt = plan.block_queries;
+  const hipError_t e = xq::launch_prefill(layout->kv_dtype, p, stream);
+  if (e != hipSuccess) return fail(XQ_EHIP, "prefill launch: %s", hipGetErrorString(e));
+  return XQ_OK;
+}
+
 // ---- scratch of the allocation-free decode ----------------------------------------------
 // xq_paged_decode_attention_noalloc keeps its split partials in this file-scope device array: one
 // copy per GPU the library runs on, held until the process ends. In host code `scratch` is only
@@ -901,6 +989,19 @@ xq_status xq_decode_attention_balanced(const xq_cache_layout* layout, const void
                    nsplits, &x);
 }
 
+int64_t xq_prefill_workspace_bytes(const xq_cache_layout* layout, int32_t n_query, int32_t num_q_heads,
+                                   int32_t start_pos, int32_t num_splits_hint) {
+  if (check_layout(layout) || n_query < 0 || start_pos < 0 || num_q_heads < 1 ||
+      num_q_heads % layout->num_kv_heads != 0 || num_q_heads / layout->num_kv_heads > xq::kMaxGroup ||
+      (int64_t)start_pos + n_query > INT32_MAX / 2)
+    return -1;
+  if (n_query == 0) return 0;
+  if (num_splits_hint < 0 || !xq::prefill_tiled(layout->kv_dtype))
+    return xq_decode_workspace_bytes(layout, n_query, num_q_heads, start_pos + n_query, num_splits_hint);
+  const int32_t ns = tile_prefill_plan(layout, n_query, num_q_heads, start_pos + n_query, num_splits_hint).nsplits;
+  return xq::workspace_layout(layout->kv_dtype, n_query, num_q_heads, ns).total;
+}
+
 xq_status xq_paged_prefill_attention(const xq_cache_layout* layout, const void* q, int32_t n_query,
                                      int32_t num_q_heads, const void* k_pool, const void* v_pool,
                                      const int32_t* block_table, int32_t max_pages, int32_t start_pos,
@@ -912,6 +1013,10 @@ xq_status xq_paged_prefill_attention(const xq_cache_layout* layout, const void* 
   if (n_query == 0) return XQ_OK;
   if ((int64_t)start_pos + n_query > INT32_MAX / 2)
     return fail(XQ_EINVAL, "start_pos + n_query = %lld is too large", (long long)start_pos + n_query);
+  if (num_splits_hint >= 0 && xq::prefill_tiled(layout->kv_dtype))
+    return tile_prefill(layout, q, n_query, num_q_heads, k_pool, v_pool, block_table, max_pages, start_pos,
+                        softmax_scale, num_splits_hint, workspace, workspace_bytes, out,
+                        static_cast<hipStream_t>(stream));
   return attention(layout, q, n_query, num_q_heads, k_pool, v_pool, block_table, 0, max_pages, nullptr,
                    start_pos + 1, start_pos + n_query, softmax_scale, num_splits_hint, workspace,
                    workspace_bytes, out, static_cast<hipStream_t>(stream));

@@ -99,6 +99,18 @@ struct DecodeParams {
 
 hipError_t launch_quantize_append(int dtype, const AppendParams& p, hipStream_t stream);
 hipError_t launch_decode(int dtype, const DecodeParams& p, hipStream_t stream);
+// Merge of split partials (m, l, acc) into the rotated-back outputs: p.nsplits partitions of
+// p.tokens_per_split tokens, the partition count of row b being that of the last row of its
+// block of p.qt rows; a block with one partition is skipped (its rows are written by the kernel
+// that computed them).
+hipError_t launch_combine(int dtype, const DecodeParams& p, hipStream_t stream);
+// Chunked prefill on the tile kernel (cache types for which prefill_tiled holds): one workgroup
+// per (partition, kv head, block of p.qt = prefill_block_queries(group) queries;
+// prefill_workgroups of them), then the combine when p.nsplits > 1.
+bool prefill_tiled(int dtype);
+int prefill_block_queries(int group);
+int64_t prefill_workgroups(int32_t n_query, int32_t group, int32_t hkv, int32_t nsplits);
+hipError_t launch_prefill(int dtype, const DecodeParams& p, hipStream_t stream);
 // Waves of the decode's split kernel resident on one SIMD for the launch launch_decode would make
 // with these parameters (the register budget and the LDS of a compute unit).
 int decode_waves_per_simd(int dtype, const DecodeParams& p);

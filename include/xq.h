@@ -356,6 +356,14 @@ xq_status xq_decode_attention_balanced(const xq_cache_layout* layout, const void
                                        void* stream);
 
 /*
+ * Workspace bytes xq_paged_prefill_attention needs for these arguments (the partition partials;
+ * 0 when the chunk runs in one partition). Returns -1 on invalid arguments.
+ */
+int64_t xq_prefill_workspace_bytes(const xq_cache_layout* layout, int32_t n_query,
+                                   int32_t num_q_heads, int32_t start_pos,
+                                   int32_t num_splits_hint);
+
+/*
  * Chunked prefill attention over the paged (and, for turbo types, quantized) cache: the queries
  * of one chunk of one sequence, each attending causally to the sequence's cached rows. Defined
  * by the infero page, section "Beyond plain text decode", item "Continuous batching" (decodes
@@ -374,14 +382,18 @@ xq_status xq_decode_attention_balanced(const xq_cache_layout* layout, const void
  *   start_pos          position of query 0 (the number of rows cached before the chunk), >= 0
  *   softmax_scale      multiplies q . k
  *   num_splits_hint    as for xq_paged_decode_attention
- *   workspace          device scratch of >= xq_decode_workspace_bytes(layout, n_query,
- *                      num_q_heads, start_pos + n_query, num_splits_hint) bytes (may be NULL when
- *                      that is 0); calls that share a workspace must not overlap
+ *   workspace          device scratch of >= xq_prefill_workspace_bytes(layout, n_query,
+ *                      num_q_heads, start_pos, num_splits_hint) bytes (may be NULL when that is
+ *                      0); calls that share a workspace must not overlap
  *   out                fp32 [n_query][num_q_heads][128]
  * n_query = 0 is a no-op. start_pos + n_query must not exceed max_pages * page_size (XQ_EINVAL);
  * more than 65535 queries, a group size above 16 or 2^26 or more (split, kv head, query) units
  * give XQ_EUNSUPPORTED. The block-table entries of positions below start_pos + n_query must be
  * pages of the pool (checked only under XQ_DEBUG).
+ * Kernels: with fixed partitions (num_splits_hint < 0) the queries run on the decode's kernel,
+ * and each query's output is bitwise the decode's with the same partition when the group size
+ * is 16; otherwise turbo4 caches use a tile kernel (a workgroup dequantizes each 64-token tile
+ * once for 8 * (16 / group) queries), with its own rounding order, within the same tolerance.
  */
 xq_status xq_paged_prefill_attention(const xq_cache_layout* layout,
                                      const void* q, int32_t n_query, int32_t num_q_heads,

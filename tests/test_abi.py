@@ -164,7 +164,15 @@ def test_prefill_argument_errors(lib):
     assert _prefill_status(lib, L, hq=7) == xq.EINVAL
     assert _prefill_status(lib, L, bt=None) == xq.EINVAL
     assert _prefill_status(lib, L, n=70000, maxp=5000, start=0) == xq.EUNSUPPORTED
-    assert _prefill_status(lib, L, start=40, splits=2) == xq.EWORKSPACE  # 48 positions, 2 partitions
+    # 108 positions in 2 partitions of 64: both kernels need the partials
+    assert _prefill_status(lib, L, start=100, maxp=8, splits=2) == xq.EWORKSPACE
+    assert _prefill_status(lib, L, start=100, maxp=8, splits=-64) == xq.EWORKSPACE
+    ws = xq.xq_prefill_workspace_bytes(L, 8, 8, 100, 2)
+    assert ws == 8 * 8 * 2 * 132 * 4
+    assert xq.xq_prefill_workspace_bytes(L, 8, 8, 100, -64) == ws
+    assert xq.xq_prefill_workspace_bytes(L, 8, 8, 10, 0) == 0
+    assert xq.xq_prefill_workspace_bytes(L, 8, 7, 10, 0) == -1
+    assert xq.xq_prefill_workspace_bytes(L, -1, 8, 10, 0) == -1
     assert _prefill_status(lib, L, scale=float("nan")) == xq.EINVAL
 
 

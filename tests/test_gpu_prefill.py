@@ -34,7 +34,7 @@ def _setup(dtype, start, chunk, hq, hkv, ps, cfg):
     (4, 0, 77, 8, 2, 16), (4, 100, 77, 16, 8, 16), (4, 333, 40, 32, 8, 64), (8, 50, 33, 32, 8, 16),
     (3, 200, 65, 40, 8, 64), (2, 17, 50, 8, 8, 16), (0, 90, 45, 8, 2, 32), (16, 120, 60, 32, 8, 16),
     (4, 700, 1, 8, 2, 16), (4, 37, 50, 8, 8, 16), (3, 64, 29, 40, 8, 64), (8, 5, 70, 16, 1, 32),
-    (0, 30, 47, 24, 8, 16), (16, 3, 61, 8, 1, 16)])
+    (0, 30, 47, 24, 8, 16), (16, 3, 61, 8, 1, 16), (4, 3000, 20, 32, 8, 16), (4, 1, 300, 40, 8, 32)])
 def test_prefill_matches_oracle(dtype, start, chunk, hq, hkv, ps):
     _case("prefill", dtype, start, chunk, hq, hkv, ps)
     W, cache, bt, kv, q = _setup(dtype, start, chunk, hq, hkv, ps, 800 + dtype)
