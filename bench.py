@@ -32,7 +32,7 @@ Prints ONE JSON line. `value` is KV GB/s: the algorithmic KV bytes the decode re
 (sum_b L_b * Hkv * 2 * row_bytes) over the whole step time. `roofline` is for the decode call,
 the dominant work of the step (decode_split_kernel, plus decode_combine_kernel when a sequence
 spans several partitions): achieved = those bytes / the mean duration of the decode call, from
-one HIP event pair around K back-to-back replays of graphs holding only that call (eager
+one HIP event pair around replays of a graph holding only decode calls back to back (eager
 per-call events, also reported, include the host's launch gaps; without graphs they are used); `frac_kernel_trace` is the same bytes over the kernels' mean
 duration in the committed rocprofv3 summary of this command (while the kernel sources are the
 ones it was taken on); `traffic` is the HBM bytes the counters measured per call.
@@ -667,27 +667,29 @@ def main():
             log(f"graph of {R} steps: {m_ms * 1e3:.1f} us/step")
             del layers
         del graphs
-        # The decode call alone, replayed from graphs holding only it: one HIP event pair on the
-        # stream around K back-to-back replays, so the mean carries neither host launch gaps nor
-        # the cost of per-call event markers.
-        dgraphs = []
-        for r in runners[:64]:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                r.decode(torch.cuda.current_stream().cuda_stream)
-            dgraphs.append(g)
+        # The decode call alone: one graph holding M decode calls back to back (one per pool
+        # replica in turn, or 8 calls on the one replica), replayed so that about K calls run,
+        # with one HIP event pair on the stream around them all; the mean carries neither host
+        # launch gaps, nor per-call event markers, nor a graph launch per call.
+        M = min(64, R if R > 1 else 8)
+        dgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(dgraph):
+            cs = torch.cuda.current_stream().cuda_stream
+            for i in range(M):
+                runners[i % R].decode(cs)
         torch.cuda.synchronize()
-        ND = len(dgraphs)
-        Wd = warm(lambda i: dgraphs[i % ND].replay(), args.warmup, stream)
+        warm(lambda i: dgraph.replay(), max(1, args.warmup // M), stream)
+        nrep = max(1, K // M)
         gstart.record(stream)
-        for i in range(K):
-            dgraphs[(Wd + i) % ND].replay()
+        for _ in range(nrep):
+            dgraph.replay()
         gstop.record(stream)
         torch.cuda.synchronize()
-        dg_us = gstart.elapsed_time(gstop) / K * 1e3
+        dg_us = gstart.elapsed_time(gstop) / (nrep * M) * 1e3
         graph["decode_call_us"] = round(dg_us, 2)
-        log(f"decode call replayed alone: {dg_us:.1f} us")
-        del dgraphs
+        graph["decode_calls_timed"] = nrep * M
+        log(f"decode call, {M} a graph: {dg_us:.1f} us")
+        del dgraph
 
     kv_bytes = int(W.context_lens.astype(np.int64).sum()) * hkv * 2 * rb
     tokens = int(W.context_lens.astype(np.int64).sum())
@@ -762,10 +764,11 @@ def main():
                            "p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
                            "method": "HIP events around each eager call in the timed steps"},
         "decode_call_graph_us": graph["decode_call_us"] if graph is not None else None,
+        "decode_calls_graph_timed": graph["decode_calls_timed"] if graph is not None else None,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "duration": ("decode_call_graph_us: one HIP event pair around K back-to-back replays of "
-                                  "graphs holding only the decode call" if graph is not None
+                     "duration": ("decode_call_graph_us: one HIP event pair around replays of a graph "
+                                  "holding only decode calls, back to back" if graph is not None
                                   else "decode_call_us (eager)"),
                      "traffic": prof.get("hbm_bytes_per_launch"),
                      "frac_kernel_trace": (round(launch_bytes / (kernel_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
