@@ -78,9 +78,9 @@ constexpr int kORow = D + 4;
 constexpr int kOWave = kNC * 16 * kORow * 4;      // per wave: normalised output rows (fp32)
 static_assert(kWaves * kQWave <= kLds && kWaves * kOWave <= kLds, "query and output areas fit the tile buffer");
 
-// Position of dimension 8 j + e (e < 8) in a K row: 8 j + 2 (e & 3) + (e >> 2). The turbo4 unpack
-// below makes fp16 pairs of nibbles (e, e + 4) of one code dword, so the row holds each group of
-// eight dimensions as 0 4 1 5 2 6 3 7; the query operand is laid out the same way.
+// Position of dimension 8 j + e (e < 8) in a K row: 8 j + 2 (e & 3) + (e >> 2). The unpack below
+// makes fp16 pairs of the codes (e, e + 4) of each group of eight dimensions, so the row holds
+// each group as 0 4 1 5 2 6 3 7; the query operand is laid out the same way.
 __device__ __forceinline__ int k_pos(int e) { return 2 * (e & 3) + (e >> 2); }
 
 // Position of tile token t in a V row: the PV k slots 8 g .. 8 g + 7 of MFMA j are tokens
@@ -94,22 +94,38 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// Two biased 4-bit codes n0, n1 (n = c + 8) in bits 0..3 and 16..19 of x: the fp16 pair (c0, c1),
-// exact: 0x6400 | n is the fp16 value 1024 + n.
-__device__ __forceinline__ uint32_t nib_pair(uint32_t x) {
-  const h2 v = __builtin_bit_cast(h2, (x & 0x000f000fu) | 0x64006400u) - h2{(_Float16)1032.f, (_Float16)1032.f};
+// fp16 pair (c0, c1) of two biased codes n = c + 2^(bits - 1) in bits 0..7 and 16..23 of x (its
+// other bits zero): 0x6400 | n is the fp16 value 1024 + n, so one packed subtraction gives the
+// codes exactly.
+template <int DT>
+__device__ __forceinline__ uint32_t code_pair(uint32_t x) {
+  constexpr _Float16 off = (_Float16)(1024.f + (float)(1 << (DT - 1)));
+  const h2 v = __builtin_bit_cast(h2, x | 0x64006400u) - h2{off, off};
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// ---- one tile's raw bytes as one thread loads them (turbo4) --------------------------------
-// K: thread t holds dimensions 32 (t >> 6) .. + 31 of token t & 63 (16 bytes). V: dimensions
-// 8 (t >> 4) .. + 7 of tokens 4 (t & 15) .. + 3 (one dword each). Threads t < 64: the fp16 K and
-// V scales of token t. Tokens at or past the partition's end read as zero codes and zero scales.
-// The lanes of a wave thus write 16 different K rows and, for V, 16 different 8-byte pieces of
-// one dimension row, so that the LDS writes meet no bank conflict.
-struct Raw4 {
-  uint4 k;
-  uint32_t v[4];
+__device__ __forceinline__ uint32_t bfe(uint32_t x, int off, int w) { return __builtin_amdgcn_ubfe(x, off, w); }
+__device__ __forceinline__ uint32_t align(uint32_t hi, uint32_t lo, int shift) {
+  return __builtin_amdgcn_alignbit(hi, lo, shift);
+}
+
+// Byte i of lo into bits 0..7 and byte i of hi into bits 16..23, zeros elsewhere.
+constexpr uint32_t pair_sel(int i) {
+  return (uint32_t)i | (0x0cu << 8) | ((uint32_t)(4 + i) << 16) | (0x0cu << 24);
+}
+
+// ---- one tile's raw bytes as one thread loads them ----------------------------------------
+// K: thread t holds dimensions 32 (t >> 6) .. + 31 of token t & 63 (4 bits bytes). V: dimensions
+// 8 (t >> 4) .. + 7 of tokens 4 (t & 15) .. + 3 (bits bytes each; turbo3's three bytes start at
+// any byte, so the two dwords around them are read). Threads t < 64: the fp16 K and V scales of
+// token t. Tokens at or past the partition's end read as zero codes and zero scales. The lanes
+// of a wave thus write 16 different K rows and, for V, 16 different 8-byte pieces of one
+// dimension row, so that the LDS writes meet no bank conflict.
+template <int DT> struct Raw {
+  static constexpr int kV = DT == 8 || DT == 3 ? 2 : 1;
+  uint32_t k[DT];      // 4 DT bytes of K codes
+  uint32_t v[4][kV];   // per token: turbo8 two dwords, turbo4 one, turbo3 the dwords around its
+                       // three bytes, turbo2 one halfword
   uint32_t s;
 };
 
@@ -127,19 +143,58 @@ __device__ __forceinline__ int64_t block_addr(const Src& s, int t) {
   return (int64_t)s.bt[t >> s.page_shift] * s.page_stride + s.head_off;
 }
 
-__device__ __forceinline__ void load_raw(Raw4& R, const Src& s, int T0, int t_end, int tid) {
+template <int DT>
+__device__ __forceinline__ void load_raw(Raw<DT>& R, const Src& s, int T0, int t_end, int tid) {
+  constexpr int kRow = 16 * DT;   // code bytes of a row
   const int tk = T0 + (tid & 63);
   const int64_t kb = tk < t_end ? block_addr(s, tk) : 0;
   const int kslot = tk & s.page_mask;
-  R.k = tk < t_end ? *reinterpret_cast<const uint4*>(s.k_pool + kb + kslot * 64 + 16 * (tid >> 6))
-                   : make_uint4(0u, 0u, 0u, 0u);
+  {
+    const uint8_t* src = s.k_pool + kb + kslot * kRow + 4 * DT * (tid >> 6);
+    if constexpr (DT == 8) {
+      const uint4 a = tk < t_end ? reinterpret_cast<const uint4*>(src)[0] : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 b = tk < t_end ? reinterpret_cast<const uint4*>(src)[1] : make_uint4(0u, 0u, 0u, 0u);
+      R.k[0] = a.x; R.k[1] = a.y; R.k[2] = a.z; R.k[3] = a.w;
+      R.k[4] = b.x; R.k[5] = b.y; R.k[6] = b.z; R.k[7] = b.w;
+    } else if constexpr (DT == 4) {
+      const uint4 a = tk < t_end ? *reinterpret_cast<const uint4*>(src) : make_uint4(0u, 0u, 0u, 0u);
+      R.k[0] = a.x; R.k[1] = a.y; R.k[2] = a.z; R.k[3] = a.w;
+    } else if constexpr (DT == 3) {
+      const uint32_t* s32 = reinterpret_cast<const uint32_t*>(src);
+      R.k[0] = tk < t_end ? s32[0] : 0u;
+      R.k[1] = tk < t_end ? s32[1] : 0u;
+      R.k[2] = tk < t_end ? s32[2] : 0u;
+    } else {
+      const uint2 a = tk < t_end ? *reinterpret_cast<const uint2*>(src) : make_uint2(0u, 0u);
+      R.k[0] = a.x; R.k[1] = a.y;
+    }
+  }
   {
     const int t0 = T0 + 4 * (tid & 15);
+    const int dg = tid >> 4;
     // the four tokens share a page (pages hold at least 16 tokens and t0 is a multiple of 4)
-    const int64_t base = t0 < t_end ? block_addr(s, t0) + (t0 & s.page_mask) * 64 + 4 * (tid >> 4) : 0;
+    const int64_t base = t0 < t_end ? block_addr(s, t0) + (t0 & s.page_mask) * kRow : 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      R.v[i] = t0 + i < t_end ? *reinterpret_cast<const uint32_t*>(s.v_pool + base + 64 * i) : 0u;
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = t0 + i < t_end;
+      const uint8_t* row = s.v_pool + base + kRow * i;
+      if constexpr (DT == 8) {
+        const uint2 a = ok ? *reinterpret_cast<const uint2*>(row + 8 * dg) : make_uint2(0u, 0u);
+        R.v[i][0] = a.x;
+        R.v[i][1] = a.y;
+      } else if constexpr (DT == 4) {
+        R.v[i][0] = ok ? *reinterpret_cast<const uint32_t*>(row + 4 * dg) : 0u;
+      } else if constexpr (DT == 3) {
+        // bytes 3 dg .. 3 dg + 2 lie in dword (3 dg) / 4 and, from byte 2 of it on, the next one
+        // (never past the row's last dword: dg = 15 starts at byte 1 of dword 11)
+        const int dw = (3 * dg) >> 2;
+        const uint32_t* r32 = reinterpret_cast<const uint32_t*>(row);
+        R.v[i][0] = ok ? r32[dw] : 0u;
+        R.v[i][1] = ok && ((3 * dg) & 3) >= 2 ? r32[dw + 1] : 0u;
+      } else {
+        R.v[i][0] = ok ? (uint32_t)*reinterpret_cast<const uint16_t*>(row + 2 * dg) : 0u;
+      }
+    }
   }
   R.s = 0u;
   if (tid < kTile && tk < t_end) {
@@ -149,31 +204,63 @@ __device__ __forceinline__ void load_raw(Raw4& R, const Src& s, int T0, int t_en
   }
 }
 
-__device__ __forceinline__ void write_stage(uint8_t* st, const Raw4& R, int tid, float inv_s) {
+// K: the biased code pair (dimensions 8 j + i, 8 j + i + 4) of the thread's 32 dimensions, j, i < 4.
+template <int DT>
+__device__ __forceinline__ uint32_t k_pair(const Raw<DT>& R, int j, int i) {
+  if constexpr (DT == 8) {
+    return perm(R.k[2 * j + 1], R.k[2 * j], pair_sel(i)) ^ 0x00800080u;
+  } else if constexpr (DT == 4) {
+    return ((R.k[j] ^ 0x88888888u) >> (4 * i)) & 0x000f000fu;
+  } else if constexpr (DT == 3) {
+    // group j's 24 bits start at bit 24 j of the 96; the top bit of every 3-bit field flipped
+    constexpr uint32_t kFlip[3] = {0x24924924u, 0x49249249u, 0x92492492u};
+    const uint32_t k0 = R.k[0] ^ kFlip[0], k1 = R.k[1] ^ kFlip[1], k2 = R.k[2] ^ kFlip[2];
+    const uint32_t gj = j == 0 ? k0 : j == 1 ? align(k1, k0, 24) : j == 2 ? align(k2, k1, 16) : k2 >> 8;
+    return bfe(gj, 3 * i, 3) | (bfe(gj, 3 * i + 12, 3) << 16);
+  } else {
+    // bytes (dimensions 0-3, 8-11, 4-7, 12-15 of the dword): group j's pair i at bits 8 (j & 1) + 2 i
+    const uint32_t y = perm(R.k[j >> 1], R.k[j >> 1], 0x03010200u) ^ 0xaaaaaaaau;
+    return (y >> (8 * (j & 1) + 2 * i)) & 0x00030003u;
+  }
+}
+
+// V: the biased code pair (token 2 u, token 2 u + 1) of dimension 8 dg + e, u < 2, e < 8.
+template <int DT>
+__device__ __forceinline__ uint32_t v_pair(const Raw<DT>& R, int u, int e, int dg) {
+  const int a = 2 * u, b = 2 * u + 1;
+  if constexpr (DT == 8) {
+    return perm(R.v[b][e >> 2], R.v[a][e >> 2], pair_sel(e & 3)) ^ 0x00800080u;
+  } else if constexpr (DT == 4) {
+    const uint32_t p = perm(R.v[b][0], R.v[a][0], pair_sel(e >> 1)) ^ 0x00880088u;
+    return (p >> (4 * (e & 1))) & 0x000f000fu;
+  } else if constexpr (DT == 3) {
+    const int sh = 8 * ((3 * dg) & 3);
+    const uint32_t ga = align(R.v[a][1], R.v[a][0], sh) ^ 0x924924u;
+    const uint32_t gb = align(R.v[b][1], R.v[b][0], sh) ^ 0x924924u;
+    return bfe(ga, 3 * e, 3) | (bfe(gb, 3 * e, 3) << 16);
+  } else {
+    const uint32_t z = (R.v[a][0] | (R.v[b][0] << 16)) ^ 0xaaaaaaaau;
+    return (z >> (2 * e)) & 0x00030003u;
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void write_stage(uint8_t* st, const Raw<DT>& R, int tid, float inv_s) {
   {
     uint8_t* dst = st + (tid & 63) * kKRow + 64 * (tid >> 6);
-    const uint32_t w[4] = {R.k.x, R.k.y, R.k.z, R.k.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t x = w[j] ^ 0x88888888u;
+    for (int j = 0; j < 4; ++j)
       *reinterpret_cast<uint4*>(dst + 16 * j) =
-          make_uint4(nib_pair(x), nib_pair(x >> 4), nib_pair(x >> 8), nib_pair(x >> 12));
-    }
+          make_uint4(code_pair<DT>(k_pair<DT>(R, j, 0)), code_pair<DT>(k_pair<DT>(R, j, 1)),
+                     code_pair<DT>(k_pair<DT>(R, j, 2)), code_pair<DT>(k_pair<DT>(R, j, 3)));
   }
   {
     const int dg = tid >> 4;
     const int p0 = v_pos(4 * (tid & 15));
-    const uint32_t x0 = R.v[0] ^ 0x88888888u, x1 = R.v[1] ^ 0x88888888u;
-    const uint32_t x2 = R.v[2] ^ 0x88888888u, x3 = R.v[3] ^ 0x88888888u;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      // byte b of each token's dword (dimensions 8 dg + 2 b, + 1) into the halves of a pair
-      const uint32_t sel = (uint32_t)b | (0x0cu << 8) | ((uint32_t)(4 + b) << 16) | (0x0cu << 24);
-      const uint32_t p01 = perm(x1, x0, sel), p23 = perm(x3, x2, sel);
-      uint8_t* d0 = st + kVOff + (8 * dg + 2 * b) * kVRow + 2 * p0;
-      *reinterpret_cast<uint2*>(d0) = make_uint2(nib_pair(p01), nib_pair(p23));
-      *reinterpret_cast<uint2*>(d0 + kVRow) = make_uint2(nib_pair(p01 >> 4), nib_pair(p23 >> 4));
-    }
+    for (int e = 0; e < 8; ++e)
+      *reinterpret_cast<uint2*>(st + kVOff + (8 * dg + e) * kVRow + 2 * p0) =
+          make_uint2(code_pair<DT>(v_pair<DT>(R, 0, e, dg)), code_pair<DT>(v_pair<DT>(R, 1, e, dg)));
   }
   if (tid < kTile) {   // wave 0
     float* sc = reinterpret_cast<float*>(st + kSOff);
@@ -325,7 +412,7 @@ void prefill_tile_kernel(DecodeParams p) {
   src.head_off = (int64_t)kvh * p.block_bytes;
   src.page_shift = p.page_shift;
   src.page_mask = p.page_size - 1;
-  src.scale_off = p.page_size * 64;
+  src.scale_off = p.page_size * 16 * DT;
 
   v4f acc[kNC][8];
   float mref[kNC], lsum[kNC];
@@ -337,15 +424,15 @@ void prefill_tile_kernel(DecodeParams p) {
     for (int t = 0; t < 8; ++t) acc[n][t] = v4f{0.f, 0.f, 0.f, 0.f};
   }
 
-  Raw4 R;
-  load_raw(R, src, t_begin, t_end, tid);
+  Raw<DT> R;
+  load_raw<DT>(R, src, t_begin, t_end, tid);
   __syncthreads();                       // the query operands are read: the buffer is free
-  write_stage(smem, R, tid, inv_s);
+  write_stage<DT>(smem, R, tid, inv_s);
   __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {
     const int T0 = t_begin + it * kTile;
-    if (it + 1 < ntiles) load_raw(R, src, T0 + kTile, t_end, tid);
+    if (it + 1 < ntiles) load_raw<DT>(R, src, T0 + kTile, t_end, tid);
     const uint8_t* st = smem + (it & 1) * kStage;
     // The tile's products for both groups, with the causal mask applied (compile-time M) or not.
     auto tile = [&](auto m_t) {
@@ -450,7 +537,7 @@ void prefill_tile_kernel(DecodeParams p) {
       if (T0 + kTile > wave_lo) tile(std::true_type{});
       else tile(std::false_type{});
     }
-    if (it + 1 < ntiles) write_stage(smem + ((it + 1) & 1) * kStage, R, tid, inv_s);
+    if (it + 1 < ntiles) write_stage<DT>(smem + ((it + 1) & 1) * kStage, R, tid, inv_s);
     __syncthreads();
   }
 
@@ -524,7 +611,7 @@ void prefill_tile_kernel(DecodeParams p) {
 
 }  // namespace
 
-bool prefill_tiled(int dtype) { return dtype == 4; }
+bool prefill_tiled(int dtype) { return dtype == 8 || dtype == 4 || dtype == 3 || dtype == 2; }
 
 int prefill_block_queries(int group) { return kWaves * kNC * (16 / group); }
 
@@ -536,8 +623,17 @@ int64_t prefill_workgroups(int32_t n_query, int32_t group, int32_t hkv, int32_t 
 hipError_t launch_prefill(int dtype, const DecodeParams& p, hipStream_t stream) {
   const int64_t grid = prefill_workgroups(p.batch, p.group, p.hkv, p.nsplits);
   switch (dtype) {
+    case 8:
+      hipLaunchKernelGGL((prefill_tile_kernel<8>), dim3((unsigned)grid), dim3(kThreads), kLds, stream, p);
+      break;
     case 4:
       hipLaunchKernelGGL((prefill_tile_kernel<4>), dim3((unsigned)grid), dim3(kThreads), kLds, stream, p);
+      break;
+    case 3:
+      hipLaunchKernelGGL((prefill_tile_kernel<3>), dim3((unsigned)grid), dim3(kThreads), kLds, stream, p);
+      break;
+    case 2:
+      hipLaunchKernelGGL((prefill_tile_kernel<2>), dim3((unsigned)grid), dim3(kThreads), kLds, stream, p);
       break;
     default:
       return hipErrorInvalidValue;
