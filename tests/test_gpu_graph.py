@@ -141,3 +141,54 @@ def test_layer_steps_replay_from_one_graph():
             _check_oracle(layer[0], layer[-1], refs[i], f"replay {r}, layer {i}")
         assert bool(torch.isfinite(scratch))
     del graph
+
+
+@pytest.mark.parametrize("dtype,splits", [(4, 0), (3, 3), (8, 2)])
+def test_prefill_replays_from_a_captured_graph(dtype, splits):
+    """A prefill chunk (the tile kernel, and with several partitions its combine) captured into a
+    graph and replayed: every replay equals the eager call bit for bit and the oracle's prefill
+    within the parity bar (the infero page's chunked prefill, section "Beyond plain text
+    decode", item "Continuous batching")."""
+    print("CASE graph prefill", dtype, splits, flush=True)
+    start, chunk, hq, hkv = 600, 70, 32, 8
+    W = workloads.make(f"graph-prefill-{dtype}", 970 + dtype, dtype, [start + chunk], hq, hkv, 16)
+    cache = make_cache(W)
+    bt, _ = upload_tables(W)
+    k, v = W.kv_bits(0)
+    fill(cache, W, bt, kv={0: (k, v)})
+    r = np.random.default_rng(dtype)
+    qb = workloads.round_to_bf16_bits(r.standard_normal((chunk, hq, 128)).astype(np.float32))
+    q = to_dev(qb)
+    import bit_quantized_paged_turbo_amd as xq
+    need = xq.xq_prefill_workspace_bytes(cache.layout, chunk, hq, start, splits)
+    ws = torch.empty((max(16, need),), dtype=torch.uint8, device="cuda")
+    out = torch.empty((chunk, hq, 128), dtype=torch.float32, device="cuda")
+
+    def call():
+        cache.prefill(q, bt[0], start, W.softmax_scale, splits, out=out, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    want = out.clone()
+    ref = oracle.prefill_sequence(dtype, qb, k, v, start, W.softmax_scale)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        scratch = torch.randn(1 << 20, device="cuda").sum()     # unrelated eager work
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), f"replay {rep} differs from the eager call"
+        err = np.max(np.abs(out.cpu().numpy().astype(np.float64) - ref))
+        assert err <= TOL, f"replay {rep}: {err:.3e} from the oracle"
+        assert bool(torch.isfinite(scratch))
+    del graph
