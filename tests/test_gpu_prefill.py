@@ -122,7 +122,8 @@ def test_prefill_full_chunk_of_the_mixed_step():
 
 
 @pytest.mark.parametrize("dtype,start,chunk,hq,hkv,ps", [(16, 200, 90, 16, 8, 256), (0, 300, 33, 8, 1, 256),
-                                                         (2, 0, 130, 32, 8, 64)])
+                                                         (2, 0, 130, 32, 8, 64), (4, 700, 100, 32, 8, 256),
+                                                         (3, 1000, 40, 40, 8, 128), (8, 260, 75, 16, 16, 256)])
 def test_prefill_large_pages(dtype, start, chunk, hq, hkv, ps):
     _case("prefill-ps", dtype, start, chunk, hq, hkv, ps)
     W, cache, bt, kv, q = _setup(dtype, start, chunk, hq, hkv, ps, 860 + dtype)
