@@ -18,8 +18,8 @@ Steps are timed twice, K each after W warm-up steps (and as many more untimed on
 warm-up to 30 ms of GPU work, so that the clocks have left idle): eagerly, with HIP events around every
 decode call and every append call (on the stream they are launched on), and replayed from HIP
 graphs captured per pool replica, the way a serving engine replays its decode step; when every
-replica has its graph, also from one graph holding a step on each replica in turn, as a model's
-decode graph holds one step per layer. `value` and `ms_per_step` come from the graph replay,
+replica has its graph, also from one graph holding a step on each replica in turn (8 steps when
+there is one replica), as a model's decode graph holds one step per layer. `value` and `ms_per_step` come from the graph replay,
 else (--no-graph) from the eager launches; all figures are in `step_timing`. The new row of
 sequence b goes to position L_b - 1, so every step has the same shape and the cache content
 stays what the oracle computes.
@@ -642,29 +642,31 @@ def main():
         g_ms = gstart.elapsed_time(gstop) / K
         graph = {"ms_per_step": round(g_ms, 5), "replicas": NG}
         log(f"graph replay: {g_ms * 1e3:.1f} us/step")
-        # One graph holding a step on every replica in turn, as a model's decode graph holds one
-        # step per layer (the replicas' pools stand for the layers' caches): K steps are K // NG
-        # replays of it plus K % NG single-step replays.
-        if NG == R and R > 1:
+        # One graph holding S steps back to back, a step on every replica in turn (S = R), or 8
+        # steps on the one replica whose pools outgrow the Infinity Cache (S = 8), as a model's
+        # decode graph holds one step per layer (the replicas' pools stand for the layers'
+        # caches): K steps are K // S replays of it plus K % S single-step replays.
+        S = R if R > 1 else 8
+        if NG == R and S <= 64:
             layers = torch.cuda.CUDAGraph()
             with torch.cuda.graph(layers):
                 cs = torch.cuda.current_stream().cuda_stream
-                for r in runners:
-                    r.run(cs)
-                    r.decode(cs)
+                for i in range(S):
+                    runners[i % R].run(cs)
+                    runners[i % R].decode(cs)
             torch.cuda.synchronize()
-            warm(lambda i: layers.replay(), max(1, args.warmup // R), stream)
+            warm(lambda i: layers.replay(), max(1, args.warmup // S), stream)
             gstart.record(stream)
-            for _ in range(K // R):
+            for _ in range(K // S):
                 layers.replay()
-            for i in range(K % R):
-                graphs[i].replay()
+            for i in range(K % S):
+                graphs[i % NG].replay()
             gstop.record(stream)
             torch.cuda.synchronize()
             m_ms = gstart.elapsed_time(gstop) / K
             graph["multi_step_ms_per_step"] = round(m_ms, 5)
-            graph["steps_per_graph"] = R
-            log(f"graph of {R} steps: {m_ms * 1e3:.1f} us/step")
+            graph["steps_per_graph"] = S
+            log(f"graph of {S} steps: {m_ms * 1e3:.1f} us/step")
             del layers
         del graphs
         # The decode call alone: one graph holding M decode calls back to back (one per pool
@@ -747,7 +749,8 @@ def main():
             "chunk_append": (None if not W.chunk_tokens else "in the decode launch" if chunk is not None
                              else "separate append kernel"),
         },
-        "step_timing": {"method": (f"hip graph replay, {R} steps (one per pool replica, as one per layer) per graph"
+        "step_timing": {"method": ((f"hip graph replay, {R} steps (one per pool replica, as one per layer) per graph"
+                                    if R > 1 else "hip graph replay, 8 steps on the one pool replica per graph")
                                    if by_layers else "hip graph replay of the captured step" if by_graph
                                    else "eager launches"),
                         "eager_ms_per_step": round(step_ms, 5),
