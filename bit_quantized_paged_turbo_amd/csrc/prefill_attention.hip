@@ -26,8 +26,8 @@
 //       eight k values are one 16-byte read).
 //
 // Softmax: the decode's lazily moved log2-domain reference per column, tracking score plus the
-// fp16 exponent field of s_v, so P' stays within fp16 whatever the scales are; the normaliser
-// sum(p) is fp32. States of one query from several partitions are merged by the decode's
+// largest fp16 exponent field of the tile's s_v (the decode's per-token bound taken per tile), so
+// P' stays within fp16 whatever the scales are; the normaliser sum(p) is fp32. States of one query from several partitions are merged by the decode's
 // combine kernel (same partial format), which also rotates back; with one partition the
 // workgroup normalises, rotates back and stores itself.
 //
@@ -37,8 +37,9 @@
 // Workgroups are issued longest causal block first, with the second half of the grid in the
 // reverse order, so that the two workgroups a compute unit holds together carry about the mean
 // work. (Pairing each block's first half with the mirrored half from the chunk's end, so that
-// every workgroup carries the mean work, measured slower on MI355X: 161 against 128 us for a
-// 2,048-query chunk, the groups of a wave then running on different tile ranges.)
+// every workgroup carries the mean work, measured slower on MI355X: 161 against 133 us for a
+// 2,048-query chunk, the groups of a wave then running on different tile ranges.) The cache
+// types differ only in the tile conversion (load_raw, k_pair, v_pair).
 #include "row_codec.h"
 #include "xq_internal.h"
 
