@@ -51,6 +51,23 @@ namespace {
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// bf16 and fp8 caches hold plain (unrotated, unscaled) rows: K and V tiles are staged as bf16,
+// the bf16 query enters QK exactly in one pass, and the output is not rotated back.
+template <int DT> constexpr bool kPlain = DT == 0 || DT == kFp8;
+
+// One 16x16x32 matrix-core product on operands held as four dwords: fp16 for the turbo types,
+// bf16 for the plain ones.
+template <int DT>
+__device__ __forceinline__ v4f mma(uint4 a, uint4 b, v4f c) {
+  if constexpr (kPlain<DT>)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0,
+                                                   0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+}
 
 constexpr int D = kHeadDim;
 constexpr int kWaves = 4;
@@ -123,10 +140,12 @@ constexpr uint32_t pair_sel(int i) {
 // of a wave thus write 16 different K rows and, for V, 16 different 8-byte pieces of one
 // dimension row, so that the LDS writes meet no bank conflict.
 template <int DT> struct Raw {
-  static constexpr int kV = DT == 8 || DT == 3 ? 2 : 1;
-  uint32_t k[DT];      // 4 DT bytes of K codes
-  uint32_t v[4][kV];   // per token: turbo8 two dwords, turbo4 one, turbo3 the dwords around its
-                       // three bytes, turbo2 one halfword
+  static constexpr int kRow = row_code_bytes(DT);                     // code bytes of a row
+  static constexpr int kK = kRow / 16;                                // dwords of K per thread
+  static constexpr int kV = DT == 0 ? 4 : DT == 8 || DT == kFp8 || DT == 3 ? 2 : 1;
+  uint32_t k[kK];      // a quarter row of K
+  uint32_t v[4][kV];   // per token: bf16 four dwords, turbo8 and fp8 two, turbo4 one, turbo3 the
+                       // dwords around its three bytes, turbo2 one halfword
   uint32_t s;
 };
 
@@ -146,17 +165,18 @@ __device__ __forceinline__ int64_t block_addr(const Src& s, int t) {
 
 template <int DT>
 __device__ __forceinline__ void load_raw(Raw<DT>& R, const Src& s, int T0, int t_end, int tid) {
-  constexpr int kRow = 16 * DT;   // code bytes of a row
+  constexpr int kRow = Raw<DT>::kRow;
   const int tk = T0 + (tid & 63);
   const int64_t kb = tk < t_end ? block_addr(s, tk) : 0;
   const int kslot = tk & s.page_mask;
   {
-    const uint8_t* src = s.k_pool + kb + kslot * kRow + 4 * DT * (tid >> 6);
-    if constexpr (DT == 8) {
-      const uint4 a = tk < t_end ? reinterpret_cast<const uint4*>(src)[0] : make_uint4(0u, 0u, 0u, 0u);
-      const uint4 b = tk < t_end ? reinterpret_cast<const uint4*>(src)[1] : make_uint4(0u, 0u, 0u, 0u);
-      R.k[0] = a.x; R.k[1] = a.y; R.k[2] = a.z; R.k[3] = a.w;
-      R.k[4] = b.x; R.k[5] = b.y; R.k[6] = b.z; R.k[7] = b.w;
+    const uint8_t* src = s.k_pool + kb + kslot * kRow + (kRow / 4) * (tid >> 6);
+    if constexpr (Raw<DT>::kK >= 8) {
+#pragma unroll
+      for (int u = 0; u < Raw<DT>::kK / 4; ++u) {
+        const uint4 a = tk < t_end ? reinterpret_cast<const uint4*>(src)[u] : make_uint4(0u, 0u, 0u, 0u);
+        R.k[4 * u] = a.x; R.k[4 * u + 1] = a.y; R.k[4 * u + 2] = a.z; R.k[4 * u + 3] = a.w;
+      }
     } else if constexpr (DT == 4) {
       const uint4 a = tk < t_end ? *reinterpret_cast<const uint4*>(src) : make_uint4(0u, 0u, 0u, 0u);
       R.k[0] = a.x; R.k[1] = a.y; R.k[2] = a.z; R.k[3] = a.w;
@@ -179,7 +199,10 @@ __device__ __forceinline__ void load_raw(Raw<DT>& R, const Src& s, int T0, int t
     for (int i = 0; i < 4; ++i) {
       const bool ok = t0 + i < t_end;
       const uint8_t* row = s.v_pool + base + kRow * i;
-      if constexpr (DT == 8) {
+      if constexpr (DT == 0) {
+        const uint4 a = ok ? *reinterpret_cast<const uint4*>(row + 16 * dg) : make_uint4(0u, 0u, 0u, 0u);
+        R.v[i][0] = a.x; R.v[i][1] = a.y; R.v[i][2] = a.z; R.v[i][3] = a.w;
+      } else if constexpr (DT == 8 || DT == kFp8) {
         const uint2 a = ok ? *reinterpret_cast<const uint2*>(row + 8 * dg) : make_uint2(0u, 0u);
         R.v[i][0] = a.x;
         R.v[i][1] = a.y;
@@ -198,7 +221,7 @@ __device__ __forceinline__ void load_raw(Raw<DT>& R, const Src& s, int T0, int t
     }
   }
   R.s = 0u;
-  if (tid < kTile && tk < t_end) {
+  if (has_scales(DT) && tid < kTile && tk < t_end) {
     const int64_t off = kb + s.scale_off + 2 * kslot;
     R.s = (uint32_t)*reinterpret_cast<const uint16_t*>(s.k_pool + off) |
           ((uint32_t)*reinterpret_cast<const uint16_t*>(s.v_pool + off) << 16);
@@ -247,33 +270,63 @@ __device__ __forceinline__ uint32_t v_pair(const Raw<DT>& R, int u, int e, int d
 
 template <int DT>
 __device__ __forceinline__ void write_stage(uint8_t* st, const Raw<DT>& R, int tid, float inv_s) {
-  {
-    uint8_t* dst = st + (tid & 63) * kKRow + 64 * (tid >> 6);
+  uint8_t* kdst = st + (tid & 63) * kKRow + 64 * (tid >> 6);
+  const int dg = tid >> 4;
+  const int p0 = v_pos(4 * (tid & 15));
+  if constexpr (kPlain<DT>) {
+    // K: the quarter row as bf16, dimensions in order (fp8 widened exactly, two bytes a convert)
+    uint32_t kb[16];
+#pragma unroll
+    for (int d = 0; d < 16; ++d) {
+      if constexpr (DT == 0) {
+        kb[d] = R.k[d];
+      } else {
+        kb[d] = __builtin_bit_cast(uint32_t, (d & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(R.k[d >> 1], 1.f, true)
+                                                     : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(R.k[d >> 1], 1.f, false));
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<uint4*>(dst + 16 * j) =
+      *reinterpret_cast<uint4*>(kdst + 16 * j) = make_uint4(kb[4 * j], kb[4 * j + 1], kb[4 * j + 2], kb[4 * j + 3]);
+    // V: dimension e of tokens (0, 1) and (2, 3) as bf16 pairs
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t pr[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if constexpr (DT == 0) {
+          pr[u] = perm(R.v[2 * u + 1][e >> 1], R.v[2 * u][e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+        } else {
+          const uint32_t b = perm(R.v[2 * u + 1][e >> 2], R.v[2 * u][e >> 2],
+                                  (uint32_t)(e & 3) | ((uint32_t)(4 + (e & 3)) << 8) | 0x0c0c0000u);
+          pr[u] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b, 1.f, false));
+        }
+      }
+      *reinterpret_cast<uint2*>(st + kVOff + (8 * dg + e) * kVRow + 2 * p0) = make_uint2(pr[0], pr[1]);
+    }
+    (void)inv_s;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<uint4*>(kdst + 16 * j) =
           make_uint4(code_pair<DT>(k_pair<DT>(R, j, 0)), code_pair<DT>(k_pair<DT>(R, j, 1)),
                      code_pair<DT>(k_pair<DT>(R, j, 2)), code_pair<DT>(k_pair<DT>(R, j, 3)));
-  }
-  {
-    const int dg = tid >> 4;
-    const int p0 = v_pos(4 * (tid & 15));
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       *reinterpret_cast<uint2*>(st + kVOff + (8 * dg + e) * kVRow + 2 * p0) =
           make_uint2(code_pair<DT>(v_pair<DT>(R, 0, e, dg)), code_pair<DT>(v_pair<DT>(R, 1, e, dg)));
-  }
-  if (tid < kTile) {   // wave 0
-    float* sc = reinterpret_cast<float*>(st + kSOff);
-    const _Float16 ks = __builtin_bit_cast(_Float16, (uint16_t)(R.s & 0xffffu));
-    const _Float16 vs = __builtin_bit_cast(_Float16, (uint16_t)(R.s >> 16));
-    sc[tid] = (float)ks * inv_s;
-    sc[kTile + tid] = (float)vs;
-    // the largest fp16 exponent field of the tile's V scales
-    int e = (int)((R.s >> 26) & 31u);
+    if (tid < kTile) {   // wave 0
+      float* sc = reinterpret_cast<float*>(st + kSOff);
+      const _Float16 ks = __builtin_bit_cast(_Float16, (uint16_t)(R.s & 0xffffu));
+      const _Float16 vs = __builtin_bit_cast(_Float16, (uint16_t)(R.s >> 16));
+      sc[tid] = (float)ks * inv_s;
+      sc[kTile + tid] = (float)vs;
+      // the largest fp16 exponent field of the tile's V scales
+      int e = (int)((R.s >> 26) & 31u);
 #pragma unroll
-    for (int m = 1; m < 64; m <<= 1) e = max(e, __shfl_xor(e, m));
-    if (tid == 0) sc[2 * kTile] = (float)e;
+      for (int m = 1; m < 64; m <<= 1) e = max(e, __shfl_xor(e, m));
+      if (tid == 0) sc[2 * kTile] = (float)e;
+    }
   }
 }
 
@@ -319,7 +372,22 @@ void prefill_tile_kernel(DecodeParams p) {
     return r;
   };
 
-  // ---- queries: rotate (FWHT), scale, one power of two for the workgroup, fp16 hi/lo -----------
+  // ---- queries: rotate (FWHT), scale, one power of two for the workgroup, fp16 hi/lo (plain
+  // caches: the bf16 query rows themselves, read straight into the operand layout) ---------------
+  uint4 qh[kNC][4], ql[kNC][4];
+  float inv_s = 1.f;
+  if constexpr (kPlain<DT>) {
+#pragma unroll
+    for (int n = 0; n < kNC; ++n) {
+      const Col col = column(n, c16);
+      const uint16_t* src = p.q + ((int64_t)col.q * p.hq + col.head) * D + 8 * g;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        qh[n][m] = col.ok ? *reinterpret_cast<const uint4*>(src + 32 * m) : make_uint4(0u, 0u, 0u, 0u);
+        ql[n][m] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  } else {
   float xr[kNC][4][8];
   float am = 0.f;
   {
@@ -358,9 +426,7 @@ void prefill_tile_kernel(DecodeParams p) {
   int ex = (int)((__float_as_uint(am) >> 23) & 255u) - 126;
   ex = am > 0.f && ex < 129 ? max(ex, -85) : 14;
   const float S = __uint_as_float((uint32_t)(127 + 14 - ex) << 23);
-  const float inv_s = __uint_as_float((uint32_t)(127 - 14 + ex) << 23);
-
-  v8h qh[kNC][4], ql[kNC][4];
+  inv_s = __uint_as_float((uint32_t)(127 - 14 + ex) << 23);
   {
     uint8_t* qa = smem + w * kQWave;
     const int c = lane >> 2, k4 = lane & 3;
@@ -387,9 +453,10 @@ void prefill_tile_kernel(DecodeParams p) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const uint8_t* row = qa + n * (16 * D * 4) + c16 * (D * 2) + 2 * (32 * m + 8 * g);
-        qh[n][m] = *reinterpret_cast<const v8h*>(row);
-        ql[n][m] = *reinterpret_cast<const v8h*>(row + 16 * D * 2);
+        qh[n][m] = *reinterpret_cast<const uint4*>(row);
+        ql[n][m] = *reinterpret_cast<const uint4*>(row + 16 * D * 2);
       }
+  }
   }
 
   // causal limits: column c of group n attends to tokens < ctx_base + its query; the wave's
@@ -405,6 +472,7 @@ void prefill_tile_kernel(DecodeParams p) {
   const int wave_lo = min(t_end, p.ctx_base + wq0);
   const int wave_hi = wq0 < p.batch ? min(t_end, p.ctx_base + wq1) : t_begin;
 
+  const float qsc = p.softmax_scale * kLog2e;   // plain caches: the score scale (log2 domain)
   Src src;
   src.k_pool = p.k_pool;
   src.v_pool = p.v_pool;
@@ -413,7 +481,7 @@ void prefill_tile_kernel(DecodeParams p) {
   src.head_off = (int64_t)kvh * p.block_bytes;
   src.page_shift = p.page_shift;
   src.page_mask = p.page_size - 1;
-  src.scale_off = p.page_size * 16 * DT;
+  src.scale_off = p.page_size * Raw<DT>::kRow;
 
   v4f acc[kNC][8];
   float mref[kNC], lsum[kNC];
@@ -443,16 +511,16 @@ void prefill_tile_kernel(DecodeParams p) {
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         const uint8_t* kr = st + (16 * h + c16) * kKRow + 16 * g;
-        v8h ka[4];
+        uint4 ka[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) ka[m] = *reinterpret_cast<const v8h*>(kr + 64 * m);
+        for (int m = 0; m < 4; ++m) ka[m] = *reinterpret_cast<const uint4*>(kr + 64 * m);
 #pragma unroll
         for (int n = 0; n < kNC; ++n) {
           v4f a = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
-            a = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[m], qh[n][m], a, 0, 0, 0);
-            a = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[m], ql[n][m], a, 0, 0, 0);
+            a = mma<DT>(ka[m], qh[n][m], a);
+            if constexpr (!kPlain<DT>) a = mma<DT>(ka[m], ql[n][m], a);
           }
           s[n][h] = a;
         }
@@ -460,16 +528,17 @@ void prefill_tile_kernel(DecodeParams p) {
       // ---- softmax weights, in place of the scores, one group after the other (a group's scores
       // die as its PV operands are made). The reference tracks score + E, E the largest fp16
       // exponent field of the tile's s_v, so P' = p s_v < 2^15 (as per token in the decode); the
-      // K and V scales are read from LDS where they are used -------------------------------------
+      // K and V scales are read from LDS where they are used. Plain caches: the softmax scale in
+      // place of the K scale, no V scale (the decode's bf16 path: bf16 weights need no bound) -----
       const float* sc = reinterpret_cast<const float*>(st + kSOff);
-      const float evm = sc[2 * kTile];
-      v8h ahi[kNC][2], alo[kNC][2];
+      const float evm = kPlain<DT> ? 0.f : sc[2 * kTile];
+      uint4 ahi[kNC][2], alo[kNC][2];
 #pragma unroll
       for (int n = 0; n < kNC; ++n) {
         float mx = -INFINITY;
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-          const v4f ks = *reinterpret_cast<const v4f*>(sc + 16 * h + 4 * g);
+          const v4f ks = kPlain<DT> ? v4f{qsc, qsc, qsc, qsc} : *reinterpret_cast<const v4f*>(sc + 16 * h + 4 * g);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             float y = s[n][h][r] * ks[r];
@@ -494,15 +563,15 @@ void prefill_tile_kernel(DecodeParams p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[n][t][r] *= fr[r];
         }
-        const float mw = mref[n] - kWeightExp;
+        const float mw = kPlain<DT> ? mref[n] : mref[n] - kWeightExp;
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-          const v4f sv = *reinterpret_cast<const v4f*>(sc + kTile + 16 * h + 4 * g);
+          const v4f sv = kPlain<DT> ? v4f{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const v4f*>(sc + kTile + 16 * h + 4 * g);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float pe = __builtin_amdgcn_exp2f(s[n][h][r] - mw);
             lsum[n] += pe;
-            s[n][h][r] = pe * sv[r];
+            s[n][h][r] = kPlain<DT> ? pe : pe * sv[r];
           }
         }
 #pragma unroll
@@ -511,14 +580,22 @@ void prefill_tile_kernel(DecodeParams p) {
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) {
             const float a = s[n][2 * j + (kk >> 1)][2 * (kk & 1)], b = s[n][2 * j + (kk >> 1)][2 * (kk & 1) + 1];
-            const auto h2v = __builtin_amdgcn_cvt_pkrtz(a, b);
-            const auto l2v = __builtin_amdgcn_cvt_pkrtz(__builtin_fmaf((float)h2v[0], -1.f, a),
-                                                        __builtin_fmaf((float)h2v[1], -1.f, b));
-            hi[kk] = __builtin_bit_cast(uint32_t, h2v);
-            lo[kk] = __builtin_bit_cast(uint32_t, l2v);
+            if constexpr (kPlain<DT>) {
+              // bf16 high parts (truncation) and the bf16 remainders
+              const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+              const float ra = a - __uint_as_float(ua & 0xffff0000u), rb = b - __uint_as_float(ub & 0xffff0000u);
+              hi[kk] = perm(ub, ua, 0x07060302u);
+              lo[kk] = perm(__float_as_uint(rb), __float_as_uint(ra), 0x07060302u);
+            } else {
+              const auto h2v = __builtin_amdgcn_cvt_pkrtz(a, b);
+              const auto l2v = __builtin_amdgcn_cvt_pkrtz(__builtin_fmaf((float)h2v[0], -1.f, a),
+                                                          __builtin_fmaf((float)h2v[1], -1.f, b));
+              hi[kk] = __builtin_bit_cast(uint32_t, h2v);
+              lo[kk] = __builtin_bit_cast(uint32_t, l2v);
+            }
           }
-          ahi[n][j] = __builtin_bit_cast(v8h, make_uint4(hi[0], hi[1], hi[2], hi[3]));
-          alo[n][j] = __builtin_bit_cast(v8h, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+          ahi[n][j] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+          alo[n][j] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
         }
       }
       // ---- PV --------------------------------------------------------------------------------
@@ -526,11 +603,11 @@ void prefill_tile_kernel(DecodeParams p) {
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const v8h vb = *reinterpret_cast<const v8h*>(st + kVOff + (16 * t + c16) * kVRow + 64 * j + 16 * g);
+          const uint4 vb = *reinterpret_cast<const uint4*>(st + kVOff + (16 * t + c16) * kVRow + 64 * j + 16 * g);
 #pragma unroll
           for (int n = 0; n < kNC; ++n) {
-            acc[n][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[n][j], vb, acc[n][t], 0, 0, 0);
-            acc[n][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[n][j], vb, acc[n][t], 0, 0, 0);
+            acc[n][t] = mma<DT>(ahi[n][j], vb, acc[n][t]);
+            acc[n][t] = mma<DT>(alo[n][j], vb, acc[n][t]);
           }
         }
     };
@@ -576,14 +653,15 @@ void prefill_tile_kernel(DecodeParams p) {
         x[kk][0] = a.x; x[kk][1] = a.y; x[kk][2] = a.z; x[kk][3] = a.w;
         x[kk][4] = b.x; x[kk][5] = b.y; x[kk][6] = b.z; x[kk][7] = b.w;
       }
-      codec::fwht_row<4>(x, k4);
+      if constexpr (!kPlain<DT>) codec::fwht_row<4>(x, k4);
+      constexpr float rc = kPlain<DT> ? 1.f : kRotC;
       if (col.ok) {
         float* dst = p.out + ((int64_t)col.q * p.hq + col.head) * D;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           float4* d4 = reinterpret_cast<float4*>(dst + 8 * (k4 + 4 * kk));
-          d4[0] = make_float4(x[kk][0] * kRotC, x[kk][1] * kRotC, x[kk][2] * kRotC, x[kk][3] * kRotC);
-          d4[1] = make_float4(x[kk][4] * kRotC, x[kk][5] * kRotC, x[kk][6] * kRotC, x[kk][7] * kRotC);
+          d4[0] = make_float4(x[kk][0] * rc, x[kk][1] * rc, x[kk][2] * rc, x[kk][3] * rc);
+          d4[1] = make_float4(x[kk][4] * rc, x[kk][5] * rc, x[kk][6] * rc, x[kk][7] * rc);
         }
       }
     }
@@ -612,7 +690,9 @@ void prefill_tile_kernel(DecodeParams p) {
 
 }  // namespace
 
-bool prefill_tiled(int dtype) { return dtype == 8 || dtype == 4 || dtype == 3 || dtype == 2; }
+bool prefill_tiled(int dtype) {
+  return dtype == 8 || dtype == 4 || dtype == 3 || dtype == 2 || dtype == 0 || dtype == kFp8;
+}
 
 int prefill_block_queries(int group) { return kWaves * kNC * (16 / group); }
 
@@ -635,6 +715,12 @@ hipError_t launch_prefill(int dtype, const DecodeParams& p, hipStream_t stream) 
       break;
     case 2:
       hipLaunchKernelGGL((prefill_tile_kernel<2>), dim3((unsigned)grid), dim3(kThreads), kLds, stream, p);
+      break;
+    case 0:
+      hipLaunchKernelGGL((prefill_tile_kernel<0>), dim3((unsigned)grid), dim3(kThreads), kLds, stream, p);
+      break;
+    case kFp8:
+      hipLaunchKernelGGL((prefill_tile_kernel<kFp8>), dim3((unsigned)grid), dim3(kThreads), kLds, stream, p);
       break;
     default:
       return hipErrorInvalidValue;

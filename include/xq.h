@@ -392,9 +392,8 @@ int64_t xq_prefill_workspace_bytes(const xq_cache_layout* layout, int32_t n_quer
  * pages of the pool (checked only under XQ_DEBUG).
  * Kernels: with fixed partitions (num_splits_hint < 0) the queries run on the decode's kernel,
  * and each query's output is bitwise the decode's with the same partition when the group size
- * is 16; otherwise the turbo caches use a tile kernel (a workgroup dequantizes each 64-token
- * tile once for 8 * (16 / group) queries), with its own rounding order, within the same
- * tolerance; bf16 and fp8 caches always run on the decode's kernel.
+ * is 16; otherwise a tile kernel runs the chunk (a workgroup converts each 64-token tile once
+ * for 8 * (16 / group) queries), with its own rounding order, within the same tolerance.
  */
 xq_status xq_paged_prefill_attention(const xq_cache_layout* layout,
                                      const void* q, int32_t n_query, int32_t num_q_heads,
