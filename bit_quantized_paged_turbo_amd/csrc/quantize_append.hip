@@ -37,7 +37,10 @@ constexpr int kMaxBlocks = 1024;
 
 template <int BITS>
 __global__ __launch_bounds__(kThreads) void quantize_append_kernel(AppendParams p) {
-  codec::append_passes<BITS>(p, blockIdx.x * kWaves + (threadIdx.x >> 6), gridDim.x * kWaves, threadIdx.x & 63);
+  // the wave's first pass is the same for its 64 lanes: taken from lane 0, so the pass loop's
+  // index arithmetic runs on the scalar unit
+  const uint32_t first = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (threadIdx.x >> 6));
+  codec::append_passes<BITS>(p, first, gridDim.x * kWaves, threadIdx.x & 63);
 }
 
 }  // namespace
