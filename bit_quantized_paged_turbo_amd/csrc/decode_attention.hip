@@ -1908,15 +1908,17 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodePara
   __shared__ float o[D];
 
   // One pass: each group of 32 threads merges its splits into a running (m, l, acc) by
-  // log-sum-exp, four splits' partials loaded together; the groups are merged at the end.
+  // log-sum-exp, kU splits' partials loaded together (every load of a step in flight at once: the
+  // merge is a chain of dependent rounds of loads); the groups are merged at the end.
+  constexpr int kU = 8;
   const int s0 = t >> 5, d4 = t & 31;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float l = 0.f, mt = -INFINITY;
-  for (int sb = s0; sb < ns; sb += 4 * kCombGroups) {
-    float ms[4], ls[4];
-    float4 a[4];
+  for (int sb = s0; sb < ns; sb += kU * kCombGroups) {
+    float ms[kU], ls[kU];
+    float4 a[kU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kU; ++u) {
       const int s = sb + u * kCombGroups;
       const float* ps = part + (int64_t)(s < ns ? s : sb) * kPartialStride;
       ms[u] = s < ns ? ps[0] : -INFINITY;
@@ -1924,12 +1926,14 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodePara
       a[u] = reinterpret_cast<const float4*>(ps + 4)[d4];
     }
     // split sb < ns is real, so mn is finite; the first step scales the empty state by 0
-    const float mn = fmaxf(fmaxf(mt, fmaxf(ms[0], ms[1])), fmaxf(ms[2], ms[3]));
+    float mn = mt;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) mn = fmaxf(mn, ms[u]);
     const float fo = __builtin_amdgcn_exp2f(mt - mn);
     acc.x *= fo; acc.y *= fo; acc.z *= fo; acc.w *= fo;
     l *= fo;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kU; ++u) {
       const float f = (ms[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[u] - mn);
       acc.x += a[u].x * f; acc.y += a[u].y * f; acc.z += a[u].z * f; acc.w += a[u].w * f;
       l += ls[u] * f;   // the same for all 32 lanes of the group
