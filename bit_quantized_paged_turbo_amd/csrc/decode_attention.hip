@@ -1889,7 +1889,7 @@ void decode_split_kernel(DecodeParams p) {
 
 // Merge split partials of one (sequence, q head) and rotate back. THREADS = 32 * groups:
 // thread (s0 = t / 32, d4 = t % 32) sums dimensions 4 d4 .. 4 d4 + 3 over splits s0,
-// s0 + groups, ..., four splits per step with their loads issued together (128 threads for a
+// s0 + groups, ..., eight splits per step with their loads issued together (128 threads for a
 // few splits, 512 for many; 1024 threads measured slower on 256 splits).
 template <int DT, int kCombThreads>
 __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodeParams p) {
