@@ -396,28 +396,52 @@ def hbm_reference(xq, stream, reps: int = 5) -> dict:
 
 def time_prefill(cache, W, bt, to_dev, stream, K, Wm):
     """The chunk's queries attending causally to the chunk (xq_paged_prefill_attention from
-    position 0 over the chunk's appended rows): HIP events around each call on its stream."""
+    position 0 over the chunk's appended rows): HIP events around each call on its stream, and
+    one event pair around replays of a graph holding 8 calls back to back."""
     import torch
+    import bit_quantized_paged_turbo_amd as xq
     n, hq = W.chunk_tokens, W.num_q_heads
     g = np.random.default_rng(7)
     q = to_dev(workloads.round_to_bf16_bits(g.standard_normal((n, hq, 128)).astype(np.float32)))
     row = bt[W.batch]
-    for _ in range(Wm):
-        cache.prefill(q, row, 0, W.softmax_scale)
-    torch.cuda.synchronize()
+    out = torch.empty((n, hq, 128), dtype=torch.float32, device=q.device)
+    need = xq.xq_prefill_workspace_bytes(cache.layout, n, hq, 0, 0)
+    ws = torch.empty((max(16, need),), dtype=torch.uint8, device=q.device)
+
+    def call(_=0):
+        cache.prefill(q, row, 0, W.softmax_scale, out=out, workspace=ws)
+
+    warm(call, Wm, stream)
     ev = event_pairs(K)
     for a, b in ev:
         a.record(stream)
-        cache.prefill(q, row, 0, W.softmax_scale)
+        call()
         b.record(stream)
     torch.cuda.synchronize()
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(8):
+            call()
+    torch.cuda.synchronize()
+    warm(lambda i: graph.replay(), 1, stream)
+    nrep = max(1, K // 8)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(nrep):
+        graph.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    gms = a.elapsed_time(b) / (8 * nrep)
+    del graph
     pairs = n * (n + 1) // 2                      # (query, key) pairs of the causal chunk
     flops = 4 * 128 * hq * pairs                  # QK and PV multiply-adds
-    log(f"prefill of the {n}-token chunk: {ms * 1e3:.1f} us")
-    return {"queries": n, "start": 0, "call_us": round(ms * 1e3, 2),
-            "query_tokens_per_s": round(n / (ms * 1e-3), 1),
-            "tflops": round(flops / (ms * 1e-3) / 1e12, 3), "flops_per_call": flops}
+    log(f"prefill of the {n}-token chunk: {ms * 1e3:.1f} us per call, {gms * 1e3:.1f} us replayed 8 a graph")
+    return {"queries": n, "start": 0, "call_us": round(ms * 1e3, 2), "call_graph_us": round(gms * 1e3, 2),
+            "query_tokens_per_s": round(n / (gms * 1e-3), 1),
+            "tflops": round(flops / (gms * 1e-3) / 1e12, 3), "flops_per_call": flops,
+            "method": "call_us: HIP events around each eager call; call_graph_us (the rates' time): one event "
+                      "pair around replays of a graph of 8 calls"}
 
 
 def main():
