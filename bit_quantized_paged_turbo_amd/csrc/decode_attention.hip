@@ -60,7 +60,9 @@
 // straight to LDS (a ring of DEPTH tile slots per wave, DEPTH picked at launch from how many
 // waves share a compute unit): turbo4/turbo8 with lane offsets that leave every operand read
 // linear in the lane index and V transposed, turbo3 as the rows are stored. turbo2, bf16 and
-// fp8 load into registers, three tiles (two for bf16) in flight.
+// fp8 load into registers, three tiles (two for bf16) in flight. Where sequences have several
+// partitions, a wave raises its issue priority in step with the tiles it has left (four levels),
+// so that the waves a SIMD runs together finish together instead of in dispatch order.
 //
 // Each wave prepares the query digits of its kv head's query heads itself (rotation by an
 // in-register FWHT, scaling, digit split, packing in the operand layout), from rows fetched by
@@ -507,6 +509,19 @@ __device__ __forceinline__ void stage_tile(uint8_t* slot, const HalfAddr (&a)[2]
                                                4 * lane, a[h].scale, 0, kStream);
     }
   }
+}
+
+// Issue priority of a unit's wave when sequences have several partitions (units of about equal
+// length): a SIMD's arbiter favours its oldest wave, so of the units sharing a SIMD the ones
+// dispatched later fall behind and end the call. Each step the wave takes a priority from the
+// tiles it has left, in four levels of kPrioTiles tiles, so that the waves with the most work
+// left issue first.
+constexpr int kPrioTiles = 8;
+__device__ __forceinline__ void issue_priority(int tiles_left) {
+  if (tiles_left > 3 * kPrioTiles) __builtin_amdgcn_s_setprio(3);
+  else if (tiles_left > 2 * kPrioTiles) __builtin_amdgcn_s_setprio(2);
+  else if (tiles_left > kPrioTiles) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
 }
 
 // Operand bytes of a staged tile, read from its slot.
@@ -1487,6 +1502,7 @@ void decode_split_kernel(DecodeParams p) {
     }
   };
   const int ntiles = (tok_end - tok_begin + 31) >> 5;
+  const bool by_left = p.nsplits > 1;   // issue priority from the tiles left
   const bool fuse_late = fuse && Stage<DT>::kOn && ntiles > DEPTH - 1;
   if (fuse) load_new_row();   // ahead of every cache load, so that waiting for it waits for nothing else
   if (fuse && !fuse_late) {
@@ -1714,6 +1730,7 @@ void decode_split_kernel(DecodeParams p) {
           // two tiles per step, in slots cur and next_slot(cur)
           int cur = 0;
           for (int it = 0; it < ntiles; it += 2) {
+            if (by_left) issue_priority(ntiles - it);
             // tiles it, it + 1 are in once at most the tiles staged after them (it + 2 ..
             // it + DEPTH - 1) are outstanding
             if (it + DEPTH - 1 < ntiles) wait_vm<(DEPTH - 2) * S::kOps>();
@@ -1737,6 +1754,7 @@ void decode_split_kernel(DecodeParams p) {
       }
       int cur = 0;   // slot of tile it
       for (int it = 0; it < ntiles; ++it) {
+        if (by_left) issue_priority(ntiles - it);
         // this tile is in once at most the tiles staged after it (it + 1 .. it + DEPTH - 1) are
         // outstanding
         if (it + DEPTH - 1 < ntiles) wait_vm<(DEPTH - 1) * S::kOps>();
@@ -1774,6 +1792,7 @@ void decode_split_kernel(DecodeParams p) {
       for (int it = 0; it < ntiles;) {
 #pragma unroll
         for (int d = 0; d < kDepth; ++d) {
+          if (by_left) issue_priority(ntiles - it);
           const int ahead = it + kDepth - 1;
           if (ahead < ntiles) fetch(tb[(d + kDepth - 1) % kDepth], ahead);
           run(tb[d], it);
