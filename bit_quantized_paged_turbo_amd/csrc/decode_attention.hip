@@ -622,9 +622,10 @@ __device__ __forceinline__ void v_bytes(const Tile<DT>& t, uint32_t (&e)[8], uin
     const uint32_t sel = spread_sel((3 * col) & 3);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t n = spread3to6((uint32_t)t.v[j][1], (uint32_t)t.v[j][0], sel);   // two fields per byte
-      e[j] = ((n << 5) & 0xe0e0e0e0u) ^ 0x80808080u;       // (c + 4) << 5: the top bit flipped
-      o[j] = ((n << 2) & 0xe0e0e0e0u) ^ 0x80808080u;
+      // two fields per byte, the top bit of each flipped: c + 4
+      const uint32_t n = spread3to6((uint32_t)t.v[j][1], (uint32_t)t.v[j][0], sel) ^ 0x24242424u;
+      e[j] = (n << 5) & 0xe0e0e0e0u;                       // (c + 4) << 5
+      o[j] = (n << 2) & 0xe0e0e0e0u;
     }
   } else if constexpr (DT == 8) {
 #pragma unroll
@@ -1924,7 +1925,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodePara
   __shared__ float4 accs[kCombGroups][32];
   __shared__ float lsum[kCombGroups];
   __shared__ float msum[kCombGroups];
-  __shared__ float o[D];
+  __shared__ __attribute__((aligned(16))) float o[D];
 
   // One pass: each group of 32 threads merges its splits into a running (m, l, acc) by
   // log-sum-exp, kU splits' partials loaded together (every load of a step in flight at once: the
@@ -1980,19 +1981,20 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodePara
     o[t] = a / lt;
   }
   float* outp = p.out + ((int64_t)b * p.hq + qh) * D;
+  __syncthreads();
   if constexpr (kRotated<DT>) {
-    for (int h = 1; h < D; h <<= 1) {
-      __syncthreads();
-      float a = 0.f, c = 0.f;
-      const bool lower = t < D && (t & h) == 0;
-      if (lower) { a = o[t]; c = o[t + h]; }
-      __syncthreads();
-      if (lower) { o[t] = a + c; o[t + h] = a - c; }
+    // the inverse rotation on 16 lanes, eight elements each (the transform's stage order)
+    if (t < 16) {
+      float r[1][8];
+      const float4 x0 = reinterpret_cast<const float4*>(o)[2 * t], x1 = reinterpret_cast<const float4*>(o)[2 * t + 1];
+      r[0][0] = x0.x; r[0][1] = x0.y; r[0][2] = x0.z; r[0][3] = x0.w;
+      r[0][4] = x1.x; r[0][5] = x1.y; r[0][6] = x1.z; r[0][7] = x1.w;
+      codec::fwht_row<16>(r, t);
+      float4* d4 = reinterpret_cast<float4*>(outp + 8 * t);
+      d4[0] = make_float4(r[0][0] * kRotC, r[0][1] * kRotC, r[0][2] * kRotC, r[0][3] * kRotC);
+      d4[1] = make_float4(r[0][4] * kRotC, r[0][5] * kRotC, r[0][6] * kRotC, r[0][7] * kRotC);
     }
-    __syncthreads();
-    if (t < D) outp[t] = o[t] * kRotC;
   } else {
-    __syncthreads();
     if (t < D) outp[t] = o[t];
   }
 }
