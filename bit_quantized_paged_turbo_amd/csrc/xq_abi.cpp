@@ -301,8 +301,8 @@ xq_status attention(const xq_cache_layout* layout, const void* q, int32_t batch,
   if (g > xq::kMaxGroup) return fail(XQ_EUNSUPPORTED, "group size %d > %d", g, xq::kMaxGroup);
   if (!q || !k_pool || !v_pool || !block_tables || !out)
     return fail(XQ_EINVAL, "a required pointer is NULL");
-  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
-    return fail(XQ_EINVAL, "q and the pools must be 16-byte aligned");
+  if (!aligned16(q) || !aligned16(out) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(XQ_EINVAL, "q, out and the pools must be 16-byte aligned");
   if (max_pages_per_seq < 1) return fail(XQ_EINVAL, "max_pages_per_seq %d < 1", max_pages_per_seq);
   if ((int64_t)max_context_len > (int64_t)max_pages_per_seq * layout->page_size)
     return fail(XQ_EINVAL, "context of %d tokens exceeds max_pages * page_size", max_context_len);
@@ -430,8 +430,8 @@ xq_status tile_prefill(const xq_cache_layout* layout, const void* q, int32_t n_q
   const int32_t g = num_q_heads / layout->num_kv_heads;
   if (g > xq::kMaxGroup) return fail(XQ_EUNSUPPORTED, "group size %d > %d", g, xq::kMaxGroup);
   if (!q || !k_pool || !v_pool || !block_table || !out) return fail(XQ_EINVAL, "a required pointer is NULL");
-  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
-    return fail(XQ_EINVAL, "q and the pools must be 16-byte aligned");
+  if (!aligned16(q) || !aligned16(out) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(XQ_EINVAL, "q, out and the pools must be 16-byte aligned");
   if (max_pages < 1) return fail(XQ_EINVAL, "max_pages %d < 1", max_pages);
   const int32_t ctx = start_pos + n_query;
   if ((int64_t)ctx > (int64_t)max_pages * layout->page_size)

@@ -178,7 +178,7 @@ xq_status xq_quantize_append(const xq_cache_layout* layout,
  *   workspace          device scratch of >= xq_decode_workspace_bytes(...) bytes, 16-byte
  *                      aligned; may be NULL when that size is 0. Its contents on entry do
  *                      not matter; calls that share a workspace must not overlap.
- *   out                fp32 [batch][num_q_heads][128]
+ *   out                fp32 [batch][num_q_heads][128], 16-byte aligned
  * num_q_heads must be a multiple of num_kv_heads (XQ_EINVAL otherwise); a group size above 16,
  * a batch above 65535, more than 65535 splits or 2^26 or more (split, kv head, sequence) units
  * give XQ_EUNSUPPORTED. Block-table entries read for positions below context_lens[b] must be
@@ -385,7 +385,7 @@ int64_t xq_prefill_workspace_bytes(const xq_cache_layout* layout, int32_t n_quer
  *   workspace          device scratch of >= xq_prefill_workspace_bytes(layout, n_query,
  *                      num_q_heads, start_pos, num_splits_hint) bytes (may be NULL when that is
  *                      0); calls that share a workspace must not overlap
- *   out                fp32 [n_query][num_q_heads][128]
+ *   out                fp32 [n_query][num_q_heads][128], 16-byte aligned
  * n_query = 0 is a no-op. start_pos + n_query must not exceed max_pages * page_size (XQ_EINVAL);
  * more than 65535 queries, a group size above 16 or 2^26 or more (split, kv head, query) units
  * give XQ_EUNSUPPORTED. The block-table entries of positions below start_pos + n_query must be

@@ -102,6 +102,7 @@ def test_decode_argument_errors(lib):
     assert _decode_status(lib, L, hq=34) == xq.EUNSUPPORTED    # group 17 > 16
     assert _decode_status(lib, L, q=None) == xq.EINVAL
     assert _decode_status(lib, L, k=8) == xq.EINVAL            # misaligned pool
+    assert _decode_status(lib, L, out=8) == xq.EINVAL          # misaligned output (16-byte stores)
     assert _decode_status(lib, L, maxctx=65) == xq.EINVAL      # > maxp * page_size
     assert _decode_status(lib, L, splits=2) == xq.EWORKSPACE   # partials of two splits
     assert b"workspace" in lib.xq_last_error()
@@ -163,6 +164,7 @@ def test_prefill_argument_errors(lib):
     assert b"max_pages" in lib.xq_last_error()
     assert _prefill_status(lib, L, hq=7) == xq.EINVAL
     assert _prefill_status(lib, L, bt=None) == xq.EINVAL
+    assert _prefill_status(lib, L, out=8) == xq.EINVAL          # misaligned output
     assert _prefill_status(lib, L, n=70000, maxp=5000, start=0) == xq.EUNSUPPORTED
     # 108 positions in 2 partitions of 64: both kernels need the partials
     assert _prefill_status(lib, L, start=100, maxp=8, splits=2) == xq.EWORKSPACE
